@@ -1,0 +1,225 @@
+/*
+ * csa.h -- C ABI of the CSA / HCA long-context attention hot path (gfx950).
+ *
+ * The operations follow the description of DeepSeek-V4's hybrid attention in
+ * the b-lab.team summary of the DeepSeek-V4 report ("Core Methodological
+ * Innovations", item 1, Hybrid Attention Architecture, CSA and HCA bullets;
+ * item 4, Quantization-Aware Training bullet for the FP4 indexer path).  Where
+ * that text leaves a step open, the reading taken is stated at the function.
+ *
+ * Conventions (all functions):
+ *   - Every pointer argument except `stream` and the csa_tensor / status
+ *     structures themselves is DEVICE memory owned by the caller.  The library
+ *     never allocates or frees device memory; scratch comes in through `ws`.
+ *   - Every call only enqueues work on `stream` (a hipStream_t passed as
+ *     void*, NULL = the default stream) and returns; results are ready when
+ *     the stream has reached that point.
+ *   - Scalars, null pointers, dtype/shape support and workspace sizes are
+ *     checked on the host BEFORE anything is launched; on any error nothing
+ *     has been enqueued and the return value says why (details in
+ *     csa_last_error(), a thread-local string).  Device-resident metadata
+ *     (q_pos, raw_base, block_first, block_count, idx) is a documented
+ *     precondition and is not validated.  NaN/Inf inputs give unspecified
+ *     results.
+ *   - Results are deterministic: the same inputs give bitwise the same
+ *     outputs, independent of `batch` (each sequence's work is split only by
+ *     its own sizes; no floating-point atomics).
+ *   - Positions are absolute token positions (0-based).  Compressed block j of
+ *     block size m covers raw positions [j*m, j*m+m-1] and is visible to a
+ *     query at position t once it is complete: j*m + m - 1 <= t.  The sliding
+ *     window of a query at t is raw positions max(0, t-W+1) .. t.
+ *   - Rows of every stored tensor hold `dim` contiguous elements.
+ *
+ * Calls that overlap on one stream are ordered; calls on different streams
+ * that share a workspace race.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum csa_status {
+  CSA_OK = 0,
+  CSA_ERR_NULL = 1,        /* a required pointer is NULL                              */
+  CSA_ERR_SHAPE = 2,       /* a size/stride argument is out of range                  */
+  CSA_ERR_DTYPE = 3,       /* a dtype code is unknown or the combination is invalid   */
+  CSA_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. heads not multiple of 16) */
+  CSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns   */
+  CSA_ERR_HIP = 6          /* a HIP launch failed; see csa_last_error()               */
+} csa_status;
+
+/* Element formats of stored tensors.
+ *   CSA_F32       float32.
+ *   CSA_BF16      bfloat16 (round-to-nearest-even from fp32 when written here).
+ *   CSA_FP8_E4M3  OCP e4m3 ("fn", max 448) codes with one float32 scale per row:
+ *                 value = e4m3(code) * scale[row]; a NULL scale means 1.0.  When
+ *                 written here: scale = amax/448 in fp32 (1 for an all-zero row),
+ *                 code = RNE(x/scale) with the quotient in fp32, saturated.
+ *   CSA_MXFP4     OCP MX FP4: e2m1 codes packed two per byte (element 2i in the
+ *                 low nibble of byte i) plus one e8m0 scale byte per 32 elements:
+ *                 value = e2m1(code) * 2^(scale-127).  When written here: scale
+ *                 exponent e = floor(log2(amax)) - 2 clamped to [-127,127]
+ *                 (code 0 and all-zero elements for an all-zero block), element =
+ *                 RNE(x / 2^e) on {0,.5,1,1.5,2,3,4,6}, saturated, sign copied. */
+typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_MXFP4 = 3 } csa_dtype;
+
+/* A strided [batch, rows, dim] tensor in device memory.
+ *   data        element storage (MXFP4: packed codes).
+ *   scale       FP8: float per row; MXFP4: uint8 per 32 elements; else ignored.
+ *   stride_b    distance between batch items, in elements (MXFP4: bytes).
+ *   stride_row  distance between rows, in elements (MXFP4: bytes).
+ *   scale_stride_b / scale_stride_row: the same for `scale`, in scale entries
+ *               (FP8: floats, MXFP4: bytes).  Within a row the dim/32 MXFP4
+ *               scales are contiguous. */
+typedef struct csa_tensor {
+  void* data;
+  void* scale;
+  int32_t dtype;
+  int32_t reserved;
+  int64_t stride_b;
+  int64_t stride_row;
+  int64_t scale_stride_b;
+  int64_t scale_stride_row;
+} csa_tensor;
+
+int32_t csa_abi_version(void);
+const char* csa_status_string(csa_status s);
+const char* csa_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * (a) KV compression.  "CSA compresses the KV cache by a factor m by combining
+ * adjacent entries"; HCA does the same with m' >> m (b-lab.team summary,
+ * Core Methodological Innovations 1, CSA and HCA bullets).  Reading of the
+ * merge: c_j = sum_{r<m} softmax(logits)_r * x[j*m + r], one logit per offset,
+ * shared by every channel and block, softmax computed in fp32 (max-subtracted),
+ * terms accumulated in fp32 in ascending r.
+ *
+ *   raw          [batch, R, dim], dtype F32, BF16 or FP8_E4M3; row r of sequence
+ *                b holds absolute position raw_base[b] + r.
+ *   raw_base     [batch] int32.
+ *   logits       [m] float.
+ *   m            block size, 1..1024.
+ *   dim          row length (MXFP4 output: a multiple of 32; <= 4096).
+ *   block_first, block_count  [batch] int32: produce blocks
+ *                j = block_first[b] .. block_first[b] + block_count[b] - 1.
+ *                Precondition: their raw rows lie inside [0, R) and j indexes a
+ *                row of `out`; 0 <= block_count[b] <= max_blocks.
+ *   max_blocks   host-side upper bound of block_count (sizes the launch).
+ *   out          [batch, N_cap, dim] destination cache, dtype F32, BF16,
+ *                FP8_E4M3 (row scale written) or MXFP4 (scales written); only
+ *                rows j listed above are written.
+ * ------------------------------------------------------------------------- */
+csa_status csa_compress(const csa_tensor* raw, const int32_t* raw_base, const float* logits, int32_t m,
+                        int32_t dim, const int32_t* block_first, const int32_t* block_count, int32_t max_blocks,
+                        int32_t batch, const csa_tensor* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * (b) Lightning-indexer scores.  "The indexer computes scores using low-rank
+ * projections of query hidden states h_t to select the top-k most relevant
+ * compressed KV blocks" (b-lab.team summary, Core Methodological Innovations 1,
+ * CSA bullet); the indexer QK path is FP4 (same page, item 4, Quantization-
+ * Aware Training).  Reading of the formula (the pages give none): the
+ * DeepSeek-V3.2 lightning-indexer form
+ *     I[b,t,j] = sum_h w[b,t,h] * max(0, <q_idx[b,t,h], k_idx[b,j]>)
+ * for visible j (j*m+m-1 <= q_pos[b,t]), -inf for j >= visible count.
+ *
+ *   q_idx   [batch, tq, n_idx_heads, idx_dim]: stride_b / stride_row step batch
+ *           and query; heads*idx_dim contiguous.  dtype F32 (keys F32, BF16 or
+ *           MXFP4; with MXFP4 keys q is quantised to MXFP4 inside by the rule
+ *           above) or BF16 (keys BF16).
+ *   w       [batch, tq, n_idx_heads] float, contiguous.
+ *   k_idx   [batch, n_cap, idx_dim] compressed indexer keys: F32, BF16 or MXFP4.
+ *   q_pos   [batch, tq] int32 query positions; precondition visible <= n_cap.
+ *   n_idx_heads 1..16 (MXFP4: <= 8 ... 32 supported, see below), idx_dim: F32/BF16 a
+ *           multiple of 8 up to 256; MXFP4 exactly 64.
+ *   scores  [batch, tq, n_cap] float, contiguous (every entry written).
+ * Supported MXFP4 shape: n_idx_heads <= 32, idx_dim == 64.
+ * ------------------------------------------------------------------------- */
+csa_status csa_index_scores(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx,
+                            const int32_t* q_pos, int32_t batch, int32_t tq, int32_t n_idx_heads,
+                            int32_t idx_dim, int32_t m, int32_t n_cap, float* scores, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * (c) Top-k block selection ("select the top-k most relevant compressed KV
+ * blocks", b-lab.team summary, Core Methodological Innovations 1, CSA bullet).
+ * Reading of the order: score descending, then block index ascending; -0.0
+ * equals +0.0.  Only the visible blocks j < (q_pos+1)/m of each row take part.
+ *
+ *   scores  [batch, tq, n_cap] float.
+ *   idx     [batch, tq, k] int32 output: the selected block indices in
+ *           ascending order, then -1 for the slots beyond the visible count.
+ *   ws      workspace of at least csa_topk_workspace_size() bytes; its
+ *           contents on entry do not matter.
+ * ------------------------------------------------------------------------- */
+csa_status csa_topk(const float* scores, const int32_t* q_pos, int32_t batch, int32_t tq, int32_t n_cap,
+                    int32_t m, int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+size_t csa_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, int32_t k);
+
+/* ---------------------------------------------------------------------------
+ * (d) CSA sparse attention: attention over the selected compressed entries
+ * plus a sliding window of raw local entries ("supplemented by a sliding
+ * window of local KV entries", b-lab.team summary, Core Methodological
+ * Innovations 1, HCA bullet).  Readings: key = value = the stored row (shared
+ * MQA latent); the entry list is the selected compressed rows followed by the
+ * window's raw rows, not de-duplicated, in ONE softmax:
+ *     l_e = scale * <q[b,t,h], e>,  out = sum_e softmax(l)_e * e,
+ *     lse = log sum_e exp(l_e)  (natural log).
+ *
+ *   q       [batch, tq, heads, dim]: stride_b / stride_row step batch and query,
+ *           heads*dim contiguous.  dtype F32 with F32 caches, BF16 otherwise.
+ *   kv_cmp  [batch, N_cap, dim] compressed cache: F32, BF16 or FP8_E4M3.
+ *   idx     [batch, tq, k] int32 from csa_topk (-1 slots are skipped).
+ *           Precondition: every index >= 0 is a visible block.
+ *   kv_raw  [batch, R, dim] raw rows (same dtype as kv_cmp); row r holds
+ *           position raw_base[b] + r.  Precondition: the window of every
+ *           query lies inside it.
+ *   out     [batch, tq, heads, dim] float; lse [batch, tq, heads] float or NULL.
+ *   ws      at least csa_attn_workspace_size(batch, tq, heads, dim, k + window).
+ * Supported: F32 path heads <= 64, dim <= 512, dim % 4 == 0; BF16 / FP8 path
+ * heads a multiple of 16 up to 64 and dim == 512.
+ * ------------------------------------------------------------------------- */
+csa_status csa_sparse_attn(const csa_tensor* q, const csa_tensor* kv_cmp, const int32_t* idx, int32_t k,
+                           const csa_tensor* kv_raw, const int32_t* raw_base, int32_t window,
+                           const int32_t* q_pos, int32_t batch, int32_t tq, int32_t heads, int32_t dim,
+                           float scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * (e) HCA attention: dense attention over every complete heavily-compressed
+ * block plus the same sliding window ("reduces the KV cache by m' ... while
+ * maintaining dense attention for the remaining entries", b-lab.team summary,
+ * Core Methodological Innovations 1, HCA bullet).  Same readings and formats
+ * as csa_sparse_attn; the compressed entries of a query at t are blocks
+ * 0 .. (t+1)/m_hc - 1 of kv_hc (precondition: <= n_cap_hc).
+ *   ws  at least csa_attn_workspace_size(batch, tq, heads, dim, n_cap_hc + window).
+ * ------------------------------------------------------------------------- */
+csa_status hca_attn(const csa_tensor* q, const csa_tensor* kv_hc, int32_t m_hc, int32_t n_cap_hc,
+                    const csa_tensor* kv_raw, const int32_t* raw_base, int32_t window, const int32_t* q_pos,
+                    int32_t batch, int32_t tq, int32_t heads, int32_t dim, float scale, float* out, float* lse,
+                    void* ws, size_t ws_bytes, void* stream);
+
+size_t csa_attn_workspace_size(int32_t batch, int32_t tq, int32_t heads, int32_t dim, int32_t n_entries_max);
+
+/* ---------------------------------------------------------------------------
+ * Quantisers (the FP4 indexer path: b-lab.team summary, Core Methodological
+ * Innovations 4, Quantization-Aware Training; fp8 KV is a storage variant).
+ *   csa_quantize_mxfp4: x [rows, cols] float (cols % 32 == 0) -> codes
+ *     [rows, cols/2] uint8 and scales [rows, cols/32] uint8 (rule at CSA_MXFP4).
+ *   csa_quantize_fp8:   x [rows, cols] float -> codes [rows, cols] uint8 and
+ *     row_scale [rows] float (rule at CSA_FP8_E4M3).  cols <= 8192.
+ * ------------------------------------------------------------------------- */
+csa_status csa_quantize_mxfp4(const float* x, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                              void* stream);
+csa_status csa_quantize_fp8(const float* x, int64_t rows, int32_t cols, uint8_t* codes, float* row_scale,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H_ */

@@ -1,0 +1,255 @@
+// C ABI of the CSA / HCA hot path: host-side validation and dispatch.
+//
+// Every check runs before anything is enqueued, so a call either enqueues its
+// whole work or nothing.  Device-resident metadata (positions, bases, block
+// lists, indices) is a documented precondition and is not read on the host.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/csa.h"
+#include "kernels.h"
+
+namespace csa {
+bool attn_plain_fits(int n_entries_max);
+}
+
+namespace {
+
+thread_local std::string g_last_error;
+
+csa_status fail(csa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+csa_status ok() {
+  g_last_error.clear();
+  return CSA_OK;
+}
+
+csa_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool known_dtype(int d) { return d >= CSA_F32 && d <= CSA_MXFP4; }
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+csa_status check_tensor(const csa_tensor* t, const char* name) {
+  REQUIRE(t != nullptr, CSA_ERR_NULL, "%s is NULL", name);
+  REQUIRE(t->data != nullptr, CSA_ERR_NULL, "%s->data is NULL", name);
+  REQUIRE(known_dtype(t->dtype), CSA_ERR_DTYPE, "%s has unknown dtype %d", name, t->dtype);
+  REQUIRE(t->stride_b >= 0 && t->stride_row >= 0, CSA_ERR_SHAPE, "%s has a negative stride", name);
+  if (t->dtype == CSA_MXFP4) REQUIRE(t->scale != nullptr, CSA_ERR_NULL, "%s is MXFP4 but has no scale", name);
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_status_string(csa_status s) {
+  switch (s) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_NULL: return "null pointer";
+    case CSA_ERR_SHAPE: return "invalid shape or size";
+    case CSA_ERR_DTYPE: return "invalid dtype";
+    case CSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case CSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* csa_last_error(void) { return g_last_error.c_str(); }
+
+csa_status csa_compress(const csa_tensor* raw, const int32_t* raw_base, const float* logits, int32_t m, int32_t dim,
+                        const int32_t* block_first, const int32_t* block_count, int32_t max_blocks, int32_t batch,
+                        const csa_tensor* out, void* stream) {
+  csa_status st;
+  if ((st = check_tensor(raw, "raw")) != CSA_OK) return st;
+  if ((st = check_tensor(out, "out")) != CSA_OK) return st;
+  REQUIRE(raw_base && logits && block_first && block_count, CSA_ERR_NULL, "raw_base/logits/block_first/block_count is NULL");
+  REQUIRE(raw->dtype != CSA_MXFP4, CSA_ERR_DTYPE, "raw rows must be F32, BF16 or FP8_E4M3");
+  REQUIRE(m >= 1 && m <= 1024, CSA_ERR_SHAPE, "m=%d outside [1, 1024]", m);
+  REQUIRE(dim >= 1 && dim <= 4096, CSA_ERR_SHAPE, "dim=%d outside [1, 4096]", dim);
+  REQUIRE(batch >= 0 && max_blocks >= 0, CSA_ERR_SHAPE, "negative batch or max_blocks");
+  if (out->dtype == CSA_MXFP4) REQUIRE(dim % 32 == 0, CSA_ERR_SHAPE, "MXFP4 output needs dim %% 32 == 0 (dim=%d)", dim);
+  if (out->dtype == CSA_FP8_E4M3) REQUIRE(out->scale != nullptr, CSA_ERR_NULL, "FP8 output needs a row-scale pointer");
+  csa::CompressArgs a;
+  a.raw = csa::view_of(raw);
+  a.raw_base = raw_base;
+  a.logits = logits;
+  a.m = m;
+  a.dim = dim;
+  a.block_first = block_first;
+  a.block_count = block_count;
+  a.max_blocks = max_blocks;
+  a.batch = batch;
+  a.out = out->data;
+  a.out_scale = out->scale;
+  a.out_dtype = out->dtype;
+  a.out_sb = out->stride_b;
+  a.out_sr = out->stride_row;
+  a.out_ssb = out->scale_stride_b;
+  a.out_ssr = out->scale_stride_row;
+  return from_hip(csa::launch_compress(a, (hipStream_t)stream), "csa_compress launch");
+}
+
+csa_status csa_index_scores(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx, const int32_t* q_pos,
+                            int32_t batch, int32_t tq, int32_t n_idx_heads, int32_t idx_dim, int32_t m, int32_t n_cap,
+                            float* scores, void* stream) {
+  csa_status st;
+  if ((st = check_tensor(q_idx, "q_idx")) != CSA_OK) return st;
+  if ((st = check_tensor(k_idx, "k_idx")) != CSA_OK) return st;
+  REQUIRE(w && q_pos && scores, CSA_ERR_NULL, "w/q_pos/scores is NULL");
+  REQUIRE(batch >= 0 && tq >= 0 && n_cap >= 0, CSA_ERR_SHAPE, "negative batch, tq or n_cap");
+  REQUIRE(n_idx_heads >= 1 && idx_dim >= 1 && m >= 1, CSA_ERR_SHAPE, "n_idx_heads, idx_dim and m must be >= 1");
+  const int kd = k_idx->dtype, qd = q_idx->dtype;
+  if (kd == CSA_MXFP4) {
+    REQUIRE(qd == CSA_F32, CSA_ERR_DTYPE, "MXFP4 keys take an F32 query (quantised inside)");
+    REQUIRE(idx_dim == 64 && n_idx_heads <= 32, CSA_ERR_UNSUPPORTED,
+            "MXFP4 indexer supports idx_dim == 64 and n_idx_heads <= 32 (got %d, %d)", idx_dim, n_idx_heads);
+  } else if (kd == CSA_BF16) {
+    REQUIRE(qd == CSA_F32 || qd == CSA_BF16, CSA_ERR_DTYPE, "BF16 keys take an F32 or BF16 query");
+  } else if (kd == CSA_F32) {
+    REQUIRE(qd == CSA_F32, CSA_ERR_DTYPE, "F32 keys take an F32 query");
+  } else {
+    return fail(CSA_ERR_UNSUPPORTED, "FP8 indexer keys are not supported");
+  }
+  if (kd != CSA_MXFP4 && !(kd == CSA_BF16 && qd == CSA_BF16 && n_idx_heads == 8 && idx_dim == 64))
+    REQUIRE((int64_t)n_idx_heads * idx_dim <= 8192, CSA_ERR_UNSUPPORTED, "n_idx_heads * idx_dim > 8192");
+  csa::IndexArgs a;
+  a.q = csa::view_of(q_idx);
+  a.w = w;
+  a.k = csa::view_of(k_idx);
+  a.q_pos = q_pos;
+  a.batch = batch;
+  a.tq = tq;
+  a.heads = n_idx_heads;
+  a.dim = idx_dim;
+  a.m = m;
+  a.n_cap = n_cap;
+  a.scores = scores;
+  return from_hip(csa::launch_index_scores(a, (hipStream_t)stream), "csa_index_scores launch");
+}
+
+size_t csa_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, int32_t k) {
+  if (batch < 0 || tq < 0 || n_cap < 0 || k < 1) return 0;
+  return csa::topk_workspace_bytes((int64_t)batch * tq, n_cap, k);
+}
+
+csa_status csa_topk(const float* scores, const int32_t* q_pos, int32_t batch, int32_t tq, int32_t n_cap, int32_t m,
+                    int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(scores && q_pos && idx, CSA_ERR_NULL, "scores/q_pos/idx is NULL");
+  REQUIRE(batch >= 0 && tq >= 0 && n_cap >= 0, CSA_ERR_SHAPE, "negative batch, tq or n_cap");
+  REQUIRE(k >= 1 && m >= 1, CSA_ERR_SHAPE, "k and m must be >= 1");
+  const size_t need = csa::topk_workspace_bytes((int64_t)batch * tq, n_cap, k);
+  if (need > 0) REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "top-k needs %zu workspace bytes, got %zu", need, ws_bytes);
+  return from_hip(csa::launch_topk(scores, q_pos, batch, tq, n_cap, m, k, idx, ws, (hipStream_t)stream),
+                  "csa_topk launch");
+}
+
+size_t csa_attn_workspace_size(int32_t batch, int32_t tq, int32_t heads, int32_t dim, int32_t n_entries_max) {
+  if (batch < 0 || tq < 0 || heads < 1 || dim < 1 || n_entries_max < 0) return 0;
+  return csa::attn_workspace_bytes((int64_t)batch * tq, heads, dim, n_entries_max, tq);
+}
+
+static csa_status attn_common(const csa_tensor* q, const csa_tensor* kv, const int32_t* idx, int32_t k, int32_t m_hc,
+                              int32_t n_cap_hc, const csa_tensor* kv_raw, const int32_t* raw_base, int32_t window,
+                              const int32_t* q_pos, int32_t batch, int32_t tq, int32_t heads, int32_t dim, float scale,
+                              float* out, float* lse, void* ws, size_t ws_bytes, void* stream, int n_entries_max) {
+  csa_status st;
+  if ((st = check_tensor(q, "q")) != CSA_OK) return st;
+  if ((st = check_tensor(kv, "kv")) != CSA_OK) return st;
+  if ((st = check_tensor(kv_raw, "kv_raw")) != CSA_OK) return st;
+  REQUIRE(raw_base && q_pos && out, CSA_ERR_NULL, "raw_base/q_pos/out is NULL");
+  REQUIRE(batch >= 0 && tq >= 0 && window >= 0, CSA_ERR_SHAPE, "negative batch, tq or window");
+  REQUIRE(heads >= 1 && dim >= 1, CSA_ERR_SHAPE, "heads and dim must be >= 1");
+  REQUIRE(kv->dtype == kv_raw->dtype, CSA_ERR_DTYPE, "compressed and raw rows must share a dtype");
+  if (kv->dtype == CSA_F32) {
+    REQUIRE(q->dtype == CSA_F32, CSA_ERR_DTYPE, "F32 caches take an F32 query");
+    REQUIRE(dim <= 512 && dim % 4 == 0 && heads <= 64, CSA_ERR_UNSUPPORTED,
+            "F32 attention supports dim <= 512 (multiple of 4) and heads <= 64");
+    REQUIRE(csa::attn_plain_fits(n_entries_max), CSA_ERR_UNSUPPORTED, "F32 attention supports at most 8192 entries per query");
+  } else if (kv->dtype == CSA_BF16 || kv->dtype == CSA_FP8_E4M3) {
+    REQUIRE(q->dtype == CSA_BF16, CSA_ERR_DTYPE, "BF16/FP8 caches take a BF16 query");
+    REQUIRE(dim == 512 && heads % 16 == 0 && heads <= 64, CSA_ERR_UNSUPPORTED,
+            "BF16/FP8 attention supports dim == 512 and heads a multiple of 16 up to 64 (got %d, %d)", dim, heads);
+  } else {
+    return fail(CSA_ERR_DTYPE, "attention caches must be F32, BF16 or FP8_E4M3");
+  }
+  const size_t need = csa::attn_workspace_bytes((int64_t)batch * tq, heads, dim, n_entries_max, tq);
+  if (need > 0) REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
+  csa::AttnArgs a;
+  a.q = csa::view_of(q);
+  a.kv = csa::view_of(kv);
+  a.idx = idx;
+  a.k = k;
+  a.m_hc = m_hc;
+  a.n_cap = n_cap_hc;
+  a.raw = csa::view_of(kv_raw);
+  a.raw_base = raw_base;
+  a.window = window;
+  a.q_pos = q_pos;
+  a.batch = batch;
+  a.tq = tq;
+  a.heads = heads;
+  a.dim = dim;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  a.ws = ws;
+  return from_hip(csa::launch_attention(a, n_entries_max, (hipStream_t)stream), "attention launch");
+}
+
+csa_status csa_sparse_attn(const csa_tensor* q, const csa_tensor* kv_cmp, const int32_t* idx, int32_t k,
+                           const csa_tensor* kv_raw, const int32_t* raw_base, int32_t window, const int32_t* q_pos,
+                           int32_t batch, int32_t tq, int32_t heads, int32_t dim, float scale, float* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(idx != nullptr, CSA_ERR_NULL, "idx is NULL");
+  REQUIRE(k >= 0, CSA_ERR_SHAPE, "k=%d must be >= 0", k);
+  REQUIRE((int64_t)k + window <= (1 << 30), CSA_ERR_SHAPE, "k + window too large");
+  return attn_common(q, kv_cmp, idx, k, 0, 0, kv_raw, raw_base, window, q_pos, batch, tq, heads, dim, scale, out, lse,
+                     ws, ws_bytes, stream, k + window);
+}
+
+csa_status hca_attn(const csa_tensor* q, const csa_tensor* kv_hc, int32_t m_hc, int32_t n_cap_hc,
+                    const csa_tensor* kv_raw, const int32_t* raw_base, int32_t window, const int32_t* q_pos,
+                    int32_t batch, int32_t tq, int32_t heads, int32_t dim, float scale, float* out, float* lse,
+                    void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(m_hc >= 1 && n_cap_hc >= 0, CSA_ERR_SHAPE, "m_hc must be >= 1 and n_cap_hc >= 0");
+  REQUIRE((int64_t)n_cap_hc + window <= (1 << 30), CSA_ERR_SHAPE, "n_cap_hc + window too large");
+  return attn_common(q, kv_hc, nullptr, 0, m_hc, n_cap_hc, kv_raw, raw_base, window, q_pos, batch, tq, heads, dim,
+                     scale, out, lse, ws, ws_bytes, stream, n_cap_hc + window);
+}
+
+csa_status csa_quantize_mxfp4(const float* x, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                              void* stream) {
+  REQUIRE(x && codes && scales, CSA_ERR_NULL, "x/codes/scales is NULL");
+  REQUIRE(rows >= 0 && cols >= 0 && cols % 32 == 0, CSA_ERR_SHAPE, "cols must be a non-negative multiple of 32");
+  return from_hip(csa::launch_quantize_mxfp4(x, rows, cols, codes, scales, (hipStream_t)stream), "csa_quantize_mxfp4");
+}
+
+csa_status csa_quantize_fp8(const float* x, int64_t rows, int32_t cols, uint8_t* codes, float* row_scale,
+                            void* stream) {
+  REQUIRE(x && codes && row_scale, CSA_ERR_NULL, "x/codes/row_scale is NULL");
+  REQUIRE(rows >= 0 && cols >= 1 && cols <= 8192, CSA_ERR_SHAPE, "cols must be in [1, 8192]");
+  return from_hip(csa::launch_quantize_fp8(x, rows, cols, codes, row_scale, (hipStream_t)stream), "csa_quantize_fp8");
+}
+
+}  // extern "C"

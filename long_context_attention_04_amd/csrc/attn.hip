@@ -1,0 +1,394 @@
+// (d) CSA sparse attention and (e) HCA dense attention.
+//
+// Both attend over compressed entries plus a sliding window of raw local
+// entries (b-lab.team summary of DeepSeek-V4, Core Methodological Innovations
+// 1: CSA bullet for the top-k compressed blocks, HCA bullet for dense
+// attention over the heavily compressed entries and the window).  Readings:
+// key = value = the stored (shared, MQA) row; one softmax over the compressed
+// entries followed by the window rows, not de-duplicated.
+//
+// MFMA path (bf16 / fp8 caches, 16..64 heads, dim 512).  Decode attention of
+// 64 query heads against a shared 512-wide latent is a [64 x 512] x [512 x n]
+// contraction, so QK and PV both run on bf16 MFMA 16x16x32.  A workgroup
+// (4 waves) handles one query row and one contiguous split of its entry list.
+// Wave w owns latent columns [128w, 128w+128): it loads exactly that slice of
+// every entry row from HBM (16 B per lane, the MFMA B-operand layout), uses it
+// for its partial QK and stages it in LDS for PV, so every entry byte is read
+// from HBM once.  The four partial logit tiles are summed in a fixed order in
+// LDS; wave h owns the online softmax of head tile h.  The probabilities go
+// to PV as two bf16 terms (hi + lo), so PV carries ~16 significant bits of P
+// instead of bf16's 8; the staged slice is read back transposed from LDS.  Splits are merged by a second
+// kernel with a fixed-order log-sum-exp combine; the split size depends only
+// on the call shape, never on the batch, so results are batch-invariant.
+// fp8 rows keep their per-row scale out of the MFMA: it multiplies the logit
+// and the probability used for PV.
+//
+// Plain path (fp32 caches): a straightforward fp32 VALU kernel, one workgroup
+// per (query, head).
+#include "common.h"
+#include "kernels.h"
+
+namespace csa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTileE = 32;
+constexpr int kSplitDecode = 256;
+constexpr int kEsStride = 136;  // bf16 elements per staged row (128 + 8 pad)
+constexpr int kPsStride = 40;   // bf16 elements per P row (32 + 8 pad)
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct RowInfo {
+  int b, t, pos, w0, n_cmp, n_tot;
+};
+
+__device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int row) {
+  RowInfo r;
+  r.b = row / a.tq;
+  r.t = row % a.tq;
+  r.pos = a.q_pos[row];
+  r.w0 = max(0, r.pos - a.window + 1);
+  const int n_win = a.window > 0 ? r.pos - r.w0 + 1 : 0;
+  r.n_cmp = a.idx ? a.k : visible_blocks(r.pos, a.m_hc);
+  r.n_tot = r.n_cmp + n_win;
+  return r;
+}
+
+__device__ __forceinline__ int elem_bytes(int dtype) { return dtype == CSA_F32 ? 4 : dtype == CSA_BF16 ? 2 : 1; }
+
+// Byte pointer to entry e of a row's list (nullptr when the slot is empty) and its row scale.
+__device__ __forceinline__ const uint8_t* entry_ptr(const AttnArgs& a, const RowInfo& r, int row, int e, float* sc) {
+  *sc = 1.f;
+  if (e >= r.n_tot) return nullptr;
+  if (e < r.n_cmp) {
+    const int j = a.idx ? a.idx[(int64_t)row * a.k + e] : e;
+    if (j < 0) return nullptr;
+    if (a.kv.dtype == CSA_FP8_E4M3 && a.kv.scale) *sc = ((const float*)a.kv.scale)[(int64_t)r.b * a.kv.ssb + (int64_t)j * a.kv.ssr];
+    return (const uint8_t*)a.kv.data + ((int64_t)r.b * a.kv.sb + (int64_t)j * a.kv.sr) * elem_bytes(a.kv.dtype);
+  }
+  const int64_t rr = (int64_t)(r.w0 + (e - r.n_cmp)) - a.raw_base[r.b];
+  if (a.raw.dtype == CSA_FP8_E4M3 && a.raw.scale) *sc = ((const float*)a.raw.scale)[(int64_t)r.b * a.raw.ssb + rr * a.raw.ssr];
+  return (const uint8_t*)a.raw.data + ((int64_t)r.b * a.raw.sb + rr * a.raw.sr) * elem_bytes(a.raw.dtype);
+}
+
+template <bool FP8>
+__device__ __forceinline__ v8bf load8(const uint8_t* p, int col) {
+  v8bf v;
+  if (!p) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (__bf16)0.f;
+    return v;
+  }
+  if constexpr (!FP8) {
+    return *(const v8bf*)(p + 2 * col);
+  } else {
+    const uint2 c = *(const uint2*)(p + col);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t byte = ((i < 4 ? c.x : c.y) >> (8 * (i & 3))) & 0xffu;
+      v[i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(e4m3_to_f32(byte)) >> 16));  // exact
+    }
+    return v;
+  }
+}
+
+template <int NHT, bool FP8>
+__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a, int split, int nsplit_max, int partial) {
+  const int s = blockIdx.x;
+  const int row = blockIdx.y;
+  const RowInfo ri = row_info(a, row);
+  const int nsplit = max(1, (ri.n_tot + split - 1) / split);
+  if (s >= nsplit) return;
+  const int e_begin = s * split, e_end = min(ri.n_tot, e_begin + split);
+
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int g = lane / 16, n = lane % 16;
+
+  __shared__ float red[4][64][kTileE];
+  __shared__ __attribute__((aligned(16))) uint16_t Es[4][kTileE][kEsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[2][64][kPsStride];  // P = hi + lo, both bf16
+  __shared__ float al[64];
+  __shared__ float ev_scale[kTileE];  // 0 for an empty slot
+  __shared__ float fin_m[64], fin_l[64];
+
+  // q operands: head 16*ht + n, latent columns 128w + 32kk + 8g .. +7
+  v8bf qa[NHT][4];
+  const uint16_t* qp = (const uint16_t*)a.q.data + (int64_t)ri.b * a.q.sb + (int64_t)ri.t * a.q.sr;
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qa[ht][kk] = *(const v8bf*)(qp + (16 * ht + n) * 512 + 128 * w + 32 * kk + 8 * g);
+
+  const float sl2 = a.scale * kLog2e;
+  float m_run = kNegInf, l_run = 0.f;  // softmax lanes: head 16w + lane/4
+  v4f O[NHT][8];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) O[ht][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  for (int e0 = e_begin; e0 < e_end; e0 += kTileE) {
+    v8bf bq[2][4];
+#pragma unroll
+    for (int et = 0; et < 2; ++et) {
+      const int e = e0 + 16 * et + n;
+      float sc;
+      const uint8_t* p = e < e_end ? entry_ptr(a, ri, row, e, &sc) : nullptr;
+      if (w == 0 && g == 0) ev_scale[16 * et + n] = p ? (FP8 ? sc : 1.f) : 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) bq[et][kk] = load8<FP8>(p, 128 * w + 32 * kk + 8 * g);
+    }
+    // partial logits over this wave's 128 columns
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+      for (int et = 0; et < 2; ++et) {
+        v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ht][kk], bq[et][kk], c, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[w][16 * ht + 4 * g + r][16 * et + n] = c[r];
+      }
+#pragma unroll
+    for (int et = 0; et < 2; ++et)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) *(v8bf*)&Es[w][16 * et + n][32 * kk + 8 * g] = bq[et][kk];
+    __syncthreads();
+
+    if (w < NHT) {  // online softmax of head tile w: lane -> head 16w + lane/4, entries 8*(lane%4) .. +7
+      const int h = 16 * w + lane / 4, eb = 8 * (lane % 4);
+      float sv[8], esc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        esc[i] = ev_scale[eb + i];
+        const float x = ((red[0][h][eb + i] + red[1][h][eb + i]) + red[2][h][eb + i]) + red[3][h][eb + i];
+        sv[i] = esc[i] != 0.f ? x * esc[i] * sl2 : kNegInf;
+      }
+      float tmax = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sv[i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 1));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 2));
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = m_new == kNegInf ? 1.f : exp2f(m_run - m_new);
+      float psum = 0.f;
+      uint16_t pb[8], pl[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = m_new == kNegInf ? 0.f : exp2f(sv[i] - m_new);
+        psum += p;
+        const float pv = FP8 ? p * esc[i] : p;
+        pb[i] = f32_to_bf16_bits(pv);
+        pl[i] = f32_to_bf16_bits(pv - bf16_bits_to_f32(pb[i]));  // exact remainder, rounded once more
+      }
+      psum += __shfl_xor(psum, 1);
+      psum += __shfl_xor(psum, 2);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      uint4 pk;
+      pk.x = pb[0] | ((uint32_t)pb[1] << 16);
+      pk.y = pb[2] | ((uint32_t)pb[3] << 16);
+      pk.z = pb[4] | ((uint32_t)pb[5] << 16);
+      pk.w = pb[6] | ((uint32_t)pb[7] << 16);
+      *(uint4*)&Ps[0][h][eb] = pk;
+      pk.x = pl[0] | ((uint32_t)pl[1] << 16);
+      pk.y = pl[2] | ((uint32_t)pl[3] << 16);
+      pk.z = pl[4] | ((uint32_t)pl[5] << 16);
+      pk.w = pl[6] | ((uint32_t)pl[7] << 16);
+      *(uint4*)&Ps[1][h][eb] = pk;
+      if ((lane & 3) == 0) al[h] = alpha;
+    }
+    __syncthreads();
+
+    // O[heads, this wave's columns] = O * alpha + P[heads, 32] . E[32, columns]
+    v8bf pa[NHT], pal[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      pa[ht] = *(const v8bf*)&Ps[0][16 * ht + n][8 * g];
+      pal[ht] = *(const v8bf*)&Ps[1][16 * ht + n][8 * g];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float alr = al[16 * ht + 4 * g + r];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) O[ht][ct][r] *= alr;
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      v8bf vb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vb[i] = __builtin_bit_cast(__bf16, Es[w][8 * g + i][16 * ct + n]);
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        O[ht][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[ht], vb, O[ht][ct], 0, 0, 0);
+        O[ht][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pal[ht], vb, O[ht][ct], 0, 0, 0);
+      }
+    }
+  }
+
+  if (w < NHT && (lane & 3) == 0) {
+    fin_m[16 * w + lane / 4] = m_run;
+    fin_l[16 * w + lane / 4] = l_run;
+  }
+  __syncthreads();
+  const int H = a.heads;
+  if (partial) {
+    float* po = (float*)a.ws + (((int64_t)row * nsplit_max + s) * H) * 512;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) po[(16 * ht + 4 * g + r) * 512 + 128 * w + 16 * ct + n] = O[ht][ct][r];
+    float* pml = (float*)a.ws + (int64_t)gridDim.y * nsplit_max * H * 512 + (((int64_t)row * nsplit_max + s) * H) * 2;
+    if (threadIdx.x < H) {
+      pml[2 * threadIdx.x] = fin_m[threadIdx.x];
+      pml[2 * threadIdx.x + 1] = fin_l[threadIdx.x];
+    }
+  } else {
+    float* po = a.out + (int64_t)row * H * 512;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 16 * ht + 4 * g + r;
+        const float L = fin_l[h];
+        const float f = L > 0.f ? 1.0f * __fdiv_rn(1.0f, L) : 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) po[h * 512 + 128 * w + 16 * ct + n] = O[ht][ct][r] * f;
+      }
+    if (a.lse && threadIdx.x < H) {
+      const float L = fin_l[threadIdx.x];
+      a.lse[(int64_t)row * H + threadIdx.x] = L > 0.f ? (fin_m[threadIdx.x] + log2f(L)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// Fixed-order log-sum-exp merge of the splits of one (row, head).
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int split, int nsplit_max, int dim) {
+  const int row = blockIdx.x, h = blockIdx.y;
+  const RowInfo ri = row_info(a, row);
+  const int nsplit = max(1, (ri.n_tot + split - 1) / split);
+  const int H = a.heads;
+  const float* pml = (const float*)a.ws + (int64_t)gridDim.x * nsplit_max * H * dim;
+  float M = kNegInf;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pml[(((int64_t)row * nsplit_max + s) * H + h) * 2]);
+  float L = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const int64_t o = (((int64_t)row * nsplit_max + s) * H + h) * 2;
+    L += M == kNegInf ? 0.f : pml[o + 1] * exp2f(pml[o] - M);
+  }
+  const float inv = L > 0.f ? __fdiv_rn(1.0f, L) : 0.f;
+  for (int c = threadIdx.x; c < dim; c += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const int64_t base = ((int64_t)row * nsplit_max + s) * H + h;
+      const float wgt = M == kNegInf ? 0.f : exp2f(pml[base * 2] - M) * inv;
+      acc = fmaf(((const float*)a.ws)[base * dim + c], wgt, acc);
+    }
+    a.out[((int64_t)row * H + h) * dim + c] = acc;
+  }
+  if (a.lse && threadIdx.x == 0) a.lse[(int64_t)row * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+}
+
+// ------------------------------------------------------------------ fp32 VALU path
+constexpr int kPlainThreads = 128;
+constexpr int kPlainMaxEntries = 8192;
+
+__global__ __launch_bounds__(kPlainThreads) void attn_plain_kernel(AttnArgs a) {
+  const int row = blockIdx.x, h = blockIdx.y;
+  const RowInfo ri = row_info(a, row);
+  __shared__ float logit[kPlainMaxEntries];
+  __shared__ float qs[512];
+  __shared__ float red[kPlainThreads / kWave];
+  const int D = a.dim;
+  const float* qp = (const float*)a.q.data + (int64_t)ri.b * a.q.sb + (int64_t)ri.t * a.q.sr + (int64_t)h * D;
+  for (int d = threadIdx.x; d < D; d += kPlainThreads) qs[d] = qp[d];
+  __syncthreads();
+  float mx = kNegInf;
+  for (int e = threadIdx.x; e < ri.n_tot; e += kPlainThreads) {
+    float sc;
+    const float* p = (const float*)entry_ptr(a, ri, row, e, &sc);
+    float l = kNegInf;
+    if (p) {
+      float dot = 0.f;
+      for (int d = 0; d < D; ++d) dot = fmaf(qs[d], p[d], dot);
+      l = dot * a.scale;
+    }
+    logit[e] = l;
+    mx = fmaxf(mx, l);
+  }
+  mx = wave_max(mx);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = mx;
+  __syncthreads();
+  mx = fmaxf(red[0], red[1]);
+  __syncthreads();
+  float sum = 0.f;
+  for (int e = threadIdx.x; e < ri.n_tot; e += kPlainThreads) {
+    const float p = mx == kNegInf ? 0.f : expf(logit[e] - mx);
+    logit[e] = p;
+    sum += p;
+  }
+  sum = wave_sum(sum);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = sum;
+  __syncthreads();
+  sum = red[0] + red[1];
+  const float inv = sum > 0.f ? __fdiv_rn(1.0f, sum) : 0.f;
+  for (int d = threadIdx.x; d < D; d += kPlainThreads) {
+    float acc = 0.f;
+    for (int e = 0; e < ri.n_tot; ++e) {
+      float sc;
+      const float* p = (const float*)entry_ptr(a, ri, row, e, &sc);
+      if (p) acc = fmaf(logit[e], p[d], acc);
+    }
+    a.out[((int64_t)row * a.heads + h) * D + d] = acc * inv;
+  }
+  if (a.lse && threadIdx.x == 0) a.lse[(int64_t)row * a.heads + h] = sum > 0.f ? mx + logf(sum) : kNegInf;
+}
+
+template <int NHT>
+hipError_t launch_mfma(const AttnArgs& a, int64_t rows, int split, int nsplit_max, hipStream_t s) {
+  const int partial = nsplit_max > 1;
+  dim3 grid(nsplit_max, (unsigned)rows);
+  if (a.kv.dtype == CSA_FP8_E4M3)
+    hipLaunchKernelGGL((attn_mfma_kernel<NHT, true>), grid, dim3(kThreads), 0, s, a, split, nsplit_max, partial);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<NHT, false>), grid, dim3(kThreads), 0, s, a, split, nsplit_max, partial);
+  if (partial) hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)rows, a.heads), dim3(128), 0, s, a, split, nsplit_max, 512);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int attn_split_size(int tq, int n_entries_max) { return tq == 1 ? kSplitDecode : max(n_entries_max, 1); }
+
+size_t attn_workspace_bytes(int64_t rows, int heads, int dim, int n_entries_max, int tq) {
+  const int split = attn_split_size(tq, n_entries_max);
+  const int64_t nsplit = (n_entries_max + split - 1) / split;
+  if (nsplit <= 1) return 0;
+  return (size_t)rows * nsplit * heads * (dim + 2) * sizeof(float);
+}
+
+bool attn_plain_fits(int n_entries_max) { return n_entries_max <= kPlainMaxEntries; }
+
+hipError_t launch_attention(const AttnArgs& a, int n_entries_max, hipStream_t s) {
+  const int64_t rows = (int64_t)a.batch * a.tq;
+  if (rows == 0) return hipSuccess;
+  if (a.kv.dtype == CSA_F32) {
+    hipLaunchKernelGGL(attn_plain_kernel, dim3((unsigned)rows, a.heads), dim3(kPlainThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  const int split = attn_split_size(a.tq, n_entries_max);
+  const int nsplit_max = max(1, (n_entries_max + split - 1) / split);
+  switch (a.heads / 16) {
+    case 1: return launch_mfma<1>(a, rows, split, nsplit_max, s);
+    case 2: return launch_mfma<2>(a, rows, split, nsplit_max, s);
+    case 3: return launch_mfma<3>(a, rows, split, nsplit_max, s);
+    default: return launch_mfma<4>(a, rows, split, nsplit_max, s);
+  }
+}
+
+}  // namespace csa

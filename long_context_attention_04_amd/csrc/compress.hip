@@ -1,0 +1,171 @@
+// (a) KV compression and the stored-format quantisers.
+//
+// Compression merges each block of m adjacent raw rows into one entry
+// (b-lab.team summary of DeepSeek-V4, Core Methodological Innovations 1, CSA
+// and HCA bullets).  The merge is read as a softmax-weighted sum over the m
+// offsets with one logit per offset.  The work is a short weighted reduction
+// over rows that are read once: HBM-bound, so each workgroup streams the m
+// rows of one output entry with coalesced column-parallel loads and fuses the
+// output quantisation (bf16 / fp8 row scale / MXFP4 block scale) into the
+// store.
+#include "common.h"
+#include "kernels.h"
+
+namespace csa {
+
+namespace {
+
+constexpr int kCompressThreads = 256;
+constexpr int kMaxDimPerThread = 16;  // dim <= 4096
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < (int)(blockDim.x / kWave); ++i) r = fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+// Writes one finished fp32 row (thread t holds columns t + 256*i) in the output format.
+__device__ void store_row(const float* vals, int nv, int dim, int out_dtype, void* out, int64_t off,
+                          void* out_scale, int64_t soff, float* red) {
+  const int t = threadIdx.x;
+  if (out_dtype == CSA_F32) {
+    for (int i = 0; i < nv; ++i) ((float*)out)[off + t + i * kCompressThreads] = vals[i];
+  } else if (out_dtype == CSA_BF16) {
+    for (int i = 0; i < nv; ++i) ((uint16_t*)out)[off + t + i * kCompressThreads] = f32_to_bf16_bits(vals[i]);
+  } else if (out_dtype == CSA_FP8_E4M3) {
+    float amax = 0.f;
+    for (int i = 0; i < nv; ++i) amax = fmaxf(amax, fabsf(vals[i]));
+    amax = block_max(amax, red);
+    const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    for (int i = 0; i < nv; ++i)
+      ((uint8_t*)out)[off + t + i * kCompressThreads] = (uint8_t)f32_to_e4m3(__fdiv_rn(vals[i], s));
+    if (t == 0) ((float*)out_scale)[soff] = s;
+  } else {  // MXFP4: 32 consecutive columns live in 32 consecutive lanes
+    for (int i = 0; i < nv; ++i) {
+      const int col = t + i * kCompressThreads;
+      float a = fabsf(vals[i]);
+      for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 32));
+      const int e = mx_scale_exp(a);
+      uint32_t nib = a > 0.f ? f32_to_e2m1(vals[i], e) : 0u;
+      const uint32_t hi = __shfl_down(nib, 1, 32);
+      if ((col & 1) == 0) ((uint8_t*)out)[off + col / 2] = (uint8_t)(nib | (hi << 4));
+      if ((col & 31) == 0) ((uint8_t*)out_scale)[soff + col / 32] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs a) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x;
+  const int cnt = a.block_count[b];
+  if (i >= cnt) return;
+  const int j = a.block_first[b] + i;
+  __shared__ float omega[1024];
+  __shared__ float red[kCompressThreads / kWave];
+  // omega = softmax(logits) in fp32, max-subtracted, summed in ascending offset order
+  if (threadIdx.x == 0) {
+    float mx = a.logits[0];
+    for (int r = 1; r < a.m; ++r) mx = fmaxf(mx, a.logits[r]);
+    float sum = 0.f;
+    for (int r = 0; r < a.m; ++r) {
+      const float e = expf(a.logits[r] - mx);
+      omega[r] = e;
+      sum += e;
+    }
+    for (int r = 0; r < a.m; ++r) omega[r] = __fdiv_rn(omega[r], sum);
+  }
+  __syncthreads();
+  const int64_t row0 = (int64_t)j * a.m - a.raw_base[b];
+  float acc[kMaxDimPerThread];
+  const int nv = (a.dim - threadIdx.x + kCompressThreads - 1) / kCompressThreads;
+  for (int v = 0; v < nv; ++v) acc[v] = 0.f;
+  for (int r = 0; r < a.m; ++r) {
+    const int64_t base = (int64_t)b * a.raw.sb + (row0 + r) * a.raw.sr;
+    float rs = 1.f;
+    if (a.raw.dtype == CSA_FP8_E4M3 && a.raw.scale)
+      rs = ((const float*)a.raw.scale)[(int64_t)b * a.raw.ssb + (row0 + r) * a.raw.ssr];
+    const float w = omega[r];
+    for (int v = 0; v < nv; ++v) {
+      const int col = threadIdx.x + v * kCompressThreads;
+      float x = load_elem(a.raw.data, a.raw.dtype, base + col);
+      if (a.raw.dtype == CSA_FP8_E4M3) x *= rs;
+      acc[v] = fmaf(w, x, acc[v]);
+    }
+  }
+  const int64_t off = (int64_t)b * a.out_sb + (int64_t)j * a.out_sr;
+  const int64_t soff = (int64_t)b * a.out_ssb + (int64_t)j * a.out_ssr;
+  store_row(acc, nv, a.dim, a.out_dtype, a.out, off, a.out_scale, soff, red);
+}
+
+// one thread per 32-element block
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const float* __restrict__ x, int64_t nblocks,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  const int64_t blk = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (blk >= nblocks) return;
+  const float4* p = (const float4*)(x + blk * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 f = p[i];
+    v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = mx_scale_exp(amax);
+  uint32_t w[4] = {0, 0, 0, 0};
+  if (amax > 0.f) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w[i / 8] |= f32_to_e2m1(v[i], e) << (4 * (i % 8));
+  }
+  *(uint4*)(codes + blk * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  scales[blk] = (uint8_t)(e + 127);
+}
+
+// one workgroup per row
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const float* __restrict__ x, int cols,
+                                                           uint8_t* __restrict__ codes, float* __restrict__ rs) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * cols;
+  float amax = 0.f;
+  for (int c = threadIdx.x; c < cols; c += blockDim.x) amax = fmaxf(amax, fabsf(xr[c]));
+  amax = block_max(amax, red);
+  const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  for (int c = threadIdx.x; c < cols; c += blockDim.x)
+    codes[row * cols + c] = (uint8_t)f32_to_e4m3(__fdiv_rn(xr[c], s));
+  if (threadIdx.x == 0) rs[row] = s;
+}
+
+}  // namespace
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
+  if (a.max_blocks <= 0 || a.batch <= 0) return hipSuccess;
+  dim3 grid(a.max_blocks, a.batch);
+  hipLaunchKernelGGL(compress_kernel, grid, dim3(kCompressThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp4(const float* x, int64_t rows, int cols, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s) {
+  const int64_t nblocks = rows * (cols / 32);
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, s, x, nblocks,
+                     codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const float* x, int64_t rows, int cols, uint8_t* codes, float* row_scale,
+                               hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_fp8_kernel, dim3((unsigned)rows), dim3(256), 0, s, x, cols, codes, row_scale);
+  return hipGetLastError();
+}
+
+}  // namespace csa

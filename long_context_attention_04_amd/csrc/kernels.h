@@ -1,0 +1,93 @@
+// Internal launch interface between the C ABI layer (abi.cpp) and the kernel
+// translation units.  Arguments arrive validated; launchers only enqueue.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/csa.h"
+
+namespace csa {
+
+struct TensorView {
+  const void* data;
+  const void* scale;
+  int dtype;
+  int64_t sb, sr;    // batch / row strides (elements; MXFP4: bytes)
+  int64_t ssb, ssr;  // scale strides
+};
+
+inline TensorView view_of(const csa_tensor* t) {
+  TensorView v;
+  v.data = t->data;
+  v.scale = t->scale;
+  v.dtype = t->dtype;
+  v.sb = t->stride_b;
+  v.sr = t->stride_row;
+  v.ssb = t->scale_stride_b;
+  v.ssr = t->scale_stride_row;
+  return v;
+}
+
+// ---------------------------------------------------------------- compression
+struct CompressArgs {
+  TensorView raw;
+  const int32_t* raw_base;
+  const float* logits;
+  int m, dim;
+  const int32_t* block_first;
+  const int32_t* block_count;
+  int max_blocks, batch;
+  void* out;
+  void* out_scale;
+  int out_dtype;
+  int64_t out_sb, out_sr, out_ssb, out_ssr;
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+hipError_t launch_quantize_mxfp4(const float* x, int64_t rows, int cols, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s);
+hipError_t launch_quantize_fp8(const float* x, int64_t rows, int cols, uint8_t* codes, float* row_scale,
+                               hipStream_t s);
+
+// ---------------------------------------------------------------- indexer
+struct IndexArgs {
+  TensorView q;  // [B, Tq, H_I, d_I]
+  const float* w;
+  TensorView k;  // [B, N, d_I]
+  const int32_t* q_pos;
+  int batch, tq, heads, dim, m, n_cap;
+  float* scores;
+};
+hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- top-k
+// Rows longer than this are selected by the multi-workgroup path.
+constexpr int kTopkLdsMax = 20480;
+constexpr int kTopkSlice = 8192;  // keys per workgroup in the multi-workgroup path
+size_t topk_workspace_bytes(int64_t rows, int n_cap, int k);
+hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int tq, int n_cap, int m, int k,
+                       int32_t* idx, void* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  TensorView q;        // [B, Tq, H, D]
+  TensorView kv;       // compressed cache
+  const int32_t* idx;  // CSA: [B, Tq, k]; HCA: nullptr
+  int k;               // CSA: slots per query
+  int m_hc;            // HCA block size (0 for CSA)
+  int n_cap;           // HCA cache capacity
+  TensorView raw;
+  const int32_t* raw_base;
+  int window;
+  const int32_t* q_pos;
+  int batch, tq, heads, dim;
+  float scale;
+  float* out;
+  float* lse;
+  void* ws;
+};
+int attn_split_size(int tq, int n_entries_max);
+size_t attn_workspace_bytes(int64_t rows, int heads, int dim, int n_entries_max, int tq);
+hipError_t launch_attention(const AttnArgs& a, int n_entries_max, hipStream_t s);
+
+}  // namespace csa

@@ -1,0 +1,336 @@
+"""Stage-by-stage parity of the HIP path against the CPU oracle.
+
+Each stage gets its inputs from the seeded generators (never from another HIP
+stage), runs through the C ABI, and is compared with the oracle fed the same
+stored values: bit-exact for codes and indices, within the stated tolerance
+for floating point (max over output rows of ||err||_inf / ||ref||_inf).
+Sizes span several tiles plus a ragged tail.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import formats as OF
+from tests.gpu_helpers import down, row_rel_err, sorted_unique_choice, up, up_bf16, workspace
+
+pytestmark = pytest.mark.gpu
+
+TEST_WID = 100  # seed namespace of these stage tests
+
+
+def _rng(name, salt=0):
+    return synth.rng(TEST_WID, name, salt)
+
+
+# ----------------------------------------------------------------------------- quantisers
+
+
+def _awkward_f32(rows, cols, seed_name):
+    r = _rng(seed_name)
+    x = r.standard_normal((rows, cols)).astype(np.float32) * np.exp2(r.integers(-20, 20, (rows, 1))).astype(np.float32)
+    x[0] = 0.0                                   # an all-zero row / blocks
+    x[1, :32] = np.float32(1e-40)                # subnormal block
+    x[2, :8] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32)  # e2m1 midpoints (amax 6 -> e=0)
+    x[3, ::7] = -0.0
+    return x
+
+
+def test_quantize_mxfp4_bit_exact(gpu_lib):
+    csa = gpu_lib
+    x = _awkward_f32(257, 128, "mx")
+    codes = torch.empty((257, 64), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((257, 4), dtype=torch.uint8, device="cuda")
+    csa.csa_quantize_mxfp4(up(x), 257, 128, codes, scales)
+    want_c, want_s = OF.quantize_mxfp4(x)
+    np.testing.assert_array_equal(down(scales), want_s)
+    np.testing.assert_array_equal(down(codes), want_c)
+
+
+def test_quantize_fp8_bit_exact(gpu_lib):
+    csa = gpu_lib
+    x = _awkward_f32(300, 512, "fp8")
+    codes = torch.empty((300, 512), dtype=torch.uint8, device="cuda")
+    rs = torch.empty((300,), dtype=torch.float32, device="cuda")
+    csa.csa_quantize_fp8(up(x), 300, 512, codes, rs)
+    want_c, want_s = OF.quantize_fp8_rows(x)
+    np.testing.assert_array_equal(down(rs), want_s)
+    np.testing.assert_array_equal(down(codes), want_c)
+
+
+# ----------------------------------------------------------------------------- compression
+
+
+@pytest.mark.parametrize("m,dim,in_dt,out_dt", [
+    (4, 128, "f32", "f32"), (4, 512, "bf16", "bf16"), (128, 512, "bf16", "bf16"),
+    (4, 64, "f32", "mxfp4"), (4, 512, "bf16", "fp8"), (128, 512, "fp8", "fp8"), (1, 96, "f32", "f32"),
+])
+def test_compress(gpu_lib, m, dim, in_dt, out_dt):
+    csa = gpu_lib
+    B, R = 3, 8 * m + 5
+    r = _rng(f"cmp{m}{dim}{in_dt}{out_dt}")
+    x = r.standard_normal((B, R, dim)).astype(np.float32)
+    z = r.standard_normal(m).astype(np.float32)
+    raw_base = np.array([0, 3 * m, 5 * m], dtype=np.int32)            # raw row 0 holds this position
+    first = np.array([0, 3, 6], dtype=np.int32)
+    count = np.array([8, 4, 0], dtype=np.int32)                       # ragged, one empty
+    ncap = 12
+    if in_dt == "f32":
+        raw_t, raw_v = up(x), x.astype(np.float64)
+        raw = csa.desc(raw_t, csa.F32)
+    elif in_dt == "bf16":
+        raw_t, raw_v = up_bf16(x)
+        raw = csa.desc(raw_t, csa.BF16)
+    else:
+        c, s = OF.quantize_fp8_rows(x.reshape(-1, dim))
+        raw_t, raw_s = up(c.reshape(B, R, dim)), up(s.reshape(B, R))
+        raw_v = OF.dequantize_fp8_rows(c, s).reshape(B, R, dim)
+        raw = csa.desc(raw_t, csa.FP8_E4M3, raw_s)
+    if out_dt == "f32":
+        out_t = torch.full((B, ncap, dim), float("nan"), device="cuda")
+        out = csa.desc(out_t, csa.F32)
+    elif out_dt == "bf16":
+        out_t = torch.full((B, ncap, dim), float("nan"), device="cuda", dtype=torch.bfloat16)
+        out = csa.desc(out_t, csa.BF16)
+    elif out_dt == "fp8":
+        out_t = torch.zeros((B, ncap, dim), dtype=torch.uint8, device="cuda")
+        out_s = torch.zeros((B, ncap), device="cuda")
+        out = csa.desc(out_t, csa.FP8_E4M3, out_s)
+    else:
+        out_t = torch.zeros((B, ncap, dim // 2), dtype=torch.uint8, device="cuda")
+        out_s = torch.zeros((B, ncap, dim // 32), dtype=torch.uint8, device="cuda")
+        out = csa.desc(out_t, csa.MXFP4, out_s)
+    csa.csa_compress(raw, up(raw_base), up(z), m, dim, up(first), up(count), 8, B, out)
+    want = oracle.compress(raw_v, raw_base, z.astype(np.float64), m, first, count)
+    for b in range(B):
+        j0, rows = want[b]
+        if rows.shape[0] == 0:
+            continue
+        sl = slice(j0, j0 + rows.shape[0])
+        if out_dt == "f32":
+            got = down(out_t)[b, sl]
+            assert row_rel_err(got, rows) < 1e-5
+        elif out_dt == "bf16":
+            got = down(out_t)[b, sl]
+            # one bf16 rounding of an fp32-accumulated value: within one bf16 ulp
+            assert np.all(np.abs(got - rows) <= np.abs(rows) * 2.0 ** -7 + 1e-30)
+        elif out_dt == "fp8":
+            codes, sc = down(out_t)[b, sl], down(out_s)[b, sl]
+            got = OF.dequantize_fp8_rows(codes, sc)
+            # the row scale follows the row maximum; each element within one e4m3 step
+            amax = np.abs(rows).max(axis=1)
+            np.testing.assert_allclose(sc, amax / 448.0, rtol=1e-5)
+            assert np.all(np.abs(got - rows) <= np.maximum(np.abs(rows) * 2.0 ** -3, sc[:, None] * 2.0 ** -9) + 1e-30)
+        else:
+            codes, sc = down(out_t)[b, sl], down(out_s)[b, sl]
+            got = OF.dequantize_mxfp4(codes, sc)
+            # re-quantising the oracle's value must land within one code of the GPU's
+            wc, ws = OF.quantize_mxfp4(rows.astype(np.float32))
+            assert np.all(np.abs(sc.astype(int) - ws.astype(int)) <= 1)
+            step = np.repeat(np.exp2(sc.astype(np.float64) - 127), 32, axis=1)
+            assert np.all(np.abs(got - rows) <= 2 * step + 1e-30)
+    # rows outside the requested blocks are untouched
+    if out_dt == "f32":
+        assert np.all(np.isnan(down(out_t)[2]))
+
+
+# ----------------------------------------------------------------------------- indexer
+
+
+def _index_case(name, B, Tq, HI, dI, N, m, kfmt):
+    r = _rng(name)
+    q = r.standard_normal((B, Tq, HI, dI)).astype(np.float32)
+    w = r.standard_normal((B, Tq, HI)).astype(np.float32)
+    kraw = r.standard_normal((B, N, dI)).astype(np.float32)
+    # ragged visibility: positions spread over [0, N*m) plus the full cache
+    pos = r.integers(0, N * m, (B, Tq)).astype(np.int32)
+    pos[0, 0] = N * m - 1
+    return q, w, kraw, pos
+
+
+@pytest.mark.parametrize("B,Tq,HI,dI,N,kfmt", [
+    (1, 1, 4, 32, 1024, "f32"), (2, 3, 4, 32, 777, "f32"),
+    (2, 1, 8, 64, 5000, "bf16"), (1, 37, 8, 64, 3000, "bf16"),
+    (3, 1, 8, 64, 9000, "mxfp4"), (2, 5, 8, 64, 4100, "mxfp4"), (1, 1, 32, 64, 700, "mxfp4"),
+])
+def test_index_scores(gpu_lib, B, Tq, HI, dI, N, kfmt):
+    csa = gpu_lib
+    m = 4
+    q, w, kraw, pos = _index_case(f"idx{B}{Tq}{HI}{N}{kfmt}", B, Tq, HI, dI, N, m, kfmt)
+    if kfmt == "f32":
+        qt, qv = up(q), q.astype(np.float64)
+        kt, kv = up(kraw), kraw.astype(np.float64)
+        qd, kd = csa.desc(qt, csa.F32), csa.desc(kt, csa.F32)
+    elif kfmt == "bf16":
+        qt, qv = up_bf16(q)
+        kt, kv = up_bf16(kraw)
+        qd, kd = csa.desc(qt, csa.BF16), csa.desc(kt, csa.BF16)
+    else:
+        qt = up(q)
+        qc, qs = OF.quantize_mxfp4(q)
+        qv = OF.dequantize_mxfp4(qc, qs)
+        kc, ks = OF.quantize_mxfp4(kraw)
+        kv = OF.dequantize_mxfp4(kc, ks)
+        kt, kst = up(kc), up(ks)
+        qd, kd = csa.desc(qt, csa.F32), csa.desc(kt, csa.MXFP4, kst)
+    scores = torch.full((B, Tq, N), float("nan"), device="cuda")
+    csa.csa_index_scores(qd, up(w), kd, up(pos), B, Tq, HI, dI, m, N, scores)
+    got = down(scores)
+    want = oracle.index_scores(qv, w.astype(np.float64), kv, pos, m, n_cap=N)
+    inf = np.isinf(want)
+    np.testing.assert_array_equal(np.isinf(got), inf)
+    assert not np.any(np.isnan(got))
+    fin_w = np.where(inf, 0.0, want)
+    fin_g = np.where(inf, 0.0, got)
+    assert row_rel_err(fin_g, fin_w) < 2e-6
+
+
+# ----------------------------------------------------------------------------- top-k
+
+
+@pytest.mark.parametrize("B,Tq,N,k,mode", [
+    (1, 1, 1024, 32, "normal"), (2, 4, 16896, 512, "normal"), (1, 3, 5000, 512, "ties"),
+    (2, 2, 3000, 100, "short"), (2, 1, 40000, 2048, "normal"), (1, 2, 70000, 1024, "ties"),
+    (1, 1, 30000, 700, "equal"), (3, 1, 262144, 2048, "normal"),
+])
+def test_topk_exact(gpu_lib, B, Tq, N, k, mode):
+    csa = gpu_lib
+    m = 4
+    r = _rng(f"topk{B}{Tq}{N}{k}{mode}")
+    if mode == "ties":
+        s = r.integers(-20, 20, (B, Tq, N)).astype(np.float32)
+        s[s == 0] = np.where(r.random(int((s == 0).sum())) < 0.5, -0.0, 0.0).astype(np.float32)
+    elif mode == "equal":
+        s = np.zeros((B, Tq, N), np.float32)
+    else:
+        s = r.standard_normal((B, Tq, N)).astype(np.float32)
+    pos = np.full((B, Tq), N * m - 1, np.int32)
+    if mode == "short":
+        pos[:, 0] = 4 * 40 - 1  # only 40 visible < k: padding
+        pos[-1, -1] = 4 * 100 - 1  # exactly k visible
+    elif Tq > 1:
+        pos[0, 1] = (N // 2) * m + 2  # a shorter row
+    idx = torch.full((B, Tq, k), -7, dtype=torch.int32, device="cuda")
+    ws = workspace(csa.csa_topk_workspace_size(B, Tq, N, k))
+    csa.csa_topk(up(s), up(pos), B, Tq, N, m, k, idx, ws, ws.numel())
+    got = down(idx)
+    want = oracle.topk(s.astype(np.float64), pos, m, k)
+    np.testing.assert_array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def _attn_inputs(name, B, Tq, H, D, N, R, kv_fmt):
+    r = _rng(name)
+    q = r.standard_normal((B, Tq, H, D)).astype(np.float32)
+    kvc = r.standard_normal((B, N, D)).astype(np.float32)
+    raw = r.standard_normal((B, R, D)).astype(np.float32)
+    return r, q, kvc, raw
+
+
+def _store_kv(csa, x, fmt):
+    B, N, D = x.shape
+    if fmt == "f32":
+        return csa.desc(up(x), csa.F32), x.astype(np.float64), None
+    if fmt == "bf16":
+        t, v = up_bf16(x)
+        return csa.desc(t, csa.BF16), v, t
+    c, s = OF.quantize_fp8_rows(x.reshape(-1, D))
+    t, st = up(c.reshape(B, N, D)), up(s.reshape(B, N))
+    return csa.desc(t, csa.FP8_E4M3, st), OF.dequantize_fp8_rows(c, s).reshape(B, N, D), (t, st)
+
+
+@pytest.mark.parametrize("B,Tq,H,D,k,W,fmt,tol", [
+    (1, 1, 16, 128, 32, 64, "f32", 1e-5),
+    (2, 1, 64, 512, 300, 128, "bf16", 2e-3),   # several splits + ragged tail
+    (3, 1, 64, 512, 40, 7, "bf16", 2e-3),
+    (1, 6, 32, 512, 100, 50, "bf16", 2e-3),    # several queries, one split each
+    (2, 1, 48, 512, 520, 128, "fp8", 5e-3),
+    (2, 1, 16, 512, 17, 1, "bf16", 2e-3),
+])
+def test_csa_sparse_attn(gpu_lib, B, Tq, H, D, k, W, fmt, tol):
+    csa = gpu_lib
+    m, N = 4, 4096
+    R = 1024
+    r, q, kvc, raw = _attn_inputs(f"csa{B}{Tq}{H}{k}{W}{fmt}", B, Tq, H, D, N, R, fmt)
+    # consecutive positions per sequence (a prefill chunk when Tq > 1); sequence 0 starts
+    # early, so it has few visible blocks (k slots padded with -1) and a short window
+    start = r.integers(N * m // 2, N * m - Tq, B)
+    start[0] = 3 + (W if W < 8 else 0)
+    pos = (start[:, None] + np.arange(Tq)[None]).astype(np.int32)
+    raw_base = np.maximum(0, pos[:, 0] - W - 5).astype(np.int32)
+    assert all(int(pos[b].max()) - raw_base[b] < R for b in range(B))
+    idx = np.stack([[sorted_unique_choice(r, oracle.visible_blocks(int(pos[b, t]), m), k) for t in range(Tq)]
+                    for b in range(B)])
+    qd = csa.desc(up(q), csa.F32) if fmt == "f32" else csa.desc(up_bf16(q)[0], csa.BF16)
+    qv = q.astype(np.float64) if fmt == "f32" else up_bf16(q)[1]
+    kvd, kvv, _ = _store_kv(csa, kvc, fmt)
+    rawd, rawv, _ = _store_kv(csa, raw, fmt)
+    out = torch.full((B, Tq, H, D), float("nan"), device="cuda")
+    lse = torch.full((B, Tq, H), float("nan"), device="cuda")
+    ws = workspace(csa.csa_attn_workspace_size(B, Tq, H, D, k + W))
+    scale = 1 / np.sqrt(128)
+    csa.csa_sparse_attn(qd, kvd, up(idx.astype(np.int32)), k, rawd, up(raw_base), W, up(pos), B, Tq, H, D, scale,
+                        out, lse, ws, ws.numel())
+    want, want_lse = oracle.csa_sparse_attn(qv, kvv, idx, rawv, raw_base, W, pos, scale)
+    assert row_rel_err(down(out), want) < tol
+    assert np.max(np.abs(down(lse) - want_lse)) < tol
+
+
+@pytest.mark.parametrize("B,H,mhc,ncap,W,fmt,tol", [
+    (4, 64, 128, 40, 128, "bf16", 2e-3),
+    (3, 64, 16, 700, 33, "bf16", 2e-3),
+    (2, 32, 128, 20, 128, "fp8", 5e-3),
+])
+def test_hca_attn(gpu_lib, B, H, mhc, ncap, W, fmt, tol):
+    csa = gpu_lib
+    D, Tq = 512, 1
+    R = 512
+    r, q, kvh, raw = _attn_inputs(f"hca{B}{H}{mhc}{ncap}{fmt}", B, Tq, H, D, ncap, R, fmt)
+    pos = r.integers(mhc * ncap // 2, mhc * ncap, (B, Tq)).astype(np.int32)
+    pos[0, 0] = mhc - 2  # no complete block yet: window only
+    raw_base = np.maximum(0, pos[:, 0] - W - 3).astype(np.int32)
+    qd, qv = csa.desc(up_bf16(q)[0], csa.BF16), up_bf16(q)[1]
+    kvd, kvv, _ = _store_kv(csa, kvh, fmt)
+    rawd, rawv, _ = _store_kv(csa, raw, fmt)
+    out = torch.full((B, Tq, H, D), float("nan"), device="cuda")
+    lse = torch.full((B, Tq, H), float("nan"), device="cuda")
+    ws = workspace(csa.csa_attn_workspace_size(B, Tq, H, D, ncap + W))
+    scale = 1 / np.sqrt(128)
+    csa.hca_attn(qd, kvd, mhc, ncap, rawd, up(raw_base), W, up(pos), B, Tq, H, D, scale, out, lse, ws, ws.numel())
+    want, want_lse = oracle.hca_attn(qv, kvv, mhc, rawv, raw_base, W, pos, scale)
+    assert row_rel_err(down(out), want) < tol
+    assert np.max(np.abs(down(lse) - want_lse)) < tol
+
+
+def test_attention_deterministic_and_batch_invariant(gpu_lib):
+    """Same inputs give bitwise the same outputs, and a sequence's result does not
+    depend on the other sequences in the batch."""
+    csa = gpu_lib
+    B, H, D, N, k, W, m = 4, 64, 512, 2048, 600, 128, 4
+    r, q, kvc, raw = _attn_inputs("det", B, 1, H, D, N, 512, "bf16")
+    pos = np.full((B, 1), N * m - 1, np.int32)
+    raw_base = (pos[:, 0] - 300).astype(np.int32)
+    idx = np.stack([[sorted_unique_choice(r, N, k)] for _ in range(B)]).astype(np.int32)
+    qt = up_bf16(q)[0]
+    kt = up_bf16(kvc)[0]
+    rt = up_bf16(raw)[0]
+
+    def run(sel):
+        nb = len(sel)
+        out = torch.empty((nb, 1, H, D), device="cuda")
+        lse = torch.empty((nb, 1, H), device="cuda")
+        ws = workspace(csa.csa_attn_workspace_size(nb, 1, H, D, k + W))
+        qs, ks, rs = qt[sel].contiguous(), kt[sel].contiguous(), rt[sel].contiguous()
+        csa.csa_sparse_attn(csa.desc(qs, csa.BF16), csa.desc(ks, csa.BF16), up(idx[sel]), k, csa.desc(rs, csa.BF16),
+                            up(raw_base[sel]), W, up(pos[sel]), nb, 1, H, D, 0.088, out, lse, ws, ws.numel())
+        return down(out), down(lse)
+
+    a = run([0, 1, 2, 3])
+    b = run([0, 1, 2, 3])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    for i in range(B):
+        s = run([i])
+        assert np.array_equal(s[0][0], a[0][i]) and np.array_equal(s[1][0], a[1][i])
