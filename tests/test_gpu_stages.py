@@ -114,7 +114,8 @@ def test_compress(gpu_lib, m, dim, in_dt, out_dt):
         elif out_dt == "bf16":
             got = down(out_t)[b, sl]
             # one bf16 rounding of an fp32-accumulated value: within one bf16 ulp
-            assert np.all(np.abs(got - rows) <= np.abs(rows) * 2.0 ** -7 + 1e-30)
+            # (absolute part: a merge cancelling to near zero keeps its terms' fp32 error)
+            assert np.all(np.abs(got - rows) <= np.abs(rows) * 2.0 ** -7 + 1e-6)
         elif out_dt == "fp8":
             codes, sc = down(out_t)[b, sl], down(out_s)[b, sl]
             got = OF.dequantize_fp8_rows(codes, sc)
