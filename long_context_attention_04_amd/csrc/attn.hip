@@ -95,53 +95,78 @@ __device__ __forceinline__ v8bf load8(const uint8_t* p, int col) {
   }
 }
 
+// Workgroup -> (row, split, head group).  Consecutive workgroup ids go to
+// different XCDs (round robin over 8), so the nhg head groups of one
+// (row, split) get ids 8 apart: same XCD, same L2, run side by side, and the
+// entry rows the first one fetches from HBM are L2 hits for the others.
+__device__ __forceinline__ void decode_block(int id, int nhg, int nsplit_max, int* row, int* split, int* hg) {
+  *hg = (id / 8) % nhg;
+  const int c = (id / (8 * nhg)) * 8 + id % 8;  // (row, split) pair
+  *row = c / nsplit_max;
+  *split = c % nsplit_max;
+}
+
 template <int NHT, bool FP8>
-__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a, int split, int nsplit_max, int partial) {
-  const int s = blockIdx.x;
-  const int row = blockIdx.y;
+__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a, int split, int nsplit_max, int nhg,
+                                                             int partial, int64_t rows) {
+  constexpr int HW = 16 * NHT;       // heads in this workgroup
+  constexpr int TPH = 16 / NHT;      // softmax threads per head
+  constexpr int EPT = kTileE / TPH;  // entries per softmax thread
+  int row, s, hg;
+  decode_block(blockIdx.x, nhg, nsplit_max, &row, &s, &hg);
+  if (row >= rows) return;
   const RowInfo ri = row_info(a, row);
   const int nsplit = max(1, (ri.n_tot + split - 1) / split);
   if (s >= nsplit) return;
   const int e_begin = s * split, e_end = min(ri.n_tot, e_begin + split);
+  const int h0 = hg * HW;  // first head of this workgroup
 
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int g = lane / 16, n = lane % 16;
 
-  __shared__ float red[4][64][kTileE];
+  __shared__ float red[4][HW][kTileE];
   __shared__ __attribute__((aligned(16))) uint16_t Es[4][kTileE][kEsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[2][64][kPsStride];  // P = hi + lo, both bf16
-  __shared__ float al[64];
-  __shared__ float ev_scale[kTileE];  // 0 for an empty slot
-  __shared__ float fin_m[64], fin_l[64];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[2][HW][kPsStride];  // P = hi + lo, both bf16
+  __shared__ float al[HW];
+  __shared__ float ev_scale[2][kTileE];  // per tile parity; 0 marks an empty slot
+  __shared__ float fin_m[HW], fin_l[HW];
 
-  // q operands: head 16*ht + n, latent columns 128w + 32kk + 8g .. +7
+  // q operands: head h0 + 16*ht + n, latent columns 128w + 32kk + 8g .. +7
   v8bf qa[NHT][4];
   const uint16_t* qp = (const uint16_t*)a.q.data + (int64_t)ri.b * a.q.sb + (int64_t)ri.t * a.q.sr;
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qa[ht][kk] = *(const v8bf*)(qp + (16 * ht + n) * 512 + 128 * w + 32 * kk + 8 * g);
+    for (int kk = 0; kk < 4; ++kk)
+      qa[ht][kk] = *(const v8bf*)(qp + (h0 + 16 * ht + n) * 512 + 128 * w + 32 * kk + 8 * g);
 
   const float sl2 = a.scale * kLog2e;
-  float m_run = kNegInf, l_run = 0.f;  // softmax lanes: head 16w + lane/4
+  // softmax role: thread -> head sh = tid / TPH, entries EPT*(tid % TPH) .. +EPT-1 of each tile
+  const int sh = threadIdx.x / TPH, seb = EPT * (threadIdx.x % TPH);
+  float m_run = kNegInf, l_run = 0.f;
   v4f O[NHT][8];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) O[ht][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  for (int e0 = e_begin; e0 < e_end; e0 += kTileE) {
-    v8bf bq[2][4];
+  // software pipeline: the next tile's rows are in flight while this one is processed
+  v8bf bq[2][4];
+  auto load_tile = [&](int e0, int par) {
 #pragma unroll
     for (int et = 0; et < 2; ++et) {
       const int e = e0 + 16 * et + n;
       float sc;
       const uint8_t* p = e < e_end ? entry_ptr(a, ri, row, e, &sc) : nullptr;
-      if (w == 0 && g == 0) ev_scale[16 * et + n] = p ? (FP8 ? sc : 1.f) : 0.f;
+      if (w == 0 && g == 0) ev_scale[par][16 * et + n] = p ? (FP8 ? sc : 1.f) : 0.f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) bq[et][kk] = load8<FP8>(p, 128 * w + 32 * kk + 8 * g);
     }
-    // partial logits over this wave's 128 columns
+  };
+  load_tile(e_begin, 0);
+  int par = 0;
+  for (int e0 = e_begin; e0 < e_end; e0 += kTileE, par ^= 1) {
+    // partial logits over this wave's 128 columns; stage the slice for PV
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
@@ -156,50 +181,44 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a, int spl
     for (int et = 0; et < 2; ++et)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) *(v8bf*)&Es[w][16 * et + n][32 * kk + 8 * g] = bq[et][kk];
+    if (e0 + kTileE < e_end) load_tile(e0 + kTileE, par ^ 1);
     __syncthreads();
 
-    if (w < NHT) {  // online softmax of head tile w: lane -> head 16w + lane/4, entries 8*(lane%4) .. +7
-      const int h = 16 * w + lane / 4, eb = 8 * (lane % 4);
-      float sv[8], esc[8];
+    {  // online softmax: every thread owns EPT entries of one head
+      float sv[EPT], esc[EPT];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        esc[i] = ev_scale[eb + i];
-        const float x = ((red[0][h][eb + i] + red[1][h][eb + i]) + red[2][h][eb + i]) + red[3][h][eb + i];
+      for (int i = 0; i < EPT; ++i) {
+        esc[i] = ev_scale[par][seb + i];
+        const float x = ((red[0][sh][seb + i] + red[1][sh][seb + i]) + red[2][sh][seb + i]) + red[3][sh][seb + i];
         sv[i] = esc[i] != 0.f ? x * esc[i] * sl2 : kNegInf;
       }
       float tmax = sv[0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sv[i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 1));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 2));
+      for (int i = 1; i < EPT; ++i) tmax = fmaxf(tmax, sv[i]);
+#pragma unroll
+      for (int o = 1; o < TPH; o <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = m_new == kNegInf ? 1.f : exp2f(m_run - m_new);
       float psum = 0.f;
-      uint16_t pb[8], pl[8];
+      uint16_t ph[EPT], plo[EPT];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < EPT; ++i) {
         const float p = m_new == kNegInf ? 0.f : exp2f(sv[i] - m_new);
         psum += p;
         const float pv = FP8 ? p * esc[i] : p;
-        pb[i] = f32_to_bf16_bits(pv);
-        pl[i] = f32_to_bf16_bits(pv - bf16_bits_to_f32(pb[i]));  // exact remainder, rounded once more
+        ph[i] = f32_to_bf16_bits(pv);
+        plo[i] = f32_to_bf16_bits(pv - bf16_bits_to_f32(ph[i]));  // exact remainder, rounded once more
       }
-      psum += __shfl_xor(psum, 1);
-      psum += __shfl_xor(psum, 2);
+#pragma unroll
+      for (int o = 1; o < TPH; o <<= 1) psum += __shfl_xor(psum, o);
       l_run = l_run * alpha + psum;
       m_run = m_new;
-      uint4 pk;
-      pk.x = pb[0] | ((uint32_t)pb[1] << 16);
-      pk.y = pb[2] | ((uint32_t)pb[3] << 16);
-      pk.z = pb[4] | ((uint32_t)pb[5] << 16);
-      pk.w = pb[6] | ((uint32_t)pb[7] << 16);
-      *(uint4*)&Ps[0][h][eb] = pk;
-      pk.x = pl[0] | ((uint32_t)pl[1] << 16);
-      pk.y = pl[2] | ((uint32_t)pl[3] << 16);
-      pk.z = pl[4] | ((uint32_t)pl[5] << 16);
-      pk.w = pl[6] | ((uint32_t)pl[7] << 16);
-      *(uint4*)&Ps[1][h][eb] = pk;
-      if ((lane & 3) == 0) al[h] = alpha;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        Ps[0][sh][seb + i] = ph[i];
+        Ps[1][sh][seb + i] = plo[i];
+      }
+      if (threadIdx.x % TPH == 0) al[sh] = alpha;
     }
     __syncthreads();
 
@@ -229,69 +248,89 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a, int spl
     }
   }
 
-  if (w < NHT && (lane & 3) == 0) {
-    fin_m[16 * w + lane / 4] = m_run;
-    fin_l[16 * w + lane / 4] = l_run;
+  if (threadIdx.x % TPH == 0) {
+    fin_m[sh] = m_run;
+    fin_l[sh] = l_run;
   }
   __syncthreads();
   const int H = a.heads;
   if (partial) {
-    float* po = (float*)a.ws + (((int64_t)row * nsplit_max + s) * H) * 512;
+    float* po = (float*)a.ws + (((int64_t)row * nsplit_max + s) * H + h0) * 512;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r) po[(16 * ht + 4 * g + r) * 512 + 128 * w + 16 * ct + n] = O[ht][ct][r];
-    float* pml = (float*)a.ws + (int64_t)gridDim.y * nsplit_max * H * 512 + (((int64_t)row * nsplit_max + s) * H) * 2;
-    if (threadIdx.x < H) {
+    float* pml = (float*)a.ws + rows * nsplit_max * H * 512 + (((int64_t)row * nsplit_max + s) * H + h0) * 2;
+    if (threadIdx.x < HW) {
       pml[2 * threadIdx.x] = fin_m[threadIdx.x];
       pml[2 * threadIdx.x + 1] = fin_l[threadIdx.x];
     }
   } else {
-    float* po = a.out + (int64_t)row * H * 512;
+    float* po = a.out + ((int64_t)row * H + h0) * 512;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 16 * ht + 4 * g + r;
         const float L = fin_l[h];
-        const float f = L > 0.f ? 1.0f * __fdiv_rn(1.0f, L) : 0.f;
+        const float f = L > 0.f ? __fdiv_rn(1.0f, L) : 0.f;
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) po[h * 512 + 128 * w + 16 * ct + n] = O[ht][ct][r] * f;
       }
-    if (a.lse && threadIdx.x < H) {
+    if (a.lse && threadIdx.x < HW) {
       const float L = fin_l[threadIdx.x];
-      a.lse[(int64_t)row * H + threadIdx.x] = L > 0.f ? (fin_m[threadIdx.x] + log2f(L)) * kLn2 : kNegInf;
+      a.lse[(int64_t)row * H + h0 + threadIdx.x] = L > 0.f ? (fin_m[threadIdx.x] + log2f(L)) * kLn2 : kNegInf;
     }
   }
 }
 
-// Fixed-order log-sum-exp merge of the splits of one (row, head).
-__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int split, int nsplit_max, int dim) {
+// Fixed-order log-sum-exp merge of the splits of one (row, head); one pass over
+// the partials with every split's row in flight at once.
+constexpr int kMergeMaxSplits = 64;
+
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int split, int nsplit_max, int64_t rows) {
   const int row = blockIdx.x, h = blockIdx.y;
   const RowInfo ri = row_info(a, row);
-  const int nsplit = max(1, (ri.n_tot + split - 1) / split);
+  const int nsplit = min(kMergeMaxSplits, max(1, (ri.n_tot + split - 1) / split));
   const int H = a.heads;
-  const float* pml = (const float*)a.ws + (int64_t)gridDim.x * nsplit_max * H * dim;
-  float M = kNegInf;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pml[(((int64_t)row * nsplit_max + s) * H + h) * 2]);
-  float L = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
+  const float* pml = (const float*)a.ws + rows * nsplit_max * H * 512;
+  __shared__ float wts[kMergeMaxSplits];
+  __shared__ float sh_L, sh_M;
+  if (threadIdx.x < kWave) {  // one wave forms the split weights
+    const int s = threadIdx.x;
     const int64_t o = (((int64_t)row * nsplit_max + s) * H + h) * 2;
-    L += M == kNegInf ? 0.f : pml[o + 1] * exp2f(pml[o] - M);
-  }
-  const float inv = L > 0.f ? __fdiv_rn(1.0f, L) : 0.f;
-  for (int c = threadIdx.x; c < dim; c += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const int64_t base = ((int64_t)row * nsplit_max + s) * H + h;
-      const float wgt = M == kNegInf ? 0.f : exp2f(pml[base * 2] - M) * inv;
-      acc = fmaf(((const float*)a.ws)[base * dim + c], wgt, acc);
+    const float ms = s < nsplit ? pml[o] : kNegInf;
+    const float ls = s < nsplit ? pml[o + 1] : 0.f;
+    const float M = wave_max(ms);
+    const float e = (M == kNegInf || s >= nsplit) ? 0.f : exp2f(ms - M);
+    // L = sum over splits in ascending order (fixed, independent of scheduling)
+    float L = 0.f;
+    for (int i = 0; i < nsplit; ++i) L += __shfl(ls * e, i);
+    if (s < kMergeMaxSplits) wts[s] = e;
+    if (s == 0) {
+      sh_L = L;
+      sh_M = M;
     }
-    a.out[((int64_t)row * H + h) * dim + c] = acc;
   }
-  if (a.lse && threadIdx.x == 0) a.lse[(int64_t)row * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+  __syncthreads();
+  const float L = sh_L;
+  const float inv = L > 0.f ? __fdiv_rn(1.0f, L) : 0.f;
+  const float4* src = (const float4*)((const float*)a.ws + ((int64_t)row * nsplit_max * H + h) * 512) + threadIdx.x;
+  const int64_t sstride = (int64_t)H * 512 / 4;  // float4s between consecutive splits
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int s = 0; s < nsplit; ++s) {
+    const float wgt = wts[s] * inv;
+    const float4 v = src[s * sstride];
+    acc.x = fmaf(v.x, wgt, acc.x);
+    acc.y = fmaf(v.y, wgt, acc.y);
+    acc.z = fmaf(v.z, wgt, acc.z);
+    acc.w = fmaf(v.w, wgt, acc.w);
+  }
+  ((float4*)(a.out + ((int64_t)row * H + h) * 512))[threadIdx.x] = acc;
+  if (a.lse && threadIdx.x == 0) a.lse[(int64_t)row * H + h] = L > 0.f ? (sh_M + log2f(L)) * kLn2 : kNegInf;
 }
 
 // ------------------------------------------------------------------ fp32 VALU path
@@ -352,18 +391,28 @@ __global__ __launch_bounds__(kPlainThreads) void attn_plain_kernel(AttnArgs a) {
 template <int NHT>
 hipError_t launch_mfma(const AttnArgs& a, int64_t rows, int split, int nsplit_max, hipStream_t s) {
   const int partial = nsplit_max > 1;
-  dim3 grid(nsplit_max, (unsigned)rows);
+  const int nhg = a.heads / (16 * NHT);
+  const int64_t pairs = rows * nsplit_max;
+  const int64_t blocks = (pairs + 7) / 8 * 8 * nhg;
   if (a.kv.dtype == CSA_FP8_E4M3)
-    hipLaunchKernelGGL((attn_mfma_kernel<NHT, true>), grid, dim3(kThreads), 0, s, a, split, nsplit_max, partial);
+    hipLaunchKernelGGL((attn_mfma_kernel<NHT, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a, split,
+                       nsplit_max, nhg, partial, rows);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<NHT, false>), grid, dim3(kThreads), 0, s, a, split, nsplit_max, partial);
-  if (partial) hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)rows, a.heads), dim3(128), 0, s, a, split, nsplit_max, 512);
+    hipLaunchKernelGGL((attn_mfma_kernel<NHT, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a, split,
+                       nsplit_max, nhg, partial, rows);
+  if (partial)
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)rows, a.heads), dim3(128), 0, s, a, split, nsplit_max, rows);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int attn_split_size(int tq, int n_entries_max) { return tq == 1 ? kSplitDecode : max(n_entries_max, 1); }
+// Splits depend only on the call shape (decode or not) and the entry capacity,
+// never on the batch, so each sequence's arithmetic is batch-invariant.
+int attn_split_size(int tq, int n_entries_max) {
+  const int n = max(n_entries_max, 1);
+  return tq == 1 ? min(kSplitDecode, (n + kTileE - 1) / kTileE * kTileE) : n;
+}
 
 size_t attn_workspace_bytes(int64_t rows, int heads, int dim, int n_entries_max, int tq) {
   const int split = attn_split_size(tq, n_entries_max);
@@ -383,6 +432,10 @@ hipError_t launch_attention(const AttnArgs& a, int n_entries_max, hipStream_t s)
   }
   const int split = attn_split_size(a.tq, n_entries_max);
   const int nsplit_max = max(1, (n_entries_max + split - 1) / split);
+  if (nsplit_max > kMergeMaxSplits) return hipErrorInvalidValue;
+  // decode: 16 heads per workgroup (4x the workgroups, head groups share L2);
+  // many queries per call: every head in one workgroup (entry rows read once)
+  if (a.tq == 1) return launch_mfma<1>(a, rows, split, nsplit_max, s);
   switch (a.heads / 16) {
     case 1: return launch_mfma<1>(a, rows, split, nsplit_max, s);
     case 2: return launch_mfma<2>(a, rows, split, nsplit_max, s);

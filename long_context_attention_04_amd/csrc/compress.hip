@@ -16,7 +16,7 @@ namespace csa {
 namespace {
 
 constexpr int kCompressThreads = 256;
-constexpr int kMaxDimPerThread = 16;  // dim <= 4096
+constexpr int kRowBatch = 4;
 
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
@@ -29,24 +29,34 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return r;
 }
 
-// Writes one finished fp32 row (thread t holds columns t + 256*i) in the output format.
-__device__ void store_row(const float* vals, int nv, int dim, int out_dtype, void* out, int64_t off,
-                          void* out_scale, int64_t soff, float* red) {
+// Writes one finished fp32 row (thread t holds columns t + 256*i, i < nv) in the output format.
+template <int NV>
+__device__ __forceinline__ void store_row(const float (&vals)[NV], int nv, int out_dtype, void* out, int64_t off,
+                                          void* out_scale, int64_t soff, float* red) {
   const int t = threadIdx.x;
   if (out_dtype == CSA_F32) {
-    for (int i = 0; i < nv; ++i) ((float*)out)[off + t + i * kCompressThreads] = vals[i];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (i < nv) ((float*)out)[off + t + i * kCompressThreads] = vals[i];
   } else if (out_dtype == CSA_BF16) {
-    for (int i = 0; i < nv; ++i) ((uint16_t*)out)[off + t + i * kCompressThreads] = f32_to_bf16_bits(vals[i]);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (i < nv) ((uint16_t*)out)[off + t + i * kCompressThreads] = f32_to_bf16_bits(vals[i]);
   } else if (out_dtype == CSA_FP8_E4M3) {
     float amax = 0.f;
-    for (int i = 0; i < nv; ++i) amax = fmaxf(amax, fabsf(vals[i]));
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (i < nv) amax = fmaxf(amax, fabsf(vals[i]));
     amax = block_max(amax, red);
     const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-    for (int i = 0; i < nv; ++i)
-      ((uint8_t*)out)[off + t + i * kCompressThreads] = (uint8_t)f32_to_e4m3(__fdiv_rn(vals[i], s));
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (i < nv) ((uint8_t*)out)[off + t + i * kCompressThreads] = (uint8_t)f32_to_e4m3(__fdiv_rn(vals[i], s));
     if (t == 0) ((float*)out_scale)[soff] = s;
   } else {  // MXFP4: 32 consecutive columns live in 32 consecutive lanes
-    for (int i = 0; i < nv; ++i) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (i >= nv) continue;
       const int col = t + i * kCompressThreads;
       float a = fabsf(vals[i]);
       for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 32));
@@ -59,6 +69,7 @@ __device__ void store_row(const float* vals, int nv, int dim, int out_dtype, voi
   }
 }
 
+template <int NV>  // columns per thread: dim <= 256 * NV
 __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs a) {
   const int b = blockIdx.y;
   const int i = blockIdx.x;
@@ -68,12 +79,14 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
   __shared__ float omega[1024];
   __shared__ float red[kCompressThreads / kWave];
   // omega = softmax(logits) in fp32, max-subtracted, summed in ascending offset order
-  if (threadIdx.x == 0) {
-    float mx = a.logits[0];
-    for (int r = 1; r < a.m; ++r) mx = fmaxf(mx, a.logits[r]);
+  for (int r = threadIdx.x; r < a.m; r += kCompressThreads) omega[r] = a.logits[r];
+  __syncthreads();
+  if (threadIdx.x == 0) {  // max, exponentials and their sum in ascending offset order
+    float mx = omega[0];
+    for (int r = 1; r < a.m; ++r) mx = fmaxf(mx, omega[r]);
     float sum = 0.f;
     for (int r = 0; r < a.m; ++r) {
-      const float e = expf(a.logits[r] - mx);
+      const float e = expf(omega[r] - mx);
       omega[r] = e;
       sum += e;
     }
@@ -81,25 +94,43 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
   }
   __syncthreads();
   const int64_t row0 = (int64_t)j * a.m - a.raw_base[b];
-  float acc[kMaxDimPerThread];
+  float acc[NV];
   const int nv = (a.dim - threadIdx.x + kCompressThreads - 1) / kCompressThreads;
-  for (int v = 0; v < nv; ++v) acc[v] = 0.f;
-  for (int r = 0; r < a.m; ++r) {
-    const int64_t base = (int64_t)b * a.raw.sb + (row0 + r) * a.raw.sr;
-    float rs = 1.f;
-    if (a.raw.dtype == CSA_FP8_E4M3 && a.raw.scale)
-      rs = ((const float*)a.raw.scale)[(int64_t)b * a.raw.ssb + (row0 + r) * a.raw.ssr];
-    const float w = omega[r];
-    for (int v = 0; v < nv; ++v) {
-      const int col = threadIdx.x + v * kCompressThreads;
-      float x = load_elem(a.raw.data, a.raw.dtype, base + col);
-      if (a.raw.dtype == CSA_FP8_E4M3) x *= rs;
-      acc[v] = fmaf(w, x, acc[v]);
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = 0.f;
+  // rows in groups of kRowBatch: all loads of a group are issued before its FMAs
+  // (terms are still added in ascending offset order)
+  for (int r0 = 0; r0 < a.m; r0 += kRowBatch) {
+    float x[kRowBatch][NV];
+    float rs[kRowBatch];
+#pragma unroll
+    for (int j = 0; j < kRowBatch; ++j) {
+      const int r = r0 + j;
+      rs[j] = 1.f;
+      if (r >= a.m) continue;
+      const int64_t base = (int64_t)b * a.raw.sb + (row0 + r) * a.raw.sr;
+      if (a.raw.dtype == CSA_FP8_E4M3 && a.raw.scale)
+        rs[j] = ((const float*)a.raw.scale)[(int64_t)b * a.raw.ssb + (row0 + r) * a.raw.ssr];
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        x[j][v] = v < nv ? load_elem(a.raw.data, a.raw.dtype, base + threadIdx.x + v * kCompressThreads) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kRowBatch; ++j) {
+      if (r0 + j < a.m) {
+        const float w = omega[r0 + j];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          float xv = x[j][v];
+          if (a.raw.dtype == CSA_FP8_E4M3) xv *= rs[j];
+          acc[v] = fmaf(w, xv, acc[v]);
+        }
+      }
     }
   }
   const int64_t off = (int64_t)b * a.out_sb + (int64_t)j * a.out_sr;
   const int64_t soff = (int64_t)b * a.out_ssb + (int64_t)j * a.out_ssr;
-  store_row(acc, nv, a.dim, a.out_dtype, a.out, off, a.out_scale, soff, red);
+  store_row<NV>(acc, nv, a.out_dtype, a.out, off, a.out_scale, soff, red);
 }
 
 // one thread per 32-element block
@@ -148,7 +179,12 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const float* __restri
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.max_blocks <= 0 || a.batch <= 0) return hipSuccess;
   dim3 grid(a.max_blocks, a.batch);
-  hipLaunchKernelGGL(compress_kernel, grid, dim3(kCompressThreads), 0, s, a);
+  const int nv = (a.dim + kCompressThreads - 1) / kCompressThreads;
+  if (nv <= 1) hipLaunchKernelGGL(compress_kernel<1>, grid, dim3(kCompressThreads), 0, s, a);
+  else if (nv <= 2) hipLaunchKernelGGL(compress_kernel<2>, grid, dim3(kCompressThreads), 0, s, a);
+  else if (nv <= 4) hipLaunchKernelGGL(compress_kernel<4>, grid, dim3(kCompressThreads), 0, s, a);
+  else if (nv <= 8) hipLaunchKernelGGL(compress_kernel<8>, grid, dim3(kCompressThreads), 0, s, a);
+  else hipLaunchKernelGGL(compress_kernel<16>, grid, dim3(kCompressThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -63,7 +63,7 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s);
 // ---------------------------------------------------------------- top-k
 // Rows longer than this are selected by the multi-workgroup path.
 constexpr int kTopkLdsMax = 20480;
-constexpr int kTopkSlice = 8192;  // keys per workgroup in the multi-workgroup path
+constexpr int kTopkSlice = 4096;  // keys per candidate workgroup on long rows
 size_t topk_workspace_bytes(int64_t rows, int n_cap, int k);
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int tq, int n_cap, int m, int k,
                        int32_t* idx, void* ws, hipStream_t s);
