@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA/HCA decode tokens/s at 1M ctx on 1 GPU; achieved HBM TB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 KEY_BYTES = 34  # MXFP4 indexer key: 64 e2m1 codes (32 B) + 2 e8m0 scales
-INDEX_KERNEL = "index_mxfp4_kernel"
+INDEX_KERNEL = "index_mxfp4_kernel<4>"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "index_mxfp4_csa_decode_1m_b8_pmc.txt")
 INDEX_SOURCE = os.path.join(ROOT, "long_context_attention_04_amd", "csrc", "index.hip")
 
@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the oracle's timed sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="repeat the oracle sample up to this long")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="also run one plain device copy of this size (a known-size reference for HBM counters)")
     return ap.parse_args()
 
 
@@ -285,6 +287,14 @@ def main():
         "stages_us_eager": stages,
         "roofline": roof,
     }
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(torch, layers[0], args.cpu_seqs, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -15,9 +15,10 @@
 // every entry row from HBM (16 B per lane, the MFMA B-operand layout), uses it
 // for its partial QK and stages it in LDS for PV, so every entry byte is read
 // from HBM once.  The four partial logit tiles are summed in a fixed order in
-// LDS; wave h owns the online softmax of head tile h.  The probabilities go
-// to PV as two bf16 terms (hi + lo), so PV carries ~16 significant bits of P
-// instead of bf16's 8; the staged slice is read back transposed from LDS.  Splits are merged by a second
+// LDS and all 256 threads run the online softmax.  The probabilities go to
+// PV as two bf16 terms (hi + lo), so PV carries ~16 significant bits of P
+// instead of bf16's 8; PV reads the staged slice transposed with
+// ds_read_b64_tr_b16.  Splits are merged by a second
 // kernel with a fixed-order log-sum-exp combine; the split size depends only
 // on the call shape, never on the batch, so results are batch-invariant.
 // fp8 rows keep their per-row scale out of the MFMA: it multiplies the logit
@@ -34,7 +35,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTileE = 32;
-constexpr int kSplitDecode = 256;
+constexpr int kSplitDecode = 128;
 constexpr int kEsStride = 136;  // bf16 elements per staged row (128 + 8 pad)
 constexpr int kPsStride = 40;   // bf16 elements per P row (32 + 8 pad)
 constexpr float kNegInf = -__builtin_inff();
@@ -60,11 +61,13 @@ __device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int row) {
 __device__ __forceinline__ int elem_bytes(int dtype) { return dtype == CSA_F32 ? 4 : dtype == CSA_BF16 ? 2 : 1; }
 
 // Byte pointer to entry e of a row's list (nullptr when the slot is empty) and its row scale.
-__device__ __forceinline__ const uint8_t* entry_ptr(const AttnArgs& a, const RowInfo& r, int row, int e, float* sc) {
+// `jl` (optional) holds the compressed indices of entries [jl_base, jl_base + kMaxSplit).
+__device__ __forceinline__ const uint8_t* entry_ptr(const AttnArgs& a, const RowInfo& r, int row, int e, float* sc,
+                                                    const int* jl = nullptr, int jl_base = 0) {
   *sc = 1.f;
   if (e >= r.n_tot) return nullptr;
   if (e < r.n_cmp) {
-    const int j = a.idx ? a.idx[(int64_t)row * a.k + e] : e;
+    const int j = a.idx ? (jl ? jl[e - jl_base] : a.idx[(int64_t)row * a.k + e]) : e;
     if (j < 0) return nullptr;
     if (a.kv.dtype == CSA_FP8_E4M3 && a.kv.scale) *sc = ((const float*)a.kv.scale)[(int64_t)r.b * a.kv.ssb + (int64_t)j * a.kv.ssr];
     return (const uint8_t*)a.kv.data + ((int64_t)r.b * a.kv.sb + (int64_t)j * a.kv.sr) * elem_bytes(a.kv.dtype);
@@ -130,6 +133,13 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a, int spl
   __shared__ float al[HW];
   __shared__ float ev_scale[2][kTileE];  // per tile parity; 0 marks an empty slot
   __shared__ float fin_m[HW], fin_l[HW];
+  __shared__ int jl[kSplitDecode];  // this split's compressed indices (decode splits)
+  const bool use_jl = a.idx != nullptr && split <= kSplitDecode;
+  if (use_jl) {
+    const int e = e_begin + (int)threadIdx.x;
+    if (threadIdx.x < kSplitDecode && e < min(e_end, ri.n_cmp)) jl[threadIdx.x] = a.idx[(int64_t)row * a.k + e];
+  }
+  __syncthreads();
 
   // q operands: head h0 + 16*ht + n, latent columns 128w + 32kk + 8g .. +7
   v8bf qa[NHT][4];
@@ -157,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a, int spl
     for (int et = 0; et < 2; ++et) {
       const int e = e0 + 16 * et + n;
       float sc;
-      const uint8_t* p = e < e_end ? entry_ptr(a, ri, row, e, &sc) : nullptr;
+      const uint8_t* p = e < e_end ? entry_ptr(a, ri, row, e, &sc, use_jl ? jl : nullptr, e_begin) : nullptr;
       if (w == 0 && g == 0) ev_scale[par][16 * et + n] = p ? (FP8 ? sc : 1.f) : 0.f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) bq[et][kk] = load8<FP8>(p, 128 * w + 32 * kk + 8 * g);
@@ -237,9 +247,15 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a, int spl
     }
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-      v8bf vb;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) vb[i] = __builtin_bit_cast(__bf16, Es[w][8 * g + i][16 * ct + n]);
+      // transposed read: lane (n, g) gets column 16ct+n of staged rows 8g..8g+3 (t0) and
+      // 8g+4..8g+7 (t1); the 16 lanes of a group address 4 rows x 4 column quads.
+      // (The bf16 form plus a shuffle is used on purpose: extracting elements of the
+      // i16 form one by one was miscompiled into reads of the first dword only.)
+      typedef __attribute__((address_space(3))) v4bf lds_v4bf;
+      const v4bf t0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)&Es[w][8 * g + n / 4][16 * ct + 4 * (n % 4)]);
+      const v4bf t1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)&Es[w][8 * g + 4 + n / 4][16 * ct + 4 * (n % 4)]);
+      const v8bf vb = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         O[ht][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[ht], vb, O[ht][ct], 0, 0, 0);

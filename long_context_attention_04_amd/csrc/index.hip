@@ -126,77 +126,98 @@ __global__ __launch_bounds__(256) void index_bf16_kernel(IndexArgs a) {
 }
 
 // ------------------------------------------------------------------ MXFP4 MFMA
-// heads <= 32, dim == 64.  Each wave streams groups of 32 keys; a workgroup of
-// 4 waves covers kFp4KeysPerWG keys of one query row.
-constexpr int kFp4KeysPerWave = 1024;
-constexpr int kFp4KeysPerWG = 4 * kFp4KeysPerWave;
+// heads <= 32, dim == 64.  Each wave scores one group of kFp4Unroll*32 keys:
+// it issues every key load of its group, the workgroup quantises the query
+// once (cooperatively, into LDS) while they are in flight, then each wave runs
+// one MFMA per 32 keys.  Short waves, many per SIMD,
+// keep the memory pipe full (a wave's own load latency overlaps the others').
 constexpr int kFp4Unroll = 8;
+constexpr int kFp4KeysPerWave = 32 * kFp4Unroll;
+constexpr int kFp4KeysPerWG = 4 * kFp4KeysPerWave;
 
+template <int NR>  // accumulator rows that can hold a real head: 4 (heads <= 8) or 16 (heads <= 32)
 __global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a) {
   const int row = blockIdx.y;
   const int b = row / a.tq, t = row % a.tq;
   const int wave = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int V = visible_blocks(a.q_pos[row], a.m);
-  const int wbase = blockIdx.x * kFp4KeysPerWG + wave * kFp4KeysPerWave;
-  if (wbase >= a.n_cap) return;
-
-  // A operand: row (head) m = l%32, K block kb = l/32, quantised to MXFP4 here.
+  const int g0 = blockIdx.x * kFp4KeysPerWG + wave * kFp4KeysPerWave;
   const int m = l % 32, kb = l / 32;
+  __shared__ __attribute__((aligned(16))) uint32_t qcode[32][2][4];  // [head][K block][16 B of e2m1 codes]
+  __shared__ uint32_t qscale[32][2];
+  __shared__ float wsh[32];
+  if (threadIdx.x < a.heads) wsh[threadIdx.x] = a.w[(int64_t)row * a.heads + threadIdx.x];
+
+  // 1) key codes (16 B per lane: key l%32's block l/32) and their e8m0 scales, issued
+  //    first so their latency overlaps the query quantisation below
+  const int kfirst = g0 + m;
+  const uint8_t* kc = (const uint8_t*)a.k.data + (int64_t)b * a.k.sb + (int64_t)kfirst * a.k.sr + 16 * kb;
+  const uint8_t* ks = (const uint8_t*)a.k.scale + (int64_t)b * a.k.ssb + (int64_t)kfirst * a.k.ssr + kb;
+  const int64_t cstep = 32 * a.k.sr, sstep = 32 * a.k.ssr;
+  v4i c[kFp4Unroll];
+  int sbk[kFp4Unroll];
+#pragma unroll
+  for (int u = 0; u < kFp4Unroll; ++u) {
+    const bool live = kfirst + 32 * u < V;
+    c[u] = live ? *(const v4i*)(kc + u * cstep) : (v4i){0, 0, 0, 0};
+    sbk[u] = live ? ks[u * sstep] : 127;
+  }
+  // 2) the query, quantised to MXFP4 once per workgroup: thread -> (head, K block,
+  //    element pair); the 16 threads of a 32-element block are 16 adjacent lanes
+  for (int pbase = 0; pbase < a.heads * 32; pbase += 256) {
+    const int pi = pbase + (int)threadIdx.x;
+    const int h = pi / 32, blk = (pi / 16) % 2, pr = pi % 16;
+    float2 x = make_float2(0.f, 0.f);
+    if (h < a.heads)
+      x = *(const float2*)((const float*)a.q.data + (int64_t)b * a.q.sb + (int64_t)t * a.q.sr + h * 64 + 32 * blk +
+                           2 * pr);
+    float amax = fmaxf(fabsf(x.x), fabsf(x.y));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    const int e = mx_scale_exp(amax);
+    const uint32_t byte = amax > 0.f ? (f32_to_e2m1(x.x, e) | (f32_to_e2m1(x.y, e) << 4)) : 0u;
+    // four adjacent pairs form one dword of codes
+    const uint32_t b1 = __shfl_down(byte, 1, 16), b2 = __shfl_down(byte, 2, 16), b3 = __shfl_down(byte, 3, 16);
+    if (h < a.heads) {
+      if ((pr & 3) == 0) qcode[h][blk][pr / 4] = byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      if (pr == 0) qscale[h][blk] = (uint32_t)(e + 127);
+    }
+  }
+  __syncthreads();
+  if (g0 >= a.n_cap) return;
   v8i A = {0, 0, 0, 0, 0, 0, 0, 0};
   int sa = 127;
   if (m < a.heads) {
-    const float* qp = (const float*)a.q.data + (int64_t)b * a.q.sb + (int64_t)t * a.q.sr + m * 64 + 32 * kb;
-    float v[32];
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) { v[i] = qp[i]; amax = fmaxf(amax, fabsf(v[i])); }
-    const int e = mx_scale_exp(amax);
-    sa = e + 127;
-    if (amax > 0.f) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) A[i / 8] |= (int)(f32_to_e2m1(v[i], e) << (4 * (i % 8)));
-    }
+    const uint4 qv = *(const uint4*)&qcode[m][kb][0];
+    A[0] = (int)qv.x; A[1] = (int)qv.y; A[2] = (int)qv.z; A[3] = (int)qv.w;
+    sa = (int)qscale[m][kb];
   }
-  // head weights for this lane's accumulator rows m = 8*(r/4) + 4*(l/32) + r%4
-  float wv[16];
+  // head weights of this lane's accumulator rows h = 8*(r/4) + 4*(l/32) + r%4
+  float wv[NR];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int h = 8 * (r / 4) + 4 * (l / 32) + (r % 4);
-    wv[r] = h < a.heads ? a.w[(int64_t)row * a.heads + h] : 0.f;
+  for (int r = 0; r < NR; ++r) {
+    const int h = 8 * (r / 4) + 4 * kb + (r % 4);
+    wv[r] = h < a.heads ? wsh[h] : 0.f;
   }
-  const uint8_t* kc = (const uint8_t*)a.k.data + (int64_t)b * a.k.sb + 16 * kb;
-  const uint8_t* ks = (const uint8_t*)a.k.scale + (int64_t)b * a.k.ssb + kb;
+  // 3) scores
   float* srow = a.scores + (int64_t)row * a.n_cap;
-  const int wend = min(wbase + kFp4KeysPerWave, a.n_cap);
-
-  for (int g0 = wbase; g0 < wend; g0 += 32 * kFp4Unroll) {
-    v4i codes[kFp4Unroll];
-    int sb[kFp4Unroll];
+  const int gend = min(g0 + kFp4KeysPerWave, a.n_cap);
 #pragma unroll
-    for (int u = 0; u < kFp4Unroll; ++u) {
-      const int key = g0 + 32 * u + (l % 32);
-      if (key < V) {
-        codes[u] = *(const v4i*)(kc + (int64_t)key * a.k.sr);
-        sb[u] = ks[(int64_t)key * a.k.ssr];
-      } else {
-        codes[u] = (v4i){0, 0, 0, 0};
-        sb[u] = 127;
-      }
-    }
+  for (int u = 0; u < kFp4Unroll; ++u) {
+    v8i Bop = {c[u][0], c[u][1], c[u][2], c[u][3], 0, 0, 0, 0};
+    v16f acc;
 #pragma unroll
-    for (int u = 0; u < kFp4Unroll; ++u) {
-      v8i Bop = {codes[u][0], codes[u][1], codes[u][2], codes[u][3], 0, 0, 0, 0};
-      v16f c;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bop, acc, 4, 4, 0, sa, 0, sbk[u]);
+    float part = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) c[r] = 0.f;
-      c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bop, c, 4, 4, 0, sa, 0, sb[u]);
-      float part = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) part = fmaf(wv[r], fmaxf(c[r], 0.f), part);
-      const float other = __shfl_xor(part, 32);
-      const int key = g0 + 32 * u + l;
-      if (l < 32 && key < wend) srow[key] = key < V ? part + other : kNegInf;
-    }
+    for (int r = 0; r < NR; ++r) part = fmaf(wv[r], fmaxf(acc[r], 0.f), part);
+    const float other = __shfl_xor(part, 32);
+    const int key = g0 + 32 * u + l;
+    if (l < 32 && key < gend) srow[key] = key < V ? part + other : kNegInf;
+    // keep one accumulator tile live at a time: occupancy (many waves hiding each
+    // other's memory latency) matters more here than MFMA back-to-back issue
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -207,7 +228,10 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
   if (rows == 0 || a.n_cap == 0) return hipSuccess;
   if (a.k.dtype == CSA_MXFP4) {
     dim3 grid((a.n_cap + kFp4KeysPerWG - 1) / kFp4KeysPerWG, rows);
-    hipLaunchKernelGGL(index_mxfp4_kernel, grid, dim3(256), 0, s, a);
+    if (a.heads <= 8)
+      hipLaunchKernelGGL(index_mxfp4_kernel<4>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(index_mxfp4_kernel<16>, grid, dim3(256), 0, s, a);
   } else if (a.k.dtype == CSA_BF16 && a.q.dtype == CSA_BF16 && a.heads == 8 && a.dim == 64) {
     dim3 grid((a.n_cap + kBfKT - 1) / kBfKT, (a.tq + kBfQT - 1) / kBfQT, a.batch);
     hipLaunchKernelGGL(index_bf16_kernel, grid, dim3(256), 0, s, a);

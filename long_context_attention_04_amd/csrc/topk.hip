@@ -54,7 +54,7 @@ __device__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp /* >= 16 */, uint3
 }
 
 struct SelShared {
-  uint32_t hist[256];
+  uint32_t hist[2][256];
   uint32_t tmp[16];
   uint32_t bin, above, last_pos;
 };
@@ -65,10 +65,13 @@ struct SelShared {
 template <typename KeyFn>
 __device__ void radix_threshold(KeyFn key, int n, int k, SelShared& sh, uint32_t* T_out, uint32_t* krem_out) {
   uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
+  for (int i = threadIdx.x; i < 512; i += blockDim.x) (&sh.hist[0][0])[i] = 0;
+  __syncthreads();
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) sh.hist[i] = 0;
-    __syncthreads();
+    uint32_t* hist = sh.hist[pass & 1];
+    // the other buffer is cleared for the next pass (nobody reads it in this pass)
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) sh.hist[(pass + 1) & 1][i] = 0;
     for (int base = threadIdx.x; base < n; base += 8 * blockDim.x) {
       uint32_t kv[8];  // all loads first: one memory latency per 8 keys when key() reads memory
 #pragma unroll
@@ -79,23 +82,34 @@ __device__ void radix_threshold(KeyFn key, int n, int k, SelShared& sh, uint32_t
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = base + j * blockDim.x;
-        if (i < n && (kv[j] & mask) == prefix) atomicAdd(&sh.hist[(kv[j] >> shift) & 0xffu], 1u);
+        if (i < n && (kv[j] & mask) == prefix) atomicAdd(&hist[(kv[j] >> shift) & 0xffu], 1u);
       }
     }
     __syncthreads();
-    const uint32_t h = threadIdx.x < 256 ? sh.hist[threadIdx.x] : 0u;
-    uint32_t tot;
-    const uint32_t incl = block_incl_scan(h, sh.tmp, &tot);
-    const uint32_t above = tot - incl;  // keys in bins above this thread's bin
-    if (threadIdx.x < 256 && above < krem && above + h >= krem) {
-      sh.bin = threadIdx.x;
-      sh.above = above;
+    if (threadIdx.x < kWave) {  // one wave: lane L owns bins 4L..4L+3; suffix sums by shuffles
+      const int L = threadIdx.x;
+      const uint32_t h0 = hist[4 * L], h1 = hist[4 * L + 1], h2 = hist[4 * L + 2], h3 = hist[4 * L + 3];
+      const uint32_t mine = h0 + h1 + h2 + h3;
+      uint32_t suf = mine;  // inclusive suffix over lanes >= L
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t u = __shfl_down(suf, o);
+        if (L + o < kWave) suf += u;
+      }
+      uint32_t run = suf - mine;  // keys in bins above this lane's four
+      const uint32_t hh[4] = {h0, h1, h2, h3};
+#pragma unroll
+      for (int d = 3; d >= 0; --d) {
+        if (run < krem && run + hh[d] >= krem) {
+          sh.bin = 4 * L + d;
+          sh.above = run;
+        }
+        run += hh[d];
+      }
     }
     __syncthreads();
     prefix |= sh.bin << shift;
     mask |= 0xffu << shift;
     krem -= sh.above;
-    __syncthreads();
   }
   *T_out = prefix;
   *krem_out = krem;
