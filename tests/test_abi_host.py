@@ -1,0 +1,180 @@
+"""Host-side tests of the C ABI: the library loads, exports every declared symbol,
+and rejects invalid arguments on the host before anything is launched.
+
+No case here reaches a kernel launch: each one carries exactly one invalid
+argument, which validation catches first (so these run without a GPU, and would
+not touch one if present).  Pointers are fake non-null addresses; they are never
+dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+csa = pytest.importorskip("long_context_attention_04_amd")
+
+P = 0x10000  # fake device address: validation fails before any use
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:csa_status|size_t|int32_t|const char\*)\s+(\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(csa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in csa.h but not exported"
+    assert set(names) <= set(csa.EXPORTED)
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define CSA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert csa.abi_version() == int(m.group(1))
+
+
+def test_status_strings():
+    seen = {csa.csa_status_string(s) for s in range(7)}
+    assert len(seen) == 7
+    assert csa.csa_status_string(99) == "unknown status"
+
+
+def T(dtype, data=P, scale=None, sb=1 << 20, sr=512):
+    t = csa.CsaTensor()
+    t.data, t.scale, t.dtype, t.stride_b, t.stride_row = data, scale, dtype, sb, sr
+    return t
+
+
+def expect(status, fn, *args, match=None):
+    with pytest.raises(csa.CsaError) as ei:
+        fn(*args, stream=0)
+    assert ei.value.status == status, str(ei.value)
+    if match:
+        assert match in csa.csa_last_error()
+
+
+E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_WS = 1, 2, 3, 4, 5
+
+
+# ---------------------------------------------------------------------------- compress
+
+
+def test_compress_rejects():
+    ok_raw, ok_out = T(csa.BF16), T(csa.BF16)
+    args = dict(raw_base=P, logits=P, m=4, dim=512, block_first=P, block_count=P, max_blocks=1, batch=2)
+
+    def call(raw=ok_raw, out=ok_out, **kw):
+        a = dict(args, **kw)
+        return lambda stream: csa.csa_compress(raw, a["raw_base"], a["logits"], a["m"], a["dim"], a["block_first"],
+                                               a["block_count"], a["max_blocks"], a["batch"], out, stream)
+
+    expect(E_NULL, call(raw=T(csa.BF16, data=None)))
+    expect(E_NULL, call(logits=None))
+    expect(E_DTYPE, call(raw=T(7)))
+    expect(E_DTYPE, call(raw=T(csa.MXFP4, scale=P)), match="raw rows")
+    expect(E_SHAPE, call(m=0))
+    expect(E_SHAPE, call(m=1025))
+    expect(E_SHAPE, call(dim=4097))
+    expect(E_SHAPE, call(batch=-1))
+    expect(E_SHAPE, call(out=T(csa.MXFP4, scale=P), dim=48), match="dim % 32")
+    expect(E_NULL, call(out=T(csa.FP8_E4M3)), match="row-scale")
+    expect(E_NULL, call(out=T(csa.MXFP4)))
+    expect(E_SHAPE, call(raw=T(csa.BF16, sb=-1)))
+
+
+# ---------------------------------------------------------------------------- indexer
+
+
+def test_index_scores_rejects():
+    q, k = T(csa.F32), T(csa.MXFP4, scale=P)
+
+    def call(q=q, k=k, w=P, heads=8, dim=64, m=4, ncap=1024, batch=1, tq=1):
+        return lambda stream: csa.csa_index_scores(q, w, k, P, batch, tq, heads, dim, m, ncap, P, stream)
+
+    expect(E_NULL, call(w=None))
+    expect(E_DTYPE, call(q=T(csa.BF16)), match="F32 query")
+    expect(E_UNSUP, call(dim=128))
+    expect(E_UNSUP, call(heads=33))
+    expect(E_UNSUP, call(k=T(csa.FP8_E4M3)))
+    expect(E_DTYPE, call(q=T(csa.BF16), k=T(csa.F32)))
+    expect(E_SHAPE, call(heads=0))
+    expect(E_SHAPE, call(ncap=-5))
+    expect(E_UNSUP, call(q=T(csa.F32), k=T(csa.F32), heads=64, dim=256))
+
+
+# ---------------------------------------------------------------------------- top-k
+
+
+def test_topk_rejects_and_workspace():
+    assert csa.csa_topk_workspace_size(8, 1, 16896, 512) == 0           # LDS-resident rows
+    need = csa.csa_topk_workspace_size(8, 1, 262144, 2048)
+    assert need > 0
+    expect(E_NULL, lambda stream: csa.csa_topk(None, P, 1, 1, 100, 4, 8, P, None, 0, stream))
+    expect(E_SHAPE, lambda stream: csa.csa_topk(P, P, 1, 1, 100, 4, 0, P, None, 0, stream))
+    expect(E_SHAPE, lambda stream: csa.csa_topk(P, P, 1, 1, 100, 0, 8, P, None, 0, stream))
+    expect(E_WS, lambda stream: csa.csa_topk(P, P, 8, 1, 262144, 4, 2048, P, P, need - 1, stream))
+    expect(E_WS, lambda stream: csa.csa_topk(P, P, 8, 1, 262144, 4, 2048, P, None, need, stream))
+
+
+# ---------------------------------------------------------------------------- attention
+
+
+def test_attention_rejects_and_workspace():
+    q, kv, raw = T(csa.BF16), T(csa.BF16), T(csa.BF16)
+    need = csa.csa_attn_workspace_size(8, 1, 64, 512, 2048 + 128)
+    assert need > 0
+    assert csa.csa_attn_workspace_size(1, 1, 16, 128, 96) == 0        # one split: no workspace
+
+    def sparse(q=q, kv=kv, raw=raw, idx=P, k=2048, W=128, heads=64, dim=512, ws=P, wsb=need):
+        return lambda stream: csa.csa_sparse_attn(q, kv, idx, k, raw, P, W, P, 8, 1, heads, dim, 0.088, P, P, ws, wsb,
+                                                  stream)
+
+    expect(E_NULL, sparse(idx=None))
+    expect(E_SHAPE, sparse(k=-1))
+    expect(E_DTYPE, sparse(raw=T(csa.FP8_E4M3)), match="share a dtype")
+    expect(E_DTYPE, sparse(q=T(csa.F32)), match="BF16 query")
+    expect(E_UNSUP, sparse(heads=40))
+    expect(E_UNSUP, sparse(dim=256))
+    expect(E_UNSUP, sparse(heads=80))
+    expect(E_WS, sparse(wsb=need - 1))
+    expect(E_WS, sparse(ws=None))
+    expect(E_DTYPE, sparse(kv=T(csa.MXFP4, scale=P), raw=T(csa.MXFP4, scale=P)))
+    expect(E_UNSUP, sparse(q=T(csa.F32), kv=T(csa.F32), raw=T(csa.F32), k=9000, W=0, heads=16, dim=128))
+
+    def hca(m_hc=128, ncap=1024, heads=64):
+        return lambda stream: csa.hca_attn(q, kv, m_hc, ncap, raw, P, 128, P, 8, 1, heads, 512, 0.088, P, P, P,
+                                           1 << 40, stream)
+
+    expect(E_SHAPE, hca(m_hc=0))
+    expect(E_SHAPE, hca(ncap=-1))
+    expect(E_UNSUP, hca(heads=8))
+
+
+# ---------------------------------------------------------------------------- quantisers
+
+
+def test_quantizers_reject():
+    expect(E_NULL, lambda stream: csa.csa_quantize_mxfp4(None, 4, 64, P, P, stream))
+    expect(E_SHAPE, lambda stream: csa.csa_quantize_mxfp4(P, 4, 48, P, P, stream))
+    expect(E_SHAPE, lambda stream: csa.csa_quantize_fp8(P, 4, 0, P, P, stream))
+    expect(E_SHAPE, lambda stream: csa.csa_quantize_fp8(P, 4, 9000, P, P, stream))
+    expect(E_NULL, lambda stream: csa.csa_quantize_fp8(P, 4, 64, None, P, stream))
+
+
+def test_last_error_is_thread_local_and_cleared_by_success_path_only():
+    with pytest.raises(csa.CsaError):
+        csa.csa_quantize_fp8(P, 4, 0, P, P, stream=0)
+    msg = csa.csa_last_error()
+    assert "cols" in msg
+    import threading
+    other = []
+    threading.Thread(target=lambda: other.append(csa.csa_last_error())).start()
+    import time
+    time.sleep(0.2)
+    assert other == [""]
