@@ -53,24 +53,80 @@ __device__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp /* >= 16 */, uint3
   return v + base;
 }
 
+// Wave-wide min / max of a uint32 with DPP row ops (VALU, no LDS round trip):
+// reduce within each 16-lane row, then combine the four rows via readlane.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+  // quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+
 struct SelShared {
   uint32_t hist[2][256];
   uint32_t tmp[16];
-  uint32_t bin, above, last_pos;
+  uint32_t tmn[16], tmx[16];
+  uint32_t bin, above, cnt, last_pos;
+  uint32_t nfin;
+  __attribute__((aligned(16))) uint32_t fkey[64];
+  __attribute__((aligned(16))) uint32_t fpos[64];
+  uint32_t T, krem;
 };
 
 // Exact threshold of the top-k of n keys (key(i) for i < n, tie order = i
 // ascending; 1 <= k < n): the k-th largest key T and the number krem of its
-// copies that are taken (the lowest-positioned ones).  Four 8-bit radix passes.
+// copies that are taken (the lowest-positioned ones).
+// Radix select over the live key range: each pass splits the current range
+// [lo, hi] into <= 256 equal bins (not fixed digits, so scores that share
+// their top bits still spread out), keeps the bin holding the k-th key, and
+// stops as soon as that bin holds <= 64 keys, which one wave then ranks
+// exactly by (key desc, position asc).
 template <typename KeyFn>
 __device__ void radix_threshold(KeyFn key, int n, int k, SelShared& sh, uint32_t* T_out, uint32_t* krem_out) {
-  uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
+  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  // key range
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  for (int base = threadIdx.x; base < n; base += 8 * blockDim.x) {
+    uint32_t kv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * blockDim.x;
+      kv[j] = i < n ? key(i) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (base + j * (int)blockDim.x < n) {
+        mn = min(mn, kv[j]);
+        mx = max(mx, kv[j]);
+      }
+  }
+  mn = wave_reduce_u32<false>(mn);
+  mx = wave_reduce_u32<true>(mx);
+  if (lane == 0) {
+    sh.tmn[wv] = mn;
+    sh.tmx[wv] = mx;
+  }
   for (int i = threadIdx.x; i < 512; i += blockDim.x) (&sh.hist[0][0])[i] = 0;
   __syncthreads();
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  uint32_t lo = sh.tmn[0], hi = sh.tmx[0];
+  for (int i = 1; i < nw; ++i) {
+    lo = min(lo, sh.tmn[i]);
+    hi = max(hi, sh.tmx[i]);
+  }
+  uint32_t krem = (uint32_t)k;
+  bool finish = false;
+  for (int pass = 0; pass < 5 && !finish; ++pass) {
+    const uint32_t span = hi - lo;
+    if (span == 0) break;  // every key left in range is equal: T = lo
+    const int bits = 32 - __clz(span);
+    const int shift = bits > 8 ? bits - 8 : 0;
     uint32_t* hist = sh.hist[pass & 1];
-    // the other buffer is cleared for the next pass (nobody reads it in this pass)
     for (int i = threadIdx.x; i < 256; i += blockDim.x) sh.hist[(pass + 1) & 1][i] = 0;
     for (int base = threadIdx.x; base < n; base += 8 * blockDim.x) {
       uint32_t kv[8];  // all loads first: one memory latency per 8 keys when key() reads memory
@@ -82,7 +138,7 @@ __device__ void radix_threshold(KeyFn key, int n, int k, SelShared& sh, uint32_t
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = base + j * blockDim.x;
-        if (i < n && (kv[j] & mask) == prefix) atomicAdd(&hist[(kv[j] >> shift) & 0xffu], 1u);
+        if (i < n && kv[j] >= lo && kv[j] <= hi) atomicAdd(&hist[(kv[j] - lo) >> shift], 1u);
       }
     }
     __syncthreads();
@@ -102,46 +158,136 @@ __device__ void radix_threshold(KeyFn key, int n, int k, SelShared& sh, uint32_t
         if (run < krem && run + hh[d] >= krem) {
           sh.bin = 4 * L + d;
           sh.above = run;
+          sh.cnt = hh[d];
         }
         run += hh[d];
       }
+      if (L == 0) sh.nfin = 0;
     }
     __syncthreads();
-    prefix |= sh.bin << shift;
-    mask |= 0xffu << shift;
+    const uint32_t nlo = lo + (sh.bin << shift);
+    const uint32_t nhi = min(hi, nlo + ((1u << shift) - 1u));
     krem -= sh.above;
+    finish = sh.cnt <= 64;
+    lo = nlo;
+    hi = nhi;
   }
-  *T_out = prefix;
+  if (finish && hi != lo) {
+    // gather the <= 64 keys of [lo, hi] with their positions, then rank them in one wave
+    for (int base = threadIdx.x; base < n; base += 8 * blockDim.x) {
+      uint32_t kv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = base + j * blockDim.x;
+        kv[j] = i < n ? key(i) : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = base + j * blockDim.x;
+        if (i < n && kv[j] >= lo && kv[j] <= hi) {
+          const uint32_t slot = atomicAdd(&sh.nfin, 1u);
+          sh.fkey[slot] = kv[j];
+          sh.fpos[slot] = (uint32_t)i;
+        }
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {  // one wave ranks the <= 64 gathered keys (broadcast reads, 8 at a time)
+      const int c = (int)sh.nfin, L = threadIdx.x;
+      for (int i = c + L; i < 64; i += kWave) {  // pad to whole groups of 8 with keys that never rank
+        sh.fkey[i] = 0u;
+        sh.fpos[i] = 0xffffffffu;
+      }
+      const uint32_t myk = L < c ? sh.fkey[L] : 0u, myp = L < c ? sh.fpos[L] : 0xffffffffu;
+      uint32_t rank = 0, gt = 0;
+      for (int i0 = 0; i0 < c; i0 += 8) {
+        const uint4 k0 = *(const uint4*)&sh.fkey[i0], k1 = *(const uint4*)&sh.fkey[i0 + 4];
+        const uint4 p0 = *(const uint4*)&sh.fpos[i0], p1 = *(const uint4*)&sh.fpos[i0 + 4];
+        const uint32_t kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+        const uint32_t pp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          rank += kk[j] > myk || (kk[j] == myk && pp[j] < myp);
+          gt += kk[j] > myk;
+        }
+      }
+      if (L < c && rank == krem - 1) {
+        sh.T = myk;
+        sh.krem = krem - gt;
+      }
+    }
+    __syncthreads();
+    *T_out = sh.T;
+    *krem_out = sh.krem;
+    return;
+  }
+  *T_out = lo;  // range collapsed to one key value: take krem copies of it
   *krem_out = krem;
 }
 
 // Ascending-order compaction of the selected positions (key > T, or key == T
 // among the first krem copies).  emit(pos, rank) is called once per selected
-// position with its rank 0..k-1.  Returns (via sh.last_pos) the position of the
-// last copy of T taken.
+// position with its rank 0..k-1.  Sets sh.last_pos to the position of the last
+// copy of T taken.  Each wave owns a contiguous chunk and walks it 64 keys per
+// step (lane i <-> key base+i, conflict-free); ballots give in-wave ranks and
+// one barrier gives every wave its offsets.
 template <typename KeyFn, typename Emit>
 __device__ void compact_selected(KeyFn key, int n, uint32_t T, uint32_t krem, SelShared& sh, Emit emit) {
-  const int seg = (n + (int)blockDim.x - 1) / (int)blockDim.x;
-  const int lo = min(n, (int)threadIdx.x * seg), hi = min(n, lo + seg);
+  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  const int chunk = (n + nw * kWave - 1) / (nw * kWave) * kWave;  // whole 64-key steps per wave
+  const int lo = min(n, wv * chunk), hi = min(n, lo + chunk);
+  const uint64_t below = (1ull << lane) - 1ull;
   uint32_t gt = 0, eq = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t kv = key(i);
-    gt += kv > T;
-    eq += kv == T;
-  }
-  const uint32_t eq_before = block_incl_scan(eq, sh.tmp, nullptr) - eq;
-  const uint32_t take = eq_before >= krem ? 0u : min(eq, krem - eq_before);
-  const uint32_t sel = gt + take;
-  uint32_t rank = block_incl_scan(sel, sh.tmp, nullptr) - sel;
-  uint32_t taken = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t kv = key(i);
-    bool s = kv > T;
-    if (kv == T && taken < take) {
-      s = true;
-      if (++taken == take && eq_before + take == krem) sh.last_pos = (uint32_t)i;
+  for (int b0 = lo; b0 < hi; b0 += 4 * kWave) {
+    uint32_t kv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = b0 + j * kWave + lane;
+      kv[j] = i < hi ? key(i) : 0u;
     }
-    if (s) emit(i, rank++);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = b0 + j * kWave + lane;
+      gt += (uint32_t)__popcll(__ballot(i < hi && kv[j] > T));
+      eq += (uint32_t)__popcll(__ballot(i < hi && kv[j] == T));
+    }
+  }
+  if (lane == 0) {
+    sh.tmn[wv] = gt;
+    sh.tmx[wv] = eq;
+  }
+  __syncthreads();
+  uint32_t gt_before = 0, eq_before = 0;
+  for (int w = 0; w < wv; ++w) {
+    gt_before += sh.tmn[w];
+    eq_before += sh.tmx[w];
+  }
+  uint32_t taken_before = eq_before >= krem ? krem : eq_before;  // copies of T taken by earlier waves
+  uint32_t rank = gt_before + taken_before;
+  uint32_t eq_seen = eq_before;
+  for (int b0 = lo; b0 < hi; b0 += 4 * kWave) {
+    uint32_t kvs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = b0 + j * kWave + lane;
+      kvs[j] = i < hi ? key(i) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+    const int i = b0 + j * kWave + lane;
+    const uint32_t kv = kvs[j];
+    const bool is_eq = i < hi && kv == T;
+    const uint64_t eqm = __ballot(is_eq);
+    const uint32_t my_eq_rank = eq_seen + (uint32_t)__popcll(eqm & below);  // copies of T before me
+    const bool s = (i < hi && kv > T) || (is_eq && my_eq_rank < krem);
+    const uint64_t sm = __ballot(s);
+    if (s) {
+      emit(i, rank + (uint32_t)__popcll(sm & below));
+      if (is_eq && my_eq_rank == krem - 1) sh.last_pos = (uint32_t)i;
+    }
+    rank += (uint32_t)__popcll(sm);
+    eq_seen += (uint32_t)__popcll(eqm);
+    }
   }
   __syncthreads();
 }
