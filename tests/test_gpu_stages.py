@@ -250,6 +250,8 @@ def _store_kv(csa, x, fmt):
     (1, 6, 32, 512, 100, 50, "bf16", 2e-3),    # several queries, one split each
     (2, 1, 48, 512, 520, 128, "fp8", 5e-3),
     (2, 1, 16, 512, 17, 1, "bf16", 2e-3),
+    (1, 5, 48, 512, 64, 32, "bf16", 2e-3),     # 48 heads, several queries (three head groups)
+    (2, 3, 64, 512, 200, 64, "fp8", 5e-3),
 ])
 def test_csa_sparse_attn(gpu_lib, B, Tq, H, D, k, W, fmt, tol):
     csa = gpu_lib
@@ -335,3 +337,29 @@ def test_attention_deterministic_and_batch_invariant(gpu_lib):
     for i in range(B):
         s = run([i])
         assert np.array_equal(s[0][0], a[0][i]) and np.array_equal(s[1][0], a[1][i])
+
+
+def test_attention_fp8_zero_row_is_an_entry(gpu_lib):
+    """An all-zero fp8 row has row scale 0; it is still an entry of the softmax (logit 0,
+    contributes a zero vector), not an empty slot."""
+    csa = gpu_lib
+    B, Tq, H, D, k, W, m, N = 1, 1, 16, 512, 24, 4, 4, 256
+    r, q, kvc, raw = _attn_inputs("fp8zero", B, Tq, H, D, N, 64, "fp8")
+    q *= 0.05  # small logits, so the zero rows carry visible weight
+    idx = np.sort(r.choice(N, k, replace=False)).astype(np.int32)[None, None]
+    kvc[0, idx[0, 0, :5]] = 0.0  # five selected rows are exactly zero
+    pos = np.array([[N * m - 1]], np.int32)
+    raw_base = np.array([N * m - 40], np.int32)
+    qd, qv = csa.desc(up_bf16(q)[0], csa.BF16), up_bf16(q)[1]
+    kvd, kvv, (_, kv_scale) = _store_kv(csa, kvc, "fp8")
+    kv_scale[0, torch.as_tensor(idx[0, 0, :5]).long().cuda()] = 0.0  # a zero scale: the row is still zero
+    rawd, rawv, _ = _store_kv(csa, raw, "fp8")
+    out = torch.full((B, Tq, H, D), float("nan"), device="cuda")
+    lse = torch.full((B, Tq, H), float("nan"), device="cuda")
+    ws = workspace(csa.csa_attn_workspace_size(B, Tq, H, D, k + W))
+    scale = 1 / np.sqrt(128)
+    csa.csa_sparse_attn(qd, kvd, up(idx), k, rawd, up(raw_base), W, up(pos), B, Tq, H, D, scale, out, lse, ws,
+                        ws.numel())
+    want, want_lse = oracle.csa_sparse_attn(qv, kvv, idx, rawv, raw_base, W, pos, scale)
+    assert row_rel_err(down(out), want) < 5e-3
+    assert np.max(np.abs(down(lse) - want_lse)) < 5e-3
