@@ -17,6 +17,7 @@ namespace {
 
 constexpr int kCompressThreads = 256;
 constexpr int kRowBatch = 4;
+constexpr float kNegInfC = -__builtin_inff();
 
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
@@ -69,64 +70,113 @@ __device__ __forceinline__ void store_row(const float (&vals)[NV], int nv, int o
   }
 }
 
-template <int NV>  // columns per thread: dim <= 256 * NV
+constexpr int kLocalSoftmaxMax = 16;  // up to this many offsets every thread forms the weights itself
+
+// One element of a stored raw row; the input format is a compile-time choice so the
+// loads of a row group are issued back to back.
+template <int IN>
+__device__ __forceinline__ float load_raw(const void* p, int64_t i) {
+  if constexpr (IN == CSA_F32) return ((const float*)p)[i];
+  else if constexpr (IN == CSA_BF16) return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+  else return e4m3_to_f32(((const uint8_t*)p)[i]);
+}
+
+template <int NV, int IN>  // columns per thread: dim <= 256 * NV; IN: raw row format
 __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs a) {
   const int b = blockIdx.y;
   const int i = blockIdx.x;
+  // independent scalars first, all in flight together (one memory round trip)
   const int cnt = a.block_count[b];
-  if (i >= cnt) return;
-  const int j = a.block_first[b] + i;
-  __shared__ float omega[1024];
+  const int jfirst = a.block_first[b];
+  const int rbase = a.raw_base[b];
+  const int m = a.m;
+  __shared__ float omega_s[1024];
   __shared__ float red[kCompressThreads / kWave];
-  // omega = softmax(logits) in fp32, max-subtracted, summed in ascending offset order
-  for (int r = threadIdx.x; r < a.m; r += kCompressThreads) omega[r] = a.logits[r];
-  __syncthreads();
-  if (threadIdx.x == 0) {  // max, exponentials and their sum in ascending offset order
-    float mx = omega[0];
-    for (int r = 1; r < a.m; ++r) mx = fmaxf(mx, omega[r]);
-    float sum = 0.f;
-    for (int r = 0; r < a.m; ++r) {
-      const float e = expf(omega[r] - mx);
-      omega[r] = e;
-      sum += e;
-    }
-    for (int r = 0; r < a.m; ++r) omega[r] = __fdiv_rn(omega[r], sum);
+  float zl[kLocalSoftmaxMax];  // logits, held by every thread when m is small
+  const bool local = m <= kLocalSoftmaxMax;
+  if (local) {
+#pragma unroll
+    for (int r = 0; r < kLocalSoftmaxMax; ++r)
+      if (r < m) zl[r] = a.logits[r];
   }
-  __syncthreads();
-  const int64_t row0 = (int64_t)j * a.m - a.raw_base[b];
+  if (i >= cnt) return;
+  const int j = jfirst + i;
+  const int64_t row0 = (int64_t)j * m - rbase;
   float acc[NV];
   const int nv = (a.dim - threadIdx.x + kCompressThreads - 1) / kCompressThreads;
 #pragma unroll
   for (int v = 0; v < NV; ++v) acc[v] = 0.f;
+
+  // omega = softmax(logits) in fp32: max-subtracted, exponentials summed in ascending
+  // offset order, each weight divided by the sum.  The same arithmetic on every thread.
+  float mx, sum;
+  if (local) {
+    mx = zl[0];
+#pragma unroll
+    for (int r = 1; r < kLocalSoftmaxMax; ++r)
+      if (r < m) mx = fmaxf(mx, zl[r]);
+    sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < kLocalSoftmaxMax; ++r)
+      if (r < m) {
+        zl[r] = expf(zl[r] - mx);
+        sum += zl[r];
+      }
+#pragma unroll
+    for (int r = 0; r < kLocalSoftmaxMax; ++r)
+      if (r < m) zl[r] = __fdiv_rn(zl[r], sum);
+  } else {
+    for (int r = threadIdx.x; r < m; r += kCompressThreads) omega_s[r] = a.logits[r];
+    __syncthreads();
+    float lm = kNegInfC;
+    for (int r = threadIdx.x; r < m; r += kCompressThreads) lm = fmaxf(lm, omega_s[r]);
+    mx = block_max(lm, red);
+    for (int r = threadIdx.x; r < m; r += kCompressThreads) omega_s[r] = expf(omega_s[r] - mx);
+    __syncthreads();
+    sum = 0.f;
+    for (int r = 0; r < m; ++r) sum += omega_s[r];  // ascending order, same on every thread
+    __syncthreads();
+    for (int r = threadIdx.x; r < m; r += kCompressThreads) omega_s[r] = __fdiv_rn(omega_s[r], sum);
+    __syncthreads();
+  }
+
   // rows in groups of kRowBatch: all loads of a group are issued before its FMAs
   // (terms are still added in ascending offset order)
-  for (int r0 = 0; r0 < a.m; r0 += kRowBatch) {
+  // Loads are unconditional (row and column clamped to valid ones), so a group's loads
+  // are all in flight together; out-of-range terms are dropped afterwards.
+  auto row_group = [&](int r0, auto wfun) {
     float x[kRowBatch][NV];
     float rs[kRowBatch];
 #pragma unroll
-    for (int j = 0; j < kRowBatch; ++j) {
-      const int r = r0 + j;
-      rs[j] = 1.f;
-      if (r >= a.m) continue;
+    for (int jj = 0; jj < kRowBatch; ++jj) {
+      const int r = min(r0 + jj, m - 1);
       const int64_t base = (int64_t)b * a.raw.sb + (row0 + r) * a.raw.sr;
-      if (a.raw.dtype == CSA_FP8_E4M3 && a.raw.scale)
-        rs[j] = ((const float*)a.raw.scale)[(int64_t)b * a.raw.ssb + (row0 + r) * a.raw.ssr];
+      rs[jj] = IN == CSA_FP8_E4M3 && a.raw.scale
+                   ? ((const float*)a.raw.scale)[(int64_t)b * a.raw.ssb + (row0 + r) * a.raw.ssr]
+                   : 1.f;
 #pragma unroll
       for (int v = 0; v < NV; ++v)
-        x[j][v] = v < nv ? load_elem(a.raw.data, a.raw.dtype, base + threadIdx.x + v * kCompressThreads) : 0.f;
+        x[jj][v] = load_raw<IN>(a.raw.data, base + min((int)threadIdx.x + v * kCompressThreads, a.dim - 1));
     }
 #pragma unroll
-    for (int j = 0; j < kRowBatch; ++j) {
-      if (r0 + j < a.m) {
-        const float w = omega[r0 + j];
+    for (int jj = 0; jj < kRowBatch; ++jj) {
+      if (r0 + jj < m) {
+        const float w = wfun(jj);
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          float xv = x[j][v];
-          if (a.raw.dtype == CSA_FP8_E4M3) xv *= rs[j];
-          acc[v] = fmaf(w, xv, acc[v]);
+          float xv = x[jj][v];
+          if (IN == CSA_FP8_E4M3) xv *= rs[jj];
+          acc[v] = fmaf(w, xv, acc[v]);  // columns beyond dim are never stored
         }
       }
     }
+  };
+  if (local) {
+#pragma unroll
+    for (int r0 = 0; r0 < kLocalSoftmaxMax; r0 += kRowBatch)
+      if (r0 < m) row_group(r0, [&](int jj) { return zl[r0 + jj]; });  // compile-time index after unrolling
+  } else {
+    for (int r0 = 0; r0 < m; r0 += kRowBatch) row_group(r0, [&](int jj) { return omega_s[r0 + jj]; });
   }
   const int64_t off = (int64_t)b * a.out_sb + (int64_t)j * a.out_sr;
   const int64_t soff = (int64_t)b * a.out_ssb + (int64_t)j * a.out_ssr;
@@ -176,16 +226,23 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const float* __restri
 
 }  // namespace
 
-hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
-  if (a.max_blocks <= 0 || a.batch <= 0) return hipSuccess;
+template <int IN>
+hipError_t launch_compress_in(const CompressArgs& a, hipStream_t s) {
   dim3 grid(a.max_blocks, a.batch);
   const int nv = (a.dim + kCompressThreads - 1) / kCompressThreads;
-  if (nv <= 1) hipLaunchKernelGGL(compress_kernel<1>, grid, dim3(kCompressThreads), 0, s, a);
-  else if (nv <= 2) hipLaunchKernelGGL(compress_kernel<2>, grid, dim3(kCompressThreads), 0, s, a);
-  else if (nv <= 4) hipLaunchKernelGGL(compress_kernel<4>, grid, dim3(kCompressThreads), 0, s, a);
-  else if (nv <= 8) hipLaunchKernelGGL(compress_kernel<8>, grid, dim3(kCompressThreads), 0, s, a);
-  else hipLaunchKernelGGL(compress_kernel<16>, grid, dim3(kCompressThreads), 0, s, a);
+  if (nv <= 1) hipLaunchKernelGGL((compress_kernel<1, IN>), grid, dim3(kCompressThreads), 0, s, a);
+  else if (nv <= 2) hipLaunchKernelGGL((compress_kernel<2, IN>), grid, dim3(kCompressThreads), 0, s, a);
+  else if (nv <= 4) hipLaunchKernelGGL((compress_kernel<4, IN>), grid, dim3(kCompressThreads), 0, s, a);
+  else if (nv <= 8) hipLaunchKernelGGL((compress_kernel<8, IN>), grid, dim3(kCompressThreads), 0, s, a);
+  else hipLaunchKernelGGL((compress_kernel<16, IN>), grid, dim3(kCompressThreads), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
+  if (a.max_blocks <= 0 || a.batch <= 0) return hipSuccess;
+  if (a.raw.dtype == CSA_F32) return launch_compress_in<CSA_F32>(a, s);
+  if (a.raw.dtype == CSA_BF16) return launch_compress_in<CSA_BF16>(a, s);
+  return launch_compress_in<CSA_FP8_E4M3>(a, s);
 }
 
 hipError_t launch_quantize_mxfp4(const float* x, int64_t rows, int cols, uint8_t* codes, uint8_t* scales,

@@ -153,11 +153,17 @@ class CsaLayer:
         self.ws_attn = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
 
     # --- stages -------------------------------------------------------------
-    def compress(self, stream=None):
+    def compress_kv(self, stream=None):
         csa_compress(self.raw_kv.desc(), self.raw_base, self.z_kv, self.m, self.D, self.blk_first, self.blk_count,
                      self.max_blocks, self.B, self.kv_cmp.desc(), stream)
+
+    def compress_keys(self, stream=None):
         csa_compress(self.raw_ik.desc(), self.raw_base, self.z_ik, self.m, self.dI, self.blk_first, self.blk_count,
                      self.max_blocks, self.B, self.k_idx.desc(), stream)
+
+    def compress(self, stream=None):
+        self.compress_kv(stream)
+        self.compress_keys(stream)
 
     def index(self, stream=None):
         csa_index_scores(self.q_idx.desc(), self.w, self.k_idx.desc(), self.q_pos, self.B, self.tq, self.HI, self.dI,

@@ -65,6 +65,7 @@ def test_quantize_fp8_bit_exact(gpu_lib):
 @pytest.mark.parametrize("m,dim,in_dt,out_dt", [
     (4, 128, "f32", "f32"), (4, 512, "bf16", "bf16"), (128, 512, "bf16", "bf16"),
     (4, 64, "f32", "mxfp4"), (4, 512, "bf16", "fp8"), (128, 512, "fp8", "fp8"), (1, 96, "f32", "f32"),
+    (16, 256, "bf16", "bf16"), (17, 64, "f32", "f32"),  # both sides of the per-thread weight path
 ])
 def test_compress(gpu_lib, m, dim, in_dt, out_dt):
     csa = gpu_lib
