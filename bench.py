@@ -97,8 +97,8 @@ def index_kernel_us(torch, layers, reps) -> float:
 
 
 def stage_us(torch, layers, reps) -> dict:
-    names = ["compress", "index", "topk", "attention"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
+    names = list(layers[0].stage_names)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
     torch.cuda.synchronize()
     keep = backlog(torch)
     for i in range(reps):

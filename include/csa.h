@@ -163,6 +163,24 @@ csa_status csa_topk(const float* scores, const int32_t* q_pos, int32_t batch, in
 size_t csa_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, int32_t k);
 
 /* ---------------------------------------------------------------------------
+ * (b)+(c) fused: indexer scores and top-k selection in one call, for callers
+ * that need both.  Same arguments, formats and results as csa_index_scores
+ * followed by csa_topk on the scores it wrote (scores is still written, and
+ * idx equals what csa_topk returns for it, bit for bit).  With MXFP4 keys on
+ * rows longer than the single-workgroup top-k (n_cap > 20480), the indexer's
+ * workgroups also select their own 1024-block slices' top-32 candidates as
+ * they score them, so the selection pass only merges candidates; other shapes
+ * run the two stages one after the other.
+ *   ws  at least csa_index_topk_workspace_size() bytes; contents on entry do
+ *       not matter.
+ * ------------------------------------------------------------------------- */
+csa_status csa_index_topk(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx, const int32_t* q_pos,
+                          int32_t batch, int32_t tq, int32_t n_idx_heads, int32_t idx_dim, int32_t m,
+                          int32_t n_cap, int32_t k, float* scores, int32_t* idx, void* ws, size_t ws_bytes,
+                          void* stream);
+size_t csa_index_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, int32_t k);
+
+/* ---------------------------------------------------------------------------
  * (d) CSA sparse attention: attention over the selected compressed entries
  * plus a sliding window of raw local entries ("supplemented by a sliding
  * window of local KV entries", b-lab.team summary, Core Methodological

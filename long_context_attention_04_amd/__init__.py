@@ -73,6 +73,9 @@ _c = {
     "csa_index_scores": _proto("csa_index_scores", _I32, _TP, _P, _TP, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P),
     "csa_topk": _proto("csa_topk", _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P),
     "csa_topk_workspace_size": _proto("csa_topk_workspace_size", _SZ, _I32, _I32, _I32, _I32),
+    "csa_index_topk": _proto("csa_index_topk", _I32, _TP, _P, _TP, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
+                             _P, _P, _SZ, _P),
+    "csa_index_topk_workspace_size": _proto("csa_index_topk_workspace_size", _SZ, _I32, _I32, _I32, _I32),
     "csa_sparse_attn": _proto("csa_sparse_attn", _I32, _TP, _TP, _P, _I32, _TP, _P, _I32, _P, _I32, _I32, _I32,
                               _I32, _F, _P, _P, _P, _SZ, _P),
     "hca_attn": _proto("hca_attn", _I32, _TP, _TP, _I32, _I32, _TP, _P, _I32, _P, _I32, _I32, _I32, _I32, _F, _P,
@@ -153,6 +156,17 @@ def csa_topk_workspace_size(batch, tq, n_cap, k) -> int:
 def csa_topk(scores, q_pos, batch, tq, n_cap, m, k, idx, ws=None, ws_bytes=0, stream=None):
     _check(_c["csa_topk"](_ptr(scores), _ptr(q_pos), batch, tq, n_cap, m, k, _ptr(idx), _ptr(ws), ws_bytes,
                           _stream(stream)))
+
+
+def csa_index_topk_workspace_size(batch, tq, n_cap, k) -> int:
+    return _c["csa_index_topk_workspace_size"](batch, tq, n_cap, k)
+
+
+def csa_index_topk(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, k, scores, idx, ws=None,
+                   ws_bytes=0, stream=None):
+    _check(_c["csa_index_topk"](ctypes.byref(q_idx), _ptr(w), ctypes.byref(k_idx), _ptr(q_pos), batch, tq,
+                                n_idx_heads, idx_dim, m, n_cap, k, _ptr(scores), _ptr(idx), _ptr(ws), ws_bytes,
+                                _stream(stream)))
 
 
 def csa_attn_workspace_size(batch, tq, heads, dim, n_entries_max) -> int:

@@ -12,6 +12,8 @@
 #include "../../include/csa.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace csa {
 bool attn_plain_fits(int n_entries_max);
 }
@@ -110,9 +112,10 @@ csa_status csa_compress(const csa_tensor* raw, const int32_t* raw_base, const fl
   return from_hip(csa::launch_compress(a, (hipStream_t)stream), "csa_compress launch");
 }
 
-csa_status csa_index_scores(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx, const int32_t* q_pos,
-                            int32_t batch, int32_t tq, int32_t n_idx_heads, int32_t idx_dim, int32_t m, int32_t n_cap,
-                            float* scores, void* stream) {
+// Validates the indexer arguments and fills the launch description.
+static csa_status index_args(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx, const int32_t* q_pos,
+                             int32_t batch, int32_t tq, int32_t n_idx_heads, int32_t idx_dim, int32_t m,
+                             int32_t n_cap, float* scores, csa::IndexArgs* out) {
   csa_status st;
   if ((st = check_tensor(q_idx, "q_idx")) != CSA_OK) return st;
   if ((st = check_tensor(k_idx, "k_idx")) != CSA_OK) return st;
@@ -133,7 +136,7 @@ csa_status csa_index_scores(const csa_tensor* q_idx, const float* w, const csa_t
   }
   if (kd != CSA_MXFP4 && !(kd == CSA_BF16 && qd == CSA_BF16 && n_idx_heads == 8 && idx_dim == 64))
     REQUIRE((int64_t)n_idx_heads * idx_dim <= 8192, CSA_ERR_UNSUPPORTED, "n_idx_heads * idx_dim > 8192");
-  csa::IndexArgs a;
+  csa::IndexArgs& a = *out;
   a.q = csa::view_of(q_idx);
   a.w = w;
   a.k = csa::view_of(k_idx);
@@ -145,6 +148,15 @@ csa_status csa_index_scores(const csa_tensor* q_idx, const float* w, const csa_t
   a.m = m;
   a.n_cap = n_cap;
   a.scores = scores;
+  return CSA_OK;
+}
+
+csa_status csa_index_scores(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx, const int32_t* q_pos,
+                            int32_t batch, int32_t tq, int32_t n_idx_heads, int32_t idx_dim, int32_t m, int32_t n_cap,
+                            float* scores, void* stream) {
+  csa::IndexArgs a;
+  const csa_status st = index_args(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, scores, &a);
+  if (st != CSA_OK) return st;
   return from_hip(csa::launch_index_scores(a, (hipStream_t)stream), "csa_index_scores launch");
 }
 
@@ -162,6 +174,31 @@ csa_status csa_topk(const float* scores, const int32_t* q_pos, int32_t batch, in
   if (need > 0) REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "top-k needs %zu workspace bytes, got %zu", need, ws_bytes);
   return from_hip(csa::launch_topk(scores, q_pos, batch, tq, n_cap, m, k, idx, ws, (hipStream_t)stream),
                   "csa_topk launch");
+}
+
+size_t csa_index_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, int32_t k) {
+  if (batch < 0 || tq < 0 || n_cap < 0 || k < 1) return 0;
+  const int64_t rows = (int64_t)batch * tq;
+  return std::max(csa::topk_workspace_bytes(rows, n_cap, k), csa::index_topk_workspace_bytes(rows, n_cap, k));
+}
+
+csa_status csa_index_topk(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx, const int32_t* q_pos,
+                          int32_t batch, int32_t tq, int32_t n_idx_heads, int32_t idx_dim, int32_t m, int32_t n_cap,
+                          int32_t k, float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  csa::IndexArgs a;
+  csa_status st = index_args(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, scores, &a);
+  if (st != CSA_OK) return st;
+  REQUIRE(idx != nullptr, CSA_ERR_NULL, "idx is NULL");
+  REQUIRE(k >= 1, CSA_ERR_SHAPE, "k=%d must be >= 1", k);
+  const size_t need = csa_index_topk_workspace_size(batch, tq, n_cap, k);
+  if (need > 0)
+    REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "index+top-k needs %zu workspace bytes, got %zu",
+            need, ws_bytes);
+  const hipStream_t s = (hipStream_t)stream;
+  if (csa::index_topk_fused_ok(a, k)) return from_hip(csa::launch_index_topk(a, k, idx, ws, s), "csa_index_topk launch");
+  st = from_hip(csa::launch_index_scores(a, s), "csa_index_topk index launch");
+  if (st != CSA_OK) return st;
+  return from_hip(csa::launch_topk(scores, q_pos, batch, tq, n_cap, m, k, idx, ws, s), "csa_index_topk top-k launch");
 }
 
 size_t csa_attn_workspace_size(int32_t batch, int32_t tq, int32_t heads, int32_t dim, int32_t n_entries_max) {

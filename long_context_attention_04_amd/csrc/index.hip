@@ -20,6 +20,7 @@
 //  * F32 keys: plain fp32 VALU kernel (small shapes).
 #include "common.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace csa {
 
@@ -135,8 +136,15 @@ constexpr int kFp4Unroll = 8;
 constexpr int kFp4KeysPerWave = 32 * kFp4Unroll;
 constexpr int kFp4KeysPerWG = 4 * kFp4KeysPerWave;
 
-template <int NR>  // accumulator rows that can hold a real head: 4 (heads <= 8) or 16 (heads <= 32)
-__global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a) {
+// ------------------------------------------------------------------ slice top-32
+// With CAND set, each workgroup also selects the exact top-32 of its 1024-key
+// slice in (key desc, index asc) order -- key being the order-preserving integer
+// form of the score, the order the top-k uses -- and writes them in ascending
+// index order with the slice's metadata (count, truncated?, 32nd element).  The
+// keys go through LDS once; three waves then exit (freeing their registers for
+// the next workgroups' key loads) and one wave runs a barrier-free radix select.
+template <int NR, bool CAND>  // NR: accumulator rows that can hold a real head: 4 (heads <= 8) or 16 (heads <= 32)
+__global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a, CandOut co) {
   const int row = blockIdx.y;
   const int b = row / a.tq, t = row % a.tq;
   const int wave = threadIdx.x / kWave, l = threadIdx.x % kWave;
@@ -184,7 +192,7 @@ __global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a) {
     }
   }
   __syncthreads();
-  if (g0 >= a.n_cap) return;
+  if (!CAND && g0 >= a.n_cap) return;
   v8i A = {0, 0, 0, 0, 0, 0, 0, 0};
   int sa = 127;
   if (m < a.heads) {
@@ -202,6 +210,7 @@ __global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a) {
   // 3) scores
   float* srow = a.scores + (int64_t)row * a.n_cap;
   const int gend = min(g0 + kFp4KeysPerWave, a.n_cap);
+  float sc[kFp4Unroll];  // the wave's scores: tile u, key g0 + 32u + l%32 (both half-waves)
 #pragma unroll
   for (int u = 0; u < kFp4Unroll; ++u) {
     v8i Bop = {c[u][0], c[u][1], c[u][2], c[u][3], 0, 0, 0, 0};
@@ -214,10 +223,54 @@ __global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a) {
     for (int r = 0; r < NR; ++r) part = fmaf(wv[r], fmaxf(acc[r], 0.f), part);
     const float other = __shfl_xor(part, 32);
     const int key = g0 + 32 * u + l;
-    if (l < 32 && key < gend) srow[key] = key < V ? part + other : kNegInf;
+    sc[u] = part + other;  // the same value in lane l and lane l ^ 32
+    if (l < 32 && key < gend) srow[key] = key < V ? sc[u] : kNegInf;
     // keep one accumulator tile live at a time: occupancy (many waves hiding each
     // other's memory latency) matters more here than MFMA back-to-back issue
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (CAND) {
+    const int Vc = min(V, a.n_cap);
+    if (Vc <= co.k) return;  // every visible key is selected: the merge needs no candidates
+    __shared__ __attribute__((aligned(16))) uint32_t skeys[kFusedSlice];
+    __shared__ WaveSelLds sl;
+    const int slice = blockIdx.x;
+    const int start = slice * kFusedSlice;
+    const int n = max(0, min(kFusedSlice, Vc - start));  // visible keys of this slice
+    if (l < 32) {
+#pragma unroll
+      for (int u = 0; u < kFp4Unroll; ++u) skeys[wave * kFp4KeysPerWave + 32 * u + l] = float_key(sc[u]);
+    }
+    __syncthreads();
+    if (wave != 0) return;  // one wave selects; the others free their registers now
+    SliceMeta* mt = co.meta + (int64_t)row * co.nslices + slice;
+    uint2* out = co.cand + ((int64_t)row * co.nslices + slice) * kWaveTopC;
+    uint32_t kv[kWaveTopN];
+#pragma unroll
+    for (int q = 0; q < kWaveTopN / 4; ++q) {
+      const uint4 v4 = *(const uint4*)&skeys[kWaveTopN * l + 4 * q];
+      kv[4 * q] = v4.x;
+      kv[4 * q + 1] = v4.y;
+      kv[4 * q + 2] = v4.z;
+      kv[4 * q + 3] = v4.w;
+    }
+#pragma unroll
+    for (int j = 0; j < kWaveTopN; ++j)
+      if (kWaveTopN * l + j >= n) kv[j] = 0u;  // positions past the visible ones are absent
+    if (n <= kWaveTopC) {  // every slot of the slice's list: its n keys, then empty (key 0) slots
+#pragma unroll
+      for (int j = 0; j < kWaveTopN; ++j) {
+        const int p = kWaveTopN * l + j;
+        if (p < kWaveTopC) out[p] = p < n ? make_uint2(kv[j], (uint32_t)(start + p)) : make_uint2(0u, 0u);
+      }
+      if (l == 0) *mt = SliceMeta{(uint32_t)n, 0u, 0u, 0u};
+      return;
+    }
+    uint32_t T, tpos;
+    wave_top32(kv, sl, [&](uint32_t r, int j) {
+      out[r] = make_uint2(kv[j], (uint32_t)(start + kWaveTopN * l + j));
+    }, &T, &tpos);
+    if (l == 0) *mt = SliceMeta{(uint32_t)kWaveTopC, 1u, T, (uint32_t)start + tpos};
   }
 }
 
@@ -228,10 +281,11 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
   if (rows == 0 || a.n_cap == 0) return hipSuccess;
   if (a.k.dtype == CSA_MXFP4) {
     dim3 grid((a.n_cap + kFp4KeysPerWG - 1) / kFp4KeysPerWG, rows);
+    const CandOut none{};
     if (a.heads <= 8)
-      hipLaunchKernelGGL(index_mxfp4_kernel<4>, grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((index_mxfp4_kernel<4, false>), grid, dim3(256), 0, s, a, none);
     else
-      hipLaunchKernelGGL(index_mxfp4_kernel<16>, grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((index_mxfp4_kernel<16, false>), grid, dim3(256), 0, s, a, none);
   } else if (a.k.dtype == CSA_BF16 && a.q.dtype == CSA_BF16 && a.heads == 8 && a.dim == 64) {
     dim3 grid((a.n_cap + kBfKT - 1) / kBfKT, (a.tq + kBfQT - 1) / kBfQT, a.batch);
     hipLaunchKernelGGL(index_bf16_kernel, grid, dim3(256), 0, s, a);
@@ -240,6 +294,19 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
     const size_t lds = (size_t)a.heads * a.dim * sizeof(float);
     hipLaunchKernelGGL(index_plain_kernel, grid, dim3(kPlainThreads), lds, s, a);
   }
+  return hipGetLastError();
+}
+
+static_assert(kFp4KeysPerWG == kFusedSlice, "one indexer workgroup per candidate slice");
+
+hipError_t launch_index_scores_cand(const IndexArgs& a, const CandOut& c, hipStream_t s) {
+  const int rows = a.batch * a.tq;
+  if (rows == 0 || a.n_cap == 0) return hipSuccess;
+  dim3 grid((a.n_cap + kFp4KeysPerWG - 1) / kFp4KeysPerWG, rows);
+  if (a.heads <= 8)
+    hipLaunchKernelGGL((index_mxfp4_kernel<4, true>), grid, dim3(256), 0, s, a, c);
+  else
+    hipLaunchKernelGGL((index_mxfp4_kernel<16, true>), grid, dim3(256), 0, s, a, c);
   return hipGetLastError();
 }
 

@@ -68,6 +68,30 @@ size_t topk_workspace_bytes(int64_t rows, int n_cap, int k);
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int tq, int n_cap, int m, int k,
                        int32_t* idx, void* ws, hipStream_t s);
 
+// A slice's exact top-C candidates, as written by a candidate pass: up to C
+// (order-preserving score key, block index) pairs in ascending index order, and:
+struct SliceMeta {
+  uint32_t count;     // candidates written
+  uint32_t trunc;     // 1 when the slice held more than C visible keys
+  uint32_t last_key;  // C-th kept element in (key desc, index asc) order (when trunc)
+  uint32_t last_idx;
+};
+struct CandOut {
+  int C, slice, nslices;  // candidates per slice, keys per slice, slices per row
+  uint2* cand;            // [rows][nslices][C]
+  SliceMeta* meta;        // [rows][nslices]
+  int k;                  // rows with at most k visible keys need no candidates
+};
+
+// Fused (b)+(c) for MXFP4 keys on long rows: the indexer's workgroups also emit
+// their slice's top-32 candidates, and one merge pass selects the top-k.
+constexpr int kFusedSlice = 1024;  // keys per indexer workgroup
+constexpr int kFusedC = 32;
+bool index_topk_fused_ok(const IndexArgs& a, int k);
+size_t index_topk_workspace_bytes(int64_t rows, int n_cap, int k);
+hipError_t launch_index_scores_cand(const IndexArgs& a, const CandOut& c, hipStream_t s);  // index.hip
+hipError_t launch_index_topk(const IndexArgs& a, int k, int32_t* idx, void* ws, hipStream_t s);
+
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
   TensorView q;        // [B, Tq, H, D]

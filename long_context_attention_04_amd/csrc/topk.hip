@@ -26,6 +26,7 @@
 //    be selected); otherwise the workgroup selects from the whole row itself.
 #include "common.h"
 #include "kernels.h"
+#include "select.h"
 
 #include <algorithm>
 
@@ -33,266 +34,6 @@ namespace csa {
 
 namespace {
 
-// ------------------------------------------------------------------ block helpers
-// Inclusive prefix sum over the block (blockDim.x a multiple of 64, <= 1024).
-__device__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp /* >= 16 */, uint32_t* total) {
-  const int l = threadIdx.x % kWave, w = threadIdx.x / kWave, nw = blockDim.x / kWave;
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t u = __shfl_up(v, o);
-    if (l >= o) v += u;
-  }
-  if (l == kWave - 1) tmp[w] = v;
-  __syncthreads();
-  uint32_t base = 0, tot = 0;
-  for (int i = 0; i < nw; ++i) {
-    if (i < w) base += tmp[i];
-    tot += tmp[i];
-  }
-  __syncthreads();
-  if (total) *total = tot;
-  return v + base;
-}
-
-// Wave-wide min / max of a uint32 with DPP row ops (VALU, no LDS round trip):
-// reduce within each 16-lane row, then combine the four rows via readlane.
-template <bool MAX>
-__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
-  auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
-  // quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-  return op(op(r0, r1), op(r2, r3));
-}
-
-struct SelShared {
-  uint32_t hist[2][256];
-  uint32_t tmp[16];
-  uint32_t tmn[16], tmx[16];
-  uint32_t bin, above, cnt, last_pos;
-  uint32_t nfin;
-  __attribute__((aligned(16))) uint32_t fkey[64];
-  __attribute__((aligned(16))) uint32_t fpos[64];
-  uint32_t T, krem;
-};
-
-// Exact threshold of the top-k of n keys (key(i) for i < n, tie order = i
-// ascending; 1 <= k < n): the k-th largest key T and the number krem of its
-// copies that are taken (the lowest-positioned ones).
-// Radix select over the live key range: each pass splits the current range
-// [lo, hi] into <= 256 equal bins (not fixed digits, so scores that share
-// their top bits still spread out), keeps the bin holding the k-th key, and
-// stops as soon as that bin holds <= 64 keys, which one wave then ranks
-// exactly by (key desc, position asc).
-template <typename KeyFn>
-__device__ void radix_threshold(KeyFn key, int n, int k, SelShared& sh, uint32_t* T_out, uint32_t* krem_out) {
-  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
-  // key range
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  for (int base = threadIdx.x; base < n; base += 8 * blockDim.x) {
-    uint32_t kv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = base + j * blockDim.x;
-      kv[j] = i < n ? key(i) : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (base + j * (int)blockDim.x < n) {
-        mn = min(mn, kv[j]);
-        mx = max(mx, kv[j]);
-      }
-  }
-  mn = wave_reduce_u32<false>(mn);
-  mx = wave_reduce_u32<true>(mx);
-  if (lane == 0) {
-    sh.tmn[wv] = mn;
-    sh.tmx[wv] = mx;
-  }
-  for (int i = threadIdx.x; i < 512; i += blockDim.x) (&sh.hist[0][0])[i] = 0;
-  __syncthreads();
-  uint32_t lo = sh.tmn[0], hi = sh.tmx[0];
-  for (int i = 1; i < nw; ++i) {
-    lo = min(lo, sh.tmn[i]);
-    hi = max(hi, sh.tmx[i]);
-  }
-  uint32_t krem = (uint32_t)k;
-  bool finish = false;
-  for (int pass = 0; pass < 5 && !finish; ++pass) {
-    const uint32_t span = hi - lo;
-    if (span == 0) break;  // every key left in range is equal: T = lo
-    const int bits = 32 - __clz(span);
-    const int shift = bits > 8 ? bits - 8 : 0;
-    uint32_t* hist = sh.hist[pass & 1];
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) sh.hist[(pass + 1) & 1][i] = 0;
-    for (int base = threadIdx.x; base < n; base += 8 * blockDim.x) {
-      uint32_t kv[8];  // all loads first: one memory latency per 8 keys when key() reads memory
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int i = base + j * blockDim.x;
-        kv[j] = i < n ? key(i) : 0u;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int i = base + j * blockDim.x;
-        if (i < n && kv[j] >= lo && kv[j] <= hi) atomicAdd(&hist[(kv[j] - lo) >> shift], 1u);
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x < kWave) {  // one wave: lane L owns bins 4L..4L+3; suffix sums by shuffles
-      const int L = threadIdx.x;
-      const uint32_t h0 = hist[4 * L], h1 = hist[4 * L + 1], h2 = hist[4 * L + 2], h3 = hist[4 * L + 3];
-      const uint32_t mine = h0 + h1 + h2 + h3;
-      uint32_t suf = mine;  // inclusive suffix over lanes >= L
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t u = __shfl_down(suf, o);
-        if (L + o < kWave) suf += u;
-      }
-      uint32_t run = suf - mine;  // keys in bins above this lane's four
-      const uint32_t hh[4] = {h0, h1, h2, h3};
-#pragma unroll
-      for (int d = 3; d >= 0; --d) {
-        if (run < krem && run + hh[d] >= krem) {
-          sh.bin = 4 * L + d;
-          sh.above = run;
-          sh.cnt = hh[d];
-        }
-        run += hh[d];
-      }
-      if (L == 0) sh.nfin = 0;
-    }
-    __syncthreads();
-    const uint32_t nlo = lo + (sh.bin << shift);
-    const uint32_t nhi = min(hi, nlo + ((1u << shift) - 1u));
-    krem -= sh.above;
-    finish = sh.cnt <= 64;
-    lo = nlo;
-    hi = nhi;
-  }
-  if (finish && hi != lo) {
-    // gather the <= 64 keys of [lo, hi] with their positions, then rank them in one wave
-    for (int base = threadIdx.x; base < n; base += 8 * blockDim.x) {
-      uint32_t kv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int i = base + j * blockDim.x;
-        kv[j] = i < n ? key(i) : 0u;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int i = base + j * blockDim.x;
-        if (i < n && kv[j] >= lo && kv[j] <= hi) {
-          const uint32_t slot = atomicAdd(&sh.nfin, 1u);
-          sh.fkey[slot] = kv[j];
-          sh.fpos[slot] = (uint32_t)i;
-        }
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x < kWave) {  // one wave ranks the <= 64 gathered keys (broadcast reads, 8 at a time)
-      const int c = (int)sh.nfin, L = threadIdx.x;
-      for (int i = c + L; i < 64; i += kWave) {  // pad to whole groups of 8 with keys that never rank
-        sh.fkey[i] = 0u;
-        sh.fpos[i] = 0xffffffffu;
-      }
-      const uint32_t myk = L < c ? sh.fkey[L] : 0u, myp = L < c ? sh.fpos[L] : 0xffffffffu;
-      uint32_t rank = 0, gt = 0;
-      for (int i0 = 0; i0 < c; i0 += 8) {
-        const uint4 k0 = *(const uint4*)&sh.fkey[i0], k1 = *(const uint4*)&sh.fkey[i0 + 4];
-        const uint4 p0 = *(const uint4*)&sh.fpos[i0], p1 = *(const uint4*)&sh.fpos[i0 + 4];
-        const uint32_t kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-        const uint32_t pp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          rank += kk[j] > myk || (kk[j] == myk && pp[j] < myp);
-          gt += kk[j] > myk;
-        }
-      }
-      if (L < c && rank == krem - 1) {
-        sh.T = myk;
-        sh.krem = krem - gt;
-      }
-    }
-    __syncthreads();
-    *T_out = sh.T;
-    *krem_out = sh.krem;
-    return;
-  }
-  *T_out = lo;  // range collapsed to one key value: take krem copies of it
-  *krem_out = krem;
-}
-
-// Ascending-order compaction of the selected positions (key > T, or key == T
-// among the first krem copies).  emit(pos, rank) is called once per selected
-// position with its rank 0..k-1.  Sets sh.last_pos to the position of the last
-// copy of T taken.  Each wave owns a contiguous chunk and walks it 64 keys per
-// step (lane i <-> key base+i, conflict-free); ballots give in-wave ranks and
-// one barrier gives every wave its offsets.
-template <typename KeyFn, typename Emit>
-__device__ void compact_selected(KeyFn key, int n, uint32_t T, uint32_t krem, SelShared& sh, Emit emit) {
-  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
-  const int chunk = (n + nw * kWave - 1) / (nw * kWave) * kWave;  // whole 64-key steps per wave
-  const int lo = min(n, wv * chunk), hi = min(n, lo + chunk);
-  const uint64_t below = (1ull << lane) - 1ull;
-  uint32_t gt = 0, eq = 0;
-  for (int b0 = lo; b0 < hi; b0 += 4 * kWave) {
-    uint32_t kv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = b0 + j * kWave + lane;
-      kv[j] = i < hi ? key(i) : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = b0 + j * kWave + lane;
-      gt += (uint32_t)__popcll(__ballot(i < hi && kv[j] > T));
-      eq += (uint32_t)__popcll(__ballot(i < hi && kv[j] == T));
-    }
-  }
-  if (lane == 0) {
-    sh.tmn[wv] = gt;
-    sh.tmx[wv] = eq;
-  }
-  __syncthreads();
-  uint32_t gt_before = 0, eq_before = 0;
-  for (int w = 0; w < wv; ++w) {
-    gt_before += sh.tmn[w];
-    eq_before += sh.tmx[w];
-  }
-  uint32_t taken_before = eq_before >= krem ? krem : eq_before;  // copies of T taken by earlier waves
-  uint32_t rank = gt_before + taken_before;
-  uint32_t eq_seen = eq_before;
-  for (int b0 = lo; b0 < hi; b0 += 4 * kWave) {
-    uint32_t kvs[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = b0 + j * kWave + lane;
-      kvs[j] = i < hi ? key(i) : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-    const int i = b0 + j * kWave + lane;
-    const uint32_t kv = kvs[j];
-    const bool is_eq = i < hi && kv == T;
-    const uint64_t eqm = __ballot(is_eq);
-    const uint32_t my_eq_rank = eq_seen + (uint32_t)__popcll(eqm & below);  // copies of T before me
-    const bool s = (i < hi && kv > T) || (is_eq && my_eq_rank < krem);
-    const uint64_t sm = __ballot(s);
-    if (s) {
-      emit(i, rank + (uint32_t)__popcll(sm & below));
-      if (is_eq && my_eq_rank == krem - 1) sh.last_pos = (uint32_t)i;
-    }
-    rank += (uint32_t)__popcll(sm);
-    eq_seen += (uint32_t)__popcll(eqm);
-    }
-  }
-  __syncthreads();
-}
-
-// n fp32 scores -> order-preserving keys in LDS; 8 float4 loads in flight per thread.
 __device__ void load_keys(const float* __restrict__ src, int n, uint32_t* keys) {
   const bool vec = (((uintptr_t)src) & 15) == 0;
   const int n4 = vec ? n / 4 : 0;
@@ -348,12 +89,6 @@ constexpr int kCandThreads = 256;
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeCap = 8192;     // candidates a merge workgroup holds in LDS
 
-struct SliceMeta {   // per (row, slice)
-  uint32_t count;    // candidates written
-  uint32_t trunc;    // 1 when the slice held more than C visible keys
-  uint32_t last_key; // C-th kept element (the smallest kept in the order)
-  uint32_t last_idx;
-};
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -393,7 +128,7 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(const float* __
 
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float* __restrict__ scores,
                                                                    const int32_t* __restrict__ q_pos, int n_cap,
-                                                                   int m, int k, int C, int nslices,
+                                                                   int m, int k, int C, int nslices, int slice,
                                                                    const uint2* __restrict__ cand,
                                                                    const SliceMeta* __restrict__ meta,
                                                                    int32_t* __restrict__ idx) {
@@ -411,7 +146,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float* 
     return;
   }
   const float* srow = scores + row * n_cap;
-  const int ns = (V + kSlice - 1) / kSlice;
+  const int ns = (V + slice - 1) / slice;
   bool full = C == 0;
   if (!full) {
     // gather the slices' lists in slice order (= ascending index order)
@@ -425,7 +160,16 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float* 
     const int M = (int)tot;
     if (threadIdx.x < ns) cnts[threadIdx.x] = cnt;
     __syncthreads();
+    // A row that sees fewer blocks than the capacity has fewer slices: when its
+    // candidates are not more than k (and some slice was truncated, since V > k),
+    // they cannot decide the selection; the whole row does.
+    if (M <= k) full = true;
+  }
+  if (!full) {
+    const SliceMeta* mr = meta + row * nslices;
     const uint2* src = cand + row * nslices * C;
+    const uint32_t tot = (uint32_t)(offs[ns - 1] + cnts[ns - 1]);
+    const int M = (int)tot;
     const int total = ns * C;  // <= kMergeCap
     for (int base = threadIdx.x; base < total; base += 8 * kMergeThreads) {
       uint2 v[8];
@@ -472,6 +216,148 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float* 
   }
 }
 
+// Pass 1, one wave per 1024-key slice: the slice's exact top-32 by a one-wave
+// radix select (no workgroup barrier), written in ascending index order.
+constexpr int kSlice32 = kWaveTopN * kWave;  // 1024
+static_assert(kSlice32 == kFusedSlice && kWaveTopC == kFusedC, "one candidate format for both passes");
+
+__global__ __launch_bounds__(256) void topk_cand32_kernel(const float* __restrict__ scores,
+                                                          const int32_t* __restrict__ q_pos, int n_cap, int m, int k,
+                                                          int nslices, uint2* __restrict__ cand,
+                                                          SliceMeta* __restrict__ meta) {
+  __shared__ WaveSelLds sl[4];
+  const int64_t row = blockIdx.y;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), L = threadIdx.x % kWave;
+  const int g = blockIdx.x * 4 + w;
+  const int V = min(visible_blocks(q_pos[row], m), n_cap);
+  if (V <= k || g >= nslices) return;  // V <= k: the merge writes every visible index
+  const int start = g * kSlice32;
+  const int n = max(0, min(kSlice32, V - start));
+  SliceMeta* mt = meta + row * nslices + g;
+  uint2* out = cand + (row * nslices + g) * kWaveTopC;
+  // lane L: positions 16L .. 16L+15 (64 contiguous bytes)
+  const float* src = scores + row * n_cap + start + kWaveTopN * L;
+  uint32_t kv[kWaveTopN];
+  const bool vec = ((((uintptr_t)(scores + row * n_cap + start)) & 15) == 0) && kWaveTopN * L + kWaveTopN <= n;
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < kWaveTopN / 4; ++q) {
+      const float4 f = ((const float4*)src)[q];
+      kv[4 * q] = float_key(f.x);
+      kv[4 * q + 1] = float_key(f.y);
+      kv[4 * q + 2] = float_key(f.z);
+      kv[4 * q + 3] = float_key(f.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kWaveTopN; ++j) kv[j] = kWaveTopN * L + j < n ? float_key(src[j]) : 0u;
+  }
+  if (n <= kWaveTopC) {  // every slot of the slice's list: its n keys, then empty (key 0) slots
+#pragma unroll
+    for (int j = 0; j < kWaveTopN; ++j) {
+      const int p = kWaveTopN * L + j;
+      if (p < kWaveTopC) out[p] = p < n ? make_uint2(kv[j], (uint32_t)(start + p)) : make_uint2(0u, 0u);
+    }
+    if (L == 0) *mt = SliceMeta{(uint32_t)n, 0u, 0u, 0u};
+    return;
+  }
+  uint32_t T, tpos;
+  wave_top32(kv, sl[w], [&](uint32_t r, int j) {
+    out[r] = make_uint2(kv[j], (uint32_t)(start + kWaveTopN * L + j));
+  }, &T, &tpos);
+  if (L == 0) *mt = SliceMeta{(uint32_t)kWaveTopC, 1u, T, (uint32_t)start + tpos};
+}
+
+// Pass 2 of the 1024-slice scheme, one 1024-thread workgroup per row: slice s's
+// list fills slots 32s .. 32s+31 (empty slots hold key 0), so slot order is
+// ascending index order and thread t holds slots 8t .. 8t+7 in registers.  The
+// threshold is found on the registers, the compaction is one block scan, and
+// the exactness certificate is the same as above.
+constexpr int kM32PerThread = kMergeCap / kRegSelThreads;  // 8
+static_assert(kM32PerThread * kRegSelThreads == kMergeCap && kWaveTopC % kM32PerThread == 0, "slot tiling");
+
+__global__ __launch_bounds__(kRegSelThreads) void topk_merge32_kernel(const float* __restrict__ scores,
+                                                                     const int32_t* __restrict__ q_pos, int n_cap,
+                                                                     int m, int k, int nslices,
+                                                                     const uint2* __restrict__ cand,
+                                                                     const SliceMeta* __restrict__ meta,
+                                                                     int32_t* __restrict__ idx) {
+  __shared__ RegSelLds rs;
+  __shared__ SelShared sh;
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int V = min(visible_blocks(q_pos[row], m), n_cap);
+  int32_t* out = idx + row * k;
+  if (V <= k) {
+    for (int i = t; i < k; i += kRegSelThreads) out[i] = i < V ? i : -1;
+    return;
+  }
+  const int ns = (V + kSlice32 - 1) / kSlice32;  // slices holding visible keys
+  SliceMeta mm{0u, 0u, 0u, 0u};
+  if (t < ns) mm = meta[row * nslices + t];
+  uint32_t kv[kM32PerThread], iv[kM32PerThread];
+  if (kM32PerThread * t < ns * kWaveTopC) {
+    const uint4* src = (const uint4*)(cand + row * nslices * kWaveTopC) + (kM32PerThread / 2) * t;
+#pragma unroll
+    for (int q = 0; q < kM32PerThread / 2; ++q) {
+      const uint4 v = src[q];
+      kv[2 * q] = v.x;
+      iv[2 * q] = v.y;
+      kv[2 * q + 1] = v.z;
+      iv[2 * q + 1] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kM32PerThread; ++j) kv[j] = iv[j] = 0u;
+  }
+  uint32_t lo, hi, M;
+  block_key_range(kv, rs, &lo, &hi, &M);
+  // A row that sees fewer blocks than the capacity has fewer slices: when its
+  // candidates are not more than k (and some slice was truncated, since V > k),
+  // they cannot decide the selection; the whole row does.
+  bool full = M <= (uint32_t)k;
+  if (!full) {
+    uint32_t T, krem;
+    block_threshold_regs(kv, lo, hi, (uint32_t)k, rs, &T, &krem);
+    // compaction in slot order: one scan of (keys > T) | (copies of T) << 16
+    uint32_t gtc = 0, eqc = 0;
+#pragma unroll
+    for (int j = 0; j < kM32PerThread; ++j) {
+      gtc += kv[j] > T;
+      eqc += kv[j] == T;
+    }
+    const uint32_t packed = gtc | (eqc << 16);
+    uint32_t tot;
+    const uint32_t excl = block_scan_regsel(packed, rs.scan[2], &tot) - packed;
+    uint32_t eq_seen = excl >> 16;
+    uint32_t r = (excl & 0xffffu) + min(eq_seen, krem);
+#pragma unroll
+    for (int j = 0; j < kM32PerThread; ++j) {
+      const bool is_eq = kv[j] == T;
+      const bool keep = kv[j] > T || (is_eq && eq_seen < krem);
+      if (is_eq && eq_seen == krem - 1u) rs.jT = iv[j];  // the last copy of T taken
+      eq_seen += is_eq;
+      if (keep && r < (uint32_t)k) out[r] = (int32_t)iv[j];
+      r += keep;
+    }
+    __syncthreads();
+    // exact unless a truncated slice had its 32nd kept element selected
+    const uint32_t jT = rs.jT;
+    if (t < ns && mm.trunc && (mm.last_key > T || (mm.last_key == T && mm.last_idx <= jT))) rs.bad = 1u;
+    __syncthreads();
+    full = rs.bad != 0u;
+  }
+  if (full) {  // select from the whole row (slow path; any input)
+    const float* srow = scores + row * n_cap;
+    auto key = [&](int i) { return float_key(srow[i]); };
+    uint32_t T, krem;
+    radix_threshold(key, V, k, sh, &T, &krem);
+    compact_selected(key, V, T, krem, sh, [&](int pos, uint32_t r) {
+      if (r < (uint32_t)k) out[r] = pos;
+    });
+  }
+}
+
 // C for a row length: the merge holds nslices * C candidates in LDS.
 __host__ inline int cand_per_slice(int n_cap, int k) {
   const int ns = (n_cap + kSlice - 1) / kSlice;
@@ -487,7 +373,10 @@ size_t topk_workspace_bytes(int64_t rows, int n_cap, int k) {
   if (n_cap <= kTopkLdsMax) return 0;
   const int ns = (n_cap + kSlice - 1) / kSlice;
   const int C = cand_per_slice(n_cap, k);
-  return align256((size_t)rows * ns * sizeof(SliceMeta)) + align256((size_t)rows * ns * (C > 0 ? C : 1) * 8);
+  const size_t wide = align256((size_t)rows * ns * sizeof(SliceMeta)) + align256((size_t)rows * ns * (C > 0 ? C : 1) * 8);
+  const int ns32 = (n_cap + kSlice32 - 1) / kSlice32;
+  const size_t narrow = align256((size_t)rows * ns32 * sizeof(SliceMeta)) + align256((size_t)rows * ns32 * kWaveTopC * 8);
+  return std::max(wide, narrow);
 }
 
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int tq, int n_cap, int m, int k,
@@ -500,6 +389,18 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int
                        idx);
     return hipGetLastError();
   }
+  {
+    const int ns32 = (n_cap + kSlice32 - 1) / kSlice32;
+    if (ns32 <= kMergeThreads && ns32 * kWaveTopC <= kMergeCap && ns32 * kWaveTopC >= k) {
+      SliceMeta* meta = (SliceMeta*)ws;
+      uint2* cand = (uint2*)((char*)ws + align256((size_t)rows * ns32 * sizeof(SliceMeta)));
+      hipLaunchKernelGGL(topk_cand32_kernel, dim3((unsigned)((ns32 + 3) / 4), (unsigned)rows), dim3(256), 0, s, scores,
+                         q_pos, n_cap, m, k, ns32, cand, meta);
+      hipLaunchKernelGGL(topk_merge32_kernel, dim3((unsigned)rows), dim3(kRegSelThreads), 0, s, scores, q_pos, n_cap,
+                         m, k, ns32, cand, meta, idx);
+      return hipGetLastError();
+    }
+  }
   const int ns = (n_cap + kSlice - 1) / kSlice;
   const int C = cand_per_slice(n_cap, k);
   SliceMeta* meta = (SliceMeta*)ws;
@@ -508,7 +409,44 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int
     hipLaunchKernelGGL(topk_cand_kernel, dim3(ns, (unsigned)rows), dim3(kCandThreads), 0, s, scores, q_pos, n_cap, m,
                        k, C, ns, cand, meta);
   hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)rows), dim3(kMergeThreads), 0, s, scores, q_pos, n_cap, m, k, C,
-                     ns, cand, meta, idx);
+                     ns, kSlice, cand, meta, idx);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fused with the indexer
+namespace {
+__host__ inline int fused_slices(int n_cap) { return (n_cap + kFusedSlice - 1) / kFusedSlice; }
+}  // namespace
+
+bool index_topk_fused_ok(const IndexArgs& a, int k) {
+  // MXFP4 keys (the indexer that emits candidates), long rows, and a candidate set that
+  // fits the merge pass: nslices * 32 entries in LDS, one thread per slice for the scan
+  const int ns = fused_slices(a.n_cap);
+  return a.k.dtype == CSA_MXFP4 && a.n_cap > kTopkLdsMax && ns <= kMergeThreads &&
+         (int64_t)ns * kFusedC <= kMergeCap && (int64_t)ns * kFusedC >= k;
+}
+
+size_t index_topk_workspace_bytes(int64_t rows, int n_cap, int k) {
+  if (n_cap <= kTopkLdsMax) return 0;
+  const int ns = fused_slices(n_cap);
+  return align256((size_t)rows * ns * sizeof(SliceMeta)) + align256((size_t)rows * ns * kFusedC * 8);
+}
+
+hipError_t launch_index_topk(const IndexArgs& a, int k, int32_t* idx, void* ws, hipStream_t s) {
+  const int64_t rows = (int64_t)a.batch * a.tq;
+  if (rows == 0) return hipSuccess;
+  const int ns = fused_slices(a.n_cap);
+  CandOut co;
+  co.C = kFusedC;
+  co.slice = kFusedSlice;
+  co.nslices = ns;
+  co.k = k;
+  co.meta = (SliceMeta*)ws;
+  co.cand = (uint2*)((char*)ws + align256((size_t)rows * ns * sizeof(SliceMeta)));
+  hipError_t e = launch_index_scores_cand(a, co, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_merge32_kernel, dim3((unsigned)rows), dim3(kRegSelThreads), 0, s, a.scores, a.q_pos,
+                     a.n_cap, a.m, k, ns, co.cand, co.meta, idx);
   return hipGetLastError();
 }
 

@@ -25,8 +25,8 @@ import torch
 import synth
 
 from . import (BF16, F32, FP8_E4M3, MXFP4, csa_attn_workspace_size, csa_compress, csa_index_scores,
-               csa_quantize_fp8, csa_quantize_mxfp4, csa_sparse_attn, csa_topk, csa_topk_workspace_size, desc,
-               hca_attn)
+               csa_index_topk, csa_index_topk_workspace_size, csa_quantize_fp8, csa_quantize_mxfp4, csa_sparse_attn,
+               csa_topk, csa_topk_workspace_size, desc, hca_attn)
 
 DEV = "cuda"
 
@@ -138,6 +138,7 @@ class CsaLayer:
     out: torch.Tensor = None
     lse: torch.Tensor = None
     ws_topk: torch.Tensor = None
+    ws_itk: torch.Tensor = None
     ws_attn: torch.Tensor = None
     host: dict = field(default_factory=dict)  # host copies of small inputs (positions etc.)
 
@@ -149,6 +150,8 @@ class CsaLayer:
         self.lse = torch.empty((B, tq, self.H), dtype=torch.float32, device=DEV)
         n = csa_topk_workspace_size(B, tq, self.n_cap, self.k)
         self.ws_topk = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+        n = csa_index_topk_workspace_size(B, tq, self.n_cap, self.k)
+        self.ws_itk = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
         n = csa_attn_workspace_size(B, tq, self.H, self.D, self.k + self.W)
         self.ws_attn = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
 
@@ -173,19 +176,26 @@ class CsaLayer:
         csa_topk(self.scores, self.q_pos, self.B, self.tq, self.n_cap, self.m, self.k, self.idx, self.ws_topk,
                  self.ws_topk.numel(), stream)
 
+    def index_topk(self, stream=None):
+        csa_index_topk(self.q_idx.desc(), self.w, self.k_idx.desc(), self.q_pos, self.B, self.tq, self.HI, self.dI,
+                       self.m, self.n_cap, self.k, self.scores, self.idx, self.ws_itk, self.ws_itk.numel(), stream)
+
     def attend(self, stream=None):
         csa_sparse_attn(self.q.desc(), self.kv_cmp.desc(), self.idx, self.k, self.raw_kv.desc(), self.raw_base,
                         self.W, self.q_pos, self.B, self.tq, self.H, self.D, self.scale, self.out, self.lse,
                         self.ws_attn, self.ws_attn.numel(), stream)
 
+    stage_names = ("compress", "index+topk", "attention")
+
     def step(self, stream=None, marks=None):
-        """One pass of the CSA hot path.  `marks(i)` is called between stages (for timing)."""
-        for i, stage in enumerate((self.compress, self.index, self.topk, self.attend)):
+        """One pass of the CSA hot path (compress the new blocks, score and select with
+        the fused indexer + top-k, attend).  `marks(i)` is called between stages."""
+        for i, stage in enumerate((self.compress, self.index_topk, self.attend)):
             if marks:
                 marks(i)
             stage(stream)
         if marks:
-            marks(4)
+            marks(len(self.stage_names))
 
 
 @dataclass

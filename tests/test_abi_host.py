@@ -122,6 +122,22 @@ def test_topk_rejects_and_workspace():
     expect(E_WS, lambda stream: csa.csa_topk(P, P, 8, 1, 262144, 4, 2048, P, None, need, stream))
 
 
+def test_index_topk_rejects_and_workspace():
+    q, k = T(csa.F32), T(csa.MXFP4, scale=P)
+    need = csa.csa_index_topk_workspace_size(8, 1, 262144, 2048)
+    assert need >= csa.csa_topk_workspace_size(8, 1, 262144, 2048) > 0
+    assert csa.csa_index_topk_workspace_size(8, 1, 16896, 512) == 0
+
+    def call(idx=P, kk=2048, ws=P, wsb=need, heads=8):
+        return lambda stream: csa.csa_index_topk(q, P, k, P, 8, 1, heads, 64, 4, 262144, kk, P, idx, ws, wsb, stream)
+
+    expect(E_NULL, call(idx=None))
+    expect(E_SHAPE, call(kk=0))
+    expect(E_WS, call(wsb=need - 1))
+    expect(E_WS, call(ws=None))
+    expect(E_UNSUP, call(heads=33))
+
+
 # ---------------------------------------------------------------------------- attention
 
 

@@ -195,6 +195,9 @@ def test_index_scores(gpu_lib, B, Tq, HI, dI, N, kfmt):
     (1, 1, 1024, 32, "normal"), (2, 4, 16896, 512, "normal"), (1, 3, 5000, 512, "ties"),
     (2, 2, 3000, 100, "short"), (2, 1, 40000, 2048, "normal"), (1, 2, 70000, 1024, "ties"),
     (1, 1, 30000, 700, "equal"), (3, 1, 262144, 2048, "normal"),
+    (4, 2, 65536, 2048, "partial"), (3, 1, 262144, 2048, "partial"),
+    (1, 2, 70000, 1024, "extreme"), (2, 1, 262144, 2048, "extreme"), (1, 1, 16000, 512, "extreme"),
+    (1, 2, 70000, 1024, "tiny"), (2, 1, 262144, 2048, "narrow"),
 ])
 def test_topk_exact(gpu_lib, B, Tq, N, k, mode):
     csa = gpu_lib
@@ -205,12 +208,28 @@ def test_topk_exact(gpu_lib, B, Tq, N, k, mode):
         s[s == 0] = np.where(r.random(int((s == 0).sum())) < 0.5, -0.0, 0.0).astype(np.float32)
     elif mode == "equal":
         s = np.zeros((B, Tq, N), np.float32)
+    elif mode == "extreme":  # infinities and near-overflow magnitudes among normal scores
+        s = r.standard_normal((B, Tq, N)).astype(np.float32)
+        hit = r.random((B, Tq, N))
+        s[hit < 0.002] = np.inf
+        s[(hit >= 0.002) & (hit < 0.004)] = -np.inf
+        s[(hit >= 0.004) & (hit < 0.006)] = 3e38
+        s[(hit >= 0.006) & (hit < 0.008)] = -3e38
+    elif mode == "tiny":  # subnormal scores: a score span too small to divide by
+        s = (r.integers(-6, 6, (B, Tq, N)) * 1e-45).astype(np.float32)
+    elif mode == "narrow":  # distinct scores packed into a few ulps around 1
+        s = (1.0 + r.integers(0, 4000, (B, Tq, N)) * np.float32(2.0 ** -23)).astype(np.float32)
     else:
         s = r.standard_normal((B, Tq, N)).astype(np.float32)
     pos = np.full((B, Tq), N * m - 1, np.int32)
     if mode == "short":
         pos[:, 0] = 4 * 40 - 1  # only 40 visible < k: padding
         pos[-1, -1] = 4 * 100 - 1  # exactly k visible
+    elif mode == "partial":
+        # rows that see only part of the cache: their few slices hold fewer candidates
+        # than k (and one holds just over k), so the selection must fall back to the row
+        pos[:, 0] = r.integers(k * m + 4, (N // 8) * m, B)
+        pos[0, 0] = (k + 1) * m - 1
     elif Tq > 1:
         pos[0, 1] = (N // 2) * m + 2  # a shorter row
     idx = torch.full((B, Tq, k), -7, dtype=torch.int32, device="cuda")
@@ -219,6 +238,59 @@ def test_topk_exact(gpu_lib, B, Tq, N, k, mode):
     got = down(idx)
     want = oracle.topk(s.astype(np.float64), pos, m, k)
     np.testing.assert_array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------- fused index + top-k
+
+
+@pytest.mark.parametrize("B,Tq,HI,N,k,mode", [
+    (2, 1, 8, 65536, 2048, "normal"),
+    (3, 1, 8, 262144, 2048, "normal"),   # the 1M-context decode shape
+    (2, 2, 32, 40000, 1024, "normal"),   # 32 heads, ragged last slice
+    (2, 1, 8, 65536, 2048, "cluster"),   # one slice holds most top scores: the exact fallback runs
+    (1, 1, 8, 30000, 512, "equal"),      # all scores equal: the lowest indices win
+    (2, 3, 8, 40000, 2048, "short"),     # some rows see at most k blocks
+    (3, 2, 8, 262144, 2048, "partial"),  # rows seeing a fraction of the cache: few candidates
+])
+def test_index_topk_fused(gpu_lib, B, Tq, HI, N, k, mode):
+    """csa_index_topk == csa_index_scores then csa_topk, bit for bit (scores and idx),
+    and idx == the oracle's top-k of those scores."""
+    csa = gpu_lib
+    m, dI = 4, 64
+    r = _rng(f"itk{B}{Tq}{HI}{N}{k}{mode}")
+    q = r.standard_normal((B, Tq, HI, dI)).astype(np.float32)
+    w = r.standard_normal((B, Tq, HI)).astype(np.float32)
+    pos = r.integers(N * m // 2, N * m, (B, Tq)).astype(np.int32)
+    pos[0, 0] = N * m - 1
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(int(r.integers(1 << 31)))
+    kraw = torch.randn((B, N, dI), generator=gen, device="cuda")
+    if mode == "cluster":
+        w = np.abs(w)
+        kraw[:, 5 * 1024:6 * 1024] = 3.0 * up(q[:, 0, 0])[:, None, :]
+    elif mode == "equal":
+        kraw[:] = kraw[:, :1]
+    elif mode == "short":
+        pos[1, :] = r.integers(0, k * m // 2, Tq)
+    elif mode == "partial":
+        pos[:, 1] = r.integers(k * m + 4, (N // 16) * m, B)
+    kc = torch.empty((B, N, dI // 2), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((B, N, dI // 32), dtype=torch.uint8, device="cuda")
+    csa.csa_quantize_mxfp4(kraw, B * N, dI, kc, ks)
+    qd, kd = csa.desc(up(q), csa.F32), csa.desc(kc, csa.MXFP4, ks)
+    wt, pt = up(w), up(pos)
+    s1 = torch.full((B, Tq, N), float("nan"), device="cuda")
+    i1 = torch.full((B, Tq, k), -7, dtype=torch.int32, device="cuda")
+    csa.csa_index_scores(qd, wt, kd, pt, B, Tq, HI, dI, m, N, s1)
+    ws1 = workspace(csa.csa_topk_workspace_size(B, Tq, N, k))
+    csa.csa_topk(s1, pt, B, Tq, N, m, k, i1, ws1, ws1.numel())
+    s2 = torch.full((B, Tq, N), float("nan"), device="cuda")
+    i2 = torch.full((B, Tq, k), -7, dtype=torch.int32, device="cuda")
+    ws2 = workspace(csa.csa_index_topk_workspace_size(B, Tq, N, k))
+    csa.csa_index_topk(qd, wt, kd, pt, B, Tq, HI, dI, m, N, k, s2, i2, ws2, ws2.numel())
+    assert torch.equal(s1, s2)
+    np.testing.assert_array_equal(down(i2), down(i1))
+    np.testing.assert_array_equal(down(i2), oracle.topk(down(s2).astype(np.float64), pos, m, k))
 
 
 # ----------------------------------------------------------------------------- attention
