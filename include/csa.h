@@ -94,9 +94,9 @@ const char* csa_status_string(csa_status s);
 const char* csa_last_error(void);
 
 /* ---------------------------------------------------------------------------
- * (a) KV compression.  "CSA compresses the KV cache by a factor m by combining
- * adjacent entries"; HCA does the same with m' >> m (b-lab.team summary,
- * Core Methodological Innovations 1, CSA and HCA bullets).  Reading of the
+ * (a) KV compression.  CSA shrinks the KV cache m-fold by merging each run of
+ * m neighbouring entries into one; HCA does the same with a much larger m'
+ * (b-lab.team summary, Core Methodological Innovations 1, CSA and HCA bullets).  Reading of the
  * merge: c_j = sum_{r<m} softmax(logits)_r * x[j*m + r], one logit per offset,
  * shared by every channel and block, softmax computed in fp32 (max-subtracted),
  * terms accumulated in fp32 in ascending r.
@@ -121,10 +121,10 @@ csa_status csa_compress(const csa_tensor* raw, const int32_t* raw_base, const fl
                         int32_t batch, const csa_tensor* out, void* stream);
 
 /* ---------------------------------------------------------------------------
- * (b) Lightning-indexer scores.  "The indexer computes scores using low-rank
- * projections of query hidden states h_t to select the top-k most relevant
- * compressed KV blocks" (b-lab.team summary, Core Methodological Innovations 1,
- * CSA bullet); the indexer QK path is FP4 (same page, item 4, Quantization-
+ * (b) Lightning-indexer scores.  The indexer scores every compressed block
+ * from low-rank projections of the query's hidden state, and its scores pick
+ * the k blocks to attend to (b-lab.team summary, Core Methodological
+ * Innovations 1, CSA bullet); the indexer QK path is FP4 (same page, item 4, Quantization-
  * Aware Training).  Reading of the formula (the pages give none): the
  * DeepSeek-V3.2 lightning-indexer form
  *     I[b,t,j] = sum_h w[b,t,h] * max(0, <q_idx[b,t,h], k_idx[b,j]>)
@@ -147,8 +147,8 @@ csa_status csa_index_scores(const csa_tensor* q_idx, const float* w, const csa_t
                             int32_t idx_dim, int32_t m, int32_t n_cap, float* scores, void* stream);
 
 /* ---------------------------------------------------------------------------
- * (c) Top-k block selection ("select the top-k most relevant compressed KV
- * blocks", b-lab.team summary, Core Methodological Innovations 1, CSA bullet).
+ * (c) Top-k block selection: the k highest-scoring compressed blocks of each
+ * query (b-lab.team summary, Core Methodological Innovations 1, CSA bullet).
  * Reading of the order: score descending, then block index ascending; -0.0
  * equals +0.0.  Only the visible blocks j < (q_pos+1)/m of each row take part.
  *
@@ -182,8 +182,8 @@ size_t csa_index_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, i
 
 /* ---------------------------------------------------------------------------
  * (d) CSA sparse attention: attention over the selected compressed entries
- * plus a sliding window of raw local entries ("supplemented by a sliding
- * window of local KV entries", b-lab.team summary, Core Methodological
+ * plus a sliding window of raw local entries, which both CSA and HCA add to
+ * keep fine-grained local context (b-lab.team summary, Core Methodological
  * Innovations 1, HCA bullet).  Readings: key = value = the stored row (shared
  * MQA latent); the entry list is the selected compressed rows followed by the
  * window's raw rows, not de-duplicated, in ONE softmax:
@@ -210,9 +210,9 @@ csa_status csa_sparse_attn(const csa_tensor* q, const csa_tensor* kv_cmp, const 
 
 /* ---------------------------------------------------------------------------
  * (e) HCA attention: dense attention over every complete heavily-compressed
- * block plus the same sliding window ("reduces the KV cache by m' ... while
- * maintaining dense attention for the remaining entries", b-lab.team summary,
- * Core Methodological Innovations 1, HCA bullet).  Same readings and formats
+ * block plus the same sliding window: HCA compresses m'-fold and then attends
+ * densely to everything that remains (b-lab.team summary, Core Methodological
+ * Innovations 1, HCA bullet).  Same readings and formats
  * as csa_sparse_attn; the compressed entries of a query at t are blocks
  * 0 .. (t+1)/m_hc - 1 of kv_hc (precondition: <= n_cap_hc).
  *   ws  at least csa_attn_workspace_size(batch, tq, heads, dim, n_cap_hc + window).

@@ -1,6 +1,6 @@
 // (c) Per-query top-k selection of compressed blocks.
 //
-// The indexer's scores choose "the top-k most relevant compressed KV blocks"
+// The indexer's scores pick the k compressed blocks each query attends to
 // (b-lab.team summary of DeepSeek-V4, Core Methodological Innovations 1, CSA
 // bullet).  Reading of the order: score descending, then block index
 // ascending; the selected set is written in ascending index order, padded
