@@ -120,6 +120,28 @@ csa_status csa_compress(const csa_tensor* raw, const int32_t* raw_base, const fl
                         int32_t dim, const int32_t* block_first, const int32_t* block_count, int32_t max_blocks,
                         int32_t batch, const csa_tensor* out, void* stream);
 
+/* Several independent compressions in one launch (e.g. the KV stream and the
+ * indexer-key stream of a decode step, whose short chains of dependent loads
+ * then overlap).  Each job has exactly the arguments, preconditions and result
+ * of one csa_compress call; jobs must not write the same output rows.  The job
+ * array is HOST memory, read before the call returns; n_jobs <= 4.  Any
+ * invalid job fails the whole call (nothing is enqueued); the error message
+ * names the job. */
+#define CSA_MAX_COMPRESS_JOBS 4
+typedef struct csa_compress_job {
+  csa_tensor raw;
+  const int32_t* raw_base;
+  const float* logits;
+  int32_t m;
+  int32_t dim;
+  const int32_t* block_first;
+  const int32_t* block_count;
+  int32_t max_blocks;
+  int32_t batch;
+  csa_tensor out;
+} csa_compress_job;
+csa_status csa_compress_jobs(const csa_compress_job* jobs, int32_t n_jobs, void* stream);
+
 /* ---------------------------------------------------------------------------
  * (b) Lightning-indexer scores.  The indexer scores every compressed block
  * from low-rank projections of the query's hidden state, and its scores pick

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m long_context_attention_04_amd.build` "
+        f"{LIB_PATH} is not built; run `python long_context_attention_04_amd/build.py` "
         "(or __graft_entry__.build()) first")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -50,6 +50,23 @@ class CsaTensor(ctypes.Structure):
     ]
 
 
+class CsaCompressJob(ctypes.Structure):
+    _fields_ = [
+        ("raw", CsaTensor),
+        ("raw_base", ctypes.c_void_p),
+        ("logits", ctypes.c_void_p),
+        ("m", ctypes.c_int32),
+        ("dim", ctypes.c_int32),
+        ("block_first", ctypes.c_void_p),
+        ("block_count", ctypes.c_void_p),
+        ("max_blocks", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("out", CsaTensor),
+    ]
+
+
+MAX_COMPRESS_JOBS = 4
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -70,6 +87,7 @@ _c = {
     "csa_status_string": _proto("csa_status_string", ctypes.c_char_p, _I32),
     "csa_last_error": _proto("csa_last_error", ctypes.c_char_p),
     "csa_compress": _proto("csa_compress", _I32, _TP, _P, _P, _I32, _I32, _P, _P, _I32, _I32, _TP, _P),
+    "csa_compress_jobs": _proto("csa_compress_jobs", _I32, ctypes.POINTER(CsaCompressJob), _I32, _P),
     "csa_index_scores": _proto("csa_index_scores", _I32, _TP, _P, _TP, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P),
     "csa_topk": _proto("csa_topk", _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P),
     "csa_topk_workspace_size": _proto("csa_topk_workspace_size", _SZ, _I32, _I32, _I32, _I32),
@@ -142,6 +160,16 @@ def csa_last_error() -> str:
 def csa_compress(raw, raw_base, logits, m, dim, block_first, block_count, max_blocks, batch, out, stream=None):
     _check(_c["csa_compress"](ctypes.byref(raw), _ptr(raw_base), _ptr(logits), m, dim, _ptr(block_first),
                               _ptr(block_count), max_blocks, batch, ctypes.byref(out), _stream(stream)))
+
+
+def csa_compress_jobs(jobs, stream=None):
+    """jobs: sequence of (raw, raw_base, logits, m, dim, block_first, block_count, max_blocks, batch, out),
+    each exactly the arguments of one csa_compress call; one launch for all of them."""
+    arr = (CsaCompressJob * max(len(jobs), 1))()
+    for i, (raw, raw_base, logits, m, dim, first, count, max_blocks, batch, out) in enumerate(jobs):
+        arr[i] = CsaCompressJob(raw, _ptr(raw_base), _ptr(logits), m, dim, _ptr(first), _ptr(count), max_blocks,
+                                batch, out)
+    _check(_c["csa_compress_jobs"](arr, len(jobs), _stream(stream)))
 
 
 def csa_index_scores(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, scores, stream=None):

@@ -1,6 +1,7 @@
 """Builds libcsa.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m long_context_attention_04_amd.build   (or build() from Python)
+Usage: python long_context_attention_04_amd/build.py   (or __graft_entry__.build()).
+Run by path, not through the package: importing the package loads the library.
 """
 from __future__ import annotations
 

@@ -79,9 +79,10 @@ const char* csa_status_string(csa_status s) {
 
 const char* csa_last_error(void) { return g_last_error.c_str(); }
 
-csa_status csa_compress(const csa_tensor* raw, const int32_t* raw_base, const float* logits, int32_t m, int32_t dim,
-                        const int32_t* block_first, const int32_t* block_count, int32_t max_blocks, int32_t batch,
-                        const csa_tensor* out, void* stream) {
+// Validates one compression's arguments and fills its launch description.
+static csa_status compress_args(const csa_tensor* raw, const int32_t* raw_base, const float* logits, int32_t m,
+                                int32_t dim, const int32_t* block_first, const int32_t* block_count,
+                                int32_t max_blocks, int32_t batch, const csa_tensor* out, csa::CompressArgs* a) {
   csa_status st;
   if ((st = check_tensor(raw, "raw")) != CSA_OK) return st;
   if ((st = check_tensor(out, "out")) != CSA_OK) return st;
@@ -92,24 +93,51 @@ csa_status csa_compress(const csa_tensor* raw, const int32_t* raw_base, const fl
   REQUIRE(batch >= 0 && max_blocks >= 0, CSA_ERR_SHAPE, "negative batch or max_blocks");
   if (out->dtype == CSA_MXFP4) REQUIRE(dim % 32 == 0, CSA_ERR_SHAPE, "MXFP4 output needs dim %% 32 == 0 (dim=%d)", dim);
   if (out->dtype == CSA_FP8_E4M3) REQUIRE(out->scale != nullptr, CSA_ERR_NULL, "FP8 output needs a row-scale pointer");
+  a->raw = csa::view_of(raw);
+  a->raw_base = raw_base;
+  a->logits = logits;
+  a->m = m;
+  a->dim = dim;
+  a->block_first = block_first;
+  a->block_count = block_count;
+  a->max_blocks = max_blocks;
+  a->batch = batch;
+  a->out = out->data;
+  a->out_scale = out->scale;
+  a->out_dtype = out->dtype;
+  a->out_sb = out->stride_b;
+  a->out_sr = out->stride_row;
+  a->out_ssb = out->scale_stride_b;
+  a->out_ssr = out->scale_stride_row;
+  return CSA_OK;
+}
+
+csa_status csa_compress(const csa_tensor* raw, const int32_t* raw_base, const float* logits, int32_t m, int32_t dim,
+                        const int32_t* block_first, const int32_t* block_count, int32_t max_blocks, int32_t batch,
+                        const csa_tensor* out, void* stream) {
   csa::CompressArgs a;
-  a.raw = csa::view_of(raw);
-  a.raw_base = raw_base;
-  a.logits = logits;
-  a.m = m;
-  a.dim = dim;
-  a.block_first = block_first;
-  a.block_count = block_count;
-  a.max_blocks = max_blocks;
-  a.batch = batch;
-  a.out = out->data;
-  a.out_scale = out->scale;
-  a.out_dtype = out->dtype;
-  a.out_sb = out->stride_b;
-  a.out_sr = out->stride_row;
-  a.out_ssb = out->scale_stride_b;
-  a.out_ssr = out->scale_stride_row;
+  const csa_status st = compress_args(raw, raw_base, logits, m, dim, block_first, block_count, max_blocks, batch,
+                                      out, &a);
+  if (st != CSA_OK) return st;
   return from_hip(csa::launch_compress(a, (hipStream_t)stream), "csa_compress launch");
+}
+
+csa_status csa_compress_jobs(const csa_compress_job* jobs, int32_t n_jobs, void* stream) {
+  REQUIRE(n_jobs >= 0 && n_jobs <= CSA_MAX_COMPRESS_JOBS, CSA_ERR_SHAPE, "n_jobs=%d outside [0, %d]", n_jobs,
+          CSA_MAX_COMPRESS_JOBS);
+  REQUIRE(jobs || n_jobs == 0, CSA_ERR_NULL, "jobs is NULL");
+  static_assert(CSA_MAX_COMPRESS_JOBS == csa::kMaxCompressJobs, "one job limit");
+  csa::CompressArgs a[CSA_MAX_COMPRESS_JOBS];
+  for (int j = 0; j < n_jobs; ++j) {
+    const csa_compress_job& J = jobs[j];
+    const csa_status st = compress_args(&J.raw, J.raw_base, J.logits, J.m, J.dim, J.block_first, J.block_count,
+                                        J.max_blocks, J.batch, &J.out, &a[j]);
+    if (st != CSA_OK) {
+      g_last_error = "job " + std::to_string(j) + ": " + g_last_error;
+      return st;
+    }
+  }
+  return from_hip(csa::launch_compress_jobs(a, n_jobs, (hipStream_t)stream), "csa_compress_jobs launch");
 }
 
 // Validates the indexer arguments and fills the launch description.

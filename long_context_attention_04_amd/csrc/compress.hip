@@ -11,6 +11,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace csa {
 
 namespace {
@@ -81,17 +83,14 @@ __device__ __forceinline__ float load_raw(const void* p, int64_t i) {
   else return e4m3_to_f32(((const uint8_t*)p)[i]);
 }
 
+// Block i of sequence b of one compression (a workgroup's whole work).
 template <int NV, int IN>  // columns per thread: dim <= 256 * NV; IN: raw row format
-__global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs a) {
-  const int b = blockIdx.y;
-  const int i = blockIdx.x;
+__device__ __forceinline__ void compress_block(const CompressArgs& a, int b, int i, float* omega_s, float* red) {
   // independent scalars first, all in flight together (one memory round trip)
   const int cnt = a.block_count[b];
   const int jfirst = a.block_first[b];
   const int rbase = a.raw_base[b];
   const int m = a.m;
-  __shared__ float omega_s[1024];
-  __shared__ float red[kCompressThreads / kWave];
   float zl[kLocalSoftmaxMax];  // logits, held by every thread when m is small
   const bool local = m <= kLocalSoftmaxMax;
   if (local) {
@@ -183,6 +182,42 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs
   store_row<NV>(acc, nv, a.out_dtype, a.out, off, a.out_scale, soff, red);
 }
 
+template <int NV, int IN>
+__global__ __launch_bounds__(kCompressThreads) void compress_kernel(CompressArgs a) {
+  __shared__ float omega_s[1024];
+  __shared__ float red[kCompressThreads / kWave];
+  compress_block<NV, IN>(a, blockIdx.y, blockIdx.x, omega_s, red);
+}
+
+// Several independent compressions in one launch (grid.z = job): small decode
+// steps are latency-bound, so their chains of dependent loads overlap instead of
+// running one launch after another.  Each job's (columns per thread, raw format)
+// variant is chosen on the host; the switch is uniform per workgroup.
+struct CompressJobs {
+  CompressArgs job[kMaxCompressJobs];
+  int variant[kMaxCompressJobs];  // 3 * log2(NV) + input format (NV in {1, 2, 4})
+};
+
+__global__ __launch_bounds__(kCompressThreads) void compress_jobs_kernel(CompressJobs js) {
+  __shared__ float omega_s[1024];
+  __shared__ float red[kCompressThreads / kWave];
+  const int z = blockIdx.z;
+  const CompressArgs& a = js.job[z];
+  const int b = blockIdx.y, i = blockIdx.x;
+  if (b >= a.batch || i >= a.max_blocks) return;
+  switch (js.variant[z]) {
+    case 0: compress_block<1, CSA_F32>(a, b, i, omega_s, red); break;
+    case 1: compress_block<1, CSA_BF16>(a, b, i, omega_s, red); break;
+    case 2: compress_block<1, CSA_FP8_E4M3>(a, b, i, omega_s, red); break;
+    case 3: compress_block<2, CSA_F32>(a, b, i, omega_s, red); break;
+    case 4: compress_block<2, CSA_BF16>(a, b, i, omega_s, red); break;
+    case 5: compress_block<2, CSA_FP8_E4M3>(a, b, i, omega_s, red); break;
+    case 6: compress_block<4, CSA_F32>(a, b, i, omega_s, red); break;
+    case 7: compress_block<4, CSA_BF16>(a, b, i, omega_s, red); break;
+    default: compress_block<4, CSA_FP8_E4M3>(a, b, i, omega_s, red); break;
+  }
+}
+
 // one thread per 32-element block
 __global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const float* __restrict__ x, int64_t nblocks,
                                                              uint8_t* __restrict__ codes,
@@ -235,6 +270,30 @@ hipError_t launch_compress_in(const CompressArgs& a, hipStream_t s) {
   else if (nv <= 4) hipLaunchKernelGGL((compress_kernel<4, IN>), grid, dim3(kCompressThreads), 0, s, a);
   else if (nv <= 8) hipLaunchKernelGGL((compress_kernel<8, IN>), grid, dim3(kCompressThreads), 0, s, a);
   else hipLaunchKernelGGL((compress_kernel<16, IN>), grid, dim3(kCompressThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_jobs(const CompressArgs* jobs, int n, hipStream_t s) {
+  CompressJobs js{};
+  int gx = 0, gy = 0, nz = 0;
+  for (int j = 0; j < n; ++j) {
+    const CompressArgs& a = jobs[j];
+    if (a.max_blocks <= 0 || a.batch <= 0) continue;
+    const int nv = (a.dim + kCompressThreads - 1) / kCompressThreads;
+    if (nv > 4) {  // wide rows: a launch of their own
+      const hipError_t e = launch_compress(a, s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    const int in = a.raw.dtype == CSA_F32 ? 0 : a.raw.dtype == CSA_BF16 ? 1 : 2;
+    js.job[nz] = a;
+    js.variant[nz] = 3 * (nv <= 1 ? 0 : nv <= 2 ? 1 : 2) + in;
+    gx = std::max(gx, a.max_blocks);
+    gy = std::max(gy, a.batch);
+    ++nz;
+  }
+  if (nz == 0) return hipSuccess;
+  hipLaunchKernelGGL(compress_jobs_kernel, dim3(gx, gy, nz), dim3(kCompressThreads), 0, s, js);
   return hipGetLastError();
 }
 

@@ -44,6 +44,8 @@ struct CompressArgs {
   int64_t out_sb, out_sr, out_ssb, out_ssr;
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+constexpr int kMaxCompressJobs = 4;
+hipError_t launch_compress_jobs(const CompressArgs* jobs, int n, hipStream_t s);  // n <= kMaxCompressJobs
 hipError_t launch_quantize_mxfp4(const float* x, int64_t rows, int cols, uint8_t* codes, uint8_t* scales,
                                  hipStream_t s);
 hipError_t launch_quantize_fp8(const float* x, int64_t rows, int cols, uint8_t* codes, float* row_scale,

@@ -24,8 +24,8 @@ import torch
 
 import synth
 
-from . import (BF16, F32, FP8_E4M3, MXFP4, csa_attn_workspace_size, csa_compress, csa_index_scores,
-               csa_index_topk, csa_index_topk_workspace_size, csa_quantize_fp8, csa_quantize_mxfp4, csa_sparse_attn,
+from . import (BF16, F32, FP8_E4M3, MXFP4, csa_attn_workspace_size, csa_compress, csa_compress_jobs,
+               csa_index_scores, csa_index_topk, csa_index_topk_workspace_size, csa_quantize_fp8, csa_quantize_mxfp4, csa_sparse_attn,
                csa_topk, csa_topk_workspace_size, desc, hca_attn)
 
 DEV = "cuda"
@@ -165,8 +165,13 @@ class CsaLayer:
                      self.max_blocks, self.B, self.k_idx.desc(), stream)
 
     def compress(self, stream=None):
-        self.compress_kv(stream)
-        self.compress_keys(stream)
+        """Both compressions of the step (KV and indexer key) in one launch."""
+        csa_compress_jobs([
+            (self.raw_kv.desc(), self.raw_base, self.z_kv, self.m, self.D, self.blk_first, self.blk_count,
+             self.max_blocks, self.B, self.kv_cmp.desc()),
+            (self.raw_ik.desc(), self.raw_base, self.z_ik, self.m, self.dI, self.blk_first, self.blk_count,
+             self.max_blocks, self.B, self.k_idx.desc()),
+        ], stream)
 
     def index(self, stream=None):
         csa_index_scores(self.q_idx.desc(), self.w, self.k_idx.desc(), self.q_pos, self.B, self.tq, self.HI, self.dI,

@@ -88,6 +88,19 @@ def test_compress_rejects():
     expect(E_SHAPE, call(raw=T(csa.BF16, sb=-1)))
 
 
+def test_compress_jobs_rejects():
+    good = (T(csa.BF16), P, P, 4, 512, P, P, 1, 2, T(csa.BF16))
+    bad = (T(csa.BF16), P, P, 0, 512, P, P, 1, 2, T(csa.BF16))  # m = 0
+    expect(E_SHAPE, lambda stream: csa.csa_compress_jobs([good] * 5, stream), match="n_jobs")
+    expect(E_SHAPE, lambda stream: csa.csa_compress_jobs([good, bad], stream), match="job 1")
+    expect(E_NULL, lambda stream: csa.csa_compress_jobs([(T(csa.BF16), P, None) + good[3:]], stream), match="job 0")
+    lib = ctypes.CDLL(csa.LIB_PATH)
+    lib.csa_compress_jobs.restype = ctypes.c_int32
+    lib.csa_compress_jobs.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    assert lib.csa_compress_jobs(None, 1, None) == E_NULL
+    assert lib.csa_compress_jobs(None, 0, None) == 0  # nothing to do, nothing launched
+
+
 # ---------------------------------------------------------------------------- indexer
 
 

@@ -137,6 +137,58 @@ def test_compress(gpu_lib, m, dim, in_dt, out_dt):
         assert np.all(np.isnan(down(out_t)[2]))
 
 
+def test_compress_jobs_match_single_calls(gpu_lib):
+    """One csa_compress_jobs launch == the same jobs as separate csa_compress calls, bit for bit
+    (every variant of the combined kernel: three input formats, 1/2/4 columns per thread, a
+    wide-row job that takes a launch of its own, and an empty job)."""
+    csa = gpu_lib
+    B = 3
+    r = _rng("cjobs")
+    specs = [(4, 512, "bf16", csa.BF16), (4, 64, "f32", csa.MXFP4), (16, 1024, "fp8", csa.FP8_E4M3),
+             (2, 200, "f32", csa.F32), (4, 2048, "bf16", csa.BF16), (3, 96, "fp8", csa.BF16)]
+    jobs_a, jobs_b, outs = [], [], []
+    for (m, dim, in_dt, out_dt) in specs:
+        R = 6 * m + 3
+        x = r.standard_normal((B, R, dim)).astype(np.float32)
+        if in_dt == "f32":
+            raw = csa.desc(up(x), csa.F32)
+        elif in_dt == "bf16":
+            raw = csa.desc(up_bf16(x)[0], csa.BF16)
+        else:
+            c, s_ = OF.quantize_fp8_rows(x.reshape(-1, dim))
+            raw = csa.desc(up(c.reshape(B, R, dim)), csa.FP8_E4M3, up(s_.reshape(B, R)))
+        z = up(r.standard_normal(m).astype(np.float32))
+        base = up(np.array([0, m, 2 * m], np.int32))
+        first = up(np.array([0, 2, 1], np.int32))
+        count = up(np.array([5, 3, 0], np.int32))
+        pair = []
+        for _ in range(2):
+            if out_dt == csa.MXFP4:
+                o = (torch.zeros((B, 8, dim // 2), dtype=torch.uint8, device="cuda"),
+                     torch.zeros((B, 8, dim // 32), dtype=torch.uint8, device="cuda"))
+            elif out_dt == csa.FP8_E4M3:
+                o = (torch.zeros((B, 8, dim), dtype=torch.uint8, device="cuda"), torch.zeros((B, 8), device="cuda"))
+            elif out_dt == csa.BF16:
+                o = (torch.zeros((B, 8, dim), dtype=torch.bfloat16, device="cuda"), None)
+            else:
+                o = (torch.zeros((B, 8, dim), device="cuda"), None)
+            pair.append(o)
+        outs.append(pair)
+        args = (raw, base, z, m, dim, first, count, 5, B)
+        jobs_a.append(args + (csa.desc(pair[0][0], out_dt, pair[0][1]),))
+        jobs_b.append(args + (csa.desc(pair[1][0], out_dt, pair[1][1]),))
+    for i in range(0, len(specs), 3):  # at most four jobs per call
+        csa.csa_compress_jobs(jobs_a[i:i + 3])
+    for j in jobs_b:
+        csa.csa_compress(*j)
+    torch.cuda.synchronize()
+    for pair in outs:
+        for ta, tb in zip(pair[0], pair[1]):
+            if ta is not None:
+                assert torch.equal(ta.view(torch.uint8) if ta.dtype == torch.bfloat16 else ta,
+                                   tb.view(torch.uint8) if tb.dtype == torch.bfloat16 else tb)
+
+
 # ----------------------------------------------------------------------------- indexer
 
 
