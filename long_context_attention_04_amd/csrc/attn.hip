@@ -10,24 +10,27 @@
 // MFMA path (bf16 / fp8 caches, 16..64 heads, dim 512).  A query row's 16..64
 // heads share one 512-wide latent row per entry, so attention is a
 // [heads x 512] x [512 x n] contraction (QK) followed by [heads x n] x [n x 512]
-// (PV), both on bf16 MFMA.  A workgroup (4 waves) takes one query row, one
-// group of 16 heads and one contiguous split of the entry list.  Each wave is
-// an independent flash-decoding worker over every 4th tile of 16 entries:
-//  * it loads whole entry rows (each lane 16 x 16 B of one row, the MFMA A
-//    layout) two tiles ahead of use, with the selection indices a further
-//    tile ahead, so row loads never wait behind an index load;
-//  * QK computes the transposed logits S^T = K Q^T (16x16x32), which leaves
-//    each lane holding four entries of one head -- exactly the A-operand
-//    layout PV needs for P, so P never moves between lanes;
+// (PV), both on bf16 MFMA.  A workgroup takes one query row, one group of 16
+// heads and one contiguous split of the entry list, with 8 waves (two per
+// SIMD, covering each other's waits).  Each wave is an independent
+// flash-decoding worker over every 8th tile of 16 entries:
+//  * it loads a tile's rows one whole row per instruction (lane L taking
+//    elements 8L .. 8L+7, the cheapest gather for the memory pipeline; the row
+//    address is scalar) one tile ahead of use, from selection indices staged
+//    in LDS once per workgroup, and stages the tile as bf16 rows in its own
+//    LDS area (fp8 rows are widened there);
+//  * QK reads the staged rows as the A operand and the workgroup's query heads
+//    (staged in LDS once) as B, giving the transposed logits S^T = K Q^T
+//    (16x16x32): each lane then holds four entries of one head -- exactly the
+//    A-operand layout PV needs for P, so P never moves between lanes;
 //  * the online softmax reduces over entries within the wave (register max,
 //    then two cross-row lane swaps) and rescales the accumulator lazily: only
 //    when a head's running maximum grows by more than 2^8, which keeps every
 //    probability <= 256 and skips almost all rescaling work;
 //  * P goes to PV as two bf16 terms (hi + lo, ~16 significant bits instead of
 //    bf16's 8), stacked along the k axis of one 16x16x32 MFMA per column tile;
-//    V is the same tile, staged in the wave's own LDS area and read transposed
-//    with ds_read_b64_tr_b16.
-// No workgroup barrier runs inside the entry loop.  At the end the four waves
+//    V is the same staged tile, read transposed with ds_read_b64_tr_b16.
+// No workgroup barrier runs inside the entry loop.  At the end the eight waves
 // combine their (max, sum, accumulator) through LDS in a fixed order; splits
 // are merged by a second kernel with a fixed-order log-sum-exp combine.  The
 // split size depends only on the call shape, never on the batch, so results
@@ -45,13 +48,16 @@ namespace csa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;  // 8: two per SIMD
 constexpr int kTile = 16;        // entries per wave step
 constexpr int kVsPitch = 528;    // bf16 per staged row: 512 + 16 pad (row stride 8 banks mod 32)
-constexpr int kMbufPitch = 516;  // floats per head row of the merge buffer (512 + 4 pad)
-// rows of staged tiles that also hold the merge buffer: 4 x 16 x 516 floats in 16 x 528 bf16 units
-constexpr int kMergeRows = (kWaves * 16 * kMbufPitch * 4 + kTile * kVsPitch * 2 - 1) / (kTile * kVsPitch * 2);
+// rows of staged tiles that also hold the merge buffer: 4 waves x 16 heads x 512 floats in 16 x 528 bf16 units
+constexpr int kMergeRows = kWaves;  // the combine buffer (4 x 16 heads x 512 floats) fits in 8 staged tiles
+static_assert(4 * 16 * 512 * 4 <= kMergeRows * kTile * kVsPitch * 2, "combine buffer fits the staging area");
+constexpr int kIdxStage = 2048;
+constexpr int kRing = 1;  // tiles of rows in flight per wave beyond the one staged (register ring)
+constexpr int kQPitch = 520;  // bf16 per staged query head row (512 + 8 pad)  // selection indices a workgroup stages (max split)
 constexpr float kRescale = 8.f;  // lazy rescale threshold (log2 units)
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
@@ -177,61 +183,78 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
   int row, s, hg;
   decode_block(blockIdx.x, nhg, nsplit_max, &row, &s, &hg);
   if (row >= rows) return;
+  const int e_begin = s * split;
+  // A CSA row's compressed entries are its k selection slots, known without reading
+  // its position, so the split's indices are staged while the position is in flight.
+  __shared__ int sidx[kIdxStage];
+  const int32_t* idx_row = a.idx ? a.idx + (int64_t)row * a.k : nullptr;
+  const int n_sel = idx_row ? max(0, min(split, a.k - e_begin)) : 0;
+  for (int t = threadIdx.x; t < n_sel; t += kThreads) sidx[t] = idx_row[e_begin + t];
   const RowInfo ri = row_info(a, row);
   const int nsplit = max(1, (ri.n_tot + split - 1) / split);
-  if (s >= nsplit) return;
+  if (s >= nsplit) return;  // workgroup-uniform: no barrier has been passed yet
   const EntrySrc src = entry_src(a, ri, row, FP8 ? 1 : 2);
-  const int e_begin = s * split, e_end = min(ri.n_tot, e_begin + split);
+  const int e_end = min(ri.n_tot, e_begin + split);
+  const int n_here = e_end - e_begin;
   const int h0 = hg * 16;  // first head of this workgroup
+  const bool sel = idx_row != nullptr && ri.n_cmp > 0;
 
   // the wave index is made visibly uniform, so per-wave control flow is scalar
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-  const int m = lane % 16, g = lane / 16;  // load role: entry m of a tile; softmax role: head m
+  const int m = lane % 16, g = lane / 16;  // operand role: entry / head m, k group g
 
-  // staged tiles during the loop; the merge buffer (kWaves x 16 x kMbufPitch floats) afterwards
+  // each wave's staged tile during the loop; the combine buffer (4 x 16 x 512 floats) afterwards
   __shared__ __attribute__((aligned(16))) uint16_t Vs[kMergeRows][kTile][kVsPitch];
-  __shared__ __attribute__((aligned(16))) float esl[kWaves][kTile];              // per-entry scale, -1 = empty
-  __shared__ float wml[kWaves][16][2];                                            // per-wave (max, sum) per head
+  __shared__ __attribute__((aligned(16))) float esl[kWaves][kTile];  // per-entry scale, -1 = empty
+  __shared__ float wml[kWaves][16][2];                                // per-wave (max, sum) per head
 
-  // Q^T as the QK B operand: head h0 + m, latent columns 32kk + 8g .. +7
+  // the workgroup's 16 query heads, staged once in LDS (the QK B operand is read from
+  // there: registers hold the row ring instead)
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[16][kQPitch];
   const uint16_t* qp = (const uint16_t*)a.q.data + (int64_t)ri.b * a.q.sb + (int64_t)ri.t * a.q.sr;
-  v8bf qb[16];
 #pragma unroll
-  for (int kk = 0; kk < 16; ++kk) qb[kk] = *(const v8bf*)(qp + (h0 + m) * 512 + 32 * kk + 8 * g);
+  for (int hh = 0; hh < 16 / kWaves; ++hh) {
+    const int h = (16 / kWaves) * w + hh;
+    *(v8bf*)&Qs[h][8 * lane] = *(const v8bf*)(qp + (h0 + h) * 512 + 8 * lane);
+  }
+  __syncthreads();  // sidx and Qs visible
 
   // This wave's tiles: w, w + 4, w + 8, ... of the split.
-  const int ntile = (e_end - e_begin + kTile - 1) / kTile;
+  const int ntile = (n_here + kTile - 1) / kTile;
   const int nt = ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0;
-  auto tile_e0 = [&](int i) { return e_begin + (w + kWaves * i) * kTile; };
 
-  // Loads are unconditional: an empty or out-of-range slot reads this query's own
-  // row instead (always a valid address), zeroes it, and is masked by a -1 scale.
+  // Row loads: one instruction per entry row, lane L taking elements 8L .. 8L+7 (a
+  // whole row per instruction, the cheapest gather for the memory pipeline), so
+  // the row address is scalar.  An empty or out-of-range slot reads this query's
+  // own row instead (always a valid address) and gets scale -1.
   const gbyte* dummy = (const gbyte*)qp;
-  const bool sel = src.idx_row != nullptr && ri.n_cmp > 0;
-  auto load_idx = [&](int i) {
-    const int e = tile_e0(i) + m;
-    return sel ? src.idx_row[min(e, ri.n_cmp - 1)] : e;
-  };
-  Raw8<FP8> kr[2][16];
-  float esc[2], scl[2];
-  bool hs[2] = {false, false};
-  auto load_tile = [&](int i, int j, int buf) {
-    const int e = tile_e0(i) + m;
+  Raw8<FP8> kr[kRing][kTile];  // [buffer][row]
+  float esc[kRing];            // lane m: entry m's scale (-1 = empty)
+  auto load_tile = [&](int i, int buf) {
+    const int el = (w + kWaves * i) * kTile + m;  // entry offset in the split (operand role)
+    const int e = e_begin + el;
     const bool cmp = e < ri.n_cmp;
+    const int j = !cmp ? 0 : sel ? sidx[min(el, n_sel - 1)] : e;
     const int64_t wr = e - ri.n_cmp;
     const bool live = i < nt && e < e_end && (!cmp || j >= 0);
     const gbyte* p = !live ? dummy
                            : cmp ? (const gbyte*)src.kv0 + (int64_t)j * src.kv_rs
                                  : (const gbyte*)src.win0 + wr * src.raw_rs;
-    esc[buf] = live ? 1.f : -1.f;
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) kr[buf][kk] = load_raw8<FP8>(p, 32 * kk + 8 * g);
+    float sc = live ? 1.f : -1.f;
     if constexpr (FP8) {
       const float* sp = nullptr;
       if (live) sp = cmp ? (src.kv_sc ? src.kv_sc + (int64_t)j * src.kv_ss : nullptr)
                          : (src.win_sc ? src.win_sc + wr * src.raw_ss : nullptr);
-      scl[buf] = *(const __attribute__((address_space(1))) float*)(sp ? sp : (const float*)qp);
-      hs[buf] = sp != nullptr;  // the stand-in value is never used
+      const float v = *(const __attribute__((address_space(1))) float*)(sp ? sp : (const float*)qp);
+      if (sp) sc = v;
+    }
+    esc[buf] = sc;
+    const uint64_t pu = (uint64_t)(uintptr_t)p;
+#pragma unroll
+    for (int r = 0; r < kTile; ++r) {
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pu, r), hi = __builtin_amdgcn_readlane((uint32_t)(pu >> 32), r);
+      const gbyte* pr = (const gbyte*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+      kr[buf][r] = load_raw8<FP8>(pr, 8 * lane);
     }
   };
 
@@ -242,51 +265,52 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
 #pragma unroll
   for (int ct = 0; ct < 32; ++ct) O[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // pipeline: rows of tiles i+1 and i+2 in flight while tile i is processed; the
-  // index of tile i+2 was loaded before tile i+1's rows, so using it never waits on them
-  const int j0 = load_idx(0), j1 = load_idx(1);
-  int jn2 = load_idx(2);
-  load_tile(0, j0, 0);
-  load_tile(1, j1, 1);
+  // pipeline: rows of the next kRing - 1 tiles in flight while tile i is processed
+#pragma unroll
+  for (int b = 0; b < kRing; ++b) load_tile(b, b);
+  typedef __attribute__((address_space(3))) v4bf lds_v4bf;
   auto step = [&](int i, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    if (g == 0) esl[w][m] = FP8 && hs[buf] ? scl[buf] : esc[buf];
-    v8bf kv[16];
-    // an fp8 stand-in row may hold NaN codes: zero it (a bf16 one is finite query data)
-    const bool dead = FP8 && esc[buf] < 0.f;
+    // stage the tile as bf16 rows in the wave's own LDS area (LDS ops of one wave run
+    // in order); an empty fp8 row is zeroed (its stand-in may hold NaN codes)
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      kv[kk] = widen8<FP8>(kr[buf][kk]);
-      if (dead) kv[kk] = (v8bf){};
+    for (int r = 0; r < kTile; ++r) {
+      v8bf v = widen8<FP8>(kr[buf][r]);
+      if (FP8 && __builtin_amdgcn_readlane(__float_as_uint(esc[buf]), r) == __float_as_uint(-1.f)) v = (v8bf){};
+      *(v8bf*)&Vs[w][r][8 * lane] = v;
     }
-    // S^T[entry 4g + r][head m] over the full latent width, four independent chains
+    if (g == 0) esl[w][m] = esc[buf];
+    // the register buffer is free: issue tile i+2's rows into it
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(i + kRing, buf);
+    __builtin_amdgcn_sched_barrier(0);
+    // S^T[entry 4g + r][head m] over the full latent width, four independent chains;
+    // A = entry m's columns 32kk + 8g .. +7 read back from the staged tile
     v4f c4[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) c4[u] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
-      c4[kk % 4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[kk], qb[kk], c4[kk % 4], 0, 0, 0);
-    // stage the tile for PV (wave-private area; LDS ops of one wave run in order)
+    for (int k4 = 0; k4 < 4; ++k4) {
+      __builtin_amdgcn_sched_barrier(0);  // bounded register use: four k blocks at a time
+      v8bf kv[4], qb[4];  // A: entry m's columns; B: Q^T, head m's columns 32kk + 8g .. +7
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) *(v8bf*)&Vs[w][m][32 * kk + 8 * g] = kv[kk];
-    // the buffer is free: issue tile i+3's index, then tile i+2's rows
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      const int j2 = jn2;
-      jn2 = load_idx(i + 3);
-      load_tile(i + 2, j2, buf);
+      for (int u = 0; u < 4; ++u) {
+        kv[u] = *(const v8bf*)&Vs[w][m][32 * (4 * k4 + u) + 8 * g];
+        qb[u] = *(const v8bf*)&Qs[m][32 * (4 * k4 + u) + 8 * g];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) c4[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[u], qb[u], c4[u], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
     const v4f acc = (c4[0] + c4[1]) + (c4[2] + c4[3]);
     const float4 ev = *(const float4*)&esl[w][4 * g];
     const float evr[4] = {ev.x, ev.y, ev.z, ev.w};
     float sv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = evr[r] >= 0.f ? acc[r] * evr[r] * sl2 : kNegInf;
+    for (int r = 0; r < 4; ++r) sv[r] = evr[r] >= 0.f ? (FP8 ? acc[r] * evr[r] : acc[r]) * sl2 : kNegInf;
     const float tmax = lane_max4rows(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
     if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescale) != 0) {  // wave-uniform
       const float m_new = fmaxf(m_run, tmax);
-      const float alpha = m_run == kNegInf ? 0.f : exp2f(m_run - m_new);
+      const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_part *= alpha;
       m_run = m_new;
       float ar[4];  // rescale factors of heads 4g + r (held by lanes 4g + r)
@@ -314,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
     float pv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = m_run == kNegInf ? 0.f : exp2f(sv[r] - m_run);
+      const float p = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m_run);
       l_part += p;
       pv[r] = FP8 ? p * evr[r] : p;
     }
@@ -330,7 +354,6 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
     }
     // V operand: lane (m, g) reads staged rows 4g .. 4g+3 at column 16ct + m (the 16 lanes of
     // a group address 4 rows x 4 column quads) and uses the four values for both halves of k.
-    typedef __attribute__((address_space(3))) v4bf lds_v4bf;
 #pragma unroll
     for (int c4 = 0; c4 < 8; ++c4) {
       __builtin_amdgcn_sched_barrier(0);
@@ -346,18 +369,11 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
         O[4 * c4 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb[u], O[4 * c4 + u], 0, 0, 0);
     }
   };
-  // Both steps of the loop body are unconditional and an odd last tile is peeled
-  // off after the loop, so every path into the loop head has both row buffers in
-  // flight: the wait counts the compiler derives then wait for exactly one tile,
-  // never for the one behind it.
-  int i = 0;
-  for (; i + 1 < nt; i += 2) {
-    step(i, std::integral_constant<int, 0>{});
-    step(i + 1, std::integral_constant<int, 1>{});
-  }
-  if (i < nt) step(i, std::integral_constant<int, 0>{});
+  // One tile's rows are in flight while the previous one is processed; the two
+  // waves sharing a SIMD cover each other's waits.
+  for (int i = 0; i < nt; ++i) step(i, std::integral_constant<int, 0>{});
 
-  // ---- combine the four waves: (max, sum) per head, then the accumulators in column chunks
+  // ---- combine the eight waves: (max, sum) per head, then the accumulators
   const float l_w = lane_sum4rows(l_part);
   if (g == 0) {
     wml[w][m][0] = m_run;
@@ -368,56 +384,83 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * g + r;
-    const float M = fmaxf(fmaxf(wml[0][h][0], wml[1][h][0]), fmaxf(wml[2][h][0], wml[3][h][0]));
+    float M = kNegInf;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, wml[v][h][0]);
     const float mw = wml[w][h][0];
     wt[r] = mw == kNegInf ? 0.f : exp2f(mw - M);
   }
-  // reducer role: wave w finalises heads 4w + lane/16, columns 8(lane%16) .. +7 of each chunk
-  const int rh = 4 * w + lane / 16, rc = 8 * (lane % 16);
-  float Mh = kNegInf, Lh = 0.f;
+  // per-head totals over the four waves (every thread, from the table above)
+  __shared__ float hML[16][2];
+  if (threadIdx.x < 16) {
+    const int h = threadIdx.x;
+    float Mh = kNegInf, Lh = 0.f;
 #pragma unroll
-  for (int v = 0; v < kWaves; ++v) Mh = fmaxf(Mh, wml[v][rh][0]);
+    for (int v = 0; v < kWaves; ++v) Mh = fmaxf(Mh, wml[v][h][0]);
 #pragma unroll
-  for (int v = 0; v < kWaves; ++v) {
-    const float mv = wml[v][rh][0];
-    Lh += mv == kNegInf ? 0.f : wml[v][rh][1] * exp2f(mv - Mh);
-  }
-  const int H = a.heads;
-  const int hglob = h0 + rh;
-  float* orow;
-  float fscale;
-  if (partial) {
-    orow = (float*)a.ws + (((int64_t)row * nsplit_max + s) * H + hglob) * 512;
-    fscale = 1.f;
-  } else {
-    orow = a.out + ((int64_t)row * H + hglob) * 512;
-    fscale = Lh > 0.f ? __fdiv_rn(1.0f, Lh) : 0.f;
-  }
-  // one pass: every wave writes its weighted accumulator (all 512 columns), then each
-  // wave sums four heads over the four buffers in a fixed order
-  float* mbuf = (float*)&Vs[0][0][0];  // [kWaves][16][kMbufPitch] floats (aliases the staging area)
-  __syncthreads();                     // all waves are done with their staged tiles
-#pragma unroll
-  for (int ct = 0; ct < 32; ++ct)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mbuf[(w * 16 + 4 * g + r) * kMbufPitch + 16 * ct + m] = O[ct][r] * wt[r];
-  __syncthreads();
-#pragma unroll
-  for (int ch = 0; ch < 4; ++ch) {
-    float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {  // fixed order over waves
-      const float4 x0 = *(const float4*)&mbuf[(v * 16 + rh) * kMbufPitch + 128 * ch + rc];
-      const float4 x1 = *(const float4*)&mbuf[(v * 16 + rh) * kMbufPitch + 128 * ch + rc + 4];
-      acc0.x += x0.x; acc0.y += x0.y; acc0.z += x0.z; acc0.w += x0.w;
-      acc1.x += x1.x; acc1.y += x1.y; acc1.z += x1.z; acc1.w += x1.w;
+    for (int v = 0; v < kWaves; ++v) {
+      const float mv = wml[v][h][0];
+      Lh += mv == kNegInf ? 0.f : wml[v][h][1] * exp2f(mv - Mh);
     }
-    acc0.x *= fscale; acc0.y *= fscale; acc0.z *= fscale; acc0.w *= fscale;
-    acc1.x *= fscale; acc1.y *= fscale; acc1.z *= fscale; acc1.w *= fscale;
-    *(float4*)&orow[128 * ch + rc] = acc0;
-    *(float4*)&orow[128 * ch + rc + 4] = acc1;
+    hML[h][0] = Mh;
+    hML[h][1] = Lh;
   }
-  if (lane % 16 == 0) {
+  // Two rounds through LDS, every sum in a fixed order: waves 4..7 write their weighted
+  // accumulators, waves 0..3 add them to their own (w + 4 onto w) and write the sums,
+  // then every thread adds the four buffers for (column, 4-head group) items.  A buffer
+  // is [4-head group][column][4 heads]: lane (m, g) stores heads 4g .. 4g+3 of one
+  // column as 16 bytes, consecutive lanes at consecutive addresses.
+  float* mbuf = (float*)&Vs[0][0][0];  // [4][4][512][4] floats (aliases the staging area)
+  float ow[32][4];                     // this wave's weighted accumulator
+  __syncthreads();                     // all waves are done with their staged tiles
+  const int wb = w % 4;
+  if (w >= 4) {
+#pragma unroll
+    for (int ct = 0; ct < 32; ++ct)
+      *(float4*)&mbuf[((wb * 4 + g) * 512 + 16 * ct + m) * 4] =
+          make_float4(O[ct][0] * wt[0], O[ct][1] * wt[1], O[ct][2] * wt[2], O[ct][3] * wt[3]);
+  }
+  __syncthreads();
+  if (w < 4) {
+#pragma unroll
+    for (int ct = 0; ct < 32; ++ct) {
+      const float4 x = *(const float4*)&mbuf[((wb * 4 + g) * 512 + 16 * ct + m) * 4];
+      ow[ct][0] = O[ct][0] * wt[0] + x.x;
+      ow[ct][1] = O[ct][1] * wt[1] + x.y;
+      ow[ct][2] = O[ct][2] * wt[2] + x.z;
+      ow[ct][3] = O[ct][3] * wt[3] + x.w;
+    }
+  }
+  __syncthreads();
+  if (w < 4) {
+#pragma unroll
+    for (int ct = 0; ct < 32; ++ct)
+      *(float4*)&mbuf[((wb * 4 + g) * 512 + 16 * ct + m) * 4] = make_float4(ow[ct][0], ow[ct][1], ow[ct][2], ow[ct][3]);
+  }
+  __syncthreads();
+  const int H = a.heads;
+  float* obase = partial ? (float*)a.ws + (((int64_t)row * nsplit_max + s) * H + h0) * 512
+                         : a.out + ((int64_t)row * H + h0) * 512;
+#pragma unroll
+  for (int it = 0; it < 512 * 4 / kThreads; ++it) {
+    const int item = threadIdx.x + kThreads * it, c = item / 4, hq = item % 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {  // fixed order over the four buffers
+      const float4 x = *(const float4*)&mbuf[((v * 4 + hq) * 512 + c) * 4];
+      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+    const float av[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float L = hML[4 * hq + r][1];
+      const float fs = partial ? 1.f : (L > 0.f ? __fdiv_rn(1.0f, L) : 0.f);
+      obase[(4 * hq + r) * 512 + c] = av[r] * fs;
+    }
+  }
+  if (threadIdx.x < 16) {
+    const int hglob = h0 + threadIdx.x;
+    const float Mh = hML[threadIdx.x][0], Lh = hML[threadIdx.x][1];
     if (partial) {
       float* pml = (float*)a.ws + rows * nsplit_max * H * 512 + (((int64_t)row * nsplit_max + s) * H + hglob) * 2;
       pml[0] = Mh;
@@ -431,20 +474,32 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
 // Fixed-order log-sum-exp merge of the splits of one (row, head); one pass over
 // the partials with every split's row in flight at once.
 constexpr int kMergeMaxSplits = 64;
+constexpr int kMergeBatch = 8;  // splits whose partial rows are loaded up front
 
 __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int split, int nsplit_max, int64_t rows) {
   const int row = blockIdx.x, h = blockIdx.y;
+  const int H = a.heads;
+  // the first kMergeBatch splits' partial rows are loaded before anything else (they
+  // depend on nothing), so the position, the (max, sum) pairs and the rows arrive together
+  const float4* src = (const float4*)((const float*)a.ws + ((int64_t)row * nsplit_max * H + h) * 512) + threadIdx.x;
+  const int64_t sstride = (int64_t)H * 512 / 4;  // float4s between consecutive splits
+  float4 pv[kMergeBatch];
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; ++j) pv[j] = j < nsplit_max ? src[j * sstride] : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* pml = (const float*)a.ws + rows * nsplit_max * H * 512;
+  float ms = kNegInf, ls = 0.f;
+  if (threadIdx.x < kWave && (int)threadIdx.x < nsplit_max) {
+    const int64_t o = (((int64_t)row * nsplit_max + threadIdx.x) * H + h) * 2;
+    ms = pml[o];
+    ls = pml[o + 1];
+  }
   const RowInfo ri = row_info(a, row);
   const int nsplit = min(kMergeMaxSplits, max(1, (ri.n_tot + split - 1) / split));
-  const int H = a.heads;
-  const float* pml = (const float*)a.ws + rows * nsplit_max * H * 512;
   __shared__ float wts[kMergeMaxSplits];
   __shared__ float sh_L, sh_M;
   if (threadIdx.x < kWave) {  // one wave forms the split weights
     const int s = threadIdx.x;
-    const int64_t o = (((int64_t)row * nsplit_max + s) * H + h) * 2;
-    const float ms = s < nsplit ? pml[o] : kNegInf;
-    const float ls = s < nsplit ? pml[o + 1] : 0.f;
+    if (s >= nsplit) ms = kNegInf, ls = 0.f;
     const float M = wave_max(ms);
     const float e = (M == kNegInf || s >= nsplit) ? 0.f : exp2f(ms - M);
     // L = sum over splits in ascending order (fixed, independent of scheduling)
@@ -459,11 +514,17 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int split, 
   __syncthreads();
   const float L = sh_L;
   const float inv = L > 0.f ? __fdiv_rn(1.0f, L) : 0.f;
-  const float4* src = (const float4*)((const float*)a.ws + ((int64_t)row * nsplit_max * H + h) * 512) + threadIdx.x;
-  const int64_t sstride = (int64_t)H * 512 / 4;  // float4s between consecutive splits
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-  for (int s = 0; s < nsplit; ++s) {
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; ++j) {
+    if (j >= nsplit) break;  // splits past this row's count are never read into the sum
+    const float wgt = wts[j] * inv;
+    acc.x = fmaf(pv[j].x, wgt, acc.x);
+    acc.y = fmaf(pv[j].y, wgt, acc.y);
+    acc.z = fmaf(pv[j].z, wgt, acc.z);
+    acc.w = fmaf(pv[j].w, wgt, acc.w);
+  }
+  for (int s = kMergeBatch; s < nsplit; ++s) {
     const float wgt = wts[s] * inv;
     const float4 v = src[s * sstride];
     acc.x = fmaf(v.x, wgt, acc.x);
@@ -555,9 +616,9 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
 // per wave); calls with many queries per sequence keep each list whole.
 int attn_split_size(int tq, int n_entries_max) {
   const int n = max(n_entries_max, 1);
-  if (tq != 1) return n;
+  if (tq != 1) return min(n, kIdxStage);
   const int round = kWaves * kTile;
-  return max(round, ((n + 7) / 8 + round - 1) / round * round);
+  return min(kIdxStage, max(round, ((n + 7) / 8 + round - 1) / round * round));
 }
 
 size_t attn_workspace_bytes(int64_t rows, int heads, int dim, int n_entries_max, int tq) {
