@@ -159,7 +159,8 @@ def test_attention_rejects_and_workspace():
     need = csa.csa_attn_workspace_size(8, 1, 64, 512, 2048 + 128)
     assert need > 0
     assert csa.csa_attn_workspace_size(1, 1, 16, 128, 60) == 0        # one split: no workspace
-    assert csa.csa_attn_workspace_size(1, 4, 16, 128, 3000) == 0      # many queries: lists stay whole
+    assert csa.csa_attn_workspace_size(1, 4, 16, 128, 2048) == 0      # many queries: lists up to 2048 stay whole
+    assert csa.csa_attn_workspace_size(1, 4, 16, 128, 3000) > 0       # longer ones are split
 
     def sparse(q=q, kv=kv, raw=raw, idx=P, k=2048, W=128, heads=64, dim=512, ws=P, wsb=need):
         return lambda stream: csa.csa_sparse_attn(q, kv, idx, k, raw, P, W, P, 8, 1, heads, dim, 0.088, P, P, ws, wsb,
