@@ -136,6 +136,44 @@ constexpr int kFp4Unroll = 8;
 constexpr int kFp4KeysPerWave = 32 * kFp4Unroll;
 constexpr int kFp4KeysPerWG = 4 * kFp4KeysPerWave;
 
+// The query of row (b, t), quantised to MXFP4 by a 256-thread workgroup into LDS:
+// thread -> (head, K block, element pair); the 16 threads of a 32-element block are
+// 16 adjacent lanes.  qcode[h][blk] = 16 B of e2m1 codes, qscale[h][blk] = e8m0.
+// Loaded first (query_pairs), quantised later (quantize_query_mxfp4), so the load
+// is not queued behind the key loads issued in between.
+constexpr int kQueryPairsMax = 4;  // heads * 32 pairs over 256 threads (heads <= 32)
+__device__ __forceinline__ void query_pairs(const IndexArgs& a, int b, int t, float2 (&x)[kQueryPairsMax]) {
+#pragma unroll
+  for (int i = 0; i < kQueryPairsMax; ++i) {
+    const int pi = 256 * i + (int)threadIdx.x;
+    const int h = pi / 32, blk = (pi / 16) % 2, pr = pi % 16;
+    x[i] = h < a.heads ? *(const float2*)((const float*)a.q.data + (int64_t)b * a.q.sb + (int64_t)t * a.q.sr + h * 64 +
+                                          32 * blk + 2 * pr)
+                       : make_float2(0.f, 0.f);
+  }
+}
+__device__ __forceinline__ void quantize_query_mxfp4(const IndexArgs& a, const float2 (&xs)[kQueryPairsMax],
+                                                     uint32_t (*qcode)[2][4], uint32_t (*qscale)[2]) {
+#pragma unroll
+  for (int i = 0; i < kQueryPairsMax; ++i) {
+    if (256 * i >= a.heads * 32) break;  // uniform
+    const int pi = 256 * i + (int)threadIdx.x;
+    const int h = pi / 32, blk = (pi / 16) % 2, pr = pi % 16;
+    const float2 x = xs[i];
+    float amax = fmaxf(fabsf(x.x), fabsf(x.y));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    const int e = mx_scale_exp(amax);
+    const uint32_t byte = amax > 0.f ? (f32_to_e2m1(x.x, e) | (f32_to_e2m1(x.y, e) << 4)) : 0u;
+    // four adjacent pairs form one dword of codes
+    const uint32_t b1 = __shfl_down(byte, 1, 16), b2 = __shfl_down(byte, 2, 16), b3 = __shfl_down(byte, 3, 16);
+    if (h < a.heads) {
+      if ((pr & 3) == 0) qcode[h][blk][pr / 4] = byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      if (pr == 0) qscale[h][blk] = (uint32_t)(e + 127);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ slice top-32
 // With CAND set, each workgroup also selects the exact top-32 of its 1024-key
 // slice in (key desc, index asc) order -- key being the order-preserving integer
@@ -156,8 +194,11 @@ __global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a, CandOut c
   __shared__ float wsh[32];
   if (threadIdx.x < a.heads) wsh[threadIdx.x] = a.w[(int64_t)row * a.heads + threadIdx.x];
 
-  // 1) key codes (16 B per lane: key l%32's block l/32) and their e8m0 scales, issued
-  //    first so their latency overlaps the query quantisation below
+  // 1) the query (loaded first: it must not queue behind the keys), then the key codes
+  //    (16 B per lane: key l%32's block l/32) and their e8m0 scales, whose latency
+  //    overlaps the query quantisation below
+  float2 qx[kQueryPairsMax];
+  query_pairs(a, b, t, qx);
   const int kfirst = g0 + m;
   const uint8_t* kc = (const uint8_t*)a.k.data + (int64_t)b * a.k.sb + (int64_t)kfirst * a.k.sr + 16 * kb;
   const uint8_t* ks = (const uint8_t*)a.k.scale + (int64_t)b * a.k.ssb + (int64_t)kfirst * a.k.ssr + kb;
@@ -170,27 +211,8 @@ __global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a, CandOut c
     c[u] = live ? *(const v4i*)(kc + u * cstep) : (v4i){0, 0, 0, 0};
     sbk[u] = live ? ks[u * sstep] : 127;
   }
-  // 2) the query, quantised to MXFP4 once per workgroup: thread -> (head, K block,
-  //    element pair); the 16 threads of a 32-element block are 16 adjacent lanes
-  for (int pbase = 0; pbase < a.heads * 32; pbase += 256) {
-    const int pi = pbase + (int)threadIdx.x;
-    const int h = pi / 32, blk = (pi / 16) % 2, pr = pi % 16;
-    float2 x = make_float2(0.f, 0.f);
-    if (h < a.heads)
-      x = *(const float2*)((const float*)a.q.data + (int64_t)b * a.q.sb + (int64_t)t * a.q.sr + h * 64 + 32 * blk +
-                           2 * pr);
-    float amax = fmaxf(fabsf(x.x), fabsf(x.y));
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
-    const int e = mx_scale_exp(amax);
-    const uint32_t byte = amax > 0.f ? (f32_to_e2m1(x.x, e) | (f32_to_e2m1(x.y, e) << 4)) : 0u;
-    // four adjacent pairs form one dword of codes
-    const uint32_t b1 = __shfl_down(byte, 1, 16), b2 = __shfl_down(byte, 2, 16), b3 = __shfl_down(byte, 3, 16);
-    if (h < a.heads) {
-      if ((pr & 3) == 0) qcode[h][blk][pr / 4] = byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
-      if (pr == 0) qscale[h][blk] = (uint32_t)(e + 127);
-    }
-  }
+  // 2) the query, quantised to MXFP4 once per workgroup
+  quantize_query_mxfp4(a, qx, qcode, qscale);
   __syncthreads();
   if (!CAND && g0 >= a.n_cap) return;
   v8i A = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -222,9 +244,13 @@ __global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a, CandOut c
 #pragma unroll
     for (int r = 0; r < NR; ++r) part = fmaf(wv[r], fmaxf(acc[r], 0.f), part);
     const float other = __shfl_xor(part, 32);
-    const int key = g0 + 32 * u + l;
     sc[u] = part + other;  // the same value in lane l and lane l ^ 32
-    if (l < 32 && key < gend) srow[key] = key < V ? sc[u] : kNegInf;
+    if (u >= kFp4Unroll / 2) {  // lanes 0-31 store tile u - 4, lanes 32-63 tile u: one store for two tiles
+      const int us = kb ? u : u - kFp4Unroll / 2;
+      const int key = g0 + 32 * us + m;
+      const float v = kb ? sc[u] : sc[u - kFp4Unroll / 2];
+      if (key < gend) srow[key] = key < V ? v : kNegInf;
+    }
     // keep one accumulator tile live at a time: occupancy (many waves hiding each
     // other's memory latency) matters more here than MFMA back-to-back issue
     __builtin_amdgcn_sched_barrier(0);
