@@ -35,9 +35,11 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA/HCA decode tokens/s at 1M ctx on 1 GPU; achieved HBM TB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 KEY_BYTES = 34  # MXFP4 indexer key: 64 e2m1 codes (32 B) + 2 e8m0 scales
-INDEX_KERNEL = "index_mxfp4_kernel<4>"
+CAND_SLICE, CAND_PER_SLICE, CAND_BYTES, META_BYTES = 1024, 32, 8, 16  # fused indexer's slice candidates
+INDEX_KERNEL = {"fused": "index_mxfp4_kernel<4, true>", "two-stage": "index_mxfp4_kernel<4, false>"}
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "index_mxfp4_csa_decode_1m_b8_pmc.txt")
-INDEX_SOURCE = os.path.join(ROOT, "long_context_attention_04_amd", "csrc", "index.hip")
+INDEX_SOURCES = [os.path.join(ROOT, "long_context_attention_04_amd", "csrc", f)
+                 for f in ("index.hip", "select.h", "common.h")]  # the indexer kernel's code
 
 
 def parse():
@@ -49,6 +51,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=6)
     ap.add_argument("--no-graph", action="store_true", help="time plain launches instead of graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--select", choices=("fused", "two-stage"), default="fused",
+                    help="index+top-k as one fused call or as scores then selection")
     ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the oracle's timed sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="repeat the oracle sample up to this long")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
@@ -81,19 +85,31 @@ def backlog(torch, ms=15.0):
         return x
 
 
-def index_kernel_us(torch, layers, reps) -> float:
-    """Mean duration of the indexer launch, HIP events on its own stream, queued behind a backlog."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+def launch_us(torch, layers, reps, launch) -> float:
+    """Mean duration of one library call (`launch(layer)`): `reps` calls queued back to back
+    behind a backlog on the stream they are launched on (torch's current stream), bracketed
+    by two HIP events, so neither host launch gaps nor per-call event records enter it."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     keep = backlog(torch)
+    e0.record()
     for i in range(reps):
-        layer = layers[i % len(layers)]
-        ev[i][0].record()
-        layer.index()
-        ev[i][1].record()
+        launch(layers[i % len(layers)])
+    e1.record()
     torch.cuda.synchronize()
     del keep
-    return float(np.mean([a.elapsed_time(b) for a, b in ev]) * 1e3)
+    return float(e0.elapsed_time(e1) * 1e3 / reps)
+
+
+def index_launch_bytes(layer, fused: bool) -> int:
+    """Algorithmic bytes of one indexer launch: every key read once, the query and head weights,
+    the scores written once, and (fused) the slices' candidates and metadata written once."""
+    B, N = layer.B, layer.n_cap
+    nbytes = B * N * KEY_BYTES + B * layer.HI * (layer.dI * 4 + 4) + B * N * 4
+    if fused:
+        ns = (N + CAND_SLICE - 1) // CAND_SLICE
+        nbytes += B * ns * (CAND_PER_SLICE * CAND_BYTES + META_BYTES)
+    return nbytes
 
 
 def stage_us(torch, layers, reps) -> dict:
@@ -111,12 +127,19 @@ def stage_us(torch, layers, reps) -> dict:
     return out
 
 
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in INDEX_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
 def pmc_traffic(kernel_launch_bytes) -> dict | None:
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches the source."""
     if not os.path.exists(PMC_SUMMARY):
         return None
     txt = open(PMC_SUMMARY).read()
-    src_hash = hashlib.sha256(open(INDEX_SOURCE, "rb").read()).hexdigest()[:16]
+    src_hash = source_hash()
     vals = {}
     for line in txt.splitlines():
         if "=" in line and not line.startswith("#"):
@@ -225,6 +248,8 @@ def main():
         print(f"bench.py times the CSA decode workloads; {name} is covered by the parity tests", file=sys.stderr)
         sys.exit(2)
     layers = [workloads.build(name, salt=s) for s in range(args.sets)]
+    for layer in layers:
+        layer.fused_select = args.select == "fused"
     torch.cuda.synchronize()
 
     # ---- eager warm-up (also validates every stage once)
@@ -265,15 +290,21 @@ def main():
     tok_s = layers[0].B / (dt / K)
 
     # ---- dominant kernel: event-timed launches, and the stage breakdown
-    idx_us = index_kernel_us(torch, layers, max(K, 20))
+    fused = args.select == "fused"
+    # the dominant kernel: the indexer (with the slices' candidate selection when fused), one launch
+    if fused:
+        idx_us = launch_us(torch, layers, max(K, 20), lambda layer: layer.index_topk_part(1))
+    else:
+        idx_us = launch_us(torch, layers, max(K, 20), lambda layer: layer.index())
+    attn_us = launch_us(torch, layers, max(K, 20), lambda layer: layer.attend())
     stages = stage_us(torch, layers, max(K // 2, 10))
     ab = algorithmic_bytes(layers[0])
-    launch_bytes = ab["keys"] + layers[0].B * layers[0].HI * (layers[0].dI * 4 + 4)
+    launch_bytes = index_launch_bytes(layers[0], fused)
     achieved = launch_bytes / (idx_us * 1e-6) / 1e9
     traffic = pmc_traffic(launch_bytes)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic["total"] if traffic else None,
-            "kernel": INDEX_KERNEL, "kernel_us": round(idx_us, 2), "bytes_per_launch": launch_bytes}
+            "kernel": INDEX_KERNEL[args.select], "kernel_us": round(idx_us, 2), "bytes_per_launch": launch_bytes}
     res = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
@@ -285,6 +316,7 @@ def main():
         "hbm_tb_s_step": round(ab["total"] / (dt / K) / 1e12, 3),
         "algorithmic_bytes_per_step": ab["total"],
         "stages_us_eager": stages,
+        "attention_call_us": round(attn_us, 2),  # csa_sparse_attn: split kernel + merge kernel
         "roofline": roof,
     }
     if args.copy_calibration:

@@ -201,6 +201,16 @@ csa_status csa_index_topk(const csa_tensor* q_idx, const float* w, const csa_ten
                           int32_t n_cap, int32_t k, float* scores, int32_t* idx, void* ws, size_t ws_bytes,
                           void* stream);
 size_t csa_index_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, int32_t k);
+/* csa_index_topk in two launches, for callers that schedule (or time) the scoring
+ * and the selection separately: part 1 scores (and, where the fused path applies,
+ * leaves the slices' candidates in ws), part 2 selects; part 3 is both, exactly
+ * csa_index_topk.  A part-2 call must follow a part-1 call with the same
+ * arguments on the same stream, with scores and ws untouched in between; its
+ * result then equals csa_index_topk's bit for bit.  idx may be NULL for part 1. */
+csa_status csa_index_topk_part(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx,
+                               const int32_t* q_pos, int32_t batch, int32_t tq, int32_t n_idx_heads,
+                               int32_t idx_dim, int32_t m, int32_t n_cap, int32_t k, float* scores, int32_t* idx,
+                               void* ws, size_t ws_bytes, int32_t part, void* stream);
 
 /* ---------------------------------------------------------------------------
  * (d) CSA sparse attention: attention over the selected compressed entries

@@ -93,6 +93,8 @@ _c = {
     "csa_topk_workspace_size": _proto("csa_topk_workspace_size", _SZ, _I32, _I32, _I32, _I32),
     "csa_index_topk": _proto("csa_index_topk", _I32, _TP, _P, _TP, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                              _P, _P, _SZ, _P),
+    "csa_index_topk_part": _proto("csa_index_topk_part", _I32, _TP, _P, _TP, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                  _I32, _P, _P, _P, _SZ, _I32, _P),
     "csa_index_topk_workspace_size": _proto("csa_index_topk_workspace_size", _SZ, _I32, _I32, _I32, _I32),
     "csa_sparse_attn": _proto("csa_sparse_attn", _I32, _TP, _TP, _P, _I32, _TP, _P, _I32, _P, _I32, _I32, _I32,
                               _I32, _F, _P, _P, _P, _SZ, _P),
@@ -195,6 +197,13 @@ def csa_index_topk(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n
     _check(_c["csa_index_topk"](ctypes.byref(q_idx), _ptr(w), ctypes.byref(k_idx), _ptr(q_pos), batch, tq,
                                 n_idx_heads, idx_dim, m, n_cap, k, _ptr(scores), _ptr(idx), _ptr(ws), ws_bytes,
                                 _stream(stream)))
+
+
+def csa_index_topk_part(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, k, scores, idx, ws,
+                        ws_bytes, part, stream=None):
+    _check(_c["csa_index_topk_part"](ctypes.byref(q_idx), _ptr(w), ctypes.byref(k_idx), _ptr(q_pos), batch, tq,
+                                     n_idx_heads, idx_dim, m, n_cap, k, _ptr(scores), _ptr(idx), _ptr(ws), ws_bytes,
+                                     part, _stream(stream)))
 
 
 def csa_attn_workspace_size(batch, tq, heads, dim, n_entries_max) -> int:

@@ -210,23 +210,39 @@ size_t csa_index_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, i
   return std::max(csa::topk_workspace_bytes(rows, n_cap, k), csa::index_topk_workspace_bytes(rows, n_cap, k));
 }
 
-csa_status csa_index_topk(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx, const int32_t* q_pos,
-                          int32_t batch, int32_t tq, int32_t n_idx_heads, int32_t idx_dim, int32_t m, int32_t n_cap,
-                          int32_t k, float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+csa_status csa_index_topk_part(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx,
+                               const int32_t* q_pos, int32_t batch, int32_t tq, int32_t n_idx_heads, int32_t idx_dim,
+                               int32_t m, int32_t n_cap, int32_t k, float* scores, int32_t* idx, void* ws,
+                               size_t ws_bytes, int32_t part, void* stream) {
   csa::IndexArgs a;
   csa_status st = index_args(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, scores, &a);
   if (st != CSA_OK) return st;
-  REQUIRE(idx != nullptr, CSA_ERR_NULL, "idx is NULL");
+  REQUIRE(part >= 1 && part <= 3, CSA_ERR_SHAPE, "part=%d must be 1 (scores), 2 (selection) or 3 (both)", part);
+  REQUIRE(idx != nullptr || !(part & 2), CSA_ERR_NULL, "idx is NULL");
   REQUIRE(k >= 1, CSA_ERR_SHAPE, "k=%d must be >= 1", k);
   const size_t need = csa_index_topk_workspace_size(batch, tq, n_cap, k);
   if (need > 0)
     REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "index+top-k needs %zu workspace bytes, got %zu",
             need, ws_bytes);
   const hipStream_t s = (hipStream_t)stream;
-  if (csa::index_topk_fused_ok(a, k)) return from_hip(csa::launch_index_topk(a, k, idx, ws, s), "csa_index_topk launch");
-  st = from_hip(csa::launch_index_scores(a, s), "csa_index_topk index launch");
-  if (st != CSA_OK) return st;
-  return from_hip(csa::launch_topk(scores, q_pos, batch, tq, n_cap, m, k, idx, ws, s), "csa_index_topk top-k launch");
+  const bool fused = csa::index_topk_fused_ok(a, k);
+  if (part & 1) {
+    st = fused ? from_hip(csa::launch_index_topk_cand(a, k, ws, s), "csa_index_topk scores launch")
+               : from_hip(csa::launch_index_scores(a, s), "csa_index_topk scores launch");
+    if (st != CSA_OK) return st;
+  }
+  if (part & 2)
+    return fused ? from_hip(csa::launch_index_topk_merge(a, k, idx, ws, s), "csa_index_topk selection launch")
+                 : from_hip(csa::launch_topk(scores, q_pos, batch, tq, n_cap, m, k, idx, ws, s),
+                            "csa_index_topk selection launch");
+  return ok();
+}
+
+csa_status csa_index_topk(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx, const int32_t* q_pos,
+                          int32_t batch, int32_t tq, int32_t n_idx_heads, int32_t idx_dim, int32_t m, int32_t n_cap,
+                          int32_t k, float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  return csa_index_topk_part(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, k, scores, idx, ws,
+                             ws_bytes, 3, stream);
 }
 
 size_t csa_attn_workspace_size(int32_t batch, int32_t tq, int32_t heads, int32_t dim, int32_t n_entries_max) {

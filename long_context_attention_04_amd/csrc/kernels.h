@@ -93,6 +93,9 @@ bool index_topk_fused_ok(const IndexArgs& a, int k);
 size_t index_topk_workspace_bytes(int64_t rows, int n_cap, int k);
 hipError_t launch_index_scores_cand(const IndexArgs& a, const CandOut& c, hipStream_t s);  // index.hip
 hipError_t launch_index_topk(const IndexArgs& a, int k, int32_t* idx, void* ws, hipStream_t s);
+// the two kernels of launch_index_topk, one launch each
+hipError_t launch_index_topk_cand(const IndexArgs& a, int k, void* ws, hipStream_t s);
+hipError_t launch_index_topk_merge(const IndexArgs& a, int k, int32_t* idx, void* ws, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

@@ -432,9 +432,9 @@ size_t index_topk_workspace_bytes(int64_t rows, int n_cap, int k) {
   return align256((size_t)rows * ns * sizeof(SliceMeta)) + align256((size_t)rows * ns * kFusedC * 8);
 }
 
-hipError_t launch_index_topk(const IndexArgs& a, int k, int32_t* idx, void* ws, hipStream_t s) {
+namespace {
+CandOut fused_cand_out(const IndexArgs& a, int k, void* ws) {
   const int64_t rows = (int64_t)a.batch * a.tq;
-  if (rows == 0) return hipSuccess;
   const int ns = fused_slices(a.n_cap);
   CandOut co;
   co.C = kFusedC;
@@ -443,11 +443,28 @@ hipError_t launch_index_topk(const IndexArgs& a, int k, int32_t* idx, void* ws, 
   co.k = k;
   co.meta = (SliceMeta*)ws;
   co.cand = (uint2*)((char*)ws + align256((size_t)rows * ns * sizeof(SliceMeta)));
-  hipError_t e = launch_index_scores_cand(a, co, s);
-  if (e != hipSuccess) return e;
+  return co;
+}
+}  // namespace
+
+hipError_t launch_index_topk_cand(const IndexArgs& a, int k, void* ws, hipStream_t s) {
+  if ((int64_t)a.batch * a.tq == 0) return hipSuccess;
+  return launch_index_scores_cand(a, fused_cand_out(a, k, ws), s);
+}
+
+hipError_t launch_index_topk_merge(const IndexArgs& a, int k, int32_t* idx, void* ws, hipStream_t s) {
+  const int64_t rows = (int64_t)a.batch * a.tq;
+  if (rows == 0) return hipSuccess;
+  const CandOut co = fused_cand_out(a, k, ws);
   hipLaunchKernelGGL(topk_merge32_kernel, dim3((unsigned)rows), dim3(kRegSelThreads), 0, s, a.scores, a.q_pos,
-                     a.n_cap, a.m, k, ns, co.cand, co.meta, idx);
+                     a.n_cap, a.m, k, co.nslices, co.cand, co.meta, idx);
   return hipGetLastError();
+}
+
+hipError_t launch_index_topk(const IndexArgs& a, int k, int32_t* idx, void* ws, hipStream_t s) {
+  const hipError_t e = launch_index_topk_cand(a, k, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_index_topk_merge(a, k, idx, ws, s);
 }
 
 }  // namespace csa

@@ -25,7 +25,7 @@ import torch
 import synth
 
 from . import (BF16, F32, FP8_E4M3, MXFP4, csa_attn_workspace_size, csa_compress, csa_compress_jobs,
-               csa_index_scores, csa_index_topk, csa_index_topk_workspace_size, csa_quantize_fp8, csa_quantize_mxfp4, csa_sparse_attn,
+               csa_index_scores, csa_index_topk, csa_index_topk_part, csa_index_topk_workspace_size, csa_quantize_fp8, csa_quantize_mxfp4, csa_sparse_attn,
                csa_topk, csa_topk_workspace_size, desc, hca_attn)
 
 DEV = "cuda"
@@ -185,17 +185,31 @@ class CsaLayer:
         csa_index_topk(self.q_idx.desc(), self.w, self.k_idx.desc(), self.q_pos, self.B, self.tq, self.HI, self.dI,
                        self.m, self.n_cap, self.k, self.scores, self.idx, self.ws_itk, self.ws_itk.numel(), stream)
 
+    def index_topk_part(self, part, stream=None):
+        """Part 1 (scores + slice candidates) or part 2 (selection) of index_topk."""
+        csa_index_topk_part(self.q_idx.desc(), self.w, self.k_idx.desc(), self.q_pos, self.B, self.tq, self.HI,
+                            self.dI, self.m, self.n_cap, self.k, self.scores, self.idx, self.ws_itk,
+                            self.ws_itk.numel(), part, stream)
+
     def attend(self, stream=None):
         csa_sparse_attn(self.q.desc(), self.kv_cmp.desc(), self.idx, self.k, self.raw_kv.desc(), self.raw_base,
                         self.W, self.q_pos, self.B, self.tq, self.H, self.D, self.scale, self.out, self.lse,
                         self.ws_attn, self.ws_attn.numel(), stream)
 
     stage_names = ("compress", "index+topk", "attention")
+    fused_select = True  # score and select with csa_index_topk (else csa_index_scores, then csa_topk)
+
+    def select(self, stream=None):
+        if self.fused_select:
+            self.index_topk(stream)
+        else:
+            self.index(stream)
+            self.topk(stream)
 
     def step(self, stream=None, marks=None):
-        """One pass of the CSA hot path (compress the new blocks, score and select with
-        the fused indexer + top-k, attend).  `marks(i)` is called between stages."""
-        for i, stage in enumerate((self.compress, self.index_topk, self.attend)):
+        """One pass of the CSA hot path (compress the new blocks, score and select the
+        top-k, attend).  `marks(i)` is called between stages."""
+        for i, stage in enumerate((self.compress, self.select, self.attend)):
             if marks:
                 marks(i)
             stage(stream)

@@ -150,6 +150,16 @@ def test_index_topk_rejects_and_workspace():
     expect(E_WS, call(ws=None))
     expect(E_UNSUP, call(heads=33))
 
+    def part(p, idx=P, wsb=need):
+        return lambda stream: csa.csa_index_topk_part(q, P, k, P, 8, 1, 8, 64, 4, 262144, 2048, P, idx, P, wsb, p,
+                                                      stream)
+
+    expect(E_SHAPE, part(0), match="part")
+    expect(E_SHAPE, part(4), match="part")
+    expect(E_NULL, part(2, idx=None))
+    expect(E_NULL, part(3, idx=None))
+    expect(E_WS, part(1, idx=None, wsb=need - 1))
+
 
 # ---------------------------------------------------------------------------- attention
 

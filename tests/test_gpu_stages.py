@@ -342,6 +342,14 @@ def test_index_topk_fused(gpu_lib, B, Tq, HI, N, k, mode):
     csa.csa_index_topk(qd, wt, kd, pt, B, Tq, HI, dI, m, N, k, s2, i2, ws2, ws2.numel())
     assert torch.equal(s1, s2)
     np.testing.assert_array_equal(down(i2), down(i1))
+    # the same call in two parts (scores + candidates, then selection)
+    s3 = torch.full((B, Tq, N), float("nan"), device="cuda")
+    i3 = torch.full((B, Tq, k), -7, dtype=torch.int32, device="cuda")
+    ws3 = workspace(csa.csa_index_topk_workspace_size(B, Tq, N, k))
+    csa.csa_index_topk_part(qd, wt, kd, pt, B, Tq, HI, dI, m, N, k, s3, None, ws3, ws3.numel(), 1)
+    csa.csa_index_topk_part(qd, wt, kd, pt, B, Tq, HI, dI, m, N, k, s3, i3, ws3, ws3.numel(), 2)
+    assert torch.equal(s3, s2)
+    np.testing.assert_array_equal(down(i3), down(i2))
     np.testing.assert_array_equal(down(i2), oracle.topk(down(s2).astype(np.float64), pos, m, k))
 
 
