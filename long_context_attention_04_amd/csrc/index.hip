@@ -293,9 +293,11 @@ __global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a, CandOut c
       return;
     }
     uint32_t T, tpos;
-    wave_top32(kv, sl, [&](uint32_t r, int j) {
-      out[r] = make_uint2(kv[j], (uint32_t)(start + kWaveTopN * l + j));
-    }, &T, &tpos);
+    wave_top32(kv, sl, &T, &tpos);
+    if (l < kWaveTopC) {  // one coalesced store of the list
+      const uint2 e = sl.res[l];
+      out[l] = make_uint2(e.x, (uint32_t)start + e.y);
+    }
     if (l == 0) *mt = SliceMeta{(uint32_t)kWaveTopC, 1u, T, (uint32_t)start + tpos};
   }
 }

@@ -270,11 +270,17 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 
 constexpr int kWaveTopC = 32;  // candidates a one-wave selection keeps
 constexpr int kWaveTopN = 16;  // keys per lane: 1024 per wave
+constexpr int kWaveTopPre = 4;  // keys per lane after the pre-filter: at most 256 survive it
 
-struct WaveSelLds {  // wave-private LDS of one selection
-  __attribute__((aligned(16))) uint32_t hist[256];
-  __attribute__((aligned(16))) uint32_t fk[64];
-  __attribute__((aligned(16))) uint32_t fp[64];
+// Wave-private LDS of one selection.  Every array has one extra slot per lane past
+// its end: a lane whose store is not wanted writes there instead, so stores need no
+// branch around them (a branch per key costs far more than the store).
+struct WaveSelLds {
+  __attribute__((aligned(16))) uint32_t hist[256 + kWave];
+  __attribute__((aligned(16))) uint32_t fk[64 + kWave];
+  __attribute__((aligned(16))) uint32_t fp[64 + kWave];
+  __attribute__((aligned(16))) uint2 pre[kWave * kWaveTopPre + kWave];  // (key, position) of pre-filter survivors
+  __attribute__((aligned(16))) uint2 res[kWaveTopC + kWave];            // the kept (key, position), by rank
 };
 
 // The float a key came from (inverse of float_key).
@@ -282,138 +288,134 @@ __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
-// Exact top-32, in (key desc, position asc) order, of the keys one wave holds
-// with no workgroup barrier: lane L holds kv[j], the key of position 16L + j;
-// absent positions hold 0 and every present key is > 0; more than 32 are present.
-// A histogram select through wave-private LDS: a first pass of 256 bins linear in
-// the score over [min, max], then radix passes in key space over the bin of the
-// 32nd key while it holds more than 64 keys; those are then ranked exactly, and a
-// compaction in position order follows.  emit(rank, j) runs on the owning lane for every kept key
-// (ranks in ascending position order).  Returns the 32nd kept element's key and
-// position (the last kept copy of it).
-template <typename Emit>
-__device__ void wave_top32(const uint32_t (&kv)[kWaveTopN], WaveSelLds& sl, Emit emit, uint32_t* T_out,
-                           uint32_t* tpos_out) {
+// The bin of the 32nd key in one histogram pass: hist holds 256 counts (lane L owns
+// bins 4L .. 4L+3); returns the bin, and the keys above it and in it.
+__device__ __forceinline__ void wave_find_bin(const WaveSelLds& sl, uint32_t krem, uint32_t* bin, uint32_t* above,
+                                              uint32_t* cnt) {
   const int L = threadIdx.x % kWave;
-  uint32_t lmx = 0u, lmn = 0xffffffffu;
+  const uint4 h4 = *(const uint4*)&sl.hist[4 * L];
+  const uint32_t hh[4] = {h4.x, h4.y, h4.z, h4.w};
+  const uint32_t incl = wave_incl_scan(hh[0] + hh[1] + hh[2] + hh[3]);
+  uint32_t run = __builtin_amdgcn_readlane(incl, kWave - 1) - incl;  // keys in the bins of lanes > L
+  int fd = -1;
+  uint32_t ab = 0, cn = 0;
 #pragma unroll
-  for (int j = 0; j < kWaveTopN; ++j) {
-    lmx = max(lmx, kv[j]);
-    lmn = kv[j] ? min(lmn, kv[j]) : lmn;
+  for (int d = 3; d >= 0; --d) {
+    const bool f = fd < 0 && run < krem && run + hh[d] >= krem;
+    fd = f ? d : fd;
+    ab = f ? run : ab;
+    cn = f ? hh[d] : cn;
+    run += hh[d];
   }
-  uint32_t lo = wave_reduce_u32<false>(lmn), hi = wave_reduce_u32<true>(lmx);
+  const uint64_t fm = __builtin_amdgcn_ballot_w64(fd >= 0);  // exactly one lane
+  const int fl = __builtin_ctzll(fm);
+  *bin = __builtin_amdgcn_readlane(4 * L + fd, fl);
+  *above = __builtin_amdgcn_readlane(ab, fl);
+  *cnt = __builtin_amdgcn_readlane(cn, fl);
+}
+
+// Exact top-32, in (key desc, position asc) order, of the keys one wave holds with
+// no workgroup barrier: lane L holds kv[j] in slot NK*L + j, slot order being
+// ascending position order, and pos(j) is that key's position; absent slots hold
+// 0, every present key is > 0, more than 32 are present and all lie in [lo, hi].
+// A histogram select through wave-private LDS: a first pass of 256 bins linear in
+// the score over [lo, hi], then radix passes in key space over the bin of the 32nd
+// key while it holds more than 64 keys.  When that bin is taken whole, or holds a
+// single key value, the threshold is known at once; otherwise its keys are ranked
+// exactly.  The kept (key, position) pairs land in sl.res[0..31] in ascending
+// position order.  Returns the 32nd kept key and the position of its last kept copy.
+template <int NK, typename PosFn>
+__device__ void wave_top32_core(const uint32_t (&kv)[NK], PosFn pos, uint32_t lo, uint32_t hi, WaveSelLds& sl,
+                                uint32_t* T_out, uint32_t* tpos_out) {
+  const int L = threadIdx.x % kWave;
   uint32_t krem = kWaveTopC;  // keys still to take from [lo, hi]
-  bool finish = false;
+  uint32_t cn = 0xffffffffu;  // keys in [lo, hi] (unknown before a pass)
   const float xlo = key_float(lo), xhi = key_float(hi);
   const float inv = 255.99f / (xhi - xlo);
   // NaN and infinite scores, or a span too small to invert, go to the key-space passes
   if (lo != hi && xhi - xlo < __builtin_inff() && inv < __builtin_inff()) {
-    // First pass in value space: 256 bins linear in the score between the smallest and
-    // largest present score.  Any non-decreasing map of the keys gives bins that are
-    // contiguous ranges of the key order, so the selection stays exact; linear bins
-    // spread scores far better than key bits (which bucket by float exponent), so the
-    // bin of the 32nd key is small and usually settles the threshold in one pass.
-    int bin[kWaveTopN];
+    // First pass in value space: 256 bins linear in the score over [lo, hi].  Any
+    // non-decreasing map of the keys gives bins that are contiguous ranges of the key
+    // order, so the selection stays exact; linear bins spread scores far better than
+    // key bits (which bucket by float exponent), so the bin of the 32nd key is small
+    // and usually settles the threshold in one pass.
+    int bin[NK];
     *(uint4*)&sl.hist[4 * L] = make_uint4(0u, 0u, 0u, 0u);  // LDS ops of one wave run in order
 #pragma unroll
-    for (int j = 0; j < kWaveTopN; ++j) {
+    for (int j = 0; j < NK; ++j) {
       const float b = (key_float(kv[j]) - xlo) * inv;
       bin[j] = kv[j] ? min(255, max(0, (int)b)) : -1;
-      if (bin[j] >= 0) atomicAdd(&sl.hist[bin[j]], 1u);
+      atomicAdd(&sl.hist[bin[j] >= 0 ? bin[j] : 256 + L], 1u);
     }
-    const uint4 h4 = *(const uint4*)&sl.hist[4 * L];
-    const uint32_t hh[4] = {h4.x, h4.y, h4.z, h4.w};
-    const uint32_t incl = wave_incl_scan(hh[0] + hh[1] + hh[2] + hh[3]);
-    uint32_t run = __builtin_amdgcn_readlane(incl, kWave - 1) - incl;  // keys in the bins of lanes > L
-    int fd = -1;
-    uint32_t above = 0, cnt = 0;
-#pragma unroll
-    for (int d = 3; d >= 0; --d) {
-      if (fd < 0 && run < krem && run + hh[d] >= krem) {
-        fd = d;
-        above = run;
-        cnt = hh[d];
-      }
-      run += hh[d];
-    }
-    const uint64_t fm = __builtin_amdgcn_ballot_w64(fd >= 0);  // exactly one lane
-    const int fl = __builtin_ctzll(fm);
-    const int fbin = (int)__builtin_amdgcn_readlane(4 * L + fd, fl);
-    krem -= __builtin_amdgcn_readlane(above, fl);
-    const uint32_t cn = __builtin_amdgcn_readlane(cnt, fl);
+    uint32_t fbin, ab;
+    wave_find_bin(sl, krem, &fbin, &ab, &cn);
+    krem -= ab;
     // the key range of that bin
     uint32_t bmx = 0u, bmn = 0xffffffffu;
 #pragma unroll
-    for (int j = 0; j < kWaveTopN; ++j)
-      if (bin[j] == fbin) {
-        bmx = max(bmx, kv[j]);
-        bmn = min(bmn, kv[j]);
-      }
+    for (int j = 0; j < NK; ++j) {
+      const bool in = bin[j] == (int)fbin;
+      bmx = in ? max(bmx, kv[j]) : bmx;
+      bmn = in ? min(bmn, kv[j]) : bmn;
+    }
     lo = wave_reduce_u32<false>(bmn);
     hi = wave_reduce_u32<true>(bmx);
-    finish = cn <= 64u;
   }
   // further passes in key space over [lo, hi] while its keys are more than 64
-  for (int pass = 0; pass < 4 && !finish && lo != hi; ++pass) {
+  for (int pass = 0; pass < 4 && cn > 64u && cn != krem && lo != hi; ++pass) {
     const uint32_t span = hi - lo;
     const int bits = 32 - __builtin_clz(span);
     const int shift = bits > 8 ? bits - 8 : 0;
     *(uint4*)&sl.hist[4 * L] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int j = 0; j < kWaveTopN; ++j)
-      if (kv[j] >= lo && kv[j] <= hi) atomicAdd(&sl.hist[(kv[j] - lo) >> shift], 1u);
-    const uint4 h4 = *(const uint4*)&sl.hist[4 * L];
-    const uint32_t hh[4] = {h4.x, h4.y, h4.z, h4.w};
-    const uint32_t incl = wave_incl_scan(hh[0] + hh[1] + hh[2] + hh[3]);
-    uint32_t run = __builtin_amdgcn_readlane(incl, kWave - 1) - incl;
-    int fd = -1;
-    uint32_t above = 0, cnt = 0;
-#pragma unroll
-    for (int d = 3; d >= 0; --d) {
-      if (fd < 0 && run < krem && run + hh[d] >= krem) {
-        fd = d;
-        above = run;
-        cnt = hh[d];
-      }
-      run += hh[d];
+    for (int j = 0; j < NK; ++j) {
+      const bool in = kv[j] >= lo && kv[j] <= hi;
+      atomicAdd(&sl.hist[in ? (kv[j] - lo) >> shift : 256u + L], 1u);
     }
-    const uint64_t fm = __builtin_amdgcn_ballot_w64(fd >= 0);
-    const int fl = __builtin_ctzll(fm);
-    const uint32_t bin = __builtin_amdgcn_readlane(4 * L + fd, fl);
-    const uint32_t ab = __builtin_amdgcn_readlane(above, fl), cn = __builtin_amdgcn_readlane(cnt, fl);
+    uint32_t bin, ab;
+    wave_find_bin(sl, krem, &bin, &ab, &cn);
     const uint32_t nlo = lo + (bin << shift);
     hi = min(hi, nlo + ((1u << shift) - 1u));
     lo = nlo;
     krem -= ab;
-    finish = cn <= 64u;
   }
+  // The threshold T and the copies of it to take: every key of [lo, hi] when the
+  // range is taken whole (T = its smallest key), krem copies of a single-valued range,
+  // else rank the <= 64 keys of the range exactly.
   uint32_t T = lo;
-  if (finish && lo != hi) {
+  const bool all_t = cn == krem;  // take every copy of T
+  if (all_t) {
+    uint32_t bmn = 0xffffffffu;
+#pragma unroll
+    for (int j = 0; j < NK; ++j) bmn = kv[j] >= lo && kv[j] <= hi ? min(bmn, kv[j]) : bmn;
+    T = wave_reduce_u32<false>(bmn);
+  } else if (lo != hi) {
     // gather the <= 64 keys of [lo, hi] with their positions, then rank them exactly
     uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < kWaveTopN; ++j) c += kv[j] >= lo && kv[j] <= hi;
+    for (int j = 0; j < NK; ++j) c += kv[j] >= lo && kv[j] <= hi;
     uint32_t o = wave_incl_scan(c) - c;
     const uint32_t nfin = __builtin_amdgcn_readlane(o + c, kWave - 1);
 #pragma unroll
-    for (int j = 0; j < kWaveTopN; ++j)
-      if (kv[j] >= lo && kv[j] <= hi) {
-        sl.fk[o] = kv[j];
-        sl.fp[o] = (uint32_t)(16 * L + j);
-        ++o;
-      }
-    if ((uint32_t)L >= nfin) {  // pad to whole quads with entries that never rank above
-      sl.fk[L] = 0u;
-      sl.fp[L] = 0xffffffffu;
+    for (int j = 0; j < NK; ++j) {
+      const bool in = kv[j] >= lo && kv[j] <= hi;
+      const uint32_t at = in ? o : 64u + L;
+      sl.fk[at] = kv[j];
+      sl.fp[at] = pos(j);
+      o += in;
     }
-    const uint32_t myk = (uint32_t)L < nfin ? sl.fk[L] : 0u, myp = (uint32_t)L < nfin ? sl.fp[L] : 0u;
+    // pad to whole quads with entries that never rank above
+    const uint32_t at = (uint32_t)L >= nfin ? (uint32_t)L : 64u + L;
+    sl.fk[at] = 0u;
+    sl.fp[at] = 0xffffffffu;
+    const uint32_t myk = sl.fk[L], myp = sl.fp[L];  // entry L (a pad when L >= nfin)
     uint32_t rank = 0, gt = 0;
     for (uint32_t i = 0; i < nfin; i += 4) {  // broadcast reads, four entries at a time
       const uint4 k4 = *(const uint4*)&sl.fk[i], p4 = *(const uint4*)&sl.fp[i];
       const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w}, pp[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        rank += kk[q] > myk || (kk[q] == myk && pp[q] < myp);
+      for (int q = 0; q < 4; ++q) {  // bitwise, not short-circuit: no branch around the loads
+        rank += (uint32_t)(kk[q] > myk) | ((uint32_t)(kk[q] == myk) & (uint32_t)(pp[q] < myp));
         gt += kk[q] > myk;
       }
     }
@@ -423,33 +425,82 @@ __device__ void wave_top32(const uint32_t (&kv)[kWaveTopN], WaveSelLds& sl, Emit
     T = __builtin_amdgcn_readlane(myk, hl);
     krem -= __builtin_amdgcn_readlane(gt, hl);  // copies of T still to take
   }
-  // compaction in position order (lane-major): keys > T and the first krem copies of T
+  // compaction in slot order (lane-major): keys > T and the first krem copies of T
   uint32_t gtc = 0, eqc = 0;
 #pragma unroll
-  for (int j = 0; j < kWaveTopN; ++j) {
+  for (int j = 0; j < NK; ++j) {
     gtc += kv[j] > T;
     eqc += kv[j] == T;
   }
-  const uint32_t eq_before = wave_incl_scan(eqc) - eqc;  // copies of T in lanes below
+  const uint32_t eq_incl = wave_incl_scan(eqc);
+  const uint32_t eq_before = eq_incl - eqc;  // copies of T in lanes below
+  if (all_t) krem = __builtin_amdgcn_readlane(eq_incl, kWave - 1);
   const uint32_t take = eq_before >= krem ? 0u : min(eqc, krem - eq_before);
   const uint32_t selc = gtc + take;
   uint32_t r = wave_incl_scan(selc) - selc;
   uint32_t seen = 0, tpos = 0;
   bool has_t = false;
 #pragma unroll
-  for (int j = 0; j < kWaveTopN; ++j) {
+  for (int j = 0; j < NK; ++j) {
     const bool is_eq = kv[j] == T;
     const bool keep = kv[j] > T || (is_eq && seen < take);
-    if (is_eq && seen < take && eq_before + seen == krem - 1u) {
-      tpos = (uint32_t)(16 * L + j);
-      has_t = true;
-    }
+    const bool last = is_eq && seen < take && eq_before + seen == krem - 1u;
+    tpos = last ? pos(j) : tpos;
+    has_t = has_t || last;
     seen += is_eq;
-    if (keep) emit(r++, j);
+    sl.res[keep ? r : (uint32_t)kWaveTopC + L] = make_uint2(kv[j], pos(j));
+    r += keep;
   }
   const uint64_t tm = __builtin_amdgcn_ballot_w64(has_t);
   *tpos_out = __builtin_amdgcn_readlane(tpos, __builtin_ctzll(tm));
   *T_out = T;
+}
+
+// Exact top-32, in (key desc, position asc) order, of the 1024 keys one wave holds:
+// lane L holds kv[j], the key of position 16L + j; absent positions hold 0, every
+// present key is > 0 and more than 32 are present.  The kept (key, position) pairs
+// land in sl.res[0..31] in ascending position order; returns the 32nd kept key and
+// the position of its last kept copy.
+// Pre-filter: each of the 32 lane pairs holds a key at least as large as the smallest
+// pair maximum tau, so at least as many keys as there are nonempty pairs are >= tau.
+// When more than 32 and at most 256 keys are >= tau, the top-32 lies among them:
+// they are compacted in position order (4 per lane) and only they are selected from.
+// Otherwise the selection runs on all 16 keys per lane.
+__device__ void wave_top32(const uint32_t (&kv)[kWaveTopN], WaveSelLds& sl, uint32_t* T_out, uint32_t* tpos_out) {
+  const int L = threadIdx.x % kWave;
+  uint32_t lmx = 0u, lmn = 0xffffffffu;
+#pragma unroll
+  for (int j = 0; j < kWaveTopN; ++j) {
+    lmx = max(lmx, kv[j]);
+    lmn = kv[j] ? min(lmn, kv[j]) : lmn;
+  }
+  // quad_perm [1,0,3,2]: the other lane of the pair
+  const uint32_t pm = max(lmx, (uint32_t)__builtin_amdgcn_update_dpp((int)lmx, (int)lmx, 0xB1, 0xF, 0xF, false));
+  const uint32_t tau = wave_reduce_u32<false>(pm ? pm : 0xffffffffu);
+  const uint32_t hi = wave_reduce_u32<true>(lmx);
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < kWaveTopN; ++j) c += kv[j] >= tau;
+  const uint32_t incl = wave_incl_scan(c);
+  const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
+  if (total > (uint32_t)kWaveTopC && total <= (uint32_t)(kWave * kWaveTopPre)) {
+    // empty slots first, then the survivors over them (LDS ops of one wave run in order)
+    *(uint4*)&sl.pre[kWaveTopPre * L] = make_uint4(0u, 0u, 0u, 0u);
+    *(uint4*)&sl.pre[kWaveTopPre * L + 2] = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t o = incl - c;
+#pragma unroll
+    for (int j = 0; j < kWaveTopN; ++j) {
+      const bool in = kv[j] >= tau;
+      sl.pre[in ? o : (uint32_t)(kWave * kWaveTopPre + L)] = make_uint2(kv[j], (uint32_t)(kWaveTopN * L + j));
+      o += in;
+    }
+    const uint4 a4 = *(const uint4*)&sl.pre[kWaveTopPre * L], b4 = *(const uint4*)&sl.pre[kWaveTopPre * L + 2];
+    const uint32_t k4[kWaveTopPre] = {a4.x, a4.z, b4.x, b4.z}, p4[kWaveTopPre] = {a4.y, a4.w, b4.y, b4.w};
+    wave_top32_core<kWaveTopPre>(k4, [&](int j) { return p4[j]; }, tau, hi, sl, T_out, tpos_out);
+  } else {
+    const uint32_t lo = wave_reduce_u32<false>(lmn);
+    wave_top32_core<kWaveTopN>(kv, [&](int j) { return (uint32_t)(kWaveTopN * L + j); }, lo, hi, sl, T_out, tpos_out);
+  }
 }
 
 

@@ -262,9 +262,11 @@ __global__ __launch_bounds__(256) void topk_cand32_kernel(const float* __restric
     return;
   }
   uint32_t T, tpos;
-  wave_top32(kv, sl[w], [&](uint32_t r, int j) {
-    out[r] = make_uint2(kv[j], (uint32_t)(start + kWaveTopN * L + j));
-  }, &T, &tpos);
+  wave_top32(kv, sl[w], &T, &tpos);
+  if (L < kWaveTopC) {  // one coalesced store of the list
+    const uint2 e = sl[w].res[L];
+    out[L] = make_uint2(e.x, (uint32_t)start + e.y);
+  }
   if (L == 0) *mt = SliceMeta{(uint32_t)kWaveTopC, 1u, T, (uint32_t)start + tpos};
 }
 
