@@ -182,20 +182,27 @@ __device__ __forceinline__ void quantize_query_mxfp4(const IndexArgs& a, const f
 // keys go through LDS once; three waves then exit (freeing their registers for
 // the next workgroups' key loads) and one wave runs a barrier-free radix select.
 template <int NR, bool CAND>  // NR: accumulator rows that can hold a real head: 4 (heads <= 8) or 16 (heads <= 32)
-__global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a, CandOut co) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6 : 4))) void index_mxfp4_kernel(IndexArgs a, CandOut co) {
   const int row = blockIdx.y;
   const int b = row / a.tq, t = row % a.tq;
   const int wave = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int V = visible_blocks(a.q_pos[row], a.m);
   const int g0 = blockIdx.x * kFp4KeysPerWG + wave * kFp4KeysPerWave;
-  const int m = l % 32, kb = l / 32;
+  // The key (within a 32-key tile) and K block this lane loads.  Up to 8 heads use a
+  // block-diagonal 16x16x128 MFMA: query heads fill rows 0-7 over K 0-63 and rows
+  // 8-15 over K 64-127, keys 0-15 of the tile fill K 0-63 and keys 16-31 K 64-127, so
+  // one MFMA scores 32 keys with a 4-register accumulator; up to 32 heads use the
+  // 32x32x64 MFMA (rows = heads, columns = keys).
+  constexpr bool kDiag = NR == 4;
+  const int m = kDiag ? 16 * (l / 32) + l % 16 : l % 32;
+  const int kb = kDiag ? (l / 16) % 2 : l / 32;
   __shared__ __attribute__((aligned(16))) uint32_t qcode[32][2][4];  // [head][K block][16 B of e2m1 codes]
   __shared__ uint32_t qscale[32][2];
   __shared__ float wsh[32];
   if (threadIdx.x < a.heads) wsh[threadIdx.x] = a.w[(int64_t)row * a.heads + threadIdx.x];
 
   // 1) the query (loaded first: it must not queue behind the keys), then the key codes
-  //    (16 B per lane: key l%32's block l/32) and their e8m0 scales, whose latency
+  //    (16 B per lane: key m's block kb) and their e8m0 scales, whose latency
   //    overlaps the query quantisation below
   float2 qx[kQueryPairsMax];
   query_pairs(a, b, t, qx);
@@ -215,14 +222,19 @@ __global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a, CandOut c
   quantize_query_mxfp4(a, qx, qcode, qscale);
   __syncthreads();
   if (!CAND && g0 >= a.n_cap) return;
+  // A operand: row l%16 (diagonal) or l%32, K block l/16 or l/32 (32 e2m1 codes each)
+  const int qrow = kDiag ? l % 16 : l % 32, qblk = kDiag ? l / 16 : l / 32;
+  const bool qlive = kDiag ? (qrow < 8) == (qblk < 2) : true;  // off-diagonal blocks are zero
+  const int qh = kDiag ? qrow % 8 : qrow;
   v8i A = {0, 0, 0, 0, 0, 0, 0, 0};
   int sa = 127;
-  if (m < a.heads) {
-    const uint4 qv = *(const uint4*)&qcode[m][kb][0];
+  if (qlive && qh < a.heads) {
+    const uint4 qv = *(const uint4*)&qcode[qh][qblk % 2][0];
     A[0] = (int)qv.x; A[1] = (int)qv.y; A[2] = (int)qv.z; A[3] = (int)qv.w;
-    sa = (int)qscale[m][kb];
+    sa = (int)qscale[qh][qblk % 2];
   }
-  // head weights of this lane's accumulator rows h = 8*(r/4) + 4*(l/32) + r%4
+  // head weights of this lane's accumulator rows h = 8*(r/4) + 4*kb + r%4 (both layouts:
+  // a diagonal lane's rows 4*(l/16) + r hold heads 4*((l/16)%2) + r)
   float wv[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
@@ -232,20 +244,28 @@ __global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a, CandOut c
   // 3) scores
   float* srow = a.scores + (int64_t)row * a.n_cap;
   const int gend = min(g0 + kFp4KeysPerWave, a.n_cap);
-  float sc[kFp4Unroll];  // the wave's scores: tile u, key g0 + 32u + l%32 (both half-waves)
+  float sc[kFp4Unroll];  // the wave's scores: tile u, key g0 + 32u + m (in lanes l and l ^ kPair)
+  constexpr int kPair = kDiag ? 16 : 32;  // the lane holding the same key's other heads
 #pragma unroll
   for (int u = 0; u < kFp4Unroll; ++u) {
     v8i Bop = {c[u][0], c[u][1], c[u][2], c[u][3], 0, 0, 0, 0};
-    v16f acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bop, acc, 4, 4, 0, sa, 0, sbk[u]);
     float part = 0.f;
+    if constexpr (kDiag) {
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bop, acc, 4, 4, 0, sa, 0, sbk[u]);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) part = fmaf(wv[r], fmaxf(acc[r], 0.f), part);
-    const float other = __shfl_xor(part, 32);
-    sc[u] = part + other;  // the same value in lane l and lane l ^ 32
-    if (u >= kFp4Unroll / 2) {  // lanes 0-31 store tile u - 4, lanes 32-63 tile u: one store for two tiles
+      for (int r = 0; r < 4; ++r) part = fmaf(wv[r], fmaxf(acc[r], 0.f), part);
+    } else {
+      v16f acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bop, acc, 4, 4, 0, sa, 0, sbk[u]);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) part = fmaf(wv[r], fmaxf(acc[r], 0.f), part);
+    }
+    const float other = __shfl_xor(part, kPair);
+    sc[u] = part + other;  // the same value in lane l and lane l ^ kPair
+    if (u >= kFp4Unroll / 2) {  // kb == 0 lanes store tile u - 4, kb == 1 lanes tile u: one store for two tiles
       const int us = kb ? u : u - kFp4Unroll / 2;
       const int key = g0 + 32 * us + m;
       const float v = kb ? sc[u] : sc[u - kFp4Unroll / 2];
@@ -263,9 +283,9 @@ __global__ __launch_bounds__(256) void index_mxfp4_kernel(IndexArgs a, CandOut c
     const int slice = blockIdx.x;
     const int start = slice * kFusedSlice;
     const int n = max(0, min(kFusedSlice, Vc - start));  // visible keys of this slice
-    if (l < 32) {
+    if (kb == 0) {  // these lanes hold every key of the wave's tiles once
 #pragma unroll
-      for (int u = 0; u < kFp4Unroll; ++u) skeys[wave * kFp4KeysPerWave + 32 * u + l] = float_key(sc[u]);
+      for (int u = 0; u < kFp4Unroll; ++u) skeys[wave * kFp4KeysPerWave + 32 * u + m] = float_key(sc[u]);
     }
     __syncthreads();
     if (wave != 0) return;  // one wave selects; the others free their registers now
