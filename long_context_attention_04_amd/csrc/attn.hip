@@ -441,9 +441,12 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
   const int H = a.heads;
   float* obase = partial ? (float*)a.ws + (((int64_t)row * nsplit_max + s) * H + h0) * 512
                          : a.out + ((int64_t)row * H + h0) * 512;
+  // item -> (4-head group, column) with the column fastest: a wave reads 64 consecutive
+  // 16-byte buffer entries (no bank conflict) and each of its stores covers 64
+  // consecutive columns of one head
 #pragma unroll
   for (int it = 0; it < 512 * 4 / kThreads; ++it) {
-    const int item = threadIdx.x + kThreads * it, c = item / 4, hq = item % 4;
+    const int item = threadIdx.x + kThreads * it, hq = item / 512, c = item % 512;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {  // fixed order over the four buffers

@@ -472,6 +472,44 @@ def test_attention_deterministic_and_batch_invariant(gpu_lib):
         assert np.array_equal(s[0][0], a[0][i]) and np.array_equal(s[1][0], a[1][i])
 
 
+def test_attention_workspace_reuse(gpu_lib):
+    """One workspace serves a sequence of CSA and HCA calls with different split
+    layouts, each giving the results of a call with a fresh workspace."""
+    csa = gpu_lib
+    B, H, D, N, k, W, m, mhc, ncap = 3, 64, 512, 2048, 600, 128, 4, 16, 700
+    r, q, kvc, raw = _attn_inputs("wsreuse", B, 1, H, D, N, 512, "bf16")
+    pos = np.full((B, 1), N * m - 1, np.int32)
+    pos[1, 0] = N * m // 3
+    raw_base = (pos[:, 0] - 300).astype(np.int32)
+    idx = np.stack([[sorted_unique_choice(r, oracle.visible_blocks(int(pos[b, 0]), m), k)] for b in range(B)])
+    idx = idx.astype(np.int32)
+    kvh = r.standard_normal((B, ncap, D)).astype(np.float32)
+    qt, kt, rt, ht = up_bf16(q)[0], up_bf16(kvc)[0], up_bf16(raw)[0], up_bf16(kvh)[0]
+    n_csa = csa.csa_attn_workspace_size(B, 1, H, D, k + W)
+    n_hca = csa.csa_attn_workspace_size(B, 1, H, D, ncap + W)
+    assert n_csa > 0 and n_hca > 0  # both calls split their lists
+
+    def call(kind, qq, ws):
+        out = torch.empty((B, 1, H, D), device="cuda")
+        lse = torch.empty((B, 1, H), device="cuda")
+        if kind == "csa":
+            csa.csa_sparse_attn(csa.desc(qq, csa.BF16), csa.desc(kt, csa.BF16), up(idx), k, csa.desc(rt, csa.BF16),
+                                up(raw_base), W, up(pos), B, 1, H, D, 0.088, out, lse, ws, ws.numel())
+        else:
+            hpos = np.minimum(pos, mhc * ncap - 1).astype(np.int32)
+            csa.hca_attn(csa.desc(qq, csa.BF16), csa.desc(ht, csa.BF16), mhc, ncap, csa.desc(rt, csa.BF16),
+                         up(raw_base), W, up(hpos), B, 1, H, D, 0.088, out, lse, ws, ws.numel())
+        return down(out), down(lse)
+
+    shared = workspace(max(n_csa, n_hca))
+    q2 = (qt.float() * 0.5).to(torch.bfloat16)
+    for kind, qq in (("csa", qt), ("hca", qt), ("csa", q2), ("hca", q2), ("csa", qt)):
+        got = call(kind, qq, shared)
+        n = n_csa if kind == "csa" else n_hca
+        fresh = call(kind, qq, workspace(n))
+        assert np.array_equal(got[0], fresh[0]) and np.array_equal(got[1], fresh[1])
+
+
 def test_attention_fp8_zero_row_is_an_entry(gpu_lib):
     """An all-zero fp8 row has row scale 0; it is still an entry of the softmax (logit 0,
     contributes a zero vector), not an empty slot."""
