@@ -63,6 +63,12 @@ def parse():
     return ap.parse_args()
 
 
+def compress_bytes(layer) -> int:
+    """The step's compressions: m raw KV rows (bf16) and m raw indexer-key rows (fp32) read per
+    sequence, one KV entry (bf16) and one MXFP4 indexer key written."""
+    return layer.B * (layer.m * (layer.D * 2 + layer.dI * 4) + layer.D * 2 + KEY_BYTES)
+
+
 def algorithmic_bytes(layer) -> dict:
     """Bytes the method must move once per step (stored operands read once + outputs written once)."""
     B, N, k, W, H, D = layer.B, layer.n_cap, layer.k, layer.W, layer.H, layer.D
@@ -70,7 +76,7 @@ def algorithmic_bytes(layer) -> dict:
     gather = B * (k + W) * D * 2
     q_out = B * H * D * 2 + B * H * D * 4 + B * H * 4
     small = B * k * 4 + B * layer.HI * (layer.dI * 4 + 4)
-    comp = B * (layer.m * (D * 2 + layer.dI * 4) + D * 2 + KEY_BYTES)
+    comp = compress_bytes(layer)
     return {"keys": keys, "gather": gather, "q_out": q_out, "small": small, "compress": comp,
             "total": keys + gather + q_out + small + comp}
 
@@ -106,12 +112,14 @@ def launch_us(torch, layers, reps, launch) -> float:
 
 def index_launch_bytes(layer, fused: bool) -> int:
     """Algorithmic bytes of one indexer launch: every key read once, the query and head weights,
-    the scores written once, and (fused) the slices' candidates and metadata written once."""
+    the scores written once, and (fused) the slices' candidates and metadata written once and the
+    step's compressions (their raw rows read, the new KV entry and indexer key written)."""
     B, N = layer.B, layer.n_cap
     nbytes = B * N * KEY_BYTES + B * layer.HI * (layer.dI * 4 + 4) + B * N * 4
     if fused:
         ns = (N + CAND_SLICE - 1) // CAND_SLICE
         nbytes += B * ns * (CAND_PER_SLICE * CAND_BYTES + META_BYTES)
+        nbytes += compress_bytes(layer)
     return nbytes
 
 
@@ -304,7 +312,7 @@ def main():
     fused = args.select == "fused"
     # the dominant kernel: the indexer (with the slices' candidate selection when fused), one launch
     if fused:
-        idx_us = launch_us(torch, layers, max(K, 20), lambda layer: layer.index_topk_part(1))
+        idx_us = launch_us(torch, layers, max(K, 20), lambda layer: layer.compress_index_topk(1))
     else:
         idx_us = launch_us(torch, layers, max(K, 20), lambda layer: layer.index())
     attn_us = launch_us(torch, layers, max(K, 20), lambda layer: layer.attend())

@@ -212,6 +212,24 @@ csa_status csa_index_topk_part(const csa_tensor* q_idx, const float* w, const cs
                                int32_t idx_dim, int32_t m, int32_t n_cap, int32_t k, float* scores, int32_t* idx,
                                void* ws, size_t ws_bytes, int32_t part, void* stream);
 
+/* (a)+(b)+(c) of one decode step in as few launches as the shapes allow: exactly
+ * csa_compress_jobs over kv_job and key_job (either may be NULL) followed by
+ * csa_index_topk_part(..., part), bit for bit, with the same arguments and
+ * requirements.  The compressions only run for part 1 or 3.  When the indexer
+ * scores MXFP4 keys with slice candidates (see csa_index_topk), tq == 1, the key
+ * job writes the very key tensor being scored (k_idx: same pointers and strides,
+ * dim 64, m <= 4, max_blocks <= 4, batch equal) and the KV job has m <= 16 and
+ * dim <= 512, both
+ * jobs run inside the indexer launch: KV blocks on extra workgroups, and each new
+ * key by the wave that scores it, before that wave reads its keys.  Otherwise the
+ * jobs run in a launch of their own first.  Errors: as csa_compress_jobs (the
+ * message names the job) and csa_index_topk_part. */
+csa_status csa_compress_index_topk(const csa_compress_job* kv_job, const csa_compress_job* key_job,
+                                   const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx,
+                                   const int32_t* q_pos, int32_t batch, int32_t tq, int32_t n_idx_heads,
+                                   int32_t idx_dim, int32_t m, int32_t n_cap, int32_t k, float* scores, int32_t* idx,
+                                   void* ws, size_t ws_bytes, int32_t part, void* stream);
+
 /* ---------------------------------------------------------------------------
  * (d) CSA sparse attention: attention over the selected compressed entries
  * plus a sliding window of raw local entries, which both CSA and HCA add to

@@ -96,6 +96,9 @@ _c = {
     "csa_index_topk_part": _proto("csa_index_topk_part", _I32, _TP, _P, _TP, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                   _I32, _P, _P, _P, _SZ, _I32, _P),
     "csa_index_topk_workspace_size": _proto("csa_index_topk_workspace_size", _SZ, _I32, _I32, _I32, _I32),
+    "csa_compress_index_topk": _proto("csa_compress_index_topk", _I32, ctypes.POINTER(CsaCompressJob),
+                                      ctypes.POINTER(CsaCompressJob), _TP, _P, _TP, _P, _I32, _I32, _I32, _I32,
+                                      _I32, _I32, _I32, _P, _P, _P, _SZ, _I32, _P),
     "csa_sparse_attn": _proto("csa_sparse_attn", _I32, _TP, _TP, _P, _I32, _TP, _P, _I32, _P, _I32, _I32, _I32,
                               _I32, _F, _P, _P, _P, _SZ, _P),
     "hca_attn": _proto("hca_attn", _I32, _TP, _TP, _I32, _I32, _TP, _P, _I32, _P, _I32, _I32, _I32, _I32, _F, _P,
@@ -204,6 +207,23 @@ def csa_index_topk_part(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim,
     _check(_c["csa_index_topk_part"](ctypes.byref(q_idx), _ptr(w), ctypes.byref(k_idx), _ptr(q_pos), batch, tq,
                                      n_idx_heads, idx_dim, m, n_cap, k, _ptr(scores), _ptr(idx), _ptr(ws), ws_bytes,
                                      part, _stream(stream)))
+
+
+def _job(j):
+    if j is None:
+        return None
+    raw, raw_base, logits, m, dim, first, count, max_blocks, batch, out = j
+    return ctypes.byref(CsaCompressJob(raw, _ptr(raw_base), _ptr(logits), m, dim, _ptr(first), _ptr(count),
+                                       max_blocks, batch, out))
+
+
+def csa_compress_index_topk(kv_job, key_job, q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, k,
+                            scores, idx, ws, ws_bytes, part=3, stream=None):
+    """csa_compress_jobs([kv_job, key_job]) then csa_index_topk_part(..., part), in as few launches as
+    the shapes allow; each job is a csa_compress argument tuple or None."""
+    _check(_c["csa_compress_index_topk"](_job(kv_job), _job(key_job), ctypes.byref(q_idx), _ptr(w),
+                                         ctypes.byref(k_idx), _ptr(q_pos), batch, tq, n_idx_heads, idx_dim, m, n_cap,
+                                         k, _ptr(scores), _ptr(idx), _ptr(ws), ws_bytes, part, _stream(stream)))
 
 
 def csa_attn_workspace_size(batch, tq, heads, dim, n_entries_max) -> int:

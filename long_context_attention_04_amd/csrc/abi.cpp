@@ -238,6 +238,77 @@ csa_status csa_index_topk_part(const csa_tensor* q_idx, const float* w, const cs
   return ok();
 }
 
+// A job the indexer launch can run: its raw-row format code (0 F32, 1 BF16, 2 FP8).
+static int raw_format(const csa::CompressArgs& c) {
+  return c.raw.dtype == CSA_F32 ? 0 : c.raw.dtype == CSA_BF16 ? 1 : 2;
+}
+
+csa_status csa_compress_index_topk(const csa_compress_job* kv_job, const csa_compress_job* key_job,
+                                   const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx,
+                                   const int32_t* q_pos, int32_t batch, int32_t tq, int32_t n_idx_heads,
+                                   int32_t idx_dim, int32_t m, int32_t n_cap, int32_t k, float* scores, int32_t* idx,
+                                   void* ws, size_t ws_bytes, int32_t part, void* stream) {
+  // every argument is validated before anything is launched
+  csa::CompressArgs jobs[2];
+  int n_jobs = 0;
+  for (const csa_compress_job* J : {kv_job, key_job}) {
+    if (!J) continue;
+    const csa_status st = compress_args(&J->raw, J->raw_base, J->logits, J->m, J->dim, J->block_first,
+                                        J->block_count, J->max_blocks, J->batch, &J->out, &jobs[n_jobs]);
+    if (st != CSA_OK) {
+      g_last_error = std::string(J == kv_job ? "kv_job: " : "key_job: ") + g_last_error;
+      return st;
+    }
+    ++n_jobs;
+  }
+  csa::IndexArgs a;
+  csa_status st = index_args(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, scores, &a);
+  if (st != CSA_OK) return st;
+  REQUIRE(part >= 1 && part <= 3, CSA_ERR_SHAPE, "part=%d must be 1 (scores), 2 (selection) or 3 (both)", part);
+  REQUIRE(idx != nullptr || !(part & 2), CSA_ERR_NULL, "idx is NULL");
+  REQUIRE(k >= 1, CSA_ERR_SHAPE, "k=%d must be >= 1", k);
+  const size_t need = csa_index_topk_workspace_size(batch, tq, n_cap, k);
+  if (need > 0)
+    REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "index+top-k needs %zu workspace bytes, got %zu",
+            need, ws_bytes);
+  const hipStream_t s = (hipStream_t)stream;
+  // The compressions run inside the indexer launch when it scores MXFP4 keys with slice
+  // candidates for single-query rows, the key job writes exactly the keys being scored
+  // and its blocks are small; otherwise they run first, on their own.
+  const csa::CompressArgs* kvc = kv_job ? &jobs[0] : nullptr;
+  const csa::CompressArgs* kyc = key_job ? &jobs[kv_job ? 1 : 0] : nullptr;
+  bool in_launch = (part & 1) && csa::index_topk_fused_ok(a, k) && tq == 1;
+  if (in_launch && kyc)
+    in_launch = kyc->out_dtype == CSA_MXFP4 && kyc->out == a.k.data && kyc->out_scale == a.k.scale &&
+                kyc->out_sb == a.k.sb && kyc->out_sr == a.k.sr && kyc->out_ssb == a.k.ssb &&
+                kyc->out_ssr == a.k.ssr && kyc->dim == idx_dim && idx_dim == 64 &&
+                kyc->m <= csa::kFusedCompressMaxM && kyc->max_blocks <= csa::kFusedCompressMaxNew &&
+                kyc->batch == batch;
+  if (in_launch && kvc) in_launch = kvc->m <= 16 && kvc->dim <= 512 && kvc->batch <= batch;
+  if (!in_launch) {
+    if ((part & 1) && n_jobs > 0) {
+      st = from_hip(csa::launch_compress_jobs(jobs, n_jobs, s), "csa_compress_index_topk compression launch");
+      if (st != CSA_OK) return st;
+    }
+    return csa_index_topk_part(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, k, scores, idx, ws,
+                               ws_bytes, part, stream);
+  }
+  csa::FusedCompress fc{};
+  if (kyc) {
+    fc.key = *kyc;
+    fc.key_in = raw_format(*kyc);
+  }
+  if (kvc && kvc->max_blocks > 0) {
+    fc.kv = *kvc;
+    fc.kv_in = raw_format(*kvc);
+  }
+  st = from_hip(csa::launch_index_topk_cand(a, k, ws, s, &fc), "csa_compress_index_topk scores launch");
+  if (st != CSA_OK) return st;
+  if (part & 2)
+    return from_hip(csa::launch_index_topk_merge(a, k, idx, ws, s), "csa_compress_index_topk selection launch");
+  return ok();
+}
+
 csa_status csa_index_topk(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx, const int32_t* q_pos,
                           int32_t batch, int32_t tq, int32_t n_idx_heads, int32_t idx_dim, int32_t m, int32_t n_cap,
                           int32_t k, float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {

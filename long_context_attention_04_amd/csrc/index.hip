@@ -19,6 +19,7 @@
 //    contraction of many queries against the same keys).
 //  * F32 keys: plain fp32 VALU kernel (small shapes).
 #include "common.h"
+#include "compress_block.h"
 #include "kernels.h"
 #include "select.h"
 
@@ -174,6 +175,64 @@ __device__ __forceinline__ void quantize_query_mxfp4(const IndexArgs& a, const f
   }
 }
 
+// ------------------------------------------------------------------ in-launch key compression
+// The wave scoring keys g0 .. g0+255 of sequence b compresses every key of that
+// range that this step completes (blocks klo .. khi-1 of indexer-key job fc.key, at
+// most kFusedCompressMaxNew of them): lane l computes element l of the 64 (the
+// compression's per-column arithmetic), the MXFP4 block scale and codes follow the
+// compression store's arithmetic (32 consecutive lanes per block), and the wave
+// stores the key to memory and, for its own scoring, to LDS (new key i: nkc[i] = 8
+// dwords of codes, nks[i] = the two scale bytes), where the lanes holding that key's
+// operand pick it up in place of what they loaded.  The first key's raw values are
+// loaded before the wave's key loads (compress_raw_load) and combined after them.
+__device__ __forceinline__ void compress_raw_load(const FusedCompress& fc, int b, int g,
+                                                  float (&x)[kFusedCompressMaxM]) {
+  const int64_t row0 = (int64_t)g * fc.key.m - fc.key.raw_base[b];
+  const int l = threadIdx.x % kWave;
+  if (fc.key_in == 0) compress_element_load<CSA_F32>(fc.key, b, row0, l, x);
+  else if (fc.key_in == 1) compress_element_load<CSA_BF16>(fc.key, b, row0, l, x);
+  else compress_element_load<CSA_FP8_E4M3>(fc.key, b, row0, l, x);
+}
+
+__device__ __forceinline__ void compress_own_keys(const FusedCompress& fc, int b, int klo, int khi,
+                                                  const float (&x0)[kFusedCompressMaxM], uint32_t (*nkc)[8],
+                                                  uint32_t (*nks)[2]) {
+  const CompressArgs& k = fc.key;
+  const int l = threadIdx.x % kWave;
+  float wz[kFusedCompressMaxM];
+#pragma unroll
+  for (int r = 0; r < kFusedCompressMaxM; ++r)
+    if (r < k.m) wz[r] = k.logits[r];
+  local_softmax(k.m, wz);
+  for (int g = klo; g < khi; ++g) {
+    float x[kFusedCompressMaxM];
+    if (g == klo) {
+#pragma unroll
+      for (int r = 0; r < kFusedCompressMaxM; ++r) x[r] = x0[r];
+    } else {
+      compress_raw_load(fc, b, g, x);
+    }
+    const float v = compress_element_combine(k.m, x, wz);
+    float am = fabsf(v);
+    for (int o = 16; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
+    const int e = mx_scale_exp(am);
+    const uint32_t nib = am > 0.f ? f32_to_e2m1(v, e) : 0u;
+    // dword q of the 32 code bytes holds elements 8q .. 8q+7, element 8q+d in nibble d
+    uint32_t word = nib;
+#pragma unroll
+    for (int d = 1; d < 8; ++d) word |= (uint32_t)__shfl_down((int)nib, d, 8) << (4 * d);
+    uint8_t* codes = (uint8_t*)k.out + (int64_t)b * k.out_sb + (int64_t)g * k.out_sr;
+    if (l % 8 == 0) {
+      *(uint32_t*)(codes + 4 * (l / 8)) = word;
+      nkc[g - klo][l / 8] = word;
+    }
+    if (l % 32 == 0) {
+      ((uint8_t*)k.out_scale)[(int64_t)b * k.out_ssb + (int64_t)g * k.out_ssr + l / 32] = (uint8_t)(e + 127);
+      nks[g - klo][l / 32] = (uint32_t)(e + 127);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ slice top-32
 // With CAND set, each workgroup also selects the exact top-32 of its 1024-key
 // slice in (key desc, index asc) order -- key being the order-preserving integer
@@ -182,12 +241,34 @@ __device__ __forceinline__ void quantize_query_mxfp4(const IndexArgs& a, const f
 // keys go through LDS once; three waves then exit (freeing their registers for
 // the next workgroups' key loads) and one wave runs a barrier-free radix select.
 template <int NR, bool CAND>  // NR: accumulator rows that can hold a real head: 4 (heads <= 8) or 16 (heads <= 32)
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6 : 4))) void index_mxfp4_kernel(IndexArgs a, CandOut co) {
-  const int row = blockIdx.y;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6 : 4))) void index_mxfp4_kernel(
+    IndexArgs a, CandOut co, FusedCompress fc) {
+  // Workgroup order (a 1-D grid): the KV compressions first (they run alongside the
+  // scoring instead of after it), then row by row, each row's slices from the last one
+  // down, so the slice holding a row's newest keys (which it compresses before
+  // scoring) starts first.  Consecutive workgroups stream consecutive key ranges.
+  const int rows = fc.rows, nextra = fc.kv.batch > 0 ? fc.kv.max_blocks : 0;
+  const int id = blockIdx.x;
+  if (id < rows * nextra) {  // a KV compression workgroup (decode: row == sequence)
+    __shared__ float cred[kCompressThreads / kWave];
+    const int b = id % rows, i = id / rows;
+    if (b >= fc.kv.batch) return;
+    if (fc.kv_in == 0) compress_block<2, CSA_F32, true>(fc.kv, b, i, nullptr, cred);
+    else if (fc.kv_in == 1) compress_block<2, CSA_BF16, true>(fc.kv, b, i, nullptr, cred);
+    else compress_block<2, CSA_FP8_E4M3, true>(fc.kv, b, i, nullptr, cred);
+    return;
+  }
+  const int sid = id - rows * nextra;
+  const int row = sid / fc.nslices;
   const int b = row / a.tq, t = row % a.tq;
-  const int wave = threadIdx.x / kWave, l = threadIdx.x % kWave;
-  const int V = visible_blocks(a.q_pos[row], a.m);
-  const int g0 = blockIdx.x * kFp4KeysPerWG + wave * kFp4KeysPerWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), l = threadIdx.x % kWave;
+  // the position and (in-launch key compression) the step's new blocks: one round trip
+  const int qp = a.q_pos[row];
+  const bool kjob = fc.key.batch > 0;
+  const int jf = kjob ? fc.key.block_first[b] : 0, jcnt = kjob ? fc.key.block_count[b] : 0;
+  const int V = visible_blocks(qp, a.m);
+  const int slice = fc.nslices - 1 - sid % fc.nslices;
+  const int g0 = slice * kFp4KeysPerWG + wave * kFp4KeysPerWave;
   // The key (within a 32-key tile) and K block this lane loads.  Up to 8 heads use a
   // block-diagonal 16x16x128 MFMA: query heads fill rows 0-7 over K 0-63 and rows
   // 8-15 over K 64-127, keys 0-15 of the tile fill K 0-63 and keys 16-31 K 64-127, so
@@ -199,13 +280,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6
   __shared__ __attribute__((aligned(16))) uint32_t qcode[32][2][4];  // [head][K block][16 B of e2m1 codes]
   __shared__ uint32_t qscale[32][2];
   __shared__ float wsh[32];
-  if (threadIdx.x < a.heads) wsh[threadIdx.x] = a.w[(int64_t)row * a.heads + threadIdx.x];
 
   // 1) the query (loaded first: it must not queue behind the keys), then the key codes
   //    (16 B per lane: key m's block kb) and their e8m0 scales, whose latency
   //    overlaps the query quantisation below
   float2 qx[kQueryPairsMax];
   query_pairs(a, b, t, qx);
+  // keys of blocks this step completes (the loads below may read stale codes for them):
+  // the wave compresses them first, stores them, and takes them from LDS before scoring
+  const int klo = max(jf, g0), khi = min(jf + min(jcnt, fc.key.max_blocks), g0 + kFp4KeysPerWave);
+  const bool own_new = kjob && klo < khi;  // wave-uniform
+  __shared__ uint32_t nkc[4][kFusedCompressMaxNew][8], nks[4][kFusedCompressMaxNew][2];
+  if (own_new) {
+    float xr[kFusedCompressMaxM];
+    compress_raw_load(fc, b, klo, xr);
+    compress_own_keys(fc, b, klo, khi, xr, nkc[wave], nks[wave]);
+  }
   const int kfirst = g0 + m;
   const uint8_t* kc = (const uint8_t*)a.k.data + (int64_t)b * a.k.sb + (int64_t)kfirst * a.k.sr + 16 * kb;
   const uint8_t* ks = (const uint8_t*)a.k.scale + (int64_t)b * a.k.ssb + (int64_t)kfirst * a.k.ssr + kb;
@@ -218,8 +308,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6
     c[u] = live ? *(const v4i*)(kc + u * cstep) : (v4i){0, 0, 0, 0};
     sbk[u] = live ? ks[u * sstep] : 127;
   }
+  // head weights, after the key loads (their wait must not hold the keys back)
+  if (threadIdx.x < a.heads) wsh[threadIdx.x] = a.w[(int64_t)row * a.heads + threadIdx.x];
   // 2) the query, quantised to MXFP4 once per workgroup
   quantize_query_mxfp4(a, qx, qcode, qscale);
+
   __syncthreads();
   if (!CAND && g0 >= a.n_cap) return;
   // A operand: row l%16 (diagonal) or l%32, K block l/16 or l/32 (32 e2m1 codes each)
@@ -232,6 +325,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6
     const uint4 qv = *(const uint4*)&qcode[qh][qblk % 2][0];
     A[0] = (int)qv.x; A[1] = (int)qv.y; A[2] = (int)qv.z; A[3] = (int)qv.w;
     sa = (int)qscale[qh][qblk % 2];
+  }
+  if (own_new) {  // the new keys' operands, from LDS (after the barrier above)
+#pragma unroll
+    for (int u = 0; u < kFp4Unroll; ++u) {
+      const int g = kfirst + 32 * u;
+      if (g >= klo && g < khi && g < V) {
+        const uint32_t* wc = nkc[wave][g - klo] + 4 * kb;
+        c[u] = (v4i){(int)wc[0], (int)wc[1], (int)wc[2], (int)wc[3]};
+        sbk[u] = (int)nks[wave][g - klo][kb];
+      }
+    }
   }
   // head weights of this lane's accumulator rows h = 8*(r/4) + 4*kb + r%4 (both layouts:
   // a diagonal lane's rows 4*(l/16) + r hold heads 4*((l/16)%2) + r)
@@ -280,7 +384,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6
     if (Vc <= co.k) return;  // every visible key is selected: the merge needs no candidates
     __shared__ __attribute__((aligned(16))) uint32_t skeys[kFusedSlice];
     __shared__ WaveSelLds sl;
-    const int slice = blockIdx.x;
     const int start = slice * kFusedSlice;
     const int n = max(0, min(kFusedSlice, Vc - start));  // visible keys of this slice
     if (kb == 0) {  // these lanes hold every key of the wave's tiles once
@@ -322,18 +425,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6
   }
 }
 
+// No in-launch compression: every workgroup scores.
+FusedCompress no_compress(int nslices, int rows) {
+  FusedCompress f{};
+  f.key.batch = 0;
+  f.kv.batch = 0;
+  f.nslices = nslices;
+  f.rows = rows;
+  return f;
+}
+
 }  // namespace
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
   const int rows = a.batch * a.tq;
   if (rows == 0 || a.n_cap == 0) return hipSuccess;
   if (a.k.dtype == CSA_MXFP4) {
-    dim3 grid((a.n_cap + kFp4KeysPerWG - 1) / kFp4KeysPerWG, rows);
+    const int nslices = (a.n_cap + kFp4KeysPerWG - 1) / kFp4KeysPerWG;
+    const dim3 grid((unsigned)(nslices * rows));
     const CandOut none{};
     if (a.heads <= 8)
-      hipLaunchKernelGGL((index_mxfp4_kernel<4, false>), grid, dim3(256), 0, s, a, none);
+      hipLaunchKernelGGL((index_mxfp4_kernel<4, false>), grid, dim3(256), 0, s, a, none, no_compress(nslices, rows));
     else
-      hipLaunchKernelGGL((index_mxfp4_kernel<16, false>), grid, dim3(256), 0, s, a, none);
+      hipLaunchKernelGGL((index_mxfp4_kernel<16, false>), grid, dim3(256), 0, s, a, none, no_compress(nslices, rows));
   } else if (a.k.dtype == CSA_BF16 && a.q.dtype == CSA_BF16 && a.heads == 8 && a.dim == 64) {
     dim3 grid((a.n_cap + kBfKT - 1) / kBfKT, (a.tq + kBfQT - 1) / kBfQT, a.batch);
     hipLaunchKernelGGL(index_bf16_kernel, grid, dim3(256), 0, s, a);
@@ -347,14 +461,19 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
 
 static_assert(kFp4KeysPerWG == kFusedSlice, "one indexer workgroup per candidate slice");
 
-hipError_t launch_index_scores_cand(const IndexArgs& a, const CandOut& c, hipStream_t s) {
+hipError_t launch_index_scores_cand(const IndexArgs& a, const CandOut& c, hipStream_t s, const FusedCompress* fc) {
   const int rows = a.batch * a.tq;
   if (rows == 0 || a.n_cap == 0) return hipSuccess;
-  dim3 grid((a.n_cap + kFp4KeysPerWG - 1) / kFp4KeysPerWG, rows);
+  const int nslices = (a.n_cap + kFp4KeysPerWG - 1) / kFp4KeysPerWG;
+  FusedCompress f = fc ? *fc : no_compress(nslices, rows);
+  f.nslices = nslices;
+  f.rows = rows;
+  const int extra = f.kv.batch > 0 ? f.kv.max_blocks : 0;  // KV compression workgroups per row
+  const dim3 grid((unsigned)((nslices + extra) * rows));
   if (a.heads <= 8)
-    hipLaunchKernelGGL((index_mxfp4_kernel<4, true>), grid, dim3(256), 0, s, a, c);
+    hipLaunchKernelGGL((index_mxfp4_kernel<4, true>), grid, dim3(256), 0, s, a, c, f);
   else
-    hipLaunchKernelGGL((index_mxfp4_kernel<16, true>), grid, dim3(256), 0, s, a, c);
+    hipLaunchKernelGGL((index_mxfp4_kernel<16, true>), grid, dim3(256), 0, s, a, c, f);
   return hipGetLastError();
 }
 

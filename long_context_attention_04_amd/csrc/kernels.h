@@ -91,10 +91,26 @@ constexpr int kFusedSlice = 1024;  // keys per indexer workgroup
 constexpr int kFusedC = 32;
 bool index_topk_fused_ok(const IndexArgs& a, int k);
 size_t index_topk_workspace_bytes(int64_t rows, int n_cap, int k);
-hipError_t launch_index_scores_cand(const IndexArgs& a, const CandOut& c, hipStream_t s);  // index.hip
+// A decode step's compressions, run by the indexer launch (index.hip): the KV
+// compression on extra workgroups, and the indexer-key compression by the waves
+// whose keys include a block just completed (they compress it, store it and score
+// it), so no launch of its own precedes the scoring.  batch == 0: no such job.
+// Preconditions (checked by the caller): tq == 1; key.out is the indexer's key
+// tensor (MXFP4, dim 64), key.m <= kFusedCompressMaxM and key.max_blocks <=
+// kFusedCompressMaxNew; kv.m <= 16, kv.dim <= 512.
+constexpr int kFusedCompressMaxM = 4;    // the indexer-key job's block size m (CSA)
+constexpr int kFusedCompressMaxNew = 4;  // and its blocks per sequence (max_blocks)
+struct FusedCompress {
+  CompressArgs key, kv;
+  int key_in, kv_in;  // raw row format of each job: 0 F32, 1 BF16, 2 FP8
+  int nslices, rows;  // scoring workgroups per row, query rows (set by the launcher)
+};
+hipError_t launch_index_scores_cand(const IndexArgs& a, const CandOut& c, hipStream_t s,
+                                    const FusedCompress* fc = nullptr);  // index.hip
 hipError_t launch_index_topk(const IndexArgs& a, int k, int32_t* idx, void* ws, hipStream_t s);
 // the two kernels of launch_index_topk, one launch each
-hipError_t launch_index_topk_cand(const IndexArgs& a, int k, void* ws, hipStream_t s);
+hipError_t launch_index_topk_cand(const IndexArgs& a, int k, void* ws, hipStream_t s,
+                                  const FusedCompress* fc = nullptr);
 hipError_t launch_index_topk_merge(const IndexArgs& a, int k, int32_t* idx, void* ws, hipStream_t s);
 
 // ---------------------------------------------------------------- attention

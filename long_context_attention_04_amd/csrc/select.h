@@ -577,7 +577,8 @@ __device__ void block_key_range(const uint32_t (&kv)[NPT], RegSelLds& rs, uint32
 // ascending; 0 = absent, present keys > 0, more than k present; [lo, hi] the
 // present range from block_key_range, whose barrier this call relies on).
 // Returns the k-th largest key T and the number krem of its copies taken (the
-// lowest-slot ones).  A first pass of 1024 bins linear in the score, then
+// lowest-slot ones; 0xffffffff when every copy is taken).  A first pass of 1024
+// bins linear in the score, then
 // key-space passes of 1024 bins over the bin of the k-th key while it holds
 // more than 64 keys; those are ranked exactly by one wave.  A non-decreasing
 // map from key to bin keeps every bin a contiguous range of the key order,
@@ -613,7 +614,7 @@ __device__ void block_threshold_regs(const uint32_t (&kv)[NPT], uint32_t lo, uin
   };
   bool finish = false, by_bin = false;
   int b[NPT];
-  uint32_t fbin = 0;
+  uint32_t fbin = 0, cn_last = 0xffffffffu;  // keys in the final range (unknown before a pass)
   const float xlo = key_float(lo), xhi = key_float(hi);
   const float inv = 1023.99f / (xhi - xlo);
   // NaN and infinite scores, or a span too small to invert, go to the key-space passes
@@ -624,7 +625,8 @@ __device__ void block_threshold_regs(const uint32_t (&kv)[NPT], uint32_t lo, uin
     uint32_t above, cn;
     pass(b, &fbin, &above, &cn);
     krem -= above;
-    if (cn <= 64u) {
+    cn_last = cn;
+    if (cn <= 64u || cn == krem) {
       finish = by_bin = true;
     } else {  // the key range of that bin (a contiguous range of the key order)
       const int w = __builtin_amdgcn_readfirstlane(t / kWave), L = t % kWave;
@@ -653,6 +655,7 @@ __device__ void block_threshold_regs(const uint32_t (&kv)[NPT], uint32_t lo, uin
   }
   // key-space passes: 32 bits at <= 10 bits per pass end in a single key after 4
   for (int p = 0; p < 4 && !finish && lo != hi; ++p) {
+    by_bin = false;
     const int bits = 32 - __builtin_clz(hi - lo);
     const int shift = bits > 10 ? bits - 10 : 0;
 #pragma unroll
@@ -663,14 +666,29 @@ __device__ void block_threshold_regs(const uint32_t (&kv)[NPT], uint32_t lo, uin
     hi = min(hi, nlo + ((1u << shift) - 1u));
     lo = nlo;
     krem -= above;
-    finish = cn <= 64u;
+    cn_last = cn;
+    finish = cn <= 64u || cn == krem;
   }
   uint32_t T = lo;
-  if (finish && (by_bin || lo != hi)) {
+  auto in_final = [&](int j) { return by_bin ? b[j] == (int)fbin : (kv[j] >= lo && kv[j] <= hi); };
+  if (finish && cn_last == krem) {
+    // the final range is taken whole: T is its smallest key, every copy of it taken
+    const int w = __builtin_amdgcn_readfirstlane(t / kWave), L = t % kWave;
+    uint32_t mn = 0xffffffffu;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) mn = in_final(j) ? min(mn, kv[j]) : mn;
+    mn = wave_reduce_u32<false>(mn);
+    if (L == 0) rs.red[0][w] = mn;
+    __syncthreads();
+    T = 0xffffffffu;
+#pragma unroll
+    for (int i = 0; i < kRegSelWaves; ++i) T = min(T, rs.red[0][i]);
+    krem = 0xffffffffu;
+  } else if (finish && (by_bin || lo != hi)) {
     // gather the <= 64 keys of the final bin with their slots, then rank them in one wave
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
-      const bool in = by_bin ? b[j] == (int)fbin : (kv[j] >= lo && kv[j] <= hi);
+      const bool in = in_final(j);
       if (in) {
         const uint32_t s = atomicAdd(&rs.nfin, 1u);
         rs.fk[s] = kv[j];
@@ -684,14 +702,14 @@ __device__ void block_threshold_regs(const uint32_t (&kv)[NPT], uint32_t lo, uin
         rs.fk[t] = 0u;
         rs.fp[t] = 0xffffffffu;
       }
-      const uint32_t myk = (uint32_t)t < c ? rs.fk[t] : 0u, myp = (uint32_t)t < c ? rs.fp[t] : 0u;
+      const uint32_t myk = rs.fk[t], myp = rs.fp[t];  // entry t (a pad when t >= c)
       uint32_t rank = 0, gt = 0;
       for (uint32_t i = 0; i < c; i += 4) {
         const uint4 k4 = *(const uint4*)&rs.fk[i], p4 = *(const uint4*)&rs.fp[i];
         const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w}, pp[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          rank += kk[q] > myk || (kk[q] == myk && pp[q] < myp);
+        for (int q = 0; q < 4; ++q) {  // bitwise, not short-circuit: no branch around the loads
+          rank += (uint32_t)(kk[q] > myk) | ((uint32_t)(kk[q] == myk) & (uint32_t)(pp[q] < myp));
           gt += kk[q] > myk;
         }
       }

@@ -286,6 +286,7 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge32_kernel(const floa
                                                                      int32_t* __restrict__ idx) {
   __shared__ RegSelLds rs;
   __shared__ SelShared sh;
+  __shared__ uint32_t ostage[kMergeCap + kRegSelThreads];  // selected indices by rank, then discard slots
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
   const int V = min(visible_blocks(q_pos[row], m), n_cap);
@@ -331,18 +332,27 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge32_kernel(const floa
     const uint32_t packed = gtc | (eqc << 16);
     uint32_t tot;
     const uint32_t excl = block_scan_regsel(packed, rs.scan[2], &tot) - packed;
+    krem = min(krem, tot >> 16);  // "every copy" made a count
     uint32_t eq_seen = excl >> 16;
     uint32_t r = (excl & 0xffffu) + min(eq_seen, krem);
+    // the k indices go to LDS (rank order), unwanted stores to this thread's discard
+    // slot, then out in one coalesced pass
+    uint32_t my_jT = 0;
+    bool has_t = false;
 #pragma unroll
     for (int j = 0; j < kM32PerThread; ++j) {
       const bool is_eq = kv[j] == T;
       const bool keep = kv[j] > T || (is_eq && eq_seen < krem);
-      if (is_eq && eq_seen == krem - 1u) rs.jT = iv[j];  // the last copy of T taken
+      const bool last = is_eq && eq_seen == krem - 1u;  // the last copy of T taken
+      my_jT = last ? iv[j] : my_jT;
+      has_t = has_t || last;
       eq_seen += is_eq;
-      if (keep && r < (uint32_t)k) out[r] = (int32_t)iv[j];
+      ostage[keep && r < (uint32_t)k ? r : (uint32_t)kMergeCap + t] = iv[j];
       r += keep;
     }
+    if (has_t) rs.jT = my_jT;
     __syncthreads();
+    for (int i = t; i < k; i += kRegSelThreads) out[i] = (int32_t)ostage[i];
     // exact unless a truncated slice had its 32nd kept element selected
     const uint32_t jT = rs.jT;
     if (t < ns && mm.trunc && (mm.last_key > T || (mm.last_key == T && mm.last_idx <= jT))) rs.bad = 1u;
@@ -449,9 +459,9 @@ CandOut fused_cand_out(const IndexArgs& a, int k, void* ws) {
 }
 }  // namespace
 
-hipError_t launch_index_topk_cand(const IndexArgs& a, int k, void* ws, hipStream_t s) {
+hipError_t launch_index_topk_cand(const IndexArgs& a, int k, void* ws, hipStream_t s, const FusedCompress* fc) {
   if ((int64_t)a.batch * a.tq == 0) return hipSuccess;
-  return launch_index_scores_cand(a, fused_cand_out(a, k, ws), s);
+  return launch_index_scores_cand(a, fused_cand_out(a, k, ws), s, fc);
 }
 
 hipError_t launch_index_topk_merge(const IndexArgs& a, int k, int32_t* idx, void* ws, hipStream_t s) {

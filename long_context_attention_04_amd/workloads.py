@@ -24,7 +24,8 @@ import torch
 
 import synth
 
-from . import (BF16, F32, FP8_E4M3, MXFP4, csa_attn_workspace_size, csa_compress, csa_compress_jobs,
+from . import (BF16, F32, FP8_E4M3, MXFP4, csa_attn_workspace_size, csa_compress, csa_compress_index_topk,
+               csa_compress_jobs,
                csa_index_scores, csa_index_topk, csa_index_topk_part, csa_index_topk_workspace_size, csa_quantize_fp8, csa_quantize_mxfp4, csa_sparse_attn,
                csa_topk, csa_topk_workspace_size, desc, hca_attn)
 
@@ -164,14 +165,24 @@ class CsaLayer:
         csa_compress(self.raw_ik.desc(), self.raw_base, self.z_ik, self.m, self.dI, self.blk_first, self.blk_count,
                      self.max_blocks, self.B, self.k_idx.desc(), stream)
 
+    def kv_job(self):
+        return (self.raw_kv.desc(), self.raw_base, self.z_kv, self.m, self.D, self.blk_first, self.blk_count,
+                self.max_blocks, self.B, self.kv_cmp.desc())
+
+    def key_job(self):
+        return (self.raw_ik.desc(), self.raw_base, self.z_ik, self.m, self.dI, self.blk_first, self.blk_count,
+                self.max_blocks, self.B, self.k_idx.desc())
+
     def compress(self, stream=None):
         """Both compressions of the step (KV and indexer key) in one launch."""
-        csa_compress_jobs([
-            (self.raw_kv.desc(), self.raw_base, self.z_kv, self.m, self.D, self.blk_first, self.blk_count,
-             self.max_blocks, self.B, self.kv_cmp.desc()),
-            (self.raw_ik.desc(), self.raw_base, self.z_ik, self.m, self.dI, self.blk_first, self.blk_count,
-             self.max_blocks, self.B, self.k_idx.desc()),
-        ], stream)
+        csa_compress_jobs([self.kv_job(), self.key_job()], stream)
+
+    def compress_index_topk(self, part=3, stream=None):
+        """compress, then index_topk (or one part of it), the compressions inside the indexer
+        launch where the shapes allow."""
+        csa_compress_index_topk(self.kv_job(), self.key_job(), self.q_idx.desc(), self.w, self.k_idx.desc(),
+                                self.q_pos, self.B, self.tq, self.HI, self.dI, self.m, self.n_cap, self.k,
+                                self.scores, self.idx, self.ws_itk, self.ws_itk.numel(), part, stream)
 
     def index(self, stream=None):
         csa_index_scores(self.q_idx.desc(), self.w, self.k_idx.desc(), self.q_pos, self.B, self.tq, self.HI, self.dI,
@@ -198,6 +209,7 @@ class CsaLayer:
 
     stage_names = ("compress", "index+topk", "attention")
     fused_select = True  # score and select with csa_index_topk (else csa_index_scores, then csa_topk)
+    fused_compress = True  # with fused_select: the compressions run inside the indexer launch
 
     def select(self, stream=None):
         if self.fused_select:
@@ -208,8 +220,13 @@ class CsaLayer:
 
     def step(self, stream=None, marks=None):
         """One pass of the CSA hot path (compress the new blocks, score and select the
-        top-k, attend).  `marks(i)` is called between stages."""
-        for i, stage in enumerate((self.compress, self.select, self.attend)):
+        top-k, attend).  `marks(i)` is called between stages; with the compressions
+        inside the indexer launch, the compress stage is empty and index+topk holds them."""
+        if self.fused_select and self.fused_compress:
+            stages = (lambda st: None, lambda st: self.compress_index_topk(3, st), self.attend)
+        else:
+            stages = (self.compress, self.select, self.attend)
+        for i, stage in enumerate(stages):
             if marks:
                 marks(i)
             stage(stream)

@@ -161,6 +161,27 @@ def test_index_topk_rejects_and_workspace():
     expect(E_WS, part(1, idx=None, wsb=need - 1))
 
 
+def test_compress_index_topk_rejects():
+    """Every argument of the combined call is checked before anything is launched: a bad job
+    is named, then the indexer's own checks apply."""
+    q, k = T(csa.F32), T(csa.MXFP4, scale=P)
+    need = csa.csa_index_topk_workspace_size(8, 1, 262144, 2048)
+    good = (T(csa.BF16), P, P, 4, 512, P, P, 1, 8, T(csa.BF16))
+
+    def call(kvj=good, kyj=None, idx=P, wsb=need, part=3, kk=2048):
+        return lambda stream: csa.csa_compress_index_topk(kvj, kyj, q, P, k, P, 8, 1, 8, 64, 4, 262144, kk, P, idx,
+                                                          P, wsb, part, stream)
+
+    bad_m = (T(csa.BF16), P, P, 0, 512, P, P, 1, 8, T(csa.BF16))
+    expect(E_SHAPE, call(kvj=bad_m), match="kv_job")
+    expect(E_NULL, call(kyj=(T(csa.F32), None, P, 4, 64, P, P, 1, 8, k)), match="key_job")
+    expect(E_DTYPE, call(kyj=(T(csa.MXFP4, scale=P), P, P, 4, 64, P, P, 1, 8, k)), match="key_job")
+    expect(E_SHAPE, call(part=0), match="part")
+    expect(E_NULL, call(idx=None))
+    expect(E_SHAPE, call(kk=0))
+    expect(E_WS, call(wsb=need - 1))
+
+
 # ---------------------------------------------------------------------------- attention
 
 

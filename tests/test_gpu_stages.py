@@ -472,6 +472,83 @@ def test_attention_deterministic_and_batch_invariant(gpu_lib):
         assert np.array_equal(s[0][0], a[0][i]) and np.array_equal(s[1][0], a[1][i])
 
 
+@pytest.mark.parametrize("kv_fmt,ik_fmt,tq", [("bf16", "f32", 1), ("fp8", "bf16", 1), ("bf16", "f32", 2)])
+def test_compress_index_topk_matches_separate_calls(gpu_lib, kv_fmt, ik_fmt, tq):
+    """csa_compress_index_topk == csa_compress_jobs then csa_index_topk_part, bit for bit: the
+    stored KV entries and indexer keys, the scores and the selection -- with new blocks on a
+    slice boundary, a sequence completing none, either part alone, and (tq=2) the shapes that
+    run the compressions in a launch of their own."""
+    csa = gpu_lib
+    B, N, HI, dI, D, m, k, R = 3, 24000, 8, 64, 512, 4, 512, 16
+    r = _rng(f"cit{kv_fmt}{ik_fmt}{tq}")
+    first = np.array([1023, 5000, 7000], np.int32)  # blocks 1023 and 1024 sit in two slices
+    count = np.array([2, 1, 0], np.int32)
+    raw_base = (m * first - m).astype(np.int32)
+    end = m * (first + count) - 1  # the token completing the last new block
+    pos = np.stack([end - (tq - 1 - t) for t in range(tq)], axis=1).astype(np.int32)
+    kraw = torch.as_tensor(r.standard_normal((B, N, dI)).astype(np.float32), device="cuda")
+    kc0 = torch.empty((B, N, dI // 2), dtype=torch.uint8, device="cuda")
+    ks0 = torch.empty((B, N, dI // 32), dtype=torch.uint8, device="cuda")
+    csa.csa_quantize_mxfp4(kraw, B * N, dI, kc0, ks0)
+    xi = r.standard_normal((B, R, dI)).astype(np.float32)
+    raw_ik = csa.desc(up(xi), csa.F32) if ik_fmt == "f32" else csa.desc(up_bf16(xi)[0], csa.BF16)
+    xk = r.standard_normal((B, R, D)).astype(np.float32)
+    if kv_fmt == "bf16":
+        raw_kv = csa.desc(up_bf16(xk)[0], csa.BF16)
+        kv0 = (torch.as_tensor(r.standard_normal((B, N, D)).astype(np.float32), device="cuda").to(torch.bfloat16),
+               None)
+    else:
+        c_, s_ = OF.quantize_fp8_rows(xk.reshape(-1, D))
+        raw_kv = csa.desc(up(c_.reshape(B, R, D)), csa.FP8_E4M3, up(s_.reshape(B, R)))
+        kv0 = (torch.randint(0, 120, (B, N, D), dtype=torch.uint8, device="cuda"), torch.rand((B, N), device="cuda"))
+    z_kv = up(r.standard_normal(m).astype(np.float32))
+    z_ik = up(r.standard_normal(m).astype(np.float32))
+    q = up(r.standard_normal((B, tq, HI, dI)).astype(np.float32))
+    w = up(r.standard_normal((B, tq, HI)).astype(np.float32))
+    dpos, dbase, dfirst, dcount = up(pos), up(raw_base), up(first), up(count)
+    kv_dt = csa.BF16 if kv_fmt == "bf16" else csa.FP8_E4M3
+
+    def state():
+        kc, ks = kc0.clone(), ks0.clone()
+        kv = (kv0[0].clone(), None if kv0[1] is None else kv0[1].clone())
+        return kc, ks, kv
+
+    def jobs(kc, ks, kv):
+        kvj = (raw_kv, dbase, z_kv, m, D, dfirst, dcount, 2, B, csa.desc(kv[0], kv_dt, kv[1]))
+        kyj = (raw_ik, dbase, z_ik, m, dI, dfirst, dcount, 2, B, csa.desc(kc, csa.MXFP4, ks))
+        return kvj, kyj
+
+    def outputs():
+        return (torch.full((B, tq, N), float("nan"), device="cuda"),
+                torch.full((B, tq, k), -7, dtype=torch.int32, device="cuda"),
+                workspace(csa.csa_index_topk_workspace_size(B, tq, N, k)))
+
+    def bits(kc, ks, kv, sc, ix):
+        kvb = kv[0].view(torch.uint8) if kv[0].dtype == torch.bfloat16 else kv[0]
+        return [kc, ks, kvb] + ([kv[1]] if kv[1] is not None else []) + [sc.view(torch.int32), ix]
+
+    # reference: the compressions, then the indexer with selection
+    kc, ks, kv = state()
+    sc, ix, ws = outputs()
+    kvj, kyj = jobs(kc, ks, kv)
+    csa.csa_compress_jobs([kvj, kyj])
+    csa.csa_index_topk_part(csa.desc(q, csa.F32), w, csa.desc(kc, csa.MXFP4, ks), dpos, B, tq, HI, dI, m, N, k, sc,
+                            ix, ws, ws.numel(), 3)
+    want = bits(kc, ks, kv, sc, ix)
+    for parts in ((3,), (1, 2)):
+        kc, ks, kv = state()
+        sc, ix, ws = outputs()
+        kvj, kyj = jobs(kc, ks, kv)
+        for part in parts:
+            csa.csa_compress_index_topk(kvj, kyj, csa.desc(q, csa.F32), w, csa.desc(kc, csa.MXFP4, ks), dpos, B, tq,
+                                        HI, dI, m, N, k, sc, ix, ws, ws.numel(), part)
+        got = bits(kc, ks, kv, sc, ix)
+        for a_, b_ in zip(want, got):
+            assert torch.equal(a_, b_)
+    # the new keys did change (the comparison is not of untouched tensors)
+    assert not torch.equal(kc[0, 1023], kc0[0, 1023]) or not torch.equal(ks[0, 1023], ks0[0, 1023])
+
+
 def test_attention_workspace_reuse(gpu_lib):
     """One workspace serves a sequence of CSA and HCA calls with different split
     layouts, each giving the results of a call with a fresh workspace."""
