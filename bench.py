@@ -42,7 +42,7 @@ CAND_SLICE, CAND_PER_SLICE, CAND_BYTES, META_BYTES = 1024, 32, 8, 16  # fused in
 INDEX_KERNEL = {"fused": "index_mxfp4_kernel<4, true>", "two-stage": "index_mxfp4_kernel<4, false>"}
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "index_mxfp4_csa_decode_1m_b8_pmc.txt")
 INDEX_SOURCES = [os.path.join(ROOT, "long_context_attention_04_amd", "csrc", f)
-                 for f in ("index.hip", "select.h", "common.h")]  # the indexer kernel's code
+                 for f in ("index.hip", "select.h", "common.h", "compress_block.h", "kernels.h")]  # the indexer kernel's code
 
 
 def parse():
