@@ -615,13 +615,14 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
 
 // Splits depend only on the call shape (decode or not) and the entry capacity,
 // never on the batch, so each sequence's arithmetic is batch-invariant.  Decode
-// cuts a row's list into about eight splits of whole 64-entry rounds (one tile
-// per wave); calls with many queries per sequence keep each list whole.
+// cuts a row's list into eight splits of whole 16-entry tiles, at least one tile
+// per wave (8 rows x 4 head groups x 8 splits fill the 256 CUs at batch 8); calls
+// with many queries per sequence keep each list whole.
 int attn_split_size(int tq, int n_entries_max) {
   const int n = max(n_entries_max, 1);
   if (tq != 1) return min(n, kIdxStage);
-  const int round = kWaves * kTile;
-  return min(kIdxStage, max(round, ((n + 7) / 8 + round - 1) / round * round));
+  const int eighth = ((n + 7) / 8 + kTile - 1) / kTile * kTile;
+  return min(kIdxStage, max(kWaves * kTile, eighth));  // at least a tile per wave
 }
 
 size_t attn_workspace_bytes(int64_t rows, int heads, int dim, int n_entries_max, int tq) {
