@@ -184,12 +184,23 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
   decode_block(blockIdx.x, nhg, nsplit_max, &row, &s, &hg);
   if (row >= rows) return;
   const int e_begin = s * split;
+  // the wave index is made visibly uniform, so per-wave control flow is scalar
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const int m = lane % 16, g = lane / 16;  // operand role: entry / head m, k group g
   // A CSA row's compressed entries are its k selection slots, known without reading
-  // its position, so the split's indices are staged while the position is in flight.
+  // its position: the indices of each wave's first tile are loaded first (that tile's
+  // rows are requested before the workgroup barrier), then the split's indices for
+  // the LDS stage, all while the position is in flight.
   __shared__ int sidx[kIdxStage];
   const int32_t* idx_row = a.idx ? a.idx + (int64_t)row * a.k : nullptr;
   const int n_sel = idx_row ? max(0, min(split, a.k - e_begin)) : 0;
-  for (int t = threadIdx.x; t < n_sel; t += kThreads) sidx[t] = idx_row[e_begin + t];
+  const int32_t* isel = idx_row + e_begin;  // this split's indices (used only when n_sel > 0)
+  const int j0 = n_sel > 0 ? isel[min(w * kTile + m, n_sel - 1)] : 0;
+  constexpr int kStagePer = kIdxStage / kThreads;
+  int stv[kStagePer];
+#pragma unroll
+  for (int q = 0; q < kStagePer; ++q)
+    stv[q] = q * kThreads < n_sel ? isel[min(q * kThreads + (int)threadIdx.x, n_sel - 1)] : 0;
   const RowInfo ri = row_info(a, row);
   const int nsplit = max(1, (ri.n_tot + split - 1) / split);
   if (s >= nsplit) return;  // workgroup-uniform: no barrier has been passed yet
@@ -198,10 +209,6 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
   const int n_here = e_end - e_begin;
   const int h0 = hg * 16;  // first head of this workgroup
   const bool sel = idx_row != nullptr && ri.n_cmp > 0;
-
-  // the wave index is made visibly uniform, so per-wave control flow is scalar
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-  const int m = lane % 16, g = lane / 16;  // operand role: entry / head m, k group g
 
   // each wave's staged tile during the loop; the combine buffer (4 x 16 x 512 floats) afterwards
   __shared__ __attribute__((aligned(16))) uint16_t Vs[kMergeRows][kTile][kVsPitch];
@@ -212,21 +219,19 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
   // there: registers hold the row ring instead)
   __shared__ __attribute__((aligned(16))) uint16_t Qs[16][kQPitch];
   const uint16_t* qp = (const uint16_t*)a.q.data + (int64_t)ri.b * a.q.sb + (int64_t)ri.t * a.q.sr;
+  v8bf qv[16 / kWaves];
 #pragma unroll
-  for (int hh = 0; hh < 16 / kWaves; ++hh) {
-    const int h = (16 / kWaves) * w + hh;
-    *(v8bf*)&Qs[h][8 * lane] = *(const v8bf*)(qp + (h0 + h) * 512 + 8 * lane);
-  }
-  __syncthreads();  // sidx and Qs visible
+  for (int hh = 0; hh < 16 / kWaves; ++hh) qv[hh] = *(const v8bf*)(qp + (h0 + (16 / kWaves) * w + hh) * 512 + 8 * lane);
 
-  // This wave's tiles: w, w + 4, w + 8, ... of the split.
+  // This wave's tiles: w, w + 8, w + 16, ... of the split.
   const int ntile = (n_here + kTile - 1) / kTile;
   const int nt = ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0;
 
   // Row loads: one instruction per entry row, lane L taking elements 8L .. 8L+7 (a
   // whole row per instruction, the cheapest gather for the memory pipeline), so
   // the row address is scalar.  An empty or out-of-range slot reads this query's
-  // own row instead (always a valid address) and gets scale -1.
+  // own row instead (always a valid address) and gets scale -1.  Tile 0 takes its
+  // indices from j0, later tiles from the LDS stage.
   const gbyte* dummy = (const gbyte*)qp;
   Raw8<FP8> kr[kRing][kTile];  // [buffer][row]
   float esc[kRing];            // lane m: entry m's scale (-1 = empty)
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
     const int el = (w + kWaves * i) * kTile + m;  // entry offset in the split (operand role)
     const int e = e_begin + el;
     const bool cmp = e < ri.n_cmp;
-    const int j = !cmp ? 0 : sel ? sidx[min(el, n_sel - 1)] : e;
+    const int j = !cmp ? 0 : sel ? (i == 0 ? j0 : sidx[min(el, n_sel - 1)]) : e;
     const int64_t wr = e - ri.n_cmp;
     const bool live = i < nt && e < e_end && (!cmp || j >= 0);
     const gbyte* p = !live ? dummy
@@ -257,6 +262,15 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
       kr[buf][r] = load_raw8<FP8>(pr, 8 * lane);
     }
   };
+  // the first tile's rows, before the stage and the barrier
+  static_assert(kRing == 1, "the prologue issues exactly one tile ahead");
+  load_tile(0, 0);
+#pragma unroll
+  for (int q = 0; q < kStagePer; ++q)
+    if (q * kThreads < n_sel && q * kThreads + (int)threadIdx.x < n_sel) sidx[q * kThreads + threadIdx.x] = stv[q];
+#pragma unroll
+  for (int hh = 0; hh < 16 / kWaves; ++hh) *(v8bf*)&Qs[(16 / kWaves) * w + hh][8 * lane] = qv[hh];
+  __syncthreads();  // sidx and Qs visible
 
   const float sl2 = a.scale * kLog2e;
   float m_run = kNegInf;  // running max of head m (log2 units), same in all four rows
@@ -265,9 +279,6 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
 #pragma unroll
   for (int ct = 0; ct < 32; ++ct) O[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // pipeline: rows of the next kRing - 1 tiles in flight while tile i is processed
-#pragma unroll
-  for (int b = 0; b < kRing; ++b) load_tile(b, b);
   typedef __attribute__((address_space(3))) v4bf lds_v4bf;
   auto step = [&](int i, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
