@@ -301,6 +301,7 @@ def test_topk_exact(gpu_lib, B, Tq, N, k, mode):
     (2, 2, 32, 40000, 1024, "normal"),   # 32 heads, ragged last slice
     (2, 1, 8, 65536, 2048, "cluster"),   # one slice holds most top scores: the exact fallback runs
     (1, 1, 8, 30000, 512, "equal"),      # all scores equal: the lowest indices win
+    (2, 1, 8, 65536, 2048, "few"),       # 40 distinct keys: many copies of the slices' 32nd score
     (2, 3, 8, 40000, 2048, "short"),     # some rows see at most k blocks
     (3, 2, 8, 262144, 2048, "partial"),  # rows seeing a fraction of the cache: few candidates
 ])
@@ -322,6 +323,9 @@ def test_index_topk_fused(gpu_lib, B, Tq, HI, N, k, mode):
         kraw[:, 5 * 1024:6 * 1024] = 3.0 * up(q[:, 0, 0])[:, None, :]
     elif mode == "equal":
         kraw[:] = kraw[:, :1]
+    elif mode == "few":
+        pick = torch.as_tensor(r.integers(0, 40, N), device="cuda").long()
+        kraw[:] = kraw[:, pick]
     elif mode == "short":
         pos[1, :] = r.integers(0, k * m // 2, Tq)
     elif mode == "partial":
