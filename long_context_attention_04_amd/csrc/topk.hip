@@ -289,17 +289,14 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge32_kernel(const floa
   __shared__ uint32_t ostage[kMergeCap + kRegSelThreads];  // selected indices by rank, then discard slots
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
-  const int V = min(visible_blocks(q_pos[row], m), n_cap);
-  int32_t* out = idx + row * k;
-  if (V <= k) {
-    for (int i = t; i < k; i += kRegSelThreads) out[i] = i < V ? i : -1;
-    return;
-  }
-  const int ns = (V + kSlice32 - 1) / kSlice32;  // slices holding visible keys
+  // The candidate lists and the slices' metadata are loaded together with the row's
+  // position (their addresses do not depend on it: one memory round trip); the slots
+  // of slices past the visible ones are cleared once it is known.
+  const int qpos = q_pos[row];
   SliceMeta mm{0u, 0u, 0u, 0u};
-  if (t < ns) mm = meta[row * nslices + t];
+  if (t < nslices) mm = meta[row * nslices + t];
   uint32_t kv[kM32PerThread], iv[kM32PerThread];
-  if (kM32PerThread * t < ns * kWaveTopC) {
+  if (kM32PerThread * t < nslices * kWaveTopC) {
     const uint4* src = (const uint4*)(cand + row * nslices * kWaveTopC) + (kM32PerThread / 2) * t;
 #pragma unroll
     for (int q = 0; q < kM32PerThread / 2; ++q) {
@@ -310,6 +307,18 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge32_kernel(const floa
       iv[2 * q + 1] = v.w;
     }
   } else {
+#pragma unroll
+    for (int j = 0; j < kM32PerThread; ++j) kv[j] = iv[j] = 0u;
+  }
+  const int V = min(visible_blocks(qpos, m), n_cap);
+  int32_t* out = idx + row * k;
+  if (V <= k) {
+    for (int i = t; i < k; i += kRegSelThreads) out[i] = i < V ? i : -1;
+    return;
+  }
+  const int ns = (V + kSlice32 - 1) / kSlice32;  // slices holding visible keys
+  if (t >= ns) mm = SliceMeta{0u, 0u, 0u, 0u};
+  if (kM32PerThread * t >= ns * kWaveTopC) {
 #pragma unroll
     for (int j = 0; j < kM32PerThread; ++j) kv[j] = iv[j] = 0u;
   }
