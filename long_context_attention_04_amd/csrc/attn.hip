@@ -469,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
     for (int r = 0; r < 4; ++r) {
       const float L = hML[4 * hq + r][1];
       const float fs = partial ? 1.f : (L > 0.f ? __fdiv_rn(1.0f, L) : 0.f);
-      obase[(4 * hq + r) * 512 + c] = av[r] * fs;
+      __builtin_nontemporal_store(av[r] * fs, &obase[(4 * hq + r) * 512 + c]);  // streamed: read by another kernel
     }
   }
   if (threadIdx.x < 16) {
@@ -483,6 +483,16 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
       a.lse[(int64_t)row * H + hglob] = Lh > 0.f ? (Mh + log2f(Lh)) * kLn2 : kNegInf;
     }
   }
+}
+
+// Streaming (non-temporal) float4 accesses: data read or written once, kept out of
+// the way of the caches.
+__device__ __forceinline__ float4 nt_load4(const float4* p) {
+  const v4f v = __builtin_nontemporal_load((const v4f*)p);
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void nt_store4(float4 x, float4* p) {
+  __builtin_nontemporal_store((v4f){x.x, x.y, x.z, x.w}, (v4f*)p);
 }
 
 // Fixed-order log-sum-exp merge of the splits of one (row, head); one pass over
@@ -499,7 +509,8 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int split, 
   const int64_t sstride = (int64_t)H * 512 / 4;  // float4s between consecutive splits
   float4 pv[kMergeBatch];
 #pragma unroll
-  for (int j = 0; j < kMergeBatch; ++j) pv[j] = j < nsplit_max ? src[j * sstride] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < kMergeBatch; ++j)
+    pv[j] = j < nsplit_max ? nt_load4(&src[j * sstride]) : make_float4(0.f, 0.f, 0.f, 0.f);
   const float* pml = (const float*)a.ws + rows * nsplit_max * H * 512;
   float ms = kNegInf, ls = 0.f;
   if (threadIdx.x < kWave && (int)threadIdx.x < nsplit_max) {
@@ -540,13 +551,13 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int split, 
   }
   for (int s = kMergeBatch; s < nsplit; ++s) {
     const float wgt = wts[s] * inv;
-    const float4 v = src[s * sstride];
+    const float4 v = nt_load4(&src[s * sstride]);
     acc.x = fmaf(v.x, wgt, acc.x);
     acc.y = fmaf(v.y, wgt, acc.y);
     acc.z = fmaf(v.z, wgt, acc.z);
     acc.w = fmaf(v.w, wgt, acc.w);
   }
-  ((float4*)(a.out + ((int64_t)row * H + h) * 512))[threadIdx.x] = acc;
+  nt_store4(acc, &((float4*)(a.out + ((int64_t)row * H + h) * 512))[threadIdx.x]);
   if (a.lse && threadIdx.x == 0) a.lse[(int64_t)row * H + h] = L > 0.f ? (sh_M + log2f(L)) * kLn2 : kNegInf;
 }
 

@@ -305,8 +305,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6
 #pragma unroll
   for (int u = 0; u < kFp4Unroll; ++u) {
     const bool live = kfirst + 32 * u < V;
-    c[u] = live ? *(const v4i*)(kc + u * cstep) : (v4i){0, 0, 0, 0};
-    sbk[u] = live ? ks[u * sstep] : 127;
+    c[u] = live ? __builtin_nontemporal_load((const v4i*)(kc + u * cstep)) : (v4i){0, 0, 0, 0};  // read once
+    sbk[u] = live ? __builtin_nontemporal_load(ks + u * sstep) : 127;
   }
   // head weights, after the key loads (their wait must not hold the keys back)
   if (threadIdx.x < a.heads) wsh[threadIdx.x] = a.w[(int64_t)row * a.heads + threadIdx.x];
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6
       const int us = kb ? u : u - kFp4Unroll / 2;
       const int key = g0 + 32 * us + m;
       const float v = kb ? sc[u] : sc[u - kFp4Unroll / 2];
-      if (key < gend) srow[key] = key < V ? v : kNegInf;
+      if (key < gend) __builtin_nontemporal_store(key < V ? v : kNegInf, &srow[key]);  // streamed
     }
     // keep one accumulator tile live at a time: occupancy (many waves hiding each
     // other's memory latency) matters more here than MFMA back-to-back issue
