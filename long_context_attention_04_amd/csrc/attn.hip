@@ -55,9 +55,9 @@ constexpr int kVsPitch = 528;    // bf16 per staged row: 512 + 16 pad (row strid
 // rows of staged tiles that also hold the merge buffer: 4 waves x 16 heads x 512 floats in 16 x 528 bf16 units
 constexpr int kMergeRows = kWaves;  // the combine buffer (4 x 16 heads x 512 floats) fits in 8 staged tiles
 static_assert(4 * 16 * 512 * 4 <= kMergeRows * kTile * kVsPitch * 2, "combine buffer fits the staging area");
-constexpr int kIdxStage = 2048;
-constexpr int kRing = 1;  // tiles of rows in flight per wave beyond the one staged (register ring)
-constexpr int kQPitch = 520;  // bf16 per staged query head row (512 + 8 pad)  // selection indices a workgroup stages (max split)
+constexpr int kIdxStage = 2048;  // selection indices a workgroup stages (the largest split)
+constexpr int kRing = 1;         // tiles of rows in flight per wave beyond the one staged (register ring)
+constexpr int kQPitch = 520;     // bf16 per staged query head row (512 + 8 pad)
 constexpr float kRescale = 8.f;  // lazy rescale threshold (log2 units)
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
