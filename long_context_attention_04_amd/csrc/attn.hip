@@ -417,12 +417,13 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
     hML[h][1] = Lh;
   }
   // Two rounds through LDS, every sum in a fixed order: waves 4..7 write their weighted
-  // accumulators, waves 0..3 add them to their own (w + 4 onto w) and write the sums,
-  // then every thread adds the four buffers for (column, 4-head group) items.  A buffer
-  // is [4-head group][column][4 heads]: lane (m, g) stores heads 4g .. 4g+3 of one
-  // column as 16 bytes, consecutive lanes at consecutive addresses.
+  // accumulators, waves 0..3 add them to their own (w + 4 onto w) in place, then every
+  // thread adds the four buffers for (column, 4-head group) items.  A buffer is
+  // [4-head group][column][4 heads]: lane (m, g) stores heads 4g .. 4g+3 of one column
+  // as 16 bytes, consecutive lanes at consecutive addresses.  A wave of 0..3 reads and
+  // then rewrites only its own lanes' entries (LDS ops of one wave run in order), so
+  // the in-place add needs no barrier and no second copy of the accumulator.
   float* mbuf = (float*)&Vs[0][0][0];  // [4][4][512][4] floats (aliases the staging area)
-  float ow[32][4];                     // this wave's weighted accumulator
   __syncthreads();                     // all waves are done with their staged tiles
   const int wb = w % 4;
   if (w >= 4) {
@@ -435,18 +436,11 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
   if (w < 4) {
 #pragma unroll
     for (int ct = 0; ct < 32; ++ct) {
-      const float4 x = *(const float4*)&mbuf[((wb * 4 + g) * 512 + 16 * ct + m) * 4];
-      ow[ct][0] = O[ct][0] * wt[0] + x.x;
-      ow[ct][1] = O[ct][1] * wt[1] + x.y;
-      ow[ct][2] = O[ct][2] * wt[2] + x.z;
-      ow[ct][3] = O[ct][3] * wt[3] + x.w;
+      float4* p = (float4*)&mbuf[((wb * 4 + g) * 512 + 16 * ct + m) * 4];
+      const float4 x = *p;
+      *p = make_float4(O[ct][0] * wt[0] + x.x, O[ct][1] * wt[1] + x.y, O[ct][2] * wt[2] + x.z,
+                       O[ct][3] * wt[3] + x.w);
     }
-  }
-  __syncthreads();
-  if (w < 4) {
-#pragma unroll
-    for (int ct = 0; ct < 32; ++ct)
-      *(float4*)&mbuf[((wb * 4 + g) * 512 + 16 * ct + m) * 4] = make_float4(ow[ct][0], ow[ct][1], ow[ct][2], ow[ct][3]);
   }
   __syncthreads();
   const int H = a.heads;
