@@ -159,10 +159,11 @@ csa_status csa_compress_jobs(const csa_compress_job* jobs, int32_t n_jobs, void*
  *   w       [batch, tq, n_idx_heads] float, contiguous.
  *   k_idx   [batch, n_cap, idx_dim] compressed indexer keys: F32, BF16 or MXFP4.
  *   q_pos   [batch, tq] int32 query positions; precondition visible <= n_cap.
- *   n_idx_heads 1..16 (MXFP4: <= 8 ... 32 supported, see below), idx_dim: F32/BF16 a
- *           multiple of 8 up to 256; MXFP4 exactly 64.
+ *   n_idx_heads, idx_dim  >= 1.  F32 / BF16 keys: n_idx_heads * idx_dim <= 8192
+ *           (8 heads of 64 with a BF16 query use bf16 MFMA, other shapes the
+ *           fp32 VALU kernel).  MXFP4 keys: idx_dim == 64 and n_idx_heads <= 32.
+ *           Anything else is CSA_ERR_UNSUPPORTED.
  *   scores  [batch, tq, n_cap] float, contiguous (every entry written).
- * Supported MXFP4 shape: n_idx_heads <= 32, idx_dim == 64.
  * ------------------------------------------------------------------------- */
 csa_status csa_index_scores(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx,
                             const int32_t* q_pos, int32_t batch, int32_t tq, int32_t n_idx_heads,
@@ -250,8 +251,10 @@ csa_status csa_compress_index_topk(const csa_compress_job* kv_job, const csa_com
  *           query lies inside it.
  *   out     [batch, tq, heads, dim] float; lse [batch, tq, heads] float or NULL.
  *   ws      at least csa_attn_workspace_size(batch, tq, heads, dim, k + window).
- * Supported: F32 path heads <= 64, dim <= 512, dim % 4 == 0; BF16 / FP8 path
- * heads a multiple of 16 up to 64 and dim == 512.
+ * Supported: F32 path heads <= 64, dim <= 512, dim % 4 == 0, k + window <=
+ * 8192; BF16 / FP8 path heads a multiple of 16 up to 64, dim == 512 and
+ * k + window <= 131072 (64 splits of at most 2048 entries).  Anything else is
+ * CSA_ERR_UNSUPPORTED, reported before any launch.
  * ------------------------------------------------------------------------- */
 csa_status csa_sparse_attn(const csa_tensor* q, const csa_tensor* kv_cmp, const int32_t* idx, int32_t k,
                            const csa_tensor* kv_raw, const int32_t* raw_base, int32_t window,

@@ -342,6 +342,11 @@ static csa_status attn_common(const csa_tensor* q, const csa_tensor* kv, const i
     REQUIRE(q->dtype == CSA_BF16, CSA_ERR_DTYPE, "BF16/FP8 caches take a BF16 query");
     REQUIRE(dim == 512 && heads % 16 == 0 && heads <= 64, CSA_ERR_UNSUPPORTED,
             "BF16/FP8 attention supports dim == 512 and heads a multiple of 16 up to 64 (got %d, %d)", dim, heads);
+    const int split = csa::attn_split_size(tq, n_entries_max);
+    const int64_t nsplit = ((int64_t)std::max(n_entries_max, 1) + split - 1) / split;
+    REQUIRE(nsplit <= csa::kAttnMaxSplits, CSA_ERR_UNSUPPORTED,
+            "BF16/FP8 attention supports at most %d entries per query (got %d)",
+            csa::kAttnMaxSplits * csa::kAttnMaxSplitEntries, n_entries_max);
   } else {
     return fail(CSA_ERR_DTYPE, "attention caches must be F32, BF16 or FP8_E4M3");
   }

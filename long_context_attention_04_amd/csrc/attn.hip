@@ -55,7 +55,7 @@ constexpr int kVsPitch = 528;    // bf16 per staged row: 512 + 16 pad (row strid
 // rows of staged tiles that also hold the merge buffer: 4 waves x 16 heads x 512 floats in 16 x 528 bf16 units
 constexpr int kMergeRows = kWaves;  // the combine buffer (4 x 16 heads x 512 floats) fits in 8 staged tiles
 static_assert(4 * 16 * 512 * 4 <= kMergeRows * kTile * kVsPitch * 2, "combine buffer fits the staging area");
-constexpr int kIdxStage = 2048;  // selection indices a workgroup stages (the largest split)
+constexpr int kIdxStage = kAttnMaxSplitEntries;  // selection indices a workgroup stages (the largest split)
 constexpr int kRing = 1;         // tiles of rows in flight per wave beyond the one staged (register ring)
 constexpr int kQPitch = 520;     // bf16 per staged query head row (512 + 8 pad)
 constexpr float kRescale = 8.f;  // lazy rescale threshold (log2 units)
@@ -491,7 +491,7 @@ __device__ __forceinline__ void nt_store4(float4 x, float4* p) {
 
 // Fixed-order log-sum-exp merge of the splits of one (row, head); one pass over
 // the partials with every split's row in flight at once.
-constexpr int kMergeMaxSplits = 64;
+constexpr int kMergeMaxSplits = kAttnMaxSplits;
 constexpr int kMergeBatch = 8;  // splits whose partial rows are loaded up front
 
 __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int split, int nsplit_max, int64_t rows) {

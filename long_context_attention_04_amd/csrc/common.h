@@ -84,12 +84,6 @@ __device__ __forceinline__ uint32_t f32_to_e2m1(float x, int e) {
   return e2m1_mag_code(a) | ((__float_as_uint(x) >> 28) & 0x8u);
 }
 
-__device__ __forceinline__ float e2m1_to_f32(uint32_t n) {
-  const float mag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
-  float v = mag[n & 7u];
-  return (n & 8u) ? -v : v;
-}
-
 // ----------------------------------------------------------------------------
 // order-preserving uint32 key of a float (descending float == descending key);
 // -0.0 is mapped to +0.0 first so the two compare equal.

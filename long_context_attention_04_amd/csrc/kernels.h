@@ -131,6 +131,10 @@ struct AttnArgs {
   float* lse;
   void* ws;
 };
+// A query row's entry list is cut into at most kAttnMaxSplits splits of at most
+// kAttnMaxSplitEntries entries each.
+constexpr int kAttnMaxSplits = 64;
+constexpr int kAttnMaxSplitEntries = 2048;
 int attn_split_size(int tq, int n_entries_max);
 size_t attn_workspace_bytes(int64_t rows, int heads, int dim, int n_entries_max, int tq);
 hipError_t launch_attention(const AttnArgs& a, int n_entries_max, hipStream_t s);

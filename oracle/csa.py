@@ -7,9 +7,10 @@ seeded input generators in ``synth``.
 
 What the pages fix (b-lab.team summary of DeepSeek-V4, "Core Methodological
 Innovations", item 1, Hybrid Attention Architecture):
-  * CSA compresses the KV cache by a factor m by combining adjacent entries,
-    then a Lightning Indexer scores compressed blocks from low-rank projections
-    of the query hidden state and the top-k blocks are attended sparsely;
+  * CSA shrinks the cache m-fold: each run of m neighbouring KV entries
+    becomes one stored entry; an indexer (the "Lightning Indexer") ranks the
+    stored entries using low-rank projections of the query's hidden state, and
+    attention then visits only the k best-ranked ones;
   * HCA compresses by m' >> m and attends densely over what remains;
   * both add a sliding window of local (uncompressed) KV entries.
 Everything else is a reading, stated where it is used:

@@ -27,7 +27,6 @@ exactly (fp32 inputs, powers of two), so the decisions are exact.
 """
 from __future__ import annotations
 
-import math
 
 import numpy as np
 
@@ -203,6 +202,3 @@ def dequantize_mxfp4(packed, scales) -> np.ndarray:
     blk = vals.reshape(vals.shape[:-1] + (vals.shape[-1] // MX_BLOCK, MX_BLOCK))
     return (blk * np.exp2(e.astype(np.float64))[..., None]).reshape(vals.shape)
 
-
-def e8m0_value(code: int) -> float:
-    return math.ldexp(1.0, int(code) - 127)

@@ -208,6 +208,10 @@ def test_attention_rejects_and_workspace():
     expect(E_WS, sparse(ws=None))
     expect(E_DTYPE, sparse(kv=T(csa.MXFP4, scale=P), raw=T(csa.MXFP4, scale=P)))
     expect(E_UNSUP, sparse(q=T(csa.F32), kv=T(csa.F32), raw=T(csa.F32), k=9000, W=0, heads=16, dim=128))
+    # more than 64 splits of 2048 entries: rejected on the host, not by a failed launch
+    big = csa.csa_attn_workspace_size(8, 1, 64, 512, 131072 + 129)
+    expect(E_UNSUP, sparse(k=131072, W=129, wsb=big), match="entries per query")
+    expect(E_UNSUP, sparse(k=131072 - 128, W=129, wsb=big), match="entries per query")
 
     def hca(m_hc=128, ncap=1024, heads=64):
         return lambda stream: csa.hca_attn(q, kv, m_hc, ncap, raw, P, 128, P, 8, 1, heads, 512, 0.088, P, P, P,
@@ -216,6 +220,7 @@ def test_attention_rejects_and_workspace():
     expect(E_SHAPE, hca(m_hc=0))
     expect(E_SHAPE, hca(ncap=-1))
     expect(E_UNSUP, hca(heads=8))
+    expect(E_UNSUP, hca(ncap=131072), match="entries per query")
 
 
 # ---------------------------------------------------------------------------- quantisers
