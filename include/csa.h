@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -186,28 +186,35 @@ csa_status csa_topk(const float* scores, const int32_t* q_pos, int32_t batch, in
 size_t csa_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, int32_t k);
 
 /* ---------------------------------------------------------------------------
- * (b)+(c) fused: indexer scores and top-k selection in one call, for callers
- * that need both.  Same arguments, formats and results as csa_index_scores
- * followed by csa_topk on the scores it wrote (scores is still written, and
- * idx equals what csa_topk returns for it, bit for bit).  With MXFP4 keys on
- * rows longer than the single-workgroup top-k (n_cap > 20480), the indexer's
- * workgroups also select their own 1024-block slices' top-32 candidates as
- * they score them, so the selection pass only merges candidates; other shapes
- * run the two stages one after the other.
- *   ws  at least csa_index_topk_workspace_size() bytes; contents on entry do
- *       not matter.
+ * (b)+(c) fused: indexer scores and top-k selection in one call.  idx equals
+ * what csa_topk returns for the scores csa_index_scores computes, bit for bit.
+ *   scores  [batch, tq, n_cap] float, or NULL.  When given, every score is
+ *           written there (exactly csa_index_scores' result).  When NULL, the
+ *           scores are not returned and, where the fused path applies, mostly
+ *           never stored at all.
+ *   ws      at least csa_index_topk_workspace_size(batch, tq, n_cap, k,
+ *           scores != NULL) bytes; its contents on entry do not matter.
+ * With MXFP4 keys on rows longer than the single-workgroup top-k (n_cap >
+ * 20480, at most 262,144), each indexer workgroup also lists its 1024-block
+ * slice's candidates as it scores them (every block at or above a cut of the
+ * slice's scores), and one merge pass selects the row's top-k from the lists,
+ * certified exact; rows the lists cannot decide (rows with few full slices, and
+ * the rare rows whose certificate fails) are selected from their scores, which
+ * are kept in the workspace or recomputed there when the caller keeps none.
+ * Other shapes run the two stages one after the other.
  * ------------------------------------------------------------------------- */
 csa_status csa_index_topk(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx, const int32_t* q_pos,
                           int32_t batch, int32_t tq, int32_t n_idx_heads, int32_t idx_dim, int32_t m,
                           int32_t n_cap, int32_t k, float* scores, int32_t* idx, void* ws, size_t ws_bytes,
                           void* stream);
-size_t csa_index_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, int32_t k);
+size_t csa_index_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, int32_t k, int32_t scores_kept);
 /* csa_index_topk in two launches, for callers that schedule (or time) the scoring
  * and the selection separately: part 1 scores (and, where the fused path applies,
  * leaves the slices' candidates in ws), part 2 selects; part 3 is both, exactly
  * csa_index_topk.  A part-2 call must follow a part-1 call with the same
  * arguments on the same stream, with scores and ws untouched in between; its
- * result then equals csa_index_topk's bit for bit.  idx may be NULL for part 1. */
+ * result then equals csa_index_topk's bit for bit.  idx may be NULL for part 1;
+ * scores may be NULL as for csa_index_topk. */
 csa_status csa_index_topk_part(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx,
                                const int32_t* q_pos, int32_t batch, int32_t tq, int32_t n_idx_heads,
                                int32_t idx_dim, int32_t m, int32_t n_cap, int32_t k, float* scores, int32_t* idx,

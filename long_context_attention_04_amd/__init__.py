@@ -95,7 +95,7 @@ _c = {
                              _P, _P, _SZ, _P),
     "csa_index_topk_part": _proto("csa_index_topk_part", _I32, _TP, _P, _TP, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                   _I32, _P, _P, _P, _SZ, _I32, _P),
-    "csa_index_topk_workspace_size": _proto("csa_index_topk_workspace_size", _SZ, _I32, _I32, _I32, _I32),
+    "csa_index_topk_workspace_size": _proto("csa_index_topk_workspace_size", _SZ, _I32, _I32, _I32, _I32, _I32),
     "csa_compress_index_topk": _proto("csa_compress_index_topk", _I32, ctypes.POINTER(CsaCompressJob),
                                       ctypes.POINTER(CsaCompressJob), _TP, _P, _TP, _P, _I32, _I32, _I32, _I32,
                                       _I32, _I32, _I32, _P, _P, _P, _SZ, _I32, _P),
@@ -191,8 +191,8 @@ def csa_topk(scores, q_pos, batch, tq, n_cap, m, k, idx, ws=None, ws_bytes=0, st
                           _stream(stream)))
 
 
-def csa_index_topk_workspace_size(batch, tq, n_cap, k) -> int:
-    return _c["csa_index_topk_workspace_size"](batch, tq, n_cap, k)
+def csa_index_topk_workspace_size(batch, tq, n_cap, k, scores_kept=True) -> int:
+    return _c["csa_index_topk_workspace_size"](batch, tq, n_cap, k, int(bool(scores_kept)))
 
 
 def csa_index_topk(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, k, scores, idx, ws=None,

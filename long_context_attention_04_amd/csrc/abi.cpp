@@ -143,11 +143,12 @@ csa_status csa_compress_jobs(const csa_compress_job* jobs, int32_t n_jobs, void*
 // Validates the indexer arguments and fills the launch description.
 static csa_status index_args(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx, const int32_t* q_pos,
                              int32_t batch, int32_t tq, int32_t n_idx_heads, int32_t idx_dim, int32_t m,
-                             int32_t n_cap, float* scores, csa::IndexArgs* out) {
+                             int32_t n_cap, float* scores, csa::IndexArgs* out, bool scores_required = true) {
   csa_status st;
   if ((st = check_tensor(q_idx, "q_idx")) != CSA_OK) return st;
   if ((st = check_tensor(k_idx, "k_idx")) != CSA_OK) return st;
-  REQUIRE(w && q_pos && scores, CSA_ERR_NULL, "w/q_pos/scores is NULL");
+  REQUIRE(w && q_pos, CSA_ERR_NULL, "w/q_pos is NULL");
+  REQUIRE(scores || !scores_required, CSA_ERR_NULL, "scores is NULL");
   REQUIRE(batch >= 0 && tq >= 0 && n_cap >= 0, CSA_ERR_SHAPE, "negative batch, tq or n_cap");
   REQUIRE(n_idx_heads >= 1 && idx_dim >= 1 && m >= 1, CSA_ERR_SHAPE, "n_idx_heads, idx_dim and m must be >= 1");
   const int kd = k_idx->dtype, qd = q_idx->dtype;
@@ -204,10 +205,30 @@ csa_status csa_topk(const float* scores, const int32_t* q_pos, int32_t batch, in
                   "csa_topk launch");
 }
 
-size_t csa_index_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, int32_t k) {
+size_t csa_index_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, int32_t k, int32_t scores_kept) {
   if (batch < 0 || tq < 0 || n_cap < 0 || k < 1) return 0;
-  const int64_t rows = (int64_t)batch * tq;
-  return std::max(csa::topk_workspace_bytes(rows, n_cap, k), csa::index_topk_workspace_bytes(rows, n_cap, k));
+  return csa::index_topk_workspace_bytes((int64_t)batch * tq, n_cap, k, scores_kept == 0);
+}
+
+// Checks the index+top-k arguments shared by the part-wise and combined calls.
+static csa_status index_topk_args(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx,
+                                  const int32_t* q_pos, int32_t batch, int32_t tq, int32_t n_idx_heads,
+                                  int32_t idx_dim, int32_t m, int32_t n_cap, int32_t k, float* scores, int32_t* idx,
+                                  void* ws, size_t ws_bytes, int32_t part, csa::IndexArgs* a) {
+  const csa_status st = index_args(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, scores, a, false);
+  if (st != CSA_OK) return st;
+  REQUIRE(part >= 1 && part <= 3, CSA_ERR_SHAPE, "part=%d must be 1 (scores), 2 (selection) or 3 (both)", part);
+  REQUIRE(idx != nullptr || !(part & 2), CSA_ERR_NULL, "idx is NULL");
+  REQUIRE(k >= 1, CSA_ERR_SHAPE, "k=%d must be >= 1", k);
+  const size_t need = csa_index_topk_workspace_size(batch, tq, n_cap, k, scores != nullptr);
+  if (need > 0)
+    REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "index+top-k needs %zu workspace bytes, got %zu",
+            need, ws_bytes);
+  // Without a caller buffer the two-stage path keeps its scores in the workspace; the
+  // fused path writes none (short rows excepted, which it keeps there itself).
+  if (scores == nullptr && !csa::index_topk_fused_ok(*a, k))
+    a->scores = (float*)((char*)ws + csa::index_topk_score_offset((int64_t)batch * tq, n_cap, k));
+  return CSA_OK;
 }
 
 csa_status csa_index_topk_part(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx,
@@ -215,15 +236,9 @@ csa_status csa_index_topk_part(const csa_tensor* q_idx, const float* w, const cs
                                int32_t m, int32_t n_cap, int32_t k, float* scores, int32_t* idx, void* ws,
                                size_t ws_bytes, int32_t part, void* stream) {
   csa::IndexArgs a;
-  csa_status st = index_args(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, scores, &a);
+  csa_status st = index_topk_args(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, k, scores, idx,
+                                  ws, ws_bytes, part, &a);
   if (st != CSA_OK) return st;
-  REQUIRE(part >= 1 && part <= 3, CSA_ERR_SHAPE, "part=%d must be 1 (scores), 2 (selection) or 3 (both)", part);
-  REQUIRE(idx != nullptr || !(part & 2), CSA_ERR_NULL, "idx is NULL");
-  REQUIRE(k >= 1, CSA_ERR_SHAPE, "k=%d must be >= 1", k);
-  const size_t need = csa_index_topk_workspace_size(batch, tq, n_cap, k);
-  if (need > 0)
-    REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "index+top-k needs %zu workspace bytes, got %zu",
-            need, ws_bytes);
   const hipStream_t s = (hipStream_t)stream;
   const bool fused = csa::index_topk_fused_ok(a, k);
   if (part & 1) {
@@ -233,7 +248,7 @@ csa_status csa_index_topk_part(const csa_tensor* q_idx, const float* w, const cs
   }
   if (part & 2)
     return fused ? from_hip(csa::launch_index_topk_merge(a, k, idx, ws, s), "csa_index_topk selection launch")
-                 : from_hip(csa::launch_topk(scores, q_pos, batch, tq, n_cap, m, k, idx, ws, s),
+                 : from_hip(csa::launch_topk(a.scores, q_pos, batch, tq, n_cap, m, k, idx, ws, s),
                             "csa_index_topk selection launch");
   return ok();
 }
@@ -262,15 +277,9 @@ csa_status csa_compress_index_topk(const csa_compress_job* kv_job, const csa_com
     ++n_jobs;
   }
   csa::IndexArgs a;
-  csa_status st = index_args(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, scores, &a);
+  csa_status st = index_topk_args(q_idx, w, k_idx, q_pos, batch, tq, n_idx_heads, idx_dim, m, n_cap, k, scores, idx,
+                                  ws, ws_bytes, part, &a);
   if (st != CSA_OK) return st;
-  REQUIRE(part >= 1 && part <= 3, CSA_ERR_SHAPE, "part=%d must be 1 (scores), 2 (selection) or 3 (both)", part);
-  REQUIRE(idx != nullptr || !(part & 2), CSA_ERR_NULL, "idx is NULL");
-  REQUIRE(k >= 1, CSA_ERR_SHAPE, "k=%d must be >= 1", k);
-  const size_t need = csa_index_topk_workspace_size(batch, tq, n_cap, k);
-  if (need > 0)
-    REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "index+top-k needs %zu workspace bytes, got %zu",
-            need, ws_bytes);
   const hipStream_t s = (hipStream_t)stream;
   // The compressions run inside the indexer launch when it scores MXFP4 keys with slice
   // candidates for single-query rows, the key job writes exactly the keys being scored

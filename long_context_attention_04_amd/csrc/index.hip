@@ -21,6 +21,7 @@
 #include "common.h"
 #include "compress_block.h"
 #include "kernels.h"
+#include "index_fp4.h"
 #include "select.h"
 
 namespace csa {
@@ -128,52 +129,10 @@ __global__ __launch_bounds__(256) void index_bf16_kernel(IndexArgs a) {
 }
 
 // ------------------------------------------------------------------ MXFP4 MFMA
-// heads <= 32, dim == 64.  Each wave scores one group of kFp4Unroll*32 keys:
-// it issues every key load of its group, the workgroup quantises the query
-// once (cooperatively, into LDS) while they are in flight, then each wave runs
-// one MFMA per 32 keys.  Short waves, many per SIMD,
-// keep the memory pipe full (a wave's own load latency overlaps the others').
-constexpr int kFp4Unroll = 8;
-constexpr int kFp4KeysPerWave = 32 * kFp4Unroll;
-constexpr int kFp4KeysPerWG = 4 * kFp4KeysPerWave;
-
-// The query of row (b, t), quantised to MXFP4 by a 256-thread workgroup into LDS:
-// thread -> (head, K block, element pair); the 16 threads of a 32-element block are
-// 16 adjacent lanes.  qcode[h][blk] = 16 B of e2m1 codes, qscale[h][blk] = e8m0.
-// Loaded first (query_pairs), quantised later (quantize_query_mxfp4), so the load
-// is not queued behind the key loads issued in between.
-constexpr int kQueryPairsMax = 4;  // heads * 32 pairs over 256 threads (heads <= 32)
-__device__ __forceinline__ void query_pairs(const IndexArgs& a, int b, int t, float2 (&x)[kQueryPairsMax]) {
-#pragma unroll
-  for (int i = 0; i < kQueryPairsMax; ++i) {
-    const int pi = 256 * i + (int)threadIdx.x;
-    const int h = pi / 32, blk = (pi / 16) % 2, pr = pi % 16;
-    x[i] = h < a.heads ? *(const float2*)((const float*)a.q.data + (int64_t)b * a.q.sb + (int64_t)t * a.q.sr + h * 64 +
-                                          32 * blk + 2 * pr)
-                       : make_float2(0.f, 0.f);
-  }
-}
-__device__ __forceinline__ void quantize_query_mxfp4(const IndexArgs& a, const float2 (&xs)[kQueryPairsMax],
-                                                     uint32_t (*qcode)[2][4], uint32_t (*qscale)[2]) {
-#pragma unroll
-  for (int i = 0; i < kQueryPairsMax; ++i) {
-    if (256 * i >= a.heads * 32) break;  // uniform
-    const int pi = 256 * i + (int)threadIdx.x;
-    const int h = pi / 32, blk = (pi / 16) % 2, pr = pi % 16;
-    const float2 x = xs[i];
-    float amax = fmaxf(fabsf(x.x), fabsf(x.y));
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
-    const int e = mx_scale_exp(amax);
-    const uint32_t byte = amax > 0.f ? (f32_to_e2m1(x.x, e) | (f32_to_e2m1(x.y, e) << 4)) : 0u;
-    // four adjacent pairs form one dword of codes
-    const uint32_t b1 = __shfl_down(byte, 1, 16), b2 = __shfl_down(byte, 2, 16), b3 = __shfl_down(byte, 3, 16);
-    if (h < a.heads) {
-      if ((pr & 3) == 0) qcode[h][blk][pr / 4] = byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
-      if (pr == 0) qscale[h][blk] = (uint32_t)(e + 127);
-    }
-  }
-}
+// heads <= 32, dim == 64.  Each wave scores 8 tiles of 32 keys (256 keys, one
+// scaled FP4 MFMA per tile; index_fp4.h), a workgroup 1024 keys: one candidate
+// slice.  The query is quantised to MXFP4 once per workgroup into LDS while the
+// keys are in flight.  Short waves, many per SIMD, keep the memory pipe full.
 
 // ------------------------------------------------------------------ in-launch key compression
 // The wave scoring keys g0 .. g0+255 of sequence b compresses every key of that
@@ -184,7 +143,10 @@ __device__ __forceinline__ void quantize_query_mxfp4(const IndexArgs& a, const f
 // stores the key to memory and, for its own scoring, to LDS (new key i: nkc[i] = 8
 // dwords of codes, nks[i] = the two scale bytes), where the lanes holding that key's
 // operand pick it up in place of what they loaded.  The first key's raw values are
-// loaded before the wave's key loads (compress_raw_load) and combined after them.
+// loaded early and combined after the wave's scoring pass, whose score for that key
+// is then replaced: the key's tile is scored again with every other key's operand
+// zero (one key's score depends on its own column only, so the bits are those a
+// pass over the stored key gives).
 __device__ __forceinline__ void compress_raw_load(const FusedCompress& fc, int b, int g,
                                                   float (&x)[kFusedCompressMaxM]) {
   const int64_t row0 = (int64_t)g * fc.key.m - fc.key.raw_base[b];
@@ -233,13 +195,12 @@ __device__ __forceinline__ void compress_own_keys(const FusedCompress& fc, int b
   }
 }
 
-// ------------------------------------------------------------------ slice top-32
-// With CAND set, each workgroup also selects the exact top-32 of its 1024-key
-// slice in (key desc, index asc) order -- key being the order-preserving integer
-// form of the score, the order the top-k uses -- and writes them in ascending
-// index order with the slice's metadata (count, truncated?, 32nd element).  The
-// keys go through LDS once; three waves then exit (freeing their registers for
-// the next workgroups' key loads) and one wave runs a barrier-free radix select.
+// With CAND set, each workgroup also writes its 1024-key slice's candidate list
+// (emit_slice_list: every key at or above a cheap cut, else the exact top-32) with
+// the slice's metadata.  The keys go through LDS once; three waves then exit (freeing
+// their registers for the next workgroups' key loads) and one wave builds the list.
+// Scores are written where a.scores points; without it, only short rows' scores go to
+// co.row_scores (their selection reads them).
 template <int NR, bool CAND>  // NR: accumulator rows that can hold a real head: 4 (heads <= 8) or 16 (heads <= 32)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6 : 4))) void index_mxfp4_kernel(
     IndexArgs a, CandOut co, FusedCompress fc) {
@@ -262,138 +223,115 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6
   const int row = sid / fc.nslices;
   const int b = row / a.tq, t = row % a.tq;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), l = threadIdx.x % kWave;
-  // the position and (in-launch key compression) the step's new blocks: one round trip
+  const int slice = fc.nslices - 1 - sid % fc.nslices;
+  const int g0 = slice * kFp4KeysPerWG + wave * kFp4KeysPerWave;
+  const Fp4Lane<NR> ln(l);
+
+  // the row's position, its query and head weights, and (in-launch key compression)
+  // the blocks this step completes, then the keys
   const int qp = a.q_pos[row];
   const bool kjob = fc.key.batch > 0;
   const int jf = kjob ? fc.key.block_first[b] : 0, jcnt = kjob ? fc.key.block_count[b] : 0;
+  float2 qx[Fp4Pairs<NR>::n];
+  fp4_query_load(a, b, t, threadIdx.x, qx);
+  __shared__ Fp4QueryLds ql;
+  if (threadIdx.x < a.heads) ql.w[threadIdx.x] = a.w[(int64_t)row * a.heads + threadIdx.x];
   const int V = visible_blocks(qp, a.m);
-  const int slice = fc.nslices - 1 - sid % fc.nslices;
-  const int g0 = slice * kFp4KeysPerWG + wave * kFp4KeysPerWave;
-  // The key (within a 32-key tile) and K block this lane loads.  Up to 8 heads use a
-  // block-diagonal 16x16x128 MFMA: query heads fill rows 0-7 over K 0-63 and rows
-  // 8-15 over K 64-127, keys 0-15 of the tile fill K 0-63 and keys 16-31 K 64-127, so
-  // one MFMA scores 32 keys with a 4-register accumulator; up to 32 heads use the
-  // 32x32x64 MFMA (rows = heads, columns = keys).
-  constexpr bool kDiag = NR == 4;
-  const int m = kDiag ? 16 * (l / 32) + l % 16 : l % 32;
-  const int kb = kDiag ? (l / 16) % 2 : l / 32;
-  __shared__ __attribute__((aligned(16))) uint32_t qcode[32][2][4];  // [head][K block][16 B of e2m1 codes]
-  __shared__ uint32_t qscale[32][2];
-  __shared__ float wsh[32];
-
-  // 1) the query (loaded first: it must not queue behind the keys), then the key codes
-  //    (16 B per lane: key m's block kb) and their e8m0 scales, whose latency
-  //    overlaps the query quantisation below
-  float2 qx[kQueryPairsMax];
-  query_pairs(a, b, t, qx);
-  // keys of blocks this step completes (the loads below may read stale codes for them):
-  // the wave compresses them first, stores them, and takes them from LDS before scoring
-  const int klo = max(jf, g0), khi = min(jf + min(jcnt, fc.key.max_blocks), g0 + kFp4KeysPerWave);
-  const bool own_new = kjob && klo < khi;  // wave-uniform
-  __shared__ uint32_t nkc[4][kFusedCompressMaxNew][8], nks[4][kFusedCompressMaxNew][2];
-  if (own_new) {
-    float xr[kFusedCompressMaxM];
-    compress_raw_load(fc, b, klo, xr);
-    compress_own_keys(fc, b, klo, khi, xr, nkc[wave], nks[wave]);
-  }
-  const int kfirst = g0 + m;
-  const uint8_t* kc = (const uint8_t*)a.k.data + (int64_t)b * a.k.sb + (int64_t)kfirst * a.k.sr + 16 * kb;
-  const uint8_t* ks = (const uint8_t*)a.k.scale + (int64_t)b * a.k.ssb + (int64_t)kfirst * a.k.ssr + kb;
-  const int64_t cstep = 32 * a.k.sr, sstep = 32 * a.k.ssr;
+  // the key codes (16 B per lane: key m's block kb) and their e8m0 scales of visible
+  // keys, read once (issued as soon as the position is known; earlier, they would
+  // hold back the query and position loads queued behind them)
+  const int kfirst = g0 + ln.m;
+  const uint8_t* kc = (const uint8_t*)a.k.data + (int64_t)b * a.k.sb + 16 * ln.kb;
+  const uint8_t* ks = (const uint8_t*)a.k.scale + (int64_t)b * a.k.ssb + ln.kb;
   v4i c[kFp4Unroll];
   int sbk[kFp4Unroll];
 #pragma unroll
   for (int u = 0; u < kFp4Unroll; ++u) {
     const bool live = kfirst + 32 * u < V;
-    c[u] = live ? __builtin_nontemporal_load((const v4i*)(kc + u * cstep)) : (v4i){0, 0, 0, 0};  // read once
-    sbk[u] = live ? __builtin_nontemporal_load(ks + u * sstep) : 127;
+    const int64_t key = min(kfirst + 32 * u, a.n_cap - 1);
+    c[u] = live ? __builtin_nontemporal_load((const v4i*)(kc + key * a.k.sr)) : (v4i){0, 0, 0, 0};
+    sbk[u] = live ? __builtin_nontemporal_load(ks + key * a.k.ssr) : 127;
   }
-  // head weights, after the key loads (their wait must not hold the keys back)
-  if (threadIdx.x < a.heads) wsh[threadIdx.x] = a.w[(int64_t)row * a.heads + threadIdx.x];
-  // 2) the query, quantised to MXFP4 once per workgroup
-  quantize_query_mxfp4(a, qx, qcode, qscale);
-
+  // keys of blocks this step completes (the loads above may have read stale codes for
+  // them): the wave compresses and stores them after its scoring pass, then rescores
+  const int klo = max(jf, g0), khi = min(jf + min(jcnt, fc.key.max_blocks), g0 + kFp4KeysPerWave);
+  const bool own_new = kjob && klo < khi;  // wave-uniform
+  fp4_query_quantize(a, threadIdx.x, qx, ql);
   __syncthreads();
   if (!CAND && g0 >= a.n_cap) return;
-  // A operand: row l%16 (diagonal) or l%32, K block l/16 or l/32 (32 e2m1 codes each)
-  const int qrow = kDiag ? l % 16 : l % 32, qblk = kDiag ? l / 16 : l / 32;
-  const bool qlive = kDiag ? (qrow < 8) == (qblk < 2) : true;  // off-diagonal blocks are zero
-  const int qh = kDiag ? qrow % 8 : qrow;
-  v8i A = {0, 0, 0, 0, 0, 0, 0, 0};
-  int sa = 127;
-  if (qlive && qh < a.heads) {
-    const uint4 qv = *(const uint4*)&qcode[qh][qblk % 2][0];
-    A[0] = (int)qv.x; A[1] = (int)qv.y; A[2] = (int)qv.z; A[3] = (int)qv.w;
-    sa = (int)qscale[qh][qblk % 2];
-  }
-  if (own_new) {  // the new keys' operands, from LDS (after the barrier above)
-#pragma unroll
-    for (int u = 0; u < kFp4Unroll; ++u) {
-      const int g = kfirst + 32 * u;
-      if (g >= klo && g < khi && g < V) {
-        const uint32_t* wc = nkc[wave][g - klo] + 4 * kb;
-        c[u] = (v4i){(int)wc[0], (int)wc[1], (int)wc[2], (int)wc[3]};
-        sbk[u] = (int)nks[wave][g - klo][kb];
-      }
-    }
-  }
-  // head weights of this lane's accumulator rows h = 8*(r/4) + 4*kb + r%4 (both layouts:
-  // a diagonal lane's rows 4*(l/16) + r hold heads 4*((l/16)%2) + r)
+
+  v8i A;
+  int sa;
   float wv[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const int h = 8 * (r / 4) + 4 * kb + (r % 4);
-    wv[r] = h < a.heads ? wsh[h] : 0.f;
-  }
-  // 3) scores
-  float* srow = a.scores + (int64_t)row * a.n_cap;
-  const int gend = min(g0 + kFp4KeysPerWave, a.n_cap);
-  float sc[kFp4Unroll];  // the wave's scores: tile u, key g0 + 32u + m (in lanes l and l ^ kPair)
-  constexpr int kPair = kDiag ? 16 : 32;  // the lane holding the same key's other heads
+  fp4_query_operand<NR>(ql, a.heads, l, &A, &sa, wv);
+  // operands of keys completed by this step (not yet stored when loaded) are zeroed
+  // before any MFMA sees them: stale bytes may hold a NaN scale, which would spoil the
+  // tile's other columns
 #pragma unroll
   for (int u = 0; u < kFp4Unroll; ++u) {
-    v8i Bop = {c[u][0], c[u][1], c[u][2], c[u][3], 0, 0, 0, 0};
-    float part = 0.f;
-    if constexpr (kDiag) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bop, acc, 4, 4, 0, sa, 0, sbk[u]);
+    const int g = kfirst + 32 * u;
+    const bool drop = own_new && g >= klo && g < khi;
+    c[u] = drop ? (v4i){0, 0, 0, 0} : c[u];
+    sbk[u] = drop ? 127 : sbk[u];
+  }
+  // 3) scores
+  float sc[kFp4Unroll];  // the wave's scores: tile u, key g0 + 32u + m (in lanes l and l ^ kPair)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part = fmaf(wv[r], fmaxf(acc[r], 0.f), part);
-    } else {
-      v16f acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bop, acc, 4, 4, 0, sa, 0, sbk[u]);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) part = fmaf(wv[r], fmaxf(acc[r], 0.f), part);
-    }
-    const float other = __shfl_xor(part, kPair);
-    sc[u] = part + other;  // the same value in lane l and lane l ^ kPair
-    if (u >= kFp4Unroll / 2) {  // kb == 0 lanes store tile u - 4, kb == 1 lanes tile u: one store for two tiles
-      const int us = kb ? u : u - kFp4Unroll / 2;
-      const int key = g0 + 32 * us + m;
-      const float v = kb ? sc[u] : sc[u - kFp4Unroll / 2];
-      if (key < gend) __builtin_nontemporal_store(key < V ? v : kNegInf, &srow[key]);  // streamed
-    }
+  for (int u = 0; u < kFp4Unroll; ++u) {
+    sc[u] = fp4_tile_score<NR>(A, sa, wv, c[u], sbk[u]);
     // keep one accumulator tile live at a time: occupancy (many waves hiding each
     // other's memory latency) matters more here than MFMA back-to-back issue
     __builtin_amdgcn_sched_barrier(0);
   }
+  if (own_new) {  // the step's new keys: compress, store, rescore their tiles
+    __shared__ uint32_t nkc[4][kFusedCompressMaxNew][8], nks[4][kFusedCompressMaxNew][2];
+    float xr[kFusedCompressMaxM];
+    compress_raw_load(fc, b, klo, xr);
+    compress_own_keys(fc, b, klo, khi, xr, nkc[wave], nks[wave]);
+#pragma unroll
+    for (int u = 0; u < kFp4Unroll; ++u) {
+      const int g = kfirst + 32 * u;
+      const bool mine = g >= klo && g < khi;
+      if (__builtin_amdgcn_ballot_w64(mine) == 0) continue;  // wave-uniform
+      v4i cn = {0, 0, 0, 0};
+      int sn = 127;
+      if (mine) {
+        const uint32_t* wc = nkc[wave][g - klo] + 4 * ln.kb;
+        cn = (v4i){(int)wc[0], (int)wc[1], (int)wc[2], (int)wc[3]};
+        sn = (int)nks[wave][g - klo][ln.kb];
+      }
+      const float s_new = fp4_tile_score<NR>(A, sa, wv, cn, sn);
+      sc[u] = mine ? s_new : sc[u];
+    }
+  }
+  const int Vc = min(V, a.n_cap);
+  float* srow = a.scores ? a.scores + (int64_t)row * a.n_cap
+                         : (CAND && Vc > co.k && index_topk_short_row(Vc, co.k) ? co.row_scores + (int64_t)row * a.n_cap
+                                                                                : nullptr);
+  if (srow) {  // kb == 0 lanes store tile u, kb == 1 lanes tile u + 4: one store for two tiles
+    const int gend = min(g0 + kFp4KeysPerWave, a.n_cap);
+#pragma unroll
+    for (int u = 0; u < kFp4Unroll / 2; ++u) {
+      const int us = ln.kb ? u + kFp4Unroll / 2 : u;
+      const int key = g0 + 32 * us + ln.m;
+      const float v = ln.kb ? sc[u + kFp4Unroll / 2] : sc[u];
+      if (key < gend) __builtin_nontemporal_store(key < V ? v : kNegInf, &srow[key]);  // streamed
+    }
+  }
   if constexpr (CAND) {
-    const int Vc = min(V, a.n_cap);
-    if (Vc <= co.k) return;  // every visible key is selected: the merge needs no candidates
+    if (Vc <= co.k || index_topk_short_row(Vc, co.k)) return;  // selected from the scores, not from lists
     __shared__ __attribute__((aligned(16))) uint32_t skeys[kFusedSlice];
-    __shared__ WaveSelLds sl;
+    __shared__ CutLds cl;
     const int start = slice * kFusedSlice;
     const int n = max(0, min(kFusedSlice, Vc - start));  // visible keys of this slice
-    if (kb == 0) {  // these lanes hold every key of the wave's tiles once
+    if (ln.kb == 0) {  // these lanes hold every key of the wave's tiles once
 #pragma unroll
-      for (int u = 0; u < kFp4Unroll; ++u) skeys[wave * kFp4KeysPerWave + 32 * u + m] = float_key(sc[u]);
+      for (int u = 0; u < kFp4Unroll; ++u) skeys[wave * kFp4KeysPerWave + 32 * u + ln.m] = float_key(sc[u]);
     }
     __syncthreads();
-    if (wave != 0) return;  // one wave selects; the others free their registers now
-    SliceMeta* mt = co.meta + (int64_t)row * co.nslices + slice;
-    uint2* out = co.cand + ((int64_t)row * co.nslices + slice) * kWaveTopC;
+    // one wave builds the list, the others free their registers now; the builder's index
+    // rotates with the workgroup so the builders of a CU's workgroups use all four SIMDs
+    if (wave != (int)(blockIdx.x % 4)) return;
     uint32_t kv[kWaveTopN];
 #pragma unroll
     for (int q = 0; q < kWaveTopN / 4; ++q) {
@@ -406,22 +344,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6
 #pragma unroll
     for (int j = 0; j < kWaveTopN; ++j)
       if (kWaveTopN * l + j >= n) kv[j] = 0u;  // positions past the visible ones are absent
-    if (n <= kWaveTopC) {  // every slot of the slice's list: its n keys, then empty (key 0) slots
-#pragma unroll
-      for (int j = 0; j < kWaveTopN; ++j) {
-        const int p = kWaveTopN * l + j;
-        if (p < kWaveTopC) out[p] = p < n ? make_uint2(kv[j], (uint32_t)(start + p)) : make_uint2(0u, 0u);
-      }
-      if (l == 0) *mt = SliceMeta{(uint32_t)n, 0u, 0u, 0u};
-      return;
-    }
-    uint32_t T, tpos;
-    wave_top32(kv, sl, &T, &tpos);
-    if (l < kWaveTopC) {  // one coalesced store of the list
-      const uint2 e = sl.res[l];
-      out[l] = make_uint2(e.x, (uint32_t)start + e.y);
-    }
-    if (l == 0) *mt = SliceMeta{(uint32_t)kWaveTopC, 1u, T, (uint32_t)start + tpos};
+    emit_slice_list(kv, n, (uint32_t)start, cl, co.cand + ((int64_t)row * co.nslices + slice) * kFusedC,
+                    co.meta + (int64_t)row * co.nslices + slice);
   }
 }
 

@@ -1,0 +1,179 @@
+// MXFP4 lightning-indexer scoring pieces shared by the indexer kernel and the
+// top-k merge's rescoring fallback: one code path, so a block rescored later
+// gets bitwise the score the indexer gave it.
+//
+// The indexer scores compressed blocks from low-rank projections of the query
+// (b-lab.team summary of DeepSeek-V4, Core Methodological Innovations 1, CSA
+// bullet) with the query-key path in FP4 (same page, item 4, Quantization-Aware
+// Training).  Reading of the score: I = sum_h w_h * relu(<q_h, kappa_j>).
+//
+// Operand layout.  A 32-key tile is scored by one scaled FP4 MFMA.  Each lane
+// loads one 16-byte MX block (32 e2m1 codes) and its e8m0 scale: exactly one
+// operand slot, so block scales are applied by the matrix core.  Up to 8 heads
+// use a block-diagonal 16x16x128 MFMA (heads in rows 0-7 over K 0-63 and again
+// in rows 8-15 over K 64-127; keys 0-15 of the tile in K 0-63, keys 16-31 in
+// K 64-127): 32 keys per MFMA with a 4-register accumulator.  Up to 32 heads
+// use the 32x32x64 MFMA (rows = heads, columns = keys).
+#pragma once
+#include "common.h"
+#include "kernels.h"
+
+namespace csa {
+namespace {
+
+constexpr int kFp4Unroll = 8;                        // 32-key tiles per wave
+constexpr int kFp4KeysPerWave = 32 * kFp4Unroll;     // 256
+constexpr int kFp4KeysPerWG = 4 * kFp4KeysPerWave;   // 1024: one candidate slice
+// Query element pairs per thread of the 256 that quantise it: heads * 32 pairs.
+template <int NR>
+struct Fp4Pairs {
+  static constexpr int n = NR == 4 ? 1 : 4;  // heads <= 8 : heads <= 32
+};
+
+// The MXFP4 query of one row and its head weights, in LDS.
+struct Fp4QueryLds {
+  __attribute__((aligned(16))) uint32_t code[32][2][4];  // [head][K block][16 B of e2m1 codes]
+  uint32_t scale[32][2];                                 // e8m0
+  float w[32];
+};
+
+// The row's fp32 query as element pairs; t in [0, 256) is the thread's index in the
+// 256-thread group that quantises it (thread -> head, K block, pair; the 16 threads of
+// a 32-element block are 16 adjacent lanes).
+// NP pairs per thread cover NP * 8 heads (NP = 1 for heads <= 8, 4 for heads <= 32).
+template <int NP>
+__device__ __forceinline__ void fp4_query_load(const IndexArgs& a, int b, int t_q, int t, float2 (&x)[NP]) {
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int pi = 256 * i + t;
+    const int h = pi / 32, blk = (pi / 16) % 2, pr = pi % 16;
+    x[i] = h < a.heads ? *(const float2*)((const float*)a.q.data + (int64_t)b * a.q.sb + (int64_t)t_q * a.q.sr +
+                                          h * 64 + 32 * blk + 2 * pr)
+                       : make_float2(0.f, 0.f);
+  }
+}
+
+// Quantises the loaded pairs to MXFP4 into LDS (same t as fp4_query_load; called by
+// whole waves of the 256-thread group).
+template <int NP>
+__device__ __forceinline__ void fp4_query_quantize(const IndexArgs& a, int t, const float2 (&xs)[NP], Fp4QueryLds& ql) {
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    if (256 * i >= a.heads * 32) break;  // uniform
+    const int pi = 256 * i + t;
+    const int h = pi / 32, blk = (pi / 16) % 2, pr = pi % 16;
+    const float2 x = xs[i];
+    float amax = fmaxf(fabsf(x.x), fabsf(x.y));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    const int e = mx_scale_exp(amax);
+    const uint32_t byte = amax > 0.f ? (f32_to_e2m1(x.x, e) | (f32_to_e2m1(x.y, e) << 4)) : 0u;
+    // four adjacent pairs form one dword of codes
+    const uint32_t b1 = __shfl_down(byte, 1, 16), b2 = __shfl_down(byte, 2, 16), b3 = __shfl_down(byte, 3, 16);
+    if (h < a.heads) {
+      if ((pr & 3) == 0) ql.code[h][blk][pr / 4] = byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      if (pr == 0) ql.scale[h][blk] = (uint32_t)(e + 127);
+    }
+  }
+}
+
+// A lane's role in the tile MFMA.  NR: accumulator rows that can hold a real head,
+// 4 (heads <= 8, block-diagonal 16x16x128) or 16 (heads <= 32, 32x32x64).
+template <int NR>
+struct Fp4Lane {
+  static constexpr bool kDiag = NR == 4;
+  static constexpr int kPair = kDiag ? 16 : 32;  // the lane holding the same key's other heads
+  int m;   // key within the 32-key tile this lane loads
+  int kb;  // K block (32 elements) of that key
+  __device__ __forceinline__ explicit Fp4Lane(int l)
+      : m(kDiag ? 16 * (l / 32) + l % 16 : l % 32), kb(kDiag ? (l / 16) % 2 : l / 32) {}
+};
+
+// The query A operand and its e8m0 scale for lane l (from LDS, after the quantising
+// group's barrier), and this lane's accumulator rows' head weights.
+template <int NR>
+__device__ __forceinline__ void fp4_query_operand(const Fp4QueryLds& ql, int heads, int l, v8i* A, int* sa,
+                                                  float (&wv)[NR]) {
+  constexpr bool kDiag = NR == 4;
+  const int qrow = kDiag ? l % 16 : l % 32, qblk = kDiag ? l / 16 : l / 32;
+  const bool qlive = kDiag ? (qrow < 8) == (qblk < 2) : true;  // off-diagonal blocks are zero
+  const int qh = kDiag ? qrow % 8 : qrow;
+  *A = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+  *sa = 127;
+  if (qlive && qh < heads) {
+    const uint4 qv = *(const uint4*)&ql.code[qh][qblk % 2][0];
+    (*A)[0] = (int)qv.x;
+    (*A)[1] = (int)qv.y;
+    (*A)[2] = (int)qv.z;
+    (*A)[3] = (int)qv.w;
+    *sa = (int)ql.scale[qh][qblk % 2];
+  }
+  // accumulator rows r hold heads 8*(r/4) + 4*kb + r%4 (both layouts)
+  const int kb = kDiag ? (l / 16) % 2 : l / 32;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int h = 8 * (r / 4) + 4 * kb + (r % 4);
+    wv[r] = h < heads ? ql.w[h] : 0.f;
+  }
+}
+
+// The score of this lane's key (tile key Fp4Lane::m), identical in lanes l and
+// l ^ kPair: one MFMA, ReLU, head weights, one cross-lane add.
+template <int NR>
+__device__ __forceinline__ float fp4_tile_score(const v8i& A, int sa, const float (&wv)[NR], v4i c, int sbk) {
+  const v8i Bop = {c[0], c[1], c[2], c[3], 0, 0, 0, 0};
+  float part = 0.f;
+  if constexpr (NR == 4) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bop, acc, 4, 4, 0, sa, 0, sbk);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part = fmaf(wv[r], fmaxf(acc[r], 0.f), part);
+  } else {
+    v16f acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bop, acc, 4, 4, 0, sa, 0, sbk);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) part = fmaf(wv[r], fmaxf(acc[r], 0.f), part);
+  }
+  const float other = __shfl_xor(part, Fp4Lane<NR>::kPair);
+  return part + other;
+}
+
+// Every visible score of one row (keys 0 .. V-1) recomputed by a whole workgroup of
+// nthreads (a multiple of 256) and written to srow: the indexer's arithmetic, tile by
+// tile.  Used when a selection must fall back to the whole row and the indexer wrote
+// no scores.  Ends with a workgroup barrier; srow is then readable by the workgroup.
+template <int NR>
+__device__ void fp4_rescore_row(const IndexArgs& a, int row, int V, Fp4QueryLds& ql, float* srow) {
+  const int b = row / a.tq, t_q = row % a.tq;
+  const int t = threadIdx.x, l = t % kWave, w = t / kWave, nw = blockDim.x / kWave;
+  if (t < 256) {
+    float2 qx[Fp4Pairs<NR>::n];
+    fp4_query_load(a, b, t_q, t, qx);
+    fp4_query_quantize(a, t, qx, ql);
+    if (t < a.heads) ql.w[t] = a.w[(int64_t)row * a.heads + t];
+  }
+  __syncthreads();
+  v8i A;
+  int sa;
+  float wv[NR];
+  fp4_query_operand<NR>(ql, a.heads, l, &A, &sa, wv);
+  const Fp4Lane<NR> ln(l);
+  const int ntile = (V + 31) / 32;
+  for (int tile = w; tile < ntile; tile += nw) {
+    const int key = 32 * tile + ln.m;
+    const bool live = key < V;
+    const int64_t kk = live ? key : 0;
+    const v4i c = live ? *(const v4i*)((const uint8_t*)a.k.data + (int64_t)b * a.k.sb + kk * a.k.sr + 16 * ln.kb)
+                       : (v4i){0, 0, 0, 0};
+    const int sbk = live ? ((const uint8_t*)a.k.scale)[(int64_t)b * a.k.ssb + kk * a.k.ssr + ln.kb] : 127;
+    const float s = fp4_tile_score<NR>(A, sa, wv, c, sbk);
+    if (ln.kb == 0 && live) srow[key] = s;
+  }
+  __threadfence();
+  __syncthreads();
+}
+
+}  // namespace
+}  // namespace csa

@@ -70,27 +70,34 @@ size_t topk_workspace_bytes(int64_t rows, int n_cap, int k);
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int tq, int n_cap, int m, int k,
                        int32_t* idx, void* ws, hipStream_t s);
 
-// A slice's exact top-C candidates, as written by a candidate pass: up to C
-// (order-preserving score key, block index) pairs in ascending index order, and:
+// A slice's candidate list, as written by a candidate pass: up to C (order-preserving
+// score key, block index) pairs in ascending index order, empty slots (0, 0) after
+// them, and:
 struct SliceMeta {
   uint32_t count;     // candidates written
-  uint32_t trunc;     // 1 when the slice held more than C visible keys
-  uint32_t last_key;  // C-th kept element in (key desc, index asc) order (when trunc)
-  uint32_t last_idx;
+  uint32_t trunc;     // 1 when some visible key of the slice was left out
+  uint32_t last_key;  // every key left out ranks strictly after (last_key, last_idx)
+  uint32_t last_idx;  //   in (key desc, index asc) order (when trunc)
 };
 struct CandOut {
   int C, slice, nslices;  // candidates per slice, keys per slice, slices per row
   uint2* cand;            // [rows][nslices][C]
   SliceMeta* meta;        // [rows][nslices]
   int k;                  // rows with at most k visible keys need no candidates
+  float* row_scores;      // [rows][n_cap] where short rows' scores go when the caller keeps none
 };
 
 // Fused (b)+(c) for MXFP4 keys on long rows: the indexer's workgroups also emit
-// their slice's top-32 candidates, and one merge pass selects the top-k.
+// their 1024-key slice's candidate list, and one merge pass selects the top-k.
 constexpr int kFusedSlice = 1024;  // keys per indexer workgroup
-constexpr int kFusedC = 32;
+constexpr int kFusedC = 24;        // list slots per slice (the slice's exact top-24)
 bool index_topk_fused_ok(const IndexArgs& a, int k);
-size_t index_topk_workspace_bytes(int64_t rows, int n_cap, int k);
+// Rows whose full slices alone cannot hold more than k candidates (each full slice
+// lists kFusedC keys) are selected from their scores: the indexer writes them.
+__host__ __device__ inline bool index_topk_short_row(int visible, int k) { return kFusedC * (visible / kFusedSlice) <= k; }
+size_t index_topk_workspace_bytes(int64_t rows, int n_cap, int k, bool scores_in_ws);
+// Where the score rows start in that workspace (when the caller keeps none).
+size_t index_topk_score_offset(int64_t rows, int n_cap, int k);
 // A decode step's compressions, run by the indexer launch (index.hip): the KV
 // compression on extra workgroups, and the indexer-key compression by the waves
 // whose keys include a block just completed (they compress it, store it and score
@@ -107,7 +114,6 @@ struct FusedCompress {
 };
 hipError_t launch_index_scores_cand(const IndexArgs& a, const CandOut& c, hipStream_t s,
                                     const FusedCompress* fc = nullptr);  // index.hip
-hipError_t launch_index_topk(const IndexArgs& a, int k, int32_t* idx, void* ws, hipStream_t s);
 // the two kernels of launch_index_topk, one launch each
 hipError_t launch_index_topk_cand(const IndexArgs& a, int k, void* ws, hipStream_t s,
                                   const FusedCompress* fc = nullptr);

@@ -5,6 +5,7 @@
 // independent of scheduling.
 #pragma once
 #include "common.h"
+#include "kernels.h"
 
 namespace csa {
 namespace {
@@ -268,241 +269,178 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
-constexpr int kWaveTopC = 32;  // candidates a one-wave selection keeps
-constexpr int kWaveTopN = 16;  // keys per lane: 1024 per wave
-constexpr int kWaveTopPre = 4;  // keys per lane after the pre-filter: at most 256 survive it
-
-// Wave-private LDS of one selection.  Every array has one extra slot per lane past
-// its end: a lane whose store is not wanted writes there instead, so stores need no
-// branch around them (a branch per key costs far more than the store).
-struct WaveSelLds {
-  __attribute__((aligned(16))) uint32_t hist[256 + kWave];
-  __attribute__((aligned(16))) uint32_t fk[64 + kWave];
-  __attribute__((aligned(16))) uint32_t fp[64 + kWave];
-  __attribute__((aligned(16))) uint2 pre[kWave * kWaveTopPre + kWave];  // (key, position) of pre-filter survivors
-  __attribute__((aligned(16))) uint2 res[kWaveTopC + kWave];            // the kept (key, position), by rank
-};
+constexpr int kWaveTopN = 16;  // keys per lane of a one-wave slice selection: 1024 per wave
 
 // The float a key came from (inverse of float_key).
 __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
-// The bin of the 32nd key in one histogram pass: hist holds 256 counts (lane L owns
-// bins 4L .. 4L+3); returns the bin, and the keys above it and in it.
-__device__ __forceinline__ void wave_find_bin(const WaveSelLds& sl, uint32_t krem, uint32_t* bin, uint32_t* above,
-                                              uint32_t* cnt) {
-  const int L = threadIdx.x % kWave;
-  const uint4 h4 = *(const uint4*)&sl.hist[4 * L];
-  const uint32_t hh[4] = {h4.x, h4.y, h4.z, h4.w};
-  const uint32_t incl = wave_incl_scan(hh[0] + hh[1] + hh[2] + hh[3]);
-  uint32_t run = __builtin_amdgcn_readlane(incl, kWave - 1) - incl;  // keys in the bins of lanes > L
-  int fd = -1;
-  uint32_t ab = 0, cn = 0;
-#pragma unroll
-  for (int d = 3; d >= 0; --d) {
-    const bool f = fd < 0 && run < krem && run + hh[d] >= krem;
-    fd = f ? d : fd;
-    ab = f ? run : ab;
-    cn = f ? hh[d] : cn;
-    run += hh[d];
-  }
-  const uint64_t fm = __builtin_amdgcn_ballot_w64(fd >= 0);  // exactly one lane
-  const int fl = __builtin_ctzll(fm);
-  *bin = __builtin_amdgcn_readlane(4 * L + fd, fl);
-  *above = __builtin_amdgcn_readlane(ab, fl);
-  *cnt = __builtin_amdgcn_readlane(cn, fl);
-}
+// ------------------------------------------------------------------ slice candidate lists
+// A slice of 1024 consecutive keys (one wave, lane L holding positions 16L .. 16L+15)
+// hands the row's top-k merge its exact top-kSliceSlots in (key desc, position asc)
+// order, listed in position order.  They are found cheaply: a cut keeps every key >=
+// tau, tau being the 32nd largest of the 64 lane maxima (so the top 32 all pass, and
+// typically about 45 keys do), and the survivors are ranked among themselves.  When
+// more than kCutMax keys pass the cut (many equal scores), the top-kSliceSlots are
+// found by a bit-by-bit threshold instead.  Every key left out ranks after the list's
+// last element, so a row's merge is exact unless that element is selected -- which
+// needs kSliceSlots of the row's top-k in one slice.
+constexpr int kSliceKeys = kWaveTopN * kWave;  // 1024
+constexpr int kSliceSlots = 24;
+constexpr int kCutMax = kWave;  // survivors of the cut ranked in one pass (one per lane)
 
-// Exact top-32, in (key desc, position asc) order, of the keys one wave holds with
-// no workgroup barrier: lane L holds kv[j] in slot NK*L + j, slot order being
-// ascending position order, and pos(j) is that key's position; absent slots hold
-// 0, every present key is > 0, more than 32 are present and all lie in [lo, hi].
-// A histogram select through wave-private LDS: a first pass of 256 bins linear in
-// the score over [lo, hi], then radix passes in key space over the bin of the 32nd
-// key while it holds more than 64 keys.  When that bin is taken whole, or holds a
-// single key value, the threshold is known at once; otherwise its keys are ranked
-// exactly.  The kept (key, position) pairs land in sl.res[0..31] in ascending
-// position order.  Returns the 32nd kept key and the position of its last kept copy.
-template <int NK, typename PosFn>
-__device__ void wave_top32_core(const uint32_t (&kv)[NK], PosFn pos, uint32_t lo, uint32_t hi, WaveSelLds& sl,
-                                uint32_t* T_out, uint32_t* tpos_out) {
+struct CutLds {
+  __attribute__((aligned(16))) uint32_t lmax[kWave];
+  __attribute__((aligned(16))) uint2 res[kCutMax + kWave];  // (key, position) staged; then discard slots
+};
+
+// Slice list format: kSliceSlots (key, index) pairs in ascending index order, empty
+// slots (0, 0) after them; metadata {count, trunc, last_key, last_idx} where trunc
+// says some visible key of the slice was left out, and every key left out ranks
+// strictly after (last_key, last_idx) in (key desc, index asc) order.
+
+// Exact top-C (C <= kSliceSlots, more than C keys present) of the keys one wave holds,
+// in (key desc, position asc) order, staged in position order in cl.res[0..C-1];
+// returns the C-th kept key and the position of its last kept copy.  The threshold is
+// built bit by bit (the largest value with at least C keys at or above it), which
+// needs only a few registers: the path for slices whose keys tie at the cut.
+__device__ void wave_topc_exact(const uint32_t (&kv)[kWaveTopN], uint32_t C, CutLds& cl, uint32_t* T_out,
+                                uint32_t* tpos_out) {
   const int L = threadIdx.x % kWave;
-  uint32_t krem = kWaveTopC;  // keys still to take from [lo, hi]
-  uint32_t cn = 0xffffffffu;  // keys in [lo, hi] (unknown before a pass)
-  const float xlo = key_float(lo), xhi = key_float(hi);
-  const float inv = 255.99f / (xhi - xlo);
-  // NaN and infinite scores, or a span too small to invert, go to the key-space passes
-  if (lo != hi && xhi - xlo < __builtin_inff() && inv < __builtin_inff()) {
-    // First pass in value space: 256 bins linear in the score over [lo, hi].  Any
-    // non-decreasing map of the keys gives bins that are contiguous ranges of the key
-    // order, so the selection stays exact; linear bins spread scores far better than
-    // key bits (which bucket by float exponent), so the bin of the 32nd key is small
-    // and usually settles the threshold in one pass.
-    int bin[NK];
-    *(uint4*)&sl.hist[4 * L] = make_uint4(0u, 0u, 0u, 0u);  // LDS ops of one wave run in order
-#pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const float b = (key_float(kv[j]) - xlo) * inv;
-      bin[j] = kv[j] ? min(255, max(0, (int)b)) : -1;
-      atomicAdd(&sl.hist[bin[j] >= 0 ? bin[j] : 256 + L], 1u);
-    }
-    uint32_t fbin, ab;
-    wave_find_bin(sl, krem, &fbin, &ab, &cn);
-    krem -= ab;
-    // the key range of that bin
-    uint32_t bmx = 0u, bmn = 0xffffffffu;
-#pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const bool in = bin[j] == (int)fbin;
-      bmx = in ? max(bmx, kv[j]) : bmx;
-      bmn = in ? min(bmn, kv[j]) : bmn;
-    }
-    lo = wave_reduce_u32<false>(bmn);
-    hi = wave_reduce_u32<true>(bmx);
-  }
-  // further passes in key space over [lo, hi] while its keys are more than 64
-  for (int pass = 0; pass < 4 && cn > 64u && cn != krem && lo != hi; ++pass) {
-    const uint32_t span = hi - lo;
-    const int bits = 32 - __builtin_clz(span);
-    const int shift = bits > 8 ? bits - 8 : 0;
-    *(uint4*)&sl.hist[4 * L] = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const bool in = kv[j] >= lo && kv[j] <= hi;
-      atomicAdd(&sl.hist[in ? (kv[j] - lo) >> shift : 256u + L], 1u);
-    }
-    uint32_t bin, ab;
-    wave_find_bin(sl, krem, &bin, &ab, &cn);
-    const uint32_t nlo = lo + (bin << shift);
-    hi = min(hi, nlo + ((1u << shift) - 1u));
-    lo = nlo;
-    krem -= ab;
-  }
-  // The threshold T and the copies of it to take: every key of [lo, hi] when the
-  // range is taken whole (T = its smallest key), krem copies of a single-valued range,
-  // else rank the <= 64 keys of the range exactly.
-  uint32_t T = lo;
-  const bool all_t = cn == krem;  // take every copy of T
-  if (all_t) {
-    uint32_t bmn = 0xffffffffu;
-#pragma unroll
-    for (int j = 0; j < NK; ++j) bmn = kv[j] >= lo && kv[j] <= hi ? min(bmn, kv[j]) : bmn;
-    T = wave_reduce_u32<false>(bmn);
-  } else if (lo != hi) {
-    // gather the <= 64 keys of [lo, hi] with their positions, then rank them exactly
+  uint32_t T = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
     uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < NK; ++j) c += kv[j] >= lo && kv[j] <= hi;
-    uint32_t o = wave_incl_scan(c) - c;
-    const uint32_t nfin = __builtin_amdgcn_readlane(o + c, kWave - 1);
-#pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const bool in = kv[j] >= lo && kv[j] <= hi;
-      const uint32_t at = in ? o : 64u + L;
-      sl.fk[at] = kv[j];
-      sl.fp[at] = pos(j);
-      o += in;
-    }
-    // pad to whole quads with entries that never rank above
-    const uint32_t at = (uint32_t)L >= nfin ? (uint32_t)L : 64u + L;
-    sl.fk[at] = 0u;
-    sl.fp[at] = 0xffffffffu;
-    const uint32_t myk = sl.fk[L], myp = sl.fp[L];  // entry L (a pad when L >= nfin)
-    uint32_t rank = 0, gt = 0;
-    for (uint32_t i = 0; i < nfin; i += 4) {  // broadcast reads, four entries at a time
-      const uint4 k4 = *(const uint4*)&sl.fk[i], p4 = *(const uint4*)&sl.fp[i];
-      const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w}, pp[4] = {p4.x, p4.y, p4.z, p4.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {  // bitwise, not short-circuit: no branch around the loads
-        rank += (uint32_t)(kk[q] > myk) | ((uint32_t)(kk[q] == myk) & (uint32_t)(pp[q] < myp));
-        gt += kk[q] > myk;
-      }
-    }
-    const bool hit = (uint32_t)L < nfin && rank == krem - 1u;
-    const uint64_t hm = __builtin_amdgcn_ballot_w64(hit);
-    const int hl = __builtin_ctzll(hm);
-    T = __builtin_amdgcn_readlane(myk, hl);
-    krem -= __builtin_amdgcn_readlane(gt, hl);  // copies of T still to take
+    for (int j = 0; j < kWaveTopN; ++j) c += kv[j] >= cand;
+    T = __builtin_amdgcn_readlane(wave_incl_scan(c), kWave - 1) >= C ? cand : T;
   }
-  // compaction in slot order (lane-major): keys > T and the first krem copies of T
   uint32_t gtc = 0, eqc = 0;
 #pragma unroll
-  for (int j = 0; j < NK; ++j) {
+  for (int j = 0; j < kWaveTopN; ++j) {
     gtc += kv[j] > T;
     eqc += kv[j] == T;
   }
-  const uint32_t eq_incl = wave_incl_scan(eqc);
-  const uint32_t eq_before = eq_incl - eqc;  // copies of T in lanes below
-  if (all_t) krem = __builtin_amdgcn_readlane(eq_incl, kWave - 1);
+  const uint32_t krem = C - __builtin_amdgcn_readlane(wave_incl_scan(gtc), kWave - 1);  // copies of T taken
+  const uint32_t eq_before = wave_incl_scan(eqc) - eqc;                                 // copies in lanes below
   const uint32_t take = eq_before >= krem ? 0u : min(eqc, krem - eq_before);
   const uint32_t selc = gtc + take;
   uint32_t r = wave_incl_scan(selc) - selc;
   uint32_t seen = 0, tpos = 0;
   bool has_t = false;
 #pragma unroll
-  for (int j = 0; j < NK; ++j) {
+  for (int j = 0; j < kWaveTopN; ++j) {
     const bool is_eq = kv[j] == T;
     const bool keep = kv[j] > T || (is_eq && seen < take);
     const bool last = is_eq && seen < take && eq_before + seen == krem - 1u;
-    tpos = last ? pos(j) : tpos;
+    tpos = last ? (uint32_t)(kWaveTopN * L + j) : tpos;
     has_t = has_t || last;
     seen += is_eq;
-    sl.res[keep ? r : (uint32_t)kWaveTopC + L] = make_uint2(kv[j], pos(j));
+    cl.res[keep ? r : (uint32_t)kCutMax + L] = make_uint2(kv[j], (uint32_t)(kWaveTopN * L + j));
     r += keep;
   }
-  const uint64_t tm = __builtin_amdgcn_ballot_w64(has_t);
-  *tpos_out = __builtin_amdgcn_readlane(tpos, __builtin_ctzll(tm));
+  *tpos_out = __builtin_amdgcn_readlane(tpos, __builtin_ctzll(__builtin_amdgcn_ballot_w64(has_t)));
   *T_out = T;
 }
 
-// Exact top-32, in (key desc, position asc) order, of the 1024 keys one wave holds:
-// lane L holds kv[j], the key of position 16L + j; absent positions hold 0, every
-// present key is > 0 and more than 32 are present.  The kept (key, position) pairs
-// land in sl.res[0..31] in ascending position order; returns the 32nd kept key and
-// the position of its last kept copy.
-// Pre-filter: each of the 32 lane pairs holds a key at least as large as the smallest
-// pair maximum tau, so at least as many keys as there are nonempty pairs are >= tau.
-// When more than 32 and at most 256 keys are >= tau, the top-32 lies among them:
-// they are compacted in position order (4 per lane) and only they are selected from.
-// Otherwise the selection runs on all 16 keys per lane.
-__device__ void wave_top32(const uint32_t (&kv)[kWaveTopN], WaveSelLds& sl, uint32_t* T_out, uint32_t* tpos_out) {
+// Rank of each lane's entry among the first `total` staged entries of cl.res in (key
+// desc, position asc) order, i.e. by the 64-bit value key << 32 | ~position (lanes >=
+// total get an entry that ranks last).  Broadcast reads eight at a time (a fixed
+// count, entries past `total` masked): a loop bounded by `total` would wait out one LDS
+// round trip per step.
+__device__ __forceinline__ uint32_t staged_rank(const CutLds& cl, uint32_t total, uint2* mine) {
   const int L = threadIdx.x % kWave;
-  uint32_t lmx = 0u, lmn = 0xffffffffu;
+  const uint2 me = (uint32_t)L < total ? cl.res[L] : make_uint2(0u, 0xffffffffu);
+  const uint64_t m64 = ((uint64_t)me.x << 32) | (uint32_t)~me.y;
+  constexpr int kBatch = 8;
+  uint32_t rank = 0;
 #pragma unroll
-  for (int j = 0; j < kWaveTopN; ++j) {
-    lmx = max(lmx, kv[j]);
-    lmn = kv[j] ? min(lmn, kv[j]) : lmn;
+  for (int i0 = 0; i0 < kCutMax / 2; i0 += kBatch) {
+    if (2 * i0 >= (int)total) break;  // wave-uniform
+    uint4 v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) v[i] = *(const uint4*)&cl.res[2 * (i0 + i)];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int e = 2 * (i0 + i);
+      const uint64_t a = ((uint64_t)v[i].x << 32) | (uint32_t)~v[i].y;
+      const uint64_t b = ((uint64_t)v[i].z << 32) | (uint32_t)~v[i].w;
+      rank += (uint32_t)(a > m64 && e < (int)total) + (uint32_t)(b > m64 && e + 1 < (int)total);
+    }
   }
-  // quad_perm [1,0,3,2]: the other lane of the pair
-  const uint32_t pm = max(lmx, (uint32_t)__builtin_amdgcn_update_dpp((int)lmx, (int)lmx, 0xB1, 0xF, 0xF, false));
-  const uint32_t tau = wave_reduce_u32<false>(pm ? pm : 0xffffffffu);
-  const uint32_t hi = wave_reduce_u32<true>(lmx);
+  *mine = me;
+  return rank;
+}
+
+// Writes the list of the n <= 1024 keys one wave holds (absent positions hold key 0,
+// present keys are > 0) for the slice whose position 0 is index `start`.
+__device__ void emit_slice_list(const uint32_t (&kv)[kWaveTopN], int n, uint32_t start, CutLds& cl, uint2* out,
+                                SliceMeta* mt) {
+  const int L = threadIdx.x % kWave;
+  if (n <= kSliceSlots) {  // every key of the slice
+#pragma unroll
+    for (int j = 0; j < kWaveTopN; ++j) {
+      const int p = kWaveTopN * L + j;
+      if (p < kSliceSlots) out[p] = p < n ? make_uint2(kv[j], start + (uint32_t)p) : make_uint2(0u, 0u);
+    }
+    if (L == 0) *mt = SliceMeta{(uint32_t)n, 0u, 0u, 0u};
+    return;
+  }
+  // tau: the 32nd largest lane maximum, with its 6 low bits cleared.  The maxima are
+  // made distinct by putting 63 - lane in those bits (so a rank is one compare per
+  // maximum); clearing them again keeps every lane at or above the 32nd maximum
+  // passing the cut, so at least 32 keys do.
+  uint32_t lmx = 0u;
+#pragma unroll
+  for (int j = 0; j < kWaveTopN; ++j) lmx = max(lmx, kv[j]);
+  const uint32_t lmu = (lmx & ~63u) | (uint32_t)(63 - L);
+  cl.lmax[L] = lmu;  // LDS ops of one wave run in order
+  uint32_t lrank = 0;
+#pragma unroll
+  for (int i = 0; i < kWave; i += 4) {
+    const uint4 v = *(const uint4*)&cl.lmax[i];  // broadcast reads
+    lrank += (uint32_t)(v.x > lmu) + (uint32_t)(v.y > lmu) + (uint32_t)(v.z > lmu) + (uint32_t)(v.w > lmu);
+  }
+  const uint32_t tau =
+      __builtin_amdgcn_readlane(lmu, __builtin_ctzll(__builtin_amdgcn_ballot_w64(lrank == 31u))) & ~63u;
   uint32_t c = 0;
 #pragma unroll
-  for (int j = 0; j < kWaveTopN; ++j) c += kv[j] >= tau;
+  for (int j = 0; j < kWaveTopN; ++j) c += kv[j] != 0u && kv[j] >= tau;
   const uint32_t incl = wave_incl_scan(c);
   const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
-  if (total > (uint32_t)kWaveTopC && total <= (uint32_t)(kWave * kWaveTopPre)) {
-    // empty slots first, then the survivors over them (LDS ops of one wave run in order)
-    *(uint4*)&sl.pre[kWaveTopPre * L] = make_uint4(0u, 0u, 0u, 0u);
-    *(uint4*)&sl.pre[kWaveTopPre * L + 2] = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t lk, li;
+  uint2 e;
+  bool keep;
+  uint32_t slot;
+  if (total <= (uint32_t)kCutMax) {
+    // stage the survivors in position order, rank them, keep the top kSliceSlots
     uint32_t o = incl - c;
 #pragma unroll
     for (int j = 0; j < kWaveTopN; ++j) {
-      const bool in = kv[j] >= tau;
-      sl.pre[in ? o : (uint32_t)(kWave * kWaveTopPre + L)] = make_uint2(kv[j], (uint32_t)(kWaveTopN * L + j));
+      const bool in = kv[j] != 0u && kv[j] >= tau;
+      cl.res[in ? o : (uint32_t)kCutMax + L] = make_uint2(kv[j], (uint32_t)(kWaveTopN * L + j));
       o += in;
     }
-    const uint4 a4 = *(const uint4*)&sl.pre[kWaveTopPre * L], b4 = *(const uint4*)&sl.pre[kWaveTopPre * L + 2];
-    const uint32_t k4[kWaveTopPre] = {a4.x, a4.z, b4.x, b4.z}, p4[kWaveTopPre] = {a4.y, a4.w, b4.y, b4.w};
-    wave_top32_core<kWaveTopPre>(k4, [&](int j) { return p4[j]; }, tau, hi, sl, T_out, tpos_out);
-  } else {
-    const uint32_t lo = wave_reduce_u32<false>(lmn);
-    wave_top32_core<kWaveTopN>(kv, [&](int j) { return (uint32_t)(kWaveTopN * L + j); }, lo, hi, sl, T_out, tpos_out);
+    const uint32_t rank = staged_rank(cl, total, &e);
+    keep = (uint32_t)L < total && rank < (uint32_t)kSliceSlots;
+    const uint64_t km = __builtin_amdgcn_ballot_w64(keep);
+    slot = (uint32_t)__builtin_popcountll(km & ((1ull << L) - 1ull));  // position order among the kept
+    const int ll = __builtin_ctzll(__builtin_amdgcn_ballot_w64((uint32_t)L < total && rank == kSliceSlots - 1u));
+    lk = __builtin_amdgcn_readlane(e.x, ll);
+    li = start + __builtin_amdgcn_readlane(e.y, ll);
+  } else {  // many keys at or above tau: the top kSliceSlots by a bit-by-bit threshold
+    uint32_t T, tpos;
+    wave_topc_exact(kv, (uint32_t)kSliceSlots, cl, &T, &tpos);
+    keep = L < kSliceSlots;
+    slot = (uint32_t)L;
+    e = cl.res[L % kSliceSlots];
+    lk = T;
+    li = start + tpos;
   }
+  if (keep) out[slot] = make_uint2(e.x, start + e.y);
+  if (L == 0) *mt = SliceMeta{(uint32_t)kSliceSlots, 1u, lk, li};
 }
-
 
 // ------------------------------------------------------------------ block top-k, keys in registers
 constexpr int kRegSelThreads = 1024;  // block size of the register-resident selection

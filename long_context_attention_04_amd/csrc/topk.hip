@@ -26,6 +26,7 @@
 //    be selected); otherwise the workgroup selects from the whole row itself.
 #include "common.h"
 #include "kernels.h"
+#include "index_fp4.h"
 #include "select.h"
 
 #include <algorithm>
@@ -87,7 +88,8 @@ __global__ __launch_bounds__(kLdsThreads) void topk_lds_kernel(const float* __re
 constexpr int kSlice = kTopkSlice;  // keys per candidate workgroup
 constexpr int kCandThreads = 256;
 constexpr int kMergeThreads = 1024;
-constexpr int kMergeCap = 8192;     // candidates a merge workgroup holds in LDS
+constexpr int kMergeCap = 8192;     // candidates a merge workgroup holds in LDS (4096-key slices)
+constexpr int kSliceMergeCap = 6144;  // list slots the 1024-slice merge holds (256 slices of 24)
 
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -216,16 +218,16 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float* 
   }
 }
 
-// Pass 1, one wave per 1024-key slice: the slice's exact top-32 by a one-wave
-// radix select (no workgroup barrier), written in ascending index order.
-constexpr int kSlice32 = kWaveTopN * kWave;  // 1024
-static_assert(kSlice32 == kFusedSlice && kWaveTopC == kFusedC, "one candidate format for both passes");
+// Pass 1 of the 1024-slice scheme, one wave per slice: the slice's candidate list
+// (emit_slice_list), from the scores in memory.
+constexpr int kSlice32 = kSliceKeys;  // 1024
+static_assert(kSlice32 == kFusedSlice && kSliceSlots == kFusedC, "one candidate format for both passes");
 
 __global__ __launch_bounds__(256) void topk_cand32_kernel(const float* __restrict__ scores,
                                                           const int32_t* __restrict__ q_pos, int n_cap, int m, int k,
                                                           int nslices, uint2* __restrict__ cand,
                                                           SliceMeta* __restrict__ meta) {
-  __shared__ WaveSelLds sl[4];
+  __shared__ CutLds cl[4];
   const int64_t row = blockIdx.y;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), L = threadIdx.x % kWave;
   const int g = blockIdx.x * 4 + w;
@@ -233,8 +235,6 @@ __global__ __launch_bounds__(256) void topk_cand32_kernel(const float* __restric
   if (V <= k || g >= nslices) return;  // V <= k: the merge writes every visible index
   const int start = g * kSlice32;
   const int n = max(0, min(kSlice32, V - start));
-  SliceMeta* mt = meta + row * nslices + g;
-  uint2* out = cand + (row * nslices + g) * kWaveTopC;
   // lane L: positions 16L .. 16L+15 (64 contiguous bytes)
   const float* src = scores + row * n_cap + start + kWaveTopN * L;
   uint32_t kv[kWaveTopN];
@@ -252,124 +252,129 @@ __global__ __launch_bounds__(256) void topk_cand32_kernel(const float* __restric
 #pragma unroll
     for (int j = 0; j < kWaveTopN; ++j) kv[j] = kWaveTopN * L + j < n ? float_key(src[j]) : 0u;
   }
-  if (n <= kWaveTopC) {  // every slot of the slice's list: its n keys, then empty (key 0) slots
-#pragma unroll
-    for (int j = 0; j < kWaveTopN; ++j) {
-      const int p = kWaveTopN * L + j;
-      if (p < kWaveTopC) out[p] = p < n ? make_uint2(kv[j], (uint32_t)(start + p)) : make_uint2(0u, 0u);
-    }
-    if (L == 0) *mt = SliceMeta{(uint32_t)n, 0u, 0u, 0u};
-    return;
-  }
-  uint32_t T, tpos;
-  wave_top32(kv, sl[w], &T, &tpos);
-  if (L < kWaveTopC) {  // one coalesced store of the list
-    const uint2 e = sl[w].res[L];
-    out[L] = make_uint2(e.x, (uint32_t)start + e.y);
-  }
-  if (L == 0) *mt = SliceMeta{(uint32_t)kWaveTopC, 1u, T, (uint32_t)start + tpos};
+  emit_slice_list(kv, n, (uint32_t)start, cl[w], cand + (row * nslices + g) * kSliceSlots,
+                  meta + row * nslices + g);
 }
 
 // Pass 2 of the 1024-slice scheme, one 1024-thread workgroup per row: slice s's
-// list fills slots 32s .. 32s+31 (empty slots hold key 0), so slot order is
-// ascending index order and thread t holds slots 8t .. 8t+7 in registers.  The
-// threshold is found on the registers, the compaction is one block scan, and
-// the exactness certificate is the same as above.
-constexpr int kM32PerThread = kMergeCap / kRegSelThreads;  // 8
-static_assert(kM32PerThread * kRegSelThreads == kMergeCap && kWaveTopC % kM32PerThread == 0, "slot tiling");
+// list fills slots 24s .. 24s+23 (empty slots hold key 0), so slot order is
+// ascending index order and thread t holds slots 6t .. 6t+5 in registers.  The
+// threshold is found on the registers, the compaction is one block scan, and the
+// result is certified exact: every key a slice left out ranks after that slice's
+// (last_key, last_idx), so the selection is exact unless such a pair is selected.
+// Otherwise -- and for rows whose full slices hold too few candidates -- the whole
+// row is selected from its scores: `scores` when the caller kept them, else
+// `row_scores`, which the indexer filled for short rows and which this kernel fills
+// by rescoring (MXFP4 keys, fp4_rescore_row) when a certificate fails.
+constexpr int kMPerThread = kSliceMergeCap / kRegSelThreads;  // 6
+static_assert(kMPerThread * kRegSelThreads == kSliceMergeCap && kSliceSlots % kMPerThread == 0, "slot tiling");
 
-__global__ __launch_bounds__(kRegSelThreads) void topk_merge32_kernel(const float* __restrict__ scores,
-                                                                     const int32_t* __restrict__ q_pos, int n_cap,
-                                                                     int m, int k, int nslices,
-                                                                     const uint2* __restrict__ cand,
-                                                                     const SliceMeta* __restrict__ meta,
-                                                                     int32_t* __restrict__ idx) {
+struct MergeArgs {
+  const float* scores;    // the row scores, when the caller keeps them (else nullptr)
+  float* row_scores;      // otherwise: [rows][n_cap] scratch rows
+  const int32_t* q_pos;
+  int n_cap, m, k, nslices;
+  const uint2* cand;
+  const SliceMeta* meta;
+  int32_t* idx;
+  int short_rows;         // 1: rows that index_topk_short_row names have their scores in row_scores
+  IndexArgs rescore;      // MXFP4 keys to rescore from (rescore.k.data == nullptr: never needed)
+};
+
+template <int NR>  // 0: no rescoring; 4 / 16: the indexer's MFMA layout (heads <= 8 / <= 32)
+__global__ __launch_bounds__(kRegSelThreads) void topk_merge_slices_kernel(MergeArgs ma) {
   __shared__ RegSelLds rs;
   __shared__ SelShared sh;
-  __shared__ uint32_t ostage[kMergeCap + kRegSelThreads];  // selected indices by rank, then discard slots
+  __shared__ __attribute__((aligned(16))) uint32_t ostage[kSliceMergeCap + kRegSelThreads];  // selected indices by rank, then discard slots
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
+  const int nslices = ma.nslices, k = ma.k;
   // The candidate lists and the slices' metadata are loaded together with the row's
-  // position (their addresses do not depend on it: one memory round trip); the slots
-  // of slices past the visible ones are cleared once it is known.
-  const int qpos = q_pos[row];
+  // position (their addresses do not depend on it: one memory round trip).
+  const int qpos = ma.q_pos[row];
   SliceMeta mm{0u, 0u, 0u, 0u};
-  if (t < nslices) mm = meta[row * nslices + t];
-  uint32_t kv[kM32PerThread], iv[kM32PerThread];
-  if (kM32PerThread * t < nslices * kWaveTopC) {
-    const uint4* src = (const uint4*)(cand + row * nslices * kWaveTopC) + (kM32PerThread / 2) * t;
+  if (t < nslices) mm = ma.meta[row * nslices + t];
+  uint32_t kv[kMPerThread], iv[kMPerThread];
+  if (kMPerThread * t < nslices * kSliceSlots) {
+    const uint4* src = (const uint4*)(ma.cand + row * nslices * kSliceSlots) + (kMPerThread / 2) * t;
+    uint4 v[kMPerThread / 2];
 #pragma unroll
-    for (int q = 0; q < kM32PerThread / 2; ++q) {
-      const uint4 v = src[q];
-      kv[2 * q] = v.x;
-      iv[2 * q] = v.y;
-      kv[2 * q + 1] = v.z;
-      iv[2 * q + 1] = v.w;
+    for (int q = 0; q < kMPerThread / 2; ++q) v[q] = src[q];
+#pragma unroll
+    for (int q = 0; q < kMPerThread / 2; ++q) {
+      kv[2 * q] = v[q].x;
+      iv[2 * q] = v[q].y;
+      kv[2 * q + 1] = v[q].z;
+      iv[2 * q + 1] = v[q].w;
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < kM32PerThread; ++j) kv[j] = iv[j] = 0u;
+    for (int j = 0; j < kMPerThread; ++j) kv[j] = iv[j] = 0u;
   }
-  const int V = min(visible_blocks(qpos, m), n_cap);
-  int32_t* out = idx + row * k;
+  const int V = min(visible_blocks(qpos, ma.m), ma.n_cap);
+  int32_t* out = ma.idx + row * k;
   if (V <= k) {
     for (int i = t; i < k; i += kRegSelThreads) out[i] = i < V ? i : -1;
     return;
   }
-  const int ns = (V + kSlice32 - 1) / kSlice32;  // slices holding visible keys
-  if (t >= ns) mm = SliceMeta{0u, 0u, 0u, 0u};
-  if (kM32PerThread * t >= ns * kWaveTopC) {
-#pragma unroll
-    for (int j = 0; j < kM32PerThread; ++j) kv[j] = iv[j] = 0u;
-  }
-  uint32_t lo, hi, M;
-  block_key_range(kv, rs, &lo, &hi, &M);
-  // A row that sees fewer blocks than the capacity has fewer slices: when its
-  // candidates are not more than k (and some slice was truncated, since V > k),
-  // they cannot decide the selection; the whole row does.
-  bool full = M <= (uint32_t)k;
+  const float* srow = ma.scores ? ma.scores + row * ma.n_cap : ma.row_scores + row * ma.n_cap;
+  bool full = ma.short_rows && index_topk_short_row(V, k);
   if (!full) {
-    uint32_t T, krem;
-    block_threshold_regs(kv, lo, hi, (uint32_t)k, rs, &T, &krem);
-    // compaction in slot order: one scan of (keys > T) | (copies of T) << 16
-    uint32_t gtc = 0, eqc = 0;
+    const int ns = (V + kSlice32 - 1) / kSlice32;  // slices holding visible keys
+    if (t >= ns) mm = SliceMeta{0u, 0u, 0u, 0u};
+    if (kMPerThread * t >= ns * kSliceSlots) {
 #pragma unroll
-    for (int j = 0; j < kM32PerThread; ++j) {
-      gtc += kv[j] > T;
-      eqc += kv[j] == T;
+      for (int j = 0; j < kMPerThread; ++j) kv[j] = iv[j] = 0u;
     }
-    const uint32_t packed = gtc | (eqc << 16);
-    uint32_t tot;
-    const uint32_t excl = block_scan_regsel(packed, rs.scan[2], &tot) - packed;
-    krem = min(krem, tot >> 16);  // "every copy" made a count
-    uint32_t eq_seen = excl >> 16;
-    uint32_t r = (excl & 0xffffu) + min(eq_seen, krem);
-    // the k indices go to LDS (rank order), unwanted stores to this thread's discard
-    // slot, then out in one coalesced pass
-    uint32_t my_jT = 0;
-    bool has_t = false;
+    uint32_t lo, hi, M;
+    block_key_range(kv, rs, &lo, &hi, &M);
+    full = M <= (uint32_t)k;  // too few candidates to decide (rows of a few slices)
+    if (!full) {
+      uint32_t T, krem;
+      block_threshold_regs(kv, lo, hi, (uint32_t)k, rs, &T, &krem);
+      // compaction in slot order: one scan of (keys > T) | (copies of T) << 16
+      uint32_t gtc = 0, eqc = 0;
 #pragma unroll
-    for (int j = 0; j < kM32PerThread; ++j) {
-      const bool is_eq = kv[j] == T;
-      const bool keep = kv[j] > T || (is_eq && eq_seen < krem);
-      const bool last = is_eq && eq_seen == krem - 1u;  // the last copy of T taken
-      my_jT = last ? iv[j] : my_jT;
-      has_t = has_t || last;
-      eq_seen += is_eq;
-      ostage[keep && r < (uint32_t)k ? r : (uint32_t)kMergeCap + t] = iv[j];
-      r += keep;
+      for (int j = 0; j < kMPerThread; ++j) {
+        gtc += kv[j] > T;
+        eqc += kv[j] == T;
+      }
+      const uint32_t packed = gtc | (eqc << 16);
+      uint32_t tot;
+      const uint32_t excl = block_scan_regsel(packed, rs.scan[2], &tot) - packed;
+      krem = min(krem, tot >> 16);  // "every copy" made a count
+      uint32_t eq_seen = excl >> 16;
+      uint32_t r = (excl & 0xffffu) + min(eq_seen, krem);
+      // the k indices go to LDS (rank order), unwanted stores to this thread's discard
+      // slot, then out in one coalesced pass
+      uint32_t my_jT = 0;
+      bool has_t = false;
+#pragma unroll
+      for (int j = 0; j < kMPerThread; ++j) {
+        const bool is_eq = kv[j] == T;
+        const bool keep = kv[j] > T || (is_eq && eq_seen < krem);
+        const bool last = is_eq && eq_seen == krem - 1u;  // the last copy of T taken
+        my_jT = last ? iv[j] : my_jT;
+        has_t = has_t || last;
+        eq_seen += is_eq;
+        ostage[keep && r < (uint32_t)k ? r : (uint32_t)kSliceMergeCap + t] = iv[j];
+        r += keep;
+      }
+      if (has_t) rs.jT = my_jT;
+      __syncthreads();
+      // exact unless some slice's (last_key, last_idx) is selected
+      const uint32_t jT = rs.jT;
+      if (t < ns && mm.trunc && (mm.last_key > T || (mm.last_key == T && mm.last_idx <= jT))) rs.bad = 1u;
+      __syncthreads();
+      full = rs.bad != 0u;
+      if (!full)
+        for (int i = t; i < k; i += kRegSelThreads) out[i] = (int32_t)ostage[i];
     }
-    if (has_t) rs.jT = my_jT;
-    __syncthreads();
-    for (int i = t; i < k; i += kRegSelThreads) out[i] = (int32_t)ostage[i];
-    // exact unless a truncated slice had its 32nd kept element selected
-    const uint32_t jT = rs.jT;
-    if (t < ns && mm.trunc && (mm.last_key > T || (mm.last_key == T && mm.last_idx <= jT))) rs.bad = 1u;
-    __syncthreads();
-    full = rs.bad != 0u;
+    if (full && !ma.scores) {  // the row's scores were not kept: recompute them
+      if constexpr (NR > 0) fp4_rescore_row<NR>(ma.rescore, (int)row, V, *(Fp4QueryLds*)ostage, ma.row_scores + row * ma.n_cap);
+    }
   }
   if (full) {  // select from the whole row (slow path; any input)
-    const float* srow = scores + row * n_cap;
     auto key = [&](int i) { return float_key(srow[i]); };
     uint32_t T, krem;
     radix_threshold(key, V, k, sh, &T, &krem);
@@ -396,7 +401,7 @@ size_t topk_workspace_bytes(int64_t rows, int n_cap, int k) {
   const int C = cand_per_slice(n_cap, k);
   const size_t wide = align256((size_t)rows * ns * sizeof(SliceMeta)) + align256((size_t)rows * ns * (C > 0 ? C : 1) * 8);
   const int ns32 = (n_cap + kSlice32 - 1) / kSlice32;
-  const size_t narrow = align256((size_t)rows * ns32 * sizeof(SliceMeta)) + align256((size_t)rows * ns32 * kWaveTopC * 8);
+  const size_t narrow = align256((size_t)rows * ns32 * sizeof(SliceMeta)) + align256((size_t)rows * ns32 * kSliceSlots * 8);
   return std::max(wide, narrow);
 }
 
@@ -412,13 +417,22 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int
   }
   {
     const int ns32 = (n_cap + kSlice32 - 1) / kSlice32;
-    if (ns32 <= kMergeThreads && ns32 * kWaveTopC <= kMergeCap && ns32 * kWaveTopC >= k) {
+    if (ns32 * kSliceSlots <= kSliceMergeCap && k <= kSliceMergeCap) {
       SliceMeta* meta = (SliceMeta*)ws;
       uint2* cand = (uint2*)((char*)ws + align256((size_t)rows * ns32 * sizeof(SliceMeta)));
       hipLaunchKernelGGL(topk_cand32_kernel, dim3((unsigned)((ns32 + 3) / 4), (unsigned)rows), dim3(256), 0, s, scores,
                          q_pos, n_cap, m, k, ns32, cand, meta);
-      hipLaunchKernelGGL(topk_merge32_kernel, dim3((unsigned)rows), dim3(kRegSelThreads), 0, s, scores, q_pos, n_cap,
-                         m, k, ns32, cand, meta, idx);
+      MergeArgs ma{};
+      ma.scores = scores;
+      ma.q_pos = q_pos;
+      ma.n_cap = n_cap;
+      ma.m = m;
+      ma.k = k;
+      ma.nslices = ns32;
+      ma.cand = cand;
+      ma.meta = meta;
+      ma.idx = idx;
+      hipLaunchKernelGGL(topk_merge_slices_kernel<0>, dim3((unsigned)rows), dim3(kRegSelThreads), 0, s, ma);
       return hipGetLastError();
     }
   }
@@ -437,20 +451,30 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int
 // ---------------------------------------------------------------- fused with the indexer
 namespace {
 __host__ inline int fused_slices(int n_cap) { return (n_cap + kFusedSlice - 1) / kFusedSlice; }
+__host__ inline size_t fused_lists_bytes(int64_t rows, int n_cap) {
+  const int ns = fused_slices(n_cap);
+  return align256((size_t)rows * ns * sizeof(SliceMeta)) + align256((size_t)rows * ns * kFusedC * 8);
+}
 }  // namespace
 
 bool index_topk_fused_ok(const IndexArgs& a, int k) {
-  // MXFP4 keys (the indexer that emits candidates), long rows, and a candidate set that
-  // fits the merge pass: nslices * 32 entries in LDS, one thread per slice for the scan
+  // MXFP4 keys (the indexer that emits lists), long rows, and lists that fit the merge
+  // pass (nslices * 64 slots in registers, one thread per slice for the certificate)
   const int ns = fused_slices(a.n_cap);
-  return a.k.dtype == CSA_MXFP4 && a.n_cap > kTopkLdsMax && ns <= kMergeThreads &&
-         (int64_t)ns * kFusedC <= kMergeCap && (int64_t)ns * kFusedC >= k;
+  return a.k.dtype == CSA_MXFP4 && a.n_cap > kTopkLdsMax && ns <= kRegSelThreads &&
+         (int64_t)ns * kFusedC <= kSliceMergeCap && k <= kSliceMergeCap;
 }
 
-size_t index_topk_workspace_bytes(int64_t rows, int n_cap, int k) {
-  if (n_cap <= kTopkLdsMax) return 0;
-  const int ns = fused_slices(n_cap);
-  return align256((size_t)rows * ns * sizeof(SliceMeta)) + align256((size_t)rows * ns * kFusedC * 8);
+// Workspace: the slice lists (and the top-k pass's own needs), then, when the caller
+// keeps no scores, one score row per query row.
+size_t index_topk_score_offset(int64_t rows, int n_cap, int k) {
+  return align256(std::max(topk_workspace_bytes(rows, n_cap, k),
+                           n_cap > kTopkLdsMax ? fused_lists_bytes(rows, n_cap) : (size_t)0));
+}
+
+size_t index_topk_workspace_bytes(int64_t rows, int n_cap, int k, bool scores_in_ws) {
+  const size_t lists = index_topk_score_offset(rows, n_cap, k);
+  return scores_in_ws ? lists + align256((size_t)rows * n_cap * sizeof(float)) : lists;
 }
 
 namespace {
@@ -464,6 +488,7 @@ CandOut fused_cand_out(const IndexArgs& a, int k, void* ws) {
   co.k = k;
   co.meta = (SliceMeta*)ws;
   co.cand = (uint2*)((char*)ws + align256((size_t)rows * ns * sizeof(SliceMeta)));
+  co.row_scores = (float*)((char*)ws + index_topk_score_offset(rows, a.n_cap, k));
   return co;
 }
 }  // namespace
@@ -477,15 +502,24 @@ hipError_t launch_index_topk_merge(const IndexArgs& a, int k, int32_t* idx, void
   const int64_t rows = (int64_t)a.batch * a.tq;
   if (rows == 0) return hipSuccess;
   const CandOut co = fused_cand_out(a, k, ws);
-  hipLaunchKernelGGL(topk_merge32_kernel, dim3((unsigned)rows), dim3(kRegSelThreads), 0, s, a.scores, a.q_pos,
-                     a.n_cap, a.m, k, co.nslices, co.cand, co.meta, idx);
+  MergeArgs ma{};
+  ma.scores = a.scores;
+  ma.row_scores = co.row_scores;
+  ma.q_pos = a.q_pos;
+  ma.n_cap = a.n_cap;
+  ma.m = a.m;
+  ma.k = k;
+  ma.nslices = co.nslices;
+  ma.cand = co.cand;
+  ma.meta = co.meta;
+  ma.idx = idx;
+  ma.short_rows = 1;
+  ma.rescore = a;
+  if (a.heads <= 8)
+    hipLaunchKernelGGL(topk_merge_slices_kernel<4>, dim3((unsigned)rows), dim3(kRegSelThreads), 0, s, ma);
+  else
+    hipLaunchKernelGGL(topk_merge_slices_kernel<16>, dim3((unsigned)rows), dim3(kRegSelThreads), 0, s, ma);
   return hipGetLastError();
-}
-
-hipError_t launch_index_topk(const IndexArgs& a, int k, int32_t* idx, void* ws, hipStream_t s) {
-  const hipError_t e = launch_index_topk_cand(a, k, ws, s);
-  if (e != hipSuccess) return e;
-  return launch_index_topk_merge(a, k, idx, ws, s);
 }
 
 }  // namespace csa

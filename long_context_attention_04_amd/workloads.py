@@ -151,7 +151,7 @@ class CsaLayer:
         self.lse = torch.empty((B, tq, self.H), dtype=torch.float32, device=DEV)
         n = csa_topk_workspace_size(B, tq, self.n_cap, self.k)
         self.ws_topk = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
-        n = csa_index_topk_workspace_size(B, tq, self.n_cap, self.k)
+        n = csa_index_topk_workspace_size(B, tq, self.n_cap, self.k, scores_kept=False)  # fits either use
         self.ws_itk = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
         n = csa_attn_workspace_size(B, tq, self.H, self.D, self.k + self.W)
         self.ws_attn = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
@@ -182,7 +182,7 @@ class CsaLayer:
         launch where the shapes allow."""
         csa_compress_index_topk(self.kv_job(), self.key_job(), self.q_idx.desc(), self.w, self.k_idx.desc(),
                                 self.q_pos, self.B, self.tq, self.HI, self.dI, self.m, self.n_cap, self.k,
-                                self.scores, self.idx, self.ws_itk, self.ws_itk.numel(), part, stream)
+                                self._scores(), self.idx, self.ws_itk, self.ws_itk.numel(), part, stream)
 
     def index(self, stream=None):
         csa_index_scores(self.q_idx.desc(), self.w, self.k_idx.desc(), self.q_pos, self.B, self.tq, self.HI, self.dI,
@@ -194,12 +194,12 @@ class CsaLayer:
 
     def index_topk(self, stream=None):
         csa_index_topk(self.q_idx.desc(), self.w, self.k_idx.desc(), self.q_pos, self.B, self.tq, self.HI, self.dI,
-                       self.m, self.n_cap, self.k, self.scores, self.idx, self.ws_itk, self.ws_itk.numel(), stream)
+                       self.m, self.n_cap, self.k, self._scores(), self.idx, self.ws_itk, self.ws_itk.numel(), stream)
 
     def index_topk_part(self, part, stream=None):
         """Part 1 (scores + slice candidates) or part 2 (selection) of index_topk."""
         csa_index_topk_part(self.q_idx.desc(), self.w, self.k_idx.desc(), self.q_pos, self.B, self.tq, self.HI,
-                            self.dI, self.m, self.n_cap, self.k, self.scores, self.idx, self.ws_itk,
+                            self.dI, self.m, self.n_cap, self.k, self._scores(), self.idx, self.ws_itk,
                             self.ws_itk.numel(), part, stream)
 
     def attend(self, stream=None):
@@ -210,6 +210,10 @@ class CsaLayer:
     stage_names = ("compress", "index+topk", "attention")
     fused_select = True  # score and select with csa_index_topk (else csa_index_scores, then csa_topk)
     fused_compress = True  # with fused_select: the compressions run inside the indexer launch
+    keep_scores = False  # with fused_select: also return every score (in self.scores)
+
+    def _scores(self):
+        return self.scores if self.keep_scores else None
 
     def select(self, stream=None):
         if self.fused_select:

@@ -149,6 +149,17 @@ def test_index_topk_rejects_and_workspace():
     expect(E_WS, call(wsb=need - 1))
     expect(E_WS, call(ws=None))
     expect(E_UNSUP, call(heads=33))
+    # without a score buffer the workspace also holds one score row per query row
+    need_ns = csa.csa_index_topk_workspace_size(8, 1, 262144, 2048, scores_kept=False)
+    assert need_ns >= need + 8 * 262144 * 4
+    assert csa.csa_index_topk_workspace_size(8, 1, 16896, 512, scores_kept=False) >= 8 * 16896 * 4
+    expect(E_WS, lambda stream: csa.csa_index_topk(q, P, k, P, 8, 1, 8, 64, 4, 262144, 2048, None, P, P, need,
+                                                   stream))
+    expect(E_WS, lambda stream: csa.csa_index_topk(q, P, k, P, 8, 1, 8, 64, 4, 262144, 2048, None, P, P,
+                                                   need_ns - 1, stream), match=str(need_ns))
+    # csa_index_scores has no selection: its scores are its result
+    expect(E_NULL, lambda stream: csa.csa_index_scores(q, P, k, P, 1, 1, 8, 64, 4, 1024, None, stream),
+           match="scores")
 
     def part(p, idx=P, wsb=need):
         return lambda stream: csa.csa_index_topk_part(q, P, k, P, 8, 1, 8, 64, 4, 262144, 2048, P, idx, P, wsb, p,

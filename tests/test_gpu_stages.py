@@ -114,9 +114,11 @@ def test_compress(gpu_lib, m, dim, in_dt, out_dt):
             assert row_rel_err(got, rows) < 1e-5
         elif out_dt == "bf16":
             got = down(out_t)[b, sl]
-            # one bf16 rounding of an fp32-accumulated value: within one bf16 ulp
-            # (absolute part: a merge cancelling to near zero keeps its terms' fp32 error)
-            assert np.all(np.abs(got - rows) <= np.abs(rows) * 2.0 ** -7 + 1e-6)
+            # one bf16 rounding of an fp32-accumulated value: within one bf16 ulp, plus the fp32
+            # merge's own error (weights and fma chain), at most (2m + 4) * 2^-24 * max_r |x_r|
+            r0 = j0 * m - raw_base[b]
+            xmax = np.abs(raw_v[b, r0:r0 + rows.shape[0] * m].reshape(rows.shape[0], m, dim)).max(axis=1)
+            assert np.all(np.abs(got - rows) <= np.abs(rows) * 2.0 ** -7 + (2 * m + 4) * 2.0 ** -24 * xmax)
         elif out_dt == "fp8":
             codes, sc = down(out_t)[b, sl], down(out_s)[b, sl]
             got = OF.dequantize_fp8_rows(codes, sc)
@@ -355,6 +357,16 @@ def test_index_topk_fused(gpu_lib, B, Tq, HI, N, k, mode):
     assert torch.equal(s3, s2)
     np.testing.assert_array_equal(down(i3), down(i2))
     np.testing.assert_array_equal(down(i2), oracle.topk(down(s2).astype(np.float64), pos, m, k))
+    # no scores kept: the same selection, in one call and in two parts (rows the lists cannot
+    # decide are selected from scores the call keeps in its workspace or recomputes there)
+    ws4 = workspace(csa.csa_index_topk_workspace_size(B, Tq, N, k, scores_kept=False))
+    for parts in ((3,), (1, 2)):
+        ws4.fill_(0xA5)  # contents on entry do not matter
+        i4 = torch.full((B, Tq, k), -7, dtype=torch.int32, device="cuda")
+        for part in parts:
+            csa.csa_index_topk_part(qd, wt, kd, pt, B, Tq, HI, dI, m, N, k, None, i4 if part & 2 else None, ws4,
+                                    ws4.numel(), part)
+        np.testing.assert_array_equal(down(i4), down(i2))
 
 
 # ----------------------------------------------------------------------------- attention
@@ -476,17 +488,23 @@ def test_attention_deterministic_and_batch_invariant(gpu_lib):
         assert np.array_equal(s[0][0], a[0][i]) and np.array_equal(s[1][0], a[1][i])
 
 
-@pytest.mark.parametrize("kv_fmt,ik_fmt,tq", [("bf16", "f32", 1), ("fp8", "bf16", 1), ("bf16", "f32", 2)])
-def test_compress_index_topk_matches_separate_calls(gpu_lib, kv_fmt, ik_fmt, tq):
+@pytest.mark.parametrize("kv_fmt,ik_fmt,tq,N,k,first", [
+    ("bf16", "f32", 1, 24000, 512, (1023, 5000, 7000)),       # short rows: selected from their scores
+    ("fp8", "bf16", 1, 24000, 512, (1023, 5000, 7000)),
+    ("bf16", "f32", 2, 24000, 512, (1023, 5000, 7000)),       # compressions in a launch of their own
+    ("bf16", "f32", 1, 131072, 1024, (1023, 90000, 131071)),  # long rows: slice lists and the merge
+])
+def test_compress_index_topk_matches_separate_calls(gpu_lib, kv_fmt, ik_fmt, tq, N, k, first):
     """csa_compress_index_topk == csa_compress_jobs then csa_index_topk_part, bit for bit: the
     stored KV entries and indexer keys, the scores and the selection -- with new blocks on a
     slice boundary, a sequence completing none, either part alone, and (tq=2) the shapes that
     run the compressions in a launch of their own."""
     csa = gpu_lib
-    B, N, HI, dI, D, m, k, R = 3, 24000, 8, 64, 512, 4, 512, 16
-    r = _rng(f"cit{kv_fmt}{ik_fmt}{tq}")
-    first = np.array([1023, 5000, 7000], np.int32)  # blocks 1023 and 1024 sit in two slices
+    B, HI, dI, D, m, R = 3, 8, 64, 512, 4, 16
+    r = _rng(f"cit{kv_fmt}{ik_fmt}{tq}{N}")
+    first = np.array(first, np.int32)  # blocks 1023 and 1024 sit in two slices
     count = np.array([2, 1, 0], np.int32)
+    count[-1] = 1 if first[-1] == N - 1 else 0  # the last block of the cache completed this step
     raw_base = (m * first - m).astype(np.int32)
     end = m * (first + count) - 1  # the token completing the last new block
     pos = np.stack([end - (tq - 1 - t) for t in range(tq)], axis=1).astype(np.int32)
@@ -525,7 +543,7 @@ def test_compress_index_topk_matches_separate_calls(gpu_lib, kv_fmt, ik_fmt, tq)
     def outputs():
         return (torch.full((B, tq, N), float("nan"), device="cuda"),
                 torch.full((B, tq, k), -7, dtype=torch.int32, device="cuda"),
-                workspace(csa.csa_index_topk_workspace_size(B, tq, N, k)))
+                workspace(csa.csa_index_topk_workspace_size(B, tq, N, k, scores_kept=False)))
 
     def bits(kc, ks, kv, sc, ix):
         kvb = kv[0].view(torch.uint8) if kv[0].dtype == torch.bfloat16 else kv[0]
@@ -547,6 +565,17 @@ def test_compress_index_topk_matches_separate_calls(gpu_lib, kv_fmt, ik_fmt, tq)
             csa.csa_compress_index_topk(kvj, kyj, csa.desc(q, csa.F32), w, csa.desc(kc, csa.MXFP4, ks), dpos, B, tq,
                                         HI, dI, m, N, k, sc, ix, ws, ws.numel(), part)
         got = bits(kc, ks, kv, sc, ix)
+        for a_, b_ in zip(want, got):
+            assert torch.equal(a_, b_)
+    # without scores: the same stored entries and selection
+    for parts in ((3,), (1, 2)):
+        kc, ks, kv = state()
+        _, ix, ws = outputs()
+        kvj, kyj = jobs(kc, ks, kv)
+        for part in parts:
+            csa.csa_compress_index_topk(kvj, kyj, csa.desc(q, csa.F32), w, csa.desc(kc, csa.MXFP4, ks), dpos, B, tq,
+                                        HI, dI, m, N, k, None, ix if part & 2 else None, ws, ws.numel(), part)
+        got = bits(kc, ks, kv, want[-2].view(torch.float32), ix)
         for a_, b_ in zip(want, got):
             assert torch.equal(a_, b_)
     # the new keys did change (the comparison is not of untouched tensors)
