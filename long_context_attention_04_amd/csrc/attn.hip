@@ -152,11 +152,22 @@ __device__ __forceinline__ v8bf widen8(Raw8<FP8> r) {
   }
 }
 
-// Workgroup -> (row, split, head group).  Consecutive workgroup ids go to
-// different XCDs (round robin over 8), so the nhg head groups of one
-// (row, split) get ids 8 apart: same XCD, same L2, run side by side, and the
-// entry rows the first one fetches from HBM are L2 hits for the others.
-__device__ __forceinline__ void decode_block(int id, int nhg, int nsplit_max, int* row, int* split, int* hg) {
+// Workgroup -> (row, split, head group).  Consecutive workgroup ids go round robin
+// over the 8 XCDs.  With at least 8 rows, every workgroup of row r runs on XCD r % 8:
+// the row's splits leave their partial results in that XCD's L2, where the split
+// merge (placed the same way) reads them, and the head groups of a split share its
+// entry rows there.  With fewer rows, the head groups of one (row, split) get ids 8
+// apart (same XCD, shared rows) and the (row, split) pairs spread over the XCDs.
+__device__ __forceinline__ void decode_block(int id, int nhg, int nsplit_max, int64_t rows, int* row, int* split,
+                                             int* hg) {
+  if (rows >= 8) {
+    const int x = id % 8, j = id / 8;
+    const int per_row = nsplit_max * nhg;
+    *row = x + 8 * (j / per_row);
+    *split = (j % per_row) / nhg;
+    *hg = j % nhg;
+    return;
+  }
   *hg = (id / 8) % nhg;
   const int c = (id / (8 * nhg)) * 8 + id % 8;  // (row, split) pair
   *row = c / nsplit_max;
@@ -181,7 +192,7 @@ template <bool FP8>
 __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int split, int nsplit_max, int nhg,
                                                              int partial, int64_t rows) {
   int row, s, hg;
-  decode_block(blockIdx.x, nhg, nsplit_max, &row, &s, &hg);
+  decode_block(blockIdx.x, nhg, nsplit_max, rows, &row, &s, &hg);
   if (row >= rows) return;
   const int e_begin = s * split;
   // the wave index is made visibly uniform, so per-wave control flow is scalar
@@ -463,7 +474,10 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
     for (int r = 0; r < 4; ++r) {
       const float L = hML[4 * hq + r][1];
       const float fs = partial ? 1.f : (L > 0.f ? __fdiv_rn(1.0f, L) : 0.f);
-      __builtin_nontemporal_store(av[r] * fs, &obase[(4 * hq + r) * 512 + c]);  // streamed: read by another kernel
+      if (partial)
+        obase[(4 * hq + r) * 512 + c] = av[r];  // kept in this XCD's L2 for the split merge
+      else
+        __builtin_nontemporal_store(av[r] * fs, &obase[(4 * hq + r) * 512 + c]);  // streamed: read once, elsewhere
     }
   }
   if (threadIdx.x < 16) {
@@ -479,12 +493,8 @@ __global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int spl
   }
 }
 
-// Streaming (non-temporal) float4 accesses: data read or written once, kept out of
-// the way of the caches.
-__device__ __forceinline__ float4 nt_load4(const float4* p) {
-  const v4f v = __builtin_nontemporal_load((const v4f*)p);
-  return make_float4(v[0], v[1], v[2], v[3]);
-}
+// Streaming (non-temporal) float4 store: data written once and read elsewhere, kept out
+// of the way of the caches.
 __device__ __forceinline__ void nt_store4(float4 x, float4* p) {
   __builtin_nontemporal_store((v4f){x.x, x.y, x.z, x.w}, (v4f*)p);
 }
@@ -504,7 +514,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int split, 
   float4 pv[kMergeBatch];
 #pragma unroll
   for (int j = 0; j < kMergeBatch; ++j)
-    pv[j] = j < nsplit_max ? nt_load4(&src[j * sstride]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    pv[j] = j < nsplit_max ? src[j * sstride] : make_float4(0.f, 0.f, 0.f, 0.f);
   const float* pml = (const float*)a.ws + rows * nsplit_max * H * 512;
   float ms = kNegInf, ls = 0.f;
   if (threadIdx.x < kWave && (int)threadIdx.x < nsplit_max) {
@@ -545,7 +555,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int split, 
   }
   for (int s = kMergeBatch; s < nsplit; ++s) {
     const float wgt = wts[s] * inv;
-    const float4 v = nt_load4(&src[s * sstride]);
+    const float4 v = src[s * sstride];
     acc.x = fmaf(v.x, wgt, acc.x);
     acc.y = fmaf(v.y, wgt, acc.y);
     acc.z = fmaf(v.z, wgt, acc.z);
@@ -615,7 +625,7 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
   const int partial = nsplit_max > 1;
   const int nhg = a.heads / 16;
   const int64_t pairs = rows * nsplit_max;
-  const int64_t blocks = (pairs + 7) / 8 * 8 * nhg;
+  const int64_t blocks = rows >= 8 ? (rows + 7) / 8 * 8 * nsplit_max * nhg : (pairs + 7) / 8 * 8 * nhg;
   if (a.kv.dtype == CSA_FP8_E4M3)
     hipLaunchKernelGGL(attn_wave_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, split, nsplit_max,
                        nhg, partial, rows);
