@@ -297,6 +297,17 @@ csa_status csa_quantize_mxfp4(const float* x, int64_t rows, int32_t cols, uint8_
 csa_status csa_quantize_fp8(const float* x, int64_t rows, int32_t cols, uint8_t* codes, float* row_scale,
                             void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement: the device's HBM streaming-read ceiling, the practical bound the
+ * bandwidth-bound stages are compared with beside the nominal peak.  Not part of
+ * the attention path.
+ *   csa_stream_read reads every byte of data[0, bytes) once (bytes % 16 == 0,
+ *   data 16-byte aligned) and writes one word per workgroup to sink, which must
+ *   hold csa_stream_read_sink_size() bytes.  Time it with events around the call.
+ * ------------------------------------------------------------------------- */
+csa_status csa_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream);
+size_t csa_stream_read_sink_size(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -106,6 +106,8 @@ _c = {
     "csa_attn_workspace_size": _proto("csa_attn_workspace_size", _SZ, _I32, _I32, _I32, _I32, _I32),
     "csa_quantize_mxfp4": _proto("csa_quantize_mxfp4", _I32, _P, _I64, _I32, _P, _P, _P),
     "csa_quantize_fp8": _proto("csa_quantize_fp8", _I32, _P, _I64, _I32, _P, _P, _P),
+    "csa_stream_read": _proto("csa_stream_read", _I32, _P, _SZ, _P, _P),
+    "csa_stream_read_sink_size": _proto("csa_stream_read_sink_size", _SZ),
 }
 
 
@@ -250,6 +252,14 @@ def csa_quantize_mxfp4(x, rows, cols, codes, scales, stream=None):
 
 def csa_quantize_fp8(x, rows, cols, codes, row_scale, stream=None):
     _check(_c["csa_quantize_fp8"](_ptr(x), rows, cols, _ptr(codes), _ptr(row_scale), _stream(stream)))
+
+
+def csa_stream_read(data, nbytes, sink, stream=None):
+    _check(_c["csa_stream_read"](_ptr(data), nbytes, _ptr(sink), _stream(stream)))
+
+
+def csa_stream_read_sink_size() -> int:
+    return _c["csa_stream_read_sink_size"]()
 
 
 EXPORTED = [k for k in _c]

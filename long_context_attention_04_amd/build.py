@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
-SOURCES = ["abi.cpp", "compress.hip", "index.hip", "topk.hip", "attn.hip"]
+SOURCES = ["abi.cpp", "compress.hip", "index.hip", "topk.hip", "attn.hip", "diag.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

@@ -418,4 +418,12 @@ csa_status csa_quantize_fp8(const float* x, int64_t rows, int32_t cols, uint8_t*
   return from_hip(csa::launch_quantize_fp8(x, rows, cols, codes, row_scale, (hipStream_t)stream), "csa_quantize_fp8");
 }
 
+size_t csa_stream_read_sink_size(void) { return (size_t)csa::kStreamReadBlocks * sizeof(uint32_t); }
+
+csa_status csa_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream) {
+  REQUIRE(data && sink, CSA_ERR_NULL, "data/sink is NULL");
+  REQUIRE(bytes % 16 == 0, CSA_ERR_SHAPE, "bytes must be a multiple of 16");
+  return from_hip(csa::launch_stream_read(data, bytes, sink, (hipStream_t)stream), "csa_stream_read launch");
+}
+
 }  // extern "C"

@@ -59,20 +59,21 @@ template <int NP>
 __device__ __forceinline__ void fp4_query_quantize(const IndexArgs& a, int t, const float2 (&xs)[NP], Fp4QueryLds& ql) {
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    if (256 * i >= a.heads * 32) break;  // uniform
-    const int pi = 256 * i + t;
-    const int h = pi / 32, blk = (pi / 16) % 2, pr = pi % 16;
-    const float2 x = xs[i];
-    float amax = fmaxf(fabsf(x.x), fabsf(x.y));
+    if (256 * i < a.heads * 32) {  // uniform
+      const int pi = 256 * i + t;
+      const int h = pi / 32, blk = (pi / 16) % 2, pr = pi % 16;
+      const float2 x = xs[i];
+      float amax = fmaxf(fabsf(x.x), fabsf(x.y));
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
-    const int e = mx_scale_exp(amax);
-    const uint32_t byte = amax > 0.f ? (f32_to_e2m1(x.x, e) | (f32_to_e2m1(x.y, e) << 4)) : 0u;
-    // four adjacent pairs form one dword of codes
-    const uint32_t b1 = __shfl_down(byte, 1, 16), b2 = __shfl_down(byte, 2, 16), b3 = __shfl_down(byte, 3, 16);
-    if (h < a.heads) {
-      if ((pr & 3) == 0) ql.code[h][blk][pr / 4] = byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
-      if (pr == 0) ql.scale[h][blk] = (uint32_t)(e + 127);
+      for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+      const int e = mx_scale_exp(amax);
+      const uint32_t byte = amax > 0.f ? (f32_to_e2m1(x.x, e) | (f32_to_e2m1(x.y, e) << 4)) : 0u;
+      // four adjacent pairs form one dword of codes
+      const uint32_t b1 = __shfl_down(byte, 1, 16), b2 = __shfl_down(byte, 2, 16), b3 = __shfl_down(byte, 3, 16);
+      if (h < a.heads) {
+        if ((pr & 3) == 0) ql.code[h][blk][pr / 4] = byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        if (pr == 0) ql.scale[h][blk] = (uint32_t)(e + 127);
+      }
     }
   }
 }
@@ -140,14 +141,19 @@ __device__ __forceinline__ float fp4_tile_score(const v8i& A, int sa, const floa
   return part + other;
 }
 
-// Every visible score of one row (keys 0 .. V-1) recomputed by a whole workgroup of
-// nthreads (a multiple of 256) and written to srow: the indexer's arithmetic, tile by
-// tile.  Used when a selection must fall back to the whole row and the indexer wrote
-// no scores.  Ends with a workgroup barrier; srow is then readable by the workgroup.
-template <int NR>
-__device__ void fp4_rescore_row(const IndexArgs& a, int row, int V, Fp4QueryLds& ql, float* srow) {
+// Scores of chosen 32-key tiles of one row (only keys < V; the rest score as
+// absent) recomputed by a whole workgroup (a multiple of 256 threads) with the
+// indexer's arithmetic, tile by tile: tile_key(i) is the first key of tile i (a
+// multiple of 32, as in the indexer), store(i, key, score, live) is called once per
+// key by the lane holding it.  Used when a selection needs scores the indexer did
+// not write.  Starts and ends with a workgroup barrier (the caller's LDS is free to
+// reuse before; ql and whatever store wrote are readable by the workgroup after).
+template <int NR, typename TileKey, typename Store>
+__device__ void fp4_rescore_tiles(const IndexArgs& a, int row, int V, Fp4QueryLds& ql, int ntile, TileKey tile_key,
+                                  Store store) {
   const int b = row / a.tq, t_q = row % a.tq;
   const int t = threadIdx.x, l = t % kWave, w = t / kWave, nw = blockDim.x / kWave;
+  __syncthreads();
   if (t < 256) {
     float2 qx[Fp4Pairs<NR>::n];
     fp4_query_load(a, b, t_q, t, qx);
@@ -160,17 +166,40 @@ __device__ void fp4_rescore_row(const IndexArgs& a, int row, int V, Fp4QueryLds&
   float wv[NR];
   fp4_query_operand<NR>(ql, a.heads, l, &A, &sa, wv);
   const Fp4Lane<NR> ln(l);
-  const int ntile = (V + 31) / 32;
-  for (int tile = w; tile < ntile; tile += nw) {
-    const int key = 32 * tile + ln.m;
-    const bool live = key < V;
-    const int64_t kk = live ? key : 0;
-    const v4i c = live ? *(const v4i*)((const uint8_t*)a.k.data + (int64_t)b * a.k.sb + kk * a.k.sr + 16 * ln.kb)
-                       : (v4i){0, 0, 0, 0};
-    const int sbk = live ? ((const uint8_t*)a.k.scale)[(int64_t)b * a.k.ssb + kk * a.k.ssr + ln.kb] : 127;
-    const float s = fp4_tile_score<NR>(A, sa, wv, c, sbk);
-    if (ln.kb == 0 && live) srow[key] = s;
+  constexpr int kU = NR == 4 ? 4 : 2;  // tiles in flight per wave: their loads are issued together
+  for (int t0 = w; t0 < ntile; t0 += kU * nw) {
+    v4i c[kU];
+    int sbk[kU], key[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int tile = t0 + u * nw;
+      key[u] = tile < ntile ? tile_key(tile) + ln.m : V;
+      const bool live = key[u] < V;
+      const int64_t kk = live ? key[u] : 0;
+      c[u] = live ? *(const v4i*)((const uint8_t*)a.k.data + (int64_t)b * a.k.sb + kk * a.k.sr + 16 * ln.kb)
+                  : (v4i){0, 0, 0, 0};
+      sbk[u] = live ? ((const uint8_t*)a.k.scale)[(int64_t)b * a.k.ssb + kk * a.k.ssr + ln.kb] : 127;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int tile = t0 + u * nw;  // wave-uniform
+      if (tile < ntile) {
+        const float s = fp4_tile_score<NR>(A, sa, wv, c[u], sbk[u]);
+        if (ln.kb == 0) store(tile, key[u], s, key[u] < V);
+      }
+    }
   }
+  __syncthreads();
+}
+
+// Every visible score of one row (keys 0 .. V-1) recomputed and written to srow.
+template <int NR>
+__device__ void fp4_rescore_row(const IndexArgs& a, int row, int V, Fp4QueryLds& ql, float* srow) {
+  fp4_rescore_tiles<NR>(
+      a, row, V, ql, (V + 31) / 32, [](int tile) { return 32 * tile; },
+      [&](int, int key, float s, bool live) {
+        if (live) srow[key] = s;
+      });
   __threadfence();
   __syncthreads();
 }

@@ -90,7 +90,7 @@ struct CandOut {
 // Fused (b)+(c) for MXFP4 keys on long rows: the indexer's workgroups also emit
 // their 1024-key slice's candidate list, and one merge pass selects the top-k.
 constexpr int kFusedSlice = 1024;  // keys per indexer workgroup
-constexpr int kFusedC = 24;        // list slots per slice (the slice's exact top-24)
+constexpr int kFusedC = 32;        // list slots per slice (the slice's exact top-32)
 bool index_topk_fused_ok(const IndexArgs& a, int k);
 // Rows whose full slices alone cannot hold more than k candidates (each full slice
 // lists kFusedC keys) are selected from their scores: the indexer writes them.
@@ -144,5 +144,9 @@ constexpr int kAttnMaxSplitEntries = 2048;
 int attn_split_size(int tq, int n_entries_max);
 size_t attn_workspace_bytes(int64_t rows, int heads, int dim, int n_entries_max, int tq);
 hipError_t launch_attention(const AttnArgs& a, int n_entries_max, hipStream_t s);
+
+// ---------------------------------------------------------------- measurement
+constexpr int kStreamReadBlocks = 2048;  // workgroups of the streaming-read probe (one sink word each)
+hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace csa

@@ -89,7 +89,7 @@ constexpr int kSlice = kTopkSlice;  // keys per candidate workgroup
 constexpr int kCandThreads = 256;
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeCap = 8192;     // candidates a merge workgroup holds in LDS (4096-key slices)
-constexpr int kSliceMergeCap = 6144;  // list slots the 1024-slice merge holds (256 slices of 24)
+constexpr int kSliceMergeCap = 8192;  // list slots the 1024-slice merge holds (256 slices of 32)
 
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -257,17 +257,28 @@ __global__ __launch_bounds__(256) void topk_cand32_kernel(const float* __restric
 }
 
 // Pass 2 of the 1024-slice scheme, one 1024-thread workgroup per row: slice s's
-// list fills slots 24s .. 24s+23 (empty slots hold key 0), so slot order is
-// ascending index order and thread t holds slots 6t .. 6t+5 in registers.  The
+// list fills slots 32s .. 32s+31 (empty slots hold key 0), so slot order is
+// ascending index order and thread t holds slots 8t .. 8t+7 in registers.  The
 // threshold is found on the registers, the compaction is one block scan, and the
 // result is certified exact: every key a slice left out ranks after that slice's
 // (last_key, last_idx), so the selection is exact unless such a pair is selected.
-// Otherwise -- and for rows whose full slices hold too few candidates -- the whole
-// row is selected from its scores: `scores` when the caller kept them, else
-// `row_scores`, which the indexer filled for short rows and which this kernel fills
-// by rescoring (MXFP4 keys, fp4_rescore_row) when a certificate fails.
-constexpr int kMPerThread = kSliceMergeCap / kRegSelThreads;  // 6
+// When some are (a slice holding more than kSliceSlots of the row's top-k), the
+// row is selected again: with the row's scores when the caller kept them; else,
+// for at most kMaxBadSlices such slices, from the other slices' lists plus every
+// key of those slices rescored with the indexer's arithmetic; else from the whole
+// row rescored.  Rows whose full slices hold too few candidates (short rows) are
+// selected from their scores, which the indexer wrote to `row_scores`.
+constexpr int kMPerThread = kSliceMergeCap / kRegSelThreads;  // 8
 static_assert(kMPerThread * kRegSelThreads == kSliceMergeCap && kSliceSlots % kMPerThread == 0, "slot tiling");
+constexpr int kMergeMaxSlices = kSliceMergeCap / kSliceSlots;  // 256
+static_assert(kMergeMaxSlices % kWave == 0 && kMergeMaxSlices <= kRegSelThreads, "slice flags per wave");
+// A failed certificate rescores up to kMaxBadSlices slices into LDS (ostage after
+// the query: kBadKeysOffset words, then kSlice32 keys per slice); more rescore the row.
+constexpr int kMaxBadSlices = 8;
+constexpr int kBadKeysOffset = 512;
+static_assert(sizeof(Fp4QueryLds) <= 4 * kBadKeysOffset &&
+                  kBadKeysOffset + kMaxBadSlices * kSlice32 <= kSliceMergeCap + kRegSelThreads,
+              "rescored slices fit in ostage");
 
 struct MergeArgs {
   const float* scores;    // the row scores, when the caller keeps them (else nullptr)
@@ -286,6 +297,8 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge_slices_kernel(Merge
   __shared__ RegSelLds rs;
   __shared__ SelShared sh;
   __shared__ __attribute__((aligned(16))) uint32_t ostage[kSliceMergeCap + kRegSelThreads];  // selected indices by rank, then discard slots
+  __shared__ uint64_t badmask[kMergeMaxSlices / kWave];
+  __shared__ int badlist[kMaxBadSlices], badstart[kMaxBadSlices];
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
   const int nslices = ma.nslices, k = ma.k;
@@ -319,6 +332,8 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge_slices_kernel(Merge
   }
   const float* srow = ma.scores ? ma.scores + row * ma.n_cap : ma.row_scores + row * ma.n_cap;
   bool full = ma.short_rows && index_topk_short_row(V, k);
+  int nbad = 0;   // slices whose certificate failed
+  int sel_n = 0;  // > 0: select from the union of good lists and rescored bad slices
   if (!full) {
     const int ns = (V + kSlice32 - 1) / kSlice32;  // slices holding visible keys
     if (t >= ns) mm = SliceMeta{0u, 0u, 0u, 0u};
@@ -362,24 +377,86 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge_slices_kernel(Merge
       }
       if (has_t) rs.jT = my_jT;
       __syncthreads();
-      // exact unless some slice's (last_key, last_idx) is selected
+      // exact unless some slice's (last_key, last_idx) is selected: such slices are
+      // "bad" (waves 0-3 cover the <= 256 slices)
       const uint32_t jT = rs.jT;
-      if (t < ns && mm.trunc && (mm.last_key > T || (mm.last_key == T && mm.last_idx <= jT))) rs.bad = 1u;
+      const bool isbad = t < ns && mm.trunc && (mm.last_key > T || (mm.last_key == T && mm.last_idx <= jT));
+      const uint64_t bm = __builtin_amdgcn_ballot_w64(isbad);
+      if (t < kMergeMaxSlices && t % kWave == 0) badmask[t / kWave] = bm;
       __syncthreads();
-      full = rs.bad != 0u;
+      nbad = 0;
+#pragma unroll
+      for (int i = 0; i < kMergeMaxSlices / kWave; ++i) nbad += __builtin_popcountll(badmask[i]);
+      full = nbad != 0;
       if (!full)
         for (int i = t; i < k; i += kRegSelThreads) out[i] = (int32_t)ostage[i];
     }
-    if (full && !ma.scores) {  // the row's scores were not kept: recompute them
-      if constexpr (NR > 0) fp4_rescore_row<NR>(ma.rescore, (int)row, V, *(Fp4QueryLds*)ostage, ma.row_scores + row * ma.n_cap);
+    if constexpr (NR > 0) {
+      if (full && !ma.scores && nbad > 0 && nbad <= kMaxBadSlices) {
+        // Rescore only the bad slices (into LDS), then select over the union of the
+        // good slices' lists and every key of the bad slices.  Exact: a good slice's
+        // omitted keys rank after the candidates' k-th key, and the union's k-th key
+        // ranks at or before it.
+        if (t < nbad) {  // the t-th bad slice (ascending) and its start in the union
+          int seen = 0, id = 0;
+          for (int i = 0; i < kMergeMaxSlices / kWave; ++i) {
+            uint64_t m = badmask[i];
+            while (m) {
+              if (seen == t) id = kWave * i + __builtin_ctzll(m);
+              ++seen;
+              m &= m - 1ull;
+            }
+          }
+          badlist[t] = id;
+          badstart[t] = kSliceSlots * id + (kSlice32 - kSliceSlots) * t;
+        }
+        uint32_t* bkeys = ostage + kBadKeysOffset;
+        fp4_rescore_tiles<NR>(
+            ma.rescore, (int)row, V, *(Fp4QueryLds*)ostage, nbad * (kSlice32 / 32),
+            [&](int tile) { return kSlice32 * badlist[tile / (kSlice32 / 32)] + 32 * (tile % (kSlice32 / 32)); },
+            [&](int tile, int key, float sc, bool live) {
+              bkeys[(tile / (kSlice32 / 32)) * kSlice32 + key % kSlice32] = live ? float_key(sc) : 0u;
+            });
+        sel_n = kSliceSlots * (ns - nbad) + kSlice32 * nbad;  // > k: it holds every candidate
+      } else if (full && !ma.scores) {  // the row's scores were not kept: recompute them all
+        fp4_rescore_row<NR>(ma.rescore, (int)row, V, *(Fp4QueryLds*)ostage, ma.row_scores + row * ma.n_cap);
+      }
     }
   }
-  if (full) {  // select from the whole row (slow path; any input)
-    auto key = [&](int i) { return float_key(srow[i]); };
+  if (full) {  // select again, from the union above or from the whole row (any input)
+    const uint2* lists = ma.cand + row * nslices * kSliceSlots;
+    const uint32_t* bkeys = ostage + kBadKeysOffset;
+    // position v -> (key, index).  Union: the slices in ascending order, kSliceSlots
+    // positions for a good slice's list, kSlice32 for a bad slice's keys.
+    auto key_at = [&](int v, uint32_t* index) -> uint32_t {
+      if (sel_n == 0) {
+        *index = (uint32_t)v;
+        return float_key(srow[v]);
+      }
+      int i = 0;
+      for (; i < nbad; ++i) {
+        const int bs = badstart[i];
+        if (v < bs) break;
+        if (v < bs + kSlice32) {
+          *index = (uint32_t)(kSlice32 * badlist[i] + (v - bs));
+          return bkeys[i * kSlice32 + (v - bs)];
+        }
+      }
+      const uint2 e = lists[v - (kSlice32 - kSliceSlots) * i];
+      *index = e.y;
+      return e.x;
+    };
+    auto key = [&](int v) {
+      uint32_t ix;
+      return key_at(v, &ix);
+    };
+    const int n = sel_n ? sel_n : V;
     uint32_t T, krem;
-    radix_threshold(key, V, k, sh, &T, &krem);
-    compact_selected(key, V, T, krem, sh, [&](int pos, uint32_t r) {
-      if (r < (uint32_t)k) out[r] = pos;
+    radix_threshold(key, n, k, sh, &T, &krem);
+    compact_selected(key, n, T, krem, sh, [&](int v, uint32_t r) {
+      uint32_t ix;
+      key_at(v, &ix);
+      if (r < (uint32_t)k) out[r] = (int32_t)ix;
     });
   }
 }

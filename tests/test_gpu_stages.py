@@ -260,6 +260,13 @@ def test_topk_exact(gpu_lib, B, Tq, N, k, mode):
     if mode == "ties":
         s = r.integers(-20, 20, (B, Tq, N)).astype(np.float32)
         s[s == 0] = np.where(r.random(int((s == 0).sum())) < 0.5, -0.0, 0.0).astype(np.float32)
+    elif mode in ("cluster2", "cluster12"):
+        w = np.abs(w)
+        hot = (5, N // 4096) if mode == "cluster2" else tuple(3 + 5 * i for i in range(12))
+        qv = up(q[:, 0, 0])[:, None, :]
+        for sl in hot:
+            noise = torch.randn((B, 1024, dI), generator=gen, device="cuda")
+            kraw[:, sl * 1024:(sl + 1) * 1024] = 3.0 * qv + 0.5 * noise
     elif mode == "equal":
         s = np.zeros((B, Tq, N), np.float32)
     elif mode == "extreme":  # infinities and near-overflow magnitudes among normal scores
@@ -306,6 +313,13 @@ def test_topk_exact(gpu_lib, B, Tq, N, k, mode):
     (2, 1, 8, 65536, 2048, "few"),       # 40 distinct keys: many copies of the slices' 32nd score
     (2, 3, 8, 40000, 2048, "short"),     # some rows see at most k blocks
     (3, 2, 8, 262144, 2048, "partial"),  # rows seeing a fraction of the cache: few candidates
+    # long rows whose slice lists cannot decide: two slices hold most top scores (those two
+    # are rescored), twelve do (the row is rescored), ties everywhere (the row is rescored)
+    (2, 1, 8, 262144, 2048, "cluster2"),
+    (2, 1, 32, 150000, 1024, "cluster2"),
+    (1, 2, 8, 262144, 2048, "cluster12"),
+    (1, 1, 8, 262144, 2048, "equal"),
+    (2, 1, 8, 262144, 2048, "few"),
 ])
 def test_index_topk_fused(gpu_lib, B, Tq, HI, N, k, mode):
     """csa_index_topk == csa_index_scores then csa_topk, bit for bit (scores and idx),
@@ -323,6 +337,13 @@ def test_index_topk_fused(gpu_lib, B, Tq, HI, N, k, mode):
     if mode == "cluster":
         w = np.abs(w)
         kraw[:, 5 * 1024:6 * 1024] = 3.0 * up(q[:, 0, 0])[:, None, :]
+    elif mode in ("cluster2", "cluster12"):
+        w = np.abs(w)
+        hot = (5, N // 4096) if mode == "cluster2" else tuple(3 + 5 * i for i in range(12))
+        qv = up(q[:, 0, 0])[:, None, :]
+        for sl in hot:
+            noise = torch.randn((B, 1024, dI), generator=gen, device="cuda")
+            kraw[:, sl * 1024:(sl + 1) * 1024] = 3.0 * qv + 0.5 * noise
     elif mode == "equal":
         kraw[:] = kraw[:, :1]
     elif mode == "few":
