@@ -32,7 +32,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -48,11 +47,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 KEY_BYTES = 34  # MXFP4 indexer key: 64 e2m1 codes (32 B) + 2 e8m0 scales
 SLICE, SLICE_SLOTS, SLOT_BYTES, META_BYTES = 1024, 32, 8, 16  # fused indexer's slice lists
-CSRC = os.path.join(ROOT, "long_context_attention_04_amd", "csrc")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "index_mxfp4_csa_decode_1m_b8_pmc.txt")
 # the sources the dominant kernel of the headline workload is built from (the counter
 # summary is valid only for the build it was taken from)
-INDEX_SOURCES = ["index.hip", "index_fp4.h", "select.h", "common.h", "compress_block.h", "kernels.h"]
 
 
 def parse():
@@ -117,13 +114,6 @@ def stream_ceiling(torch) -> dict:
             "kernel": "stream_read_kernel (csa_stream_read), best of 5"}
 
 
-def source_hash() -> str:
-    h = hashlib.sha256()
-    for f in INDEX_SOURCES:
-        h.update(open(os.path.join(CSRC, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def pmc_traffic():
     """HBM bytes per launch of the headline's dominant kernel from the committed rocprofv3 counter
     summary, when it was taken from this build (else None)."""
@@ -134,7 +124,8 @@ def pmc_traffic():
         if "=" in line and not line.startswith("#"):
             k_, v_ = line.split("=", 1)
             vals[k_.strip()] = v_.strip()
-    if vals.get("source_sha256_16") != source_hash():
+    from long_context_attention_04_amd.rocprof_summary import source_hash
+    if vals.get("source_sha256_16") != source_hash(quiet=True):
         return None
     try:
         return float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])
@@ -584,7 +575,7 @@ def main():
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.neg(src, out=dst)  # one elementwise kernel: reads n bytes, writes n bytes
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
