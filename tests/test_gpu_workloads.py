@@ -134,6 +134,7 @@ def test_csa_prefill_2k_on_64k(gpu_lib):
     name = "csa_prefill_2k_on_64k"
     wl = synth.WORKLOADS[name]
     L = workloads.build(name)
+    L.keep_scores = True
     L.step()
     torch.cuda.synchronize()
     m, N, ctx = wl.m, L.n_cap, wl.extra["context"]
@@ -165,6 +166,12 @@ def test_csa_prefill_2k_on_64k(gpu_lib):
                                           wl.window, np.array([[t]]), wl.scale)
         assert row_rel_err(g_out[tq:tq + 1], out[0]) < 2e-3
         assert np.max(np.abs(g_lse[tq] - lse[0, 0])) < 2e-3
+    # scores not kept (the call keeps them in its workspace): the same selection and outputs
+    L.keep_scores = False
+    L.step()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(L.idx)[0], g_idx)
+    np.testing.assert_array_equal(_np(L.out)[0], g_out)
 
 
 def test_hca_decode_b64_128k(gpu_lib):
