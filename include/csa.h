@@ -285,6 +285,25 @@ csa_status hca_attn(const csa_tensor* q, const csa_tensor* kv_hc, int32_t m_hc, 
 size_t csa_attn_workspace_size(int32_t batch, int32_t tq, int32_t heads, int32_t dim, int32_t n_entries_max);
 
 /* ---------------------------------------------------------------------------
+ * Allocation-free csa_sparse_attn, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and errors as csa_sparse_attn
+ * minus the workspace: the split partials live in a static device array of
+ * CSA_NOALLOC_SCRATCH_BYTES (64 MiB), one per device, held
+ * until the process ends.  Calls whose csa_attn_workspace_size exceeds it get
+ * CSA_ERR_WORKSPACE before any launch.  The call itself allocates nothing; its
+ * first call on a device looks up the array's address there.  Every call on a
+ * device shares that device's array (nothing in it needs clearing: each call
+ * writes every partial it reads), so calls that overlap in time on one device
+ * (different streams) race; calls on one stream are ordered.
+ * ------------------------------------------------------------------------- */
+csa_status csa_sparse_attn_noalloc(const csa_tensor* q, const csa_tensor* kv_cmp, const int32_t* idx, int32_t k,
+                                   const csa_tensor* kv_raw, const int32_t* raw_base, int32_t window,
+                                   const int32_t* q_pos, int32_t batch, int32_t tq, int32_t heads, int32_t dim,
+                                   float scale, float* out, float* lse, void* stream);
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* ---------------------------------------------------------------------------
  * Quantisers (the FP4 indexer path: b-lab.team summary, Core Methodological
  * Innovations 4, Quantization-Aware Training; fp8 KV is a storage variant).
  *   csa_quantize_mxfp4: x [rows, cols] float (cols % 32 == 0) -> codes

@@ -104,6 +104,8 @@ _c = {
     "hca_attn": _proto("hca_attn", _I32, _TP, _TP, _I32, _I32, _TP, _P, _I32, _P, _I32, _I32, _I32, _I32, _F, _P,
                        _P, _P, _SZ, _P),
     "csa_attn_workspace_size": _proto("csa_attn_workspace_size", _SZ, _I32, _I32, _I32, _I32, _I32),
+    "csa_sparse_attn_noalloc": _proto("csa_sparse_attn_noalloc", _I32, _TP, _TP, _P, _I32, _TP, _P, _I32, _P, _I32,
+                                      _I32, _I32, _I32, _F, _P, _P, _P),
     "csa_quantize_mxfp4": _proto("csa_quantize_mxfp4", _I32, _P, _I64, _I32, _P, _P, _P),
     "csa_quantize_fp8": _proto("csa_quantize_fp8", _I32, _P, _I64, _I32, _P, _P, _P),
     "csa_stream_read": _proto("csa_stream_read", _I32, _P, _SZ, _P, _P),
@@ -237,6 +239,16 @@ def csa_sparse_attn(q, kv_cmp, idx, k, kv_raw, raw_base, window, q_pos, batch, t
     _check(_c["csa_sparse_attn"](ctypes.byref(q), ctypes.byref(kv_cmp), _ptr(idx), k, ctypes.byref(kv_raw),
                                  _ptr(raw_base), window, _ptr(q_pos), batch, tq, heads, dim, scale, _ptr(out),
                                  _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def csa_sparse_attn_noalloc(q, kv_cmp, idx, k, kv_raw, raw_base, window, q_pos, batch, tq, heads, dim, scale, out,
+                            lse=None, stream=None):
+    _check(_c["csa_sparse_attn_noalloc"](ctypes.byref(q), ctypes.byref(kv_cmp), _ptr(idx), k, ctypes.byref(kv_raw),
+                                         _ptr(raw_base), window, _ptr(q_pos), batch, tq, heads, dim, scale, _ptr(out),
+                                         _ptr(lse), _stream(stream)))
+
+
+CSA_NOALLOC_SCRATCH_BYTES = 64 << 20  # the static scratch of csa_sparse_attn_noalloc (csa.h)
 
 
 def hca_attn(q, kv_hc, m_hc, n_cap_hc, kv_raw, raw_base, window, q_pos, batch, tq, heads, dim, scale, out, lse=None,

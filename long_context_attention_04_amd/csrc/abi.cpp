@@ -7,6 +7,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/csa.h"
@@ -330,10 +331,46 @@ size_t csa_attn_workspace_size(int32_t batch, int32_t tq, int32_t heads, int32_t
   return csa::attn_workspace_bytes((int64_t)batch * tq, heads, dim, n_entries_max, tq);
 }
 
+}  // extern "C"
+
+// ------------------------------------------------------------ allocation-free attention
+// The split partials of csa_sparse_attn_noalloc live in this file-scope device array
+// (one copy per device, held until the process ends).  Host code never passes the
+// array's name to a kernel: its device address is looked up once per device with
+// that device current and kept in g_scratch_ptr.
+namespace {
+constexpr size_t kNoAllocScratchBytes = CSA_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices];
+
+csa_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "hipGetDevice");
+  REQUIRE(dev >= 0 && dev < kNoAllocMaxDevices, CSA_ERR_UNSUPPORTED,
+          "device %d: the allocation-free entry point serves devices 0..%d", dev, kNoAllocMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return from_hip(e, "hipGetSymbolAddress(scratch)");
+    REQUIRE(p != nullptr, CSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
 static csa_status attn_common(const csa_tensor* q, const csa_tensor* kv, const int32_t* idx, int32_t k, int32_t m_hc,
                               int32_t n_cap_hc, const csa_tensor* kv_raw, const int32_t* raw_base, int32_t window,
                               const int32_t* q_pos, int32_t batch, int32_t tq, int32_t heads, int32_t dim, float scale,
-                              float* out, float* lse, void* ws, size_t ws_bytes, void* stream, int n_entries_max) {
+                              float* out, float* lse, void* ws, size_t ws_bytes, void* stream, int n_entries_max,
+                              bool use_scratch = false) {
   csa_status st;
   if ((st = check_tensor(q, "q")) != CSA_OK) return st;
   if ((st = check_tensor(kv, "kv")) != CSA_OK) return st;
@@ -360,7 +397,18 @@ static csa_status attn_common(const csa_tensor* q, const csa_tensor* kv, const i
     return fail(CSA_ERR_DTYPE, "attention caches must be F32, BF16 or FP8_E4M3");
   }
   const size_t need = csa::attn_workspace_bytes((int64_t)batch * tq, heads, dim, n_entries_max, tq);
-  if (need > 0) REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (need > 0 && !use_scratch)
+    REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (use_scratch) {  // the allocation-free entry point, after every other check
+    REQUIRE(need <= kNoAllocScratchBytes, CSA_ERR_WORKSPACE,
+            "attention needs %zu scratch bytes; csa_sparse_attn_noalloc holds at most %zu (use csa_sparse_attn with a "
+            "workspace)", need, kNoAllocScratchBytes);
+    ws = nullptr;
+    if (need > 0) {
+      const csa_status sst = scratch_address(&ws);
+      if (sst != CSA_OK) return sst;
+    }
+  }
   csa::AttnArgs a;
   a.q = csa::view_of(q);
   a.kv = csa::view_of(kv);
@@ -392,6 +440,17 @@ csa_status csa_sparse_attn(const csa_tensor* q, const csa_tensor* kv_cmp, const 
   REQUIRE((int64_t)k + window <= (1 << 30), CSA_ERR_SHAPE, "k + window too large");
   return attn_common(q, kv_cmp, idx, k, 0, 0, kv_raw, raw_base, window, q_pos, batch, tq, heads, dim, scale, out, lse,
                      ws, ws_bytes, stream, k + window);
+}
+
+csa_status csa_sparse_attn_noalloc(const csa_tensor* q, const csa_tensor* kv_cmp, const int32_t* idx, int32_t k,
+                                   const csa_tensor* kv_raw, const int32_t* raw_base, int32_t window,
+                                   const int32_t* q_pos, int32_t batch, int32_t tq, int32_t heads, int32_t dim,
+                                   float scale, float* out, float* lse, void* stream) {
+  REQUIRE(idx != nullptr, CSA_ERR_NULL, "idx is NULL");
+  REQUIRE(k >= 0, CSA_ERR_SHAPE, "k=%d must be >= 0", k);
+  REQUIRE((int64_t)k + window <= (1 << 30), CSA_ERR_SHAPE, "k + window too large");
+  return attn_common(q, kv_cmp, idx, k, 0, 0, kv_raw, raw_base, window, q_pos, batch, tq, heads, dim, scale, out, lse,
+                     nullptr, 0, stream, k + window, /*use_scratch=*/true);
 }
 
 csa_status hca_attn(const csa_tensor* q, const csa_tensor* kv_hc, int32_t m_hc, int32_t n_cap_hc,

@@ -224,6 +224,18 @@ def test_attention_rejects_and_workspace():
     expect(E_UNSUP, sparse(k=131072, W=129, wsb=big), match="entries per query")
     expect(E_UNSUP, sparse(k=131072 - 128, W=129, wsb=big), match="entries per query")
 
+    # the allocation-free entry point: the same checks, and shapes whose partials exceed
+    # its static scratch are refused
+    def noalloc(idx=P, k=2048, batch=8, heads=64):
+        return lambda stream: csa.csa_sparse_attn_noalloc(q, kv, idx, k, raw, P, 128, P, batch, 1, heads, 512, 0.088,
+                                                          P, P, stream)
+
+    expect(E_NULL, noalloc(idx=None))
+    expect(E_SHAPE, noalloc(k=-1))
+    expect(E_UNSUP, noalloc(heads=40))
+    assert csa.csa_attn_workspace_size(64, 1, 64, 512, 2048 + 128) > csa.CSA_NOALLOC_SCRATCH_BYTES
+    expect(E_WS, noalloc(batch=64), match="csa_sparse_attn_noalloc holds at most")
+
     def hca(m_hc=128, ncap=1024, heads=64):
         return lambda stream: csa.hca_attn(q, kv, m_hc, ncap, raw, P, 128, P, 8, 1, heads, 512, 0.088, P, P, P,
                                            1 << 40, stream)
