@@ -30,6 +30,10 @@ Everything else is a reading, stated where it is used:
                 by the window's raw rows, as a multiset (no de-duplication), in
                 one softmax; key = value = the stored (shared, MQA) row.
   R-scale       logits are scale * <q_h, e>, scale an argument.
+  R-query       the indexer's query is a two-stage low-rank projection of the
+                query's hidden state h (down to rank r, then up to H_I heads of
+                d_I), and its head weights a direct projection of h; no norm,
+                activation or rotary term in between.
 All arithmetic is fp64 on the (dequantised) stored values.
 """
 from __future__ import annotations
@@ -95,6 +99,32 @@ def compress(raw, raw_base, logits, m, block_first, block_count):
             rows[i] = acc
         out.append((j0, rows))
     return out
+
+
+# ----------------------------------------------------------------------------
+# indexer query from the hidden state (the step before (b))
+# ----------------------------------------------------------------------------
+
+
+def index_query(h, w_dq, w_uq, w_w, n_idx_heads: int, idx_dim: int):
+    """The indexer's per-head query and head weights from the query hidden state
+    (b-lab.team summary of DeepSeek-V4, Core Methodological Innovations 1, CSA
+    bullet: the indexer scores with low-rank projections of h_t; R-query):
+        c = W_dq h            (rank r)
+        q_I = reshape(W_uq c, [H_I, d_I])
+        w = W_w h
+
+    h [..., d], w_dq [r, d], w_uq [H_I * d_I, r], w_w [H_I, d]
+    -> (q_I [..., H_I, d_I], w [..., H_I]).
+    """
+    h = np.asarray(h, dtype=np.float64)
+    w_dq = np.asarray(w_dq, dtype=np.float64)
+    w_uq = np.asarray(w_uq, dtype=np.float64)
+    w_w = np.asarray(w_w, dtype=np.float64)
+    assert w_uq.shape == (n_idx_heads * idx_dim, w_dq.shape[0])
+    c = h @ w_dq.T
+    q = (c @ w_uq.T).reshape(h.shape[:-1] + (n_idx_heads, idx_dim))
+    return q, h @ w_w.T
 
 
 # ----------------------------------------------------------------------------

@@ -98,6 +98,47 @@ def test_compress_incremental_equals_full():
     np.testing.assert_array_equal(np.concatenate([a, b]), full)
 
 
+# ----------------------------------------------------------------------------- indexer query
+
+
+def test_index_query_hand_derived_golden():
+    g = json.load(open(os.path.join(GOLDEN, "index_query_hand.json")))
+    q, w = O.index_query(np.array(g["h"]), np.array(g["w_dq"]), np.array(g["w_uq"]), np.array(g["w_w"]),
+                         g["n_idx_heads"], g["idx_dim"])
+    np.testing.assert_array_equal(q, np.array(g["expected_q"], dtype=np.float64))
+    np.testing.assert_array_equal(w, np.array(g["expected_w"], dtype=np.float64))
+
+
+def test_index_query_brute_force_loops():
+    r = np.random.default_rng(11)
+    d, rank, HI, dI = 7, 3, 2, 4
+    h = r.standard_normal((2, 5, d))
+    wdq, wuq, ww = r.standard_normal((rank, d)), r.standard_normal((HI * dI, rank)), r.standard_normal((HI, d))
+    q, w = O.index_query(h, wdq, wuq, ww, HI, dI)
+    assert q.shape == (2, 5, HI, dI) and w.shape == (2, 5, HI)
+    for b in range(2):
+        for t in range(5):
+            c = [sum(wdq[j, i] * h[b, t, i] for i in range(d)) for j in range(rank)]
+            for hh in range(HI):
+                assert abs(w[b, t, hh] - sum(ww[hh, i] * h[b, t, i] for i in range(d))) < 1e-12
+                for e in range(dI):
+                    want = sum(wuq[hh * dI + e, j] * c[j] for j in range(rank))
+                    assert abs(q[b, t, hh, e] - want) < 1e-12
+
+
+def test_index_query_has_rank_at_most_r_and_is_linear():
+    r = np.random.default_rng(12)
+    d, rank, HI, dI = 64, 5, 4, 8
+    wdq, wuq, ww = r.standard_normal((rank, d)), r.standard_normal((HI * dI, rank)), r.standard_normal((HI, d))
+    h = r.standard_normal((40, d))
+    q, w = O.index_query(h, wdq, wuq, ww, HI, dI)
+    assert np.linalg.matrix_rank(q.reshape(40, HI * dI)) == rank  # low rank: the queries span r directions
+    a, b = 0.75, -2.5
+    q2, w2 = O.index_query(a * h[0] + b * h[1], wdq, wuq, ww, HI, dI)
+    np.testing.assert_allclose(q2, a * q[0] + b * q[1], atol=1e-10)
+    np.testing.assert_allclose(w2, a * w[0] + b * w[1], atol=1e-10)
+
+
 # ----------------------------------------------------------------------------- indexer
 
 
