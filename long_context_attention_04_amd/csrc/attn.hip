@@ -11,31 +11,24 @@
 // heads share one 512-wide latent row per entry, so attention is a
 // [heads x 512] x [512 x n] contraction (QK) followed by [heads x n] x [n x 512]
 // (PV), both on bf16 MFMA.  A workgroup takes one query row, one group of 16
-// heads and one contiguous split of the entry list, with 8 waves (two per
-// SIMD, covering each other's waits).  Each wave is an independent
-// flash-decoding worker over every 8th tile of 16 entries:
-//  * it loads a tile's rows one whole row per instruction (lane L taking
-//    elements 8L .. 8L+7, the cheapest gather for the memory pipeline; the row
-//    address is scalar) one tile ahead of use, from selection indices staged
-//    in LDS once per workgroup, and stages the tile as bf16 rows in its own
-//    LDS area (fp8 rows are widened there);
-//  * QK reads the staged rows as the A operand and the workgroup's query heads
-//    (staged in LDS once) as B, giving the transposed logits S^T = K Q^T
-//    (16x16x32): each lane then holds four entries of one head -- exactly the
-//    A-operand layout PV needs for P, so P never moves between lanes;
-//  * the online softmax reduces over entries within the wave (register max,
-//    then two cross-row lane swaps) and rescales the accumulator lazily: only
-//    when a head's running maximum grows by more than 2^8, which keeps every
-//    probability <= 256 and skips almost all rescaling work;
-//  * P goes to PV as two bf16 terms (hi + lo, ~16 significant bits instead of
-//    bf16's 8), stacked along the k axis of one 16x16x32 MFMA per column tile;
-//    V is the same staged tile, read transposed with ds_read_b64_tr_b16.
-// No workgroup barrier runs inside the entry loop.  At the end the eight waves
-// combine their (max, sum, accumulator) through LDS in a fixed order; splits
-// are merged by a second kernel with a fixed-order log-sum-exp combine.  The
-// split size depends only on the call shape, never on the batch, so results
-// are batch-invariant.  fp8 rows keep their per-row scale out of the MFMA: it
-// multiplies the logit and the probability used for PV.
+// heads and one contiguous split of the entry list, and walks the split in
+// chunks of up to 144 entries that sit whole in LDS (one 1 KB row per entry):
+//  * the chunk's rows are all requested at once, one row per wave instruction,
+//    straight into LDS (bf16; fp8 rows are widened through registers), so a
+//    chunk costs one memory round trip, not one per tile;
+//  * QK computes the transposed logits S^T = K Q^T (16x16x32), eight waves over
+//    the chunk's 16-entry tiles, with the 16 query heads held in registers as
+//    the B operand and K read from LDS;
+//  * one max per head over the chunk (online across chunks), then P as two bf16
+//    terms (hi + lo, ~16 significant bits) written to LDS in the PV operand
+//    layout; per-head sums are added in a fixed order;
+//  * PV splits the 512 latent columns over the waves (64 each), reading V
+//    transposed with ds_read_b64_tr_b16: every wave's accumulator is final for
+//    its columns, so no cross-wave combine is needed.
+// Splits are merged by a second kernel with a fixed-order log-sum-exp combine.
+// The split and chunk sizes depend only on the call shape, never on the batch,
+// so results are batch-invariant.  fp8 rows keep their per-row scale out of the
+// MFMA: it multiplies the logit and the probability used for PV.
 //
 // Plain path (fp32 caches): a straightforward fp32 VALU kernel, one workgroup
 // per (query, head).
@@ -50,15 +43,7 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;  // 8: two per SIMD
-constexpr int kTile = 16;        // entries per wave step
-constexpr int kVsPitch = 528;    // bf16 per staged row: 512 + 16 pad (row stride 8 banks mod 32)
-// rows of staged tiles that also hold the merge buffer: 4 waves x 16 heads x 512 floats in 16 x 528 bf16 units
-constexpr int kMergeRows = kWaves;  // the combine buffer (4 x 16 heads x 512 floats) fits in 8 staged tiles
-static_assert(4 * 16 * 512 * 4 <= kMergeRows * kTile * kVsPitch * 2, "combine buffer fits the staging area");
-constexpr int kIdxStage = kAttnMaxSplitEntries;  // selection indices a workgroup stages (the largest split)
-constexpr int kRing = 1;         // tiles of rows in flight per wave beyond the one staged (register ring)
-constexpr int kQPitch = 520;     // bf16 per staged query head row (512 + 8 pad)
-constexpr float kRescale = 8.f;  // lazy rescale threshold (log2 units)
+constexpr int kTile = 16;                 // entries per MFMA tile
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -188,307 +173,267 @@ __device__ __forceinline__ float lane_sum4rows(float x) {  // fixed-order sum ov
   return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
+// Chunk of a split's entries resident in LDS: kChunkMax rows of 512 bf16 (1 KB),
+// 16-byte chunk c of row r stored at position c ^ (r & 15) so that the 16 rows a
+// QK operand read touches, and the 4 rows of a transposed read, fall on distinct
+// banks.
+constexpr int kChunkMax = 144;               // entries per chunk (9 tiles of 16)
+constexpr int kChunkTiles = kChunkMax / 16;  // 9
+constexpr int kRowBytes = 1024;
+
+struct ChunkLds {
+  __attribute__((aligned(16))) uint8_t rows[kChunkMax][kRowBytes];
+  // P as the PV A operand: [tile][k group g][head m] -> 4 bf16 hi then 4 bf16 lo of
+  // entries 16*tile + 4g .. +3
+  __attribute__((aligned(16))) uint4 p[kChunkTiles][4][16];
+  float esl[kChunkMax];    // entry scale (fp8 row scale, else 1); -1 = empty slot
+  int32_t sidx[kChunkMax];  // CSA selection slots of the chunk
+  float red_max[kWaves][16], red_sum[kWaves][16];
+};
+
+__device__ __forceinline__ int swz_off(int r, int chunk16) { return r * kRowBytes + ((chunk16 ^ (r & 15)) << 4); }
+
+// One workgroup: one query row, 16 heads, one split of its entry list, processed in
+// chunks of at most kChunkMax entries.  For each chunk:
+//  * the chunk's selection slots (and fp8 scales) go to LDS, then every wave issues
+//    its rows (one row per instruction, straight into LDS for bf16; fp8 rows pass
+//    through registers to be widened);
+//  * QK: S^T = K Q^T on 16x16x32 bf16 MFMA, wave w taking 16-entry tiles w and w+8
+//    with the 16 query heads held in registers (B operand) and K read from LDS;
+//  * one workgroup max per head (online across chunks), P = exp2(s - max) written
+//    to LDS as hi + lo bf16 in the PV operand layout, per-head sums in a fixed order;
+//  * PV with the latent columns split over the waves (wave w owns columns
+//    64w .. 64w+63 of all 16 heads): the accumulator of a wave is final for its
+//    columns, so the waves never combine accumulators.
 template <bool FP8>
-__global__ __launch_bounds__(kThreads) void attn_wave_kernel(AttnArgs a, int split, int nsplit_max, int nhg,
-                                                             int partial, int64_t rows) {
+__global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a, int split, int nsplit_max, int nhg,
+                                                              int partial, int64_t rows) {
   int row, s, hg;
   decode_block(blockIdx.x, nhg, nsplit_max, rows, &row, &s, &hg);
   if (row >= rows) return;
-  const int e_begin = s * split;
-  // the wave index is made visibly uniform, so per-wave control flow is scalar
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-  const int m = lane % 16, g = lane / 16;  // operand role: entry / head m, k group g
-  // A CSA row's compressed entries are its k selection slots, known without reading
-  // its position: the indices of each wave's first tile are loaded first (that tile's
-  // rows are requested before the workgroup barrier), then the split's indices for
-  // the LDS stage, all while the position is in flight.
-  __shared__ int sidx[kIdxStage];
+  const int m = lane % 16, g = lane / 16;
+  const int t = threadIdx.x;
+  const int e_begin = s * split;
+  const int nch = (split + kChunkMax - 1) / kChunkMax;  // chunk size depends on the split only
+  const int csz = (split + nch - 1) / nch;
+  // A CSA row's compressed entries are its k selection slots, known without its
+  // position: the first chunk's slots are requested before the position, so the two
+  // memory round trips overlap.
   const int32_t* idx_row = a.idx ? a.idx + (int64_t)row * a.k : nullptr;
-  const int n_sel = idx_row ? max(0, min(split, a.k - e_begin)) : 0;
-  const int32_t* isel = idx_row + e_begin;  // this split's indices (used only when n_sel > 0)
-  const int j0 = n_sel > 0 ? isel[min(w * kTile + m, n_sel - 1)] : 0;
-  constexpr int kStagePer = kIdxStage / kThreads;
-  int stv[kStagePer];
-#pragma unroll
-  for (int q = 0; q < kStagePer; ++q)
-    stv[q] = q * kThreads < n_sel ? isel[min(q * kThreads + (int)threadIdx.x, n_sel - 1)] : 0;
+  int jn = -1;
+  if (idx_row && t < csz && e_begin + t < a.k) jn = idx_row[e_begin + t];
   const RowInfo ri = row_info(a, row);
   const int nsplit = max(1, (ri.n_tot + split - 1) / split);
-  if (s >= nsplit) return;  // workgroup-uniform: no barrier has been passed yet
+  if (s >= nsplit) return;  // workgroup-uniform, before any barrier
   const EntrySrc src = entry_src(a, ri, row, FP8 ? 1 : 2);
   const int e_end = min(ri.n_tot, e_begin + split);
-  const int n_here = e_end - e_begin;
-  const int h0 = hg * 16;  // first head of this workgroup
-  const bool sel = idx_row != nullptr && ri.n_cmp > 0;
+  const int h0 = hg * 16;
 
-  // each wave's staged tile during the loop; the combine buffer (4 x 16 x 512 floats) afterwards
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kMergeRows][kTile][kVsPitch];
-  __shared__ __attribute__((aligned(16))) float esl[kWaves][kTile];  // per-entry scale, -1 = empty
-  __shared__ float wml[kWaves][16][2];                                // per-wave (max, sum) per head
+  __shared__ ChunkLds L;
+  uint8_t* const rowb = &L.rows[0][0];  // the chunk's rows as one byte array
 
-  // the workgroup's 16 query heads, staged once in LDS (the QK B operand is read from
-  // there: registers hold the row ring instead)
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[16][kQPitch];
+  // the 16 query heads as the QK B operand: lane (head m, group g) holds columns
+  // 32kk + 8g .. +7 of head m, kk = 0 .. 15 (requested after the slots: they are
+  // first needed after the rows arrive)
   const uint16_t* qp = (const uint16_t*)a.q.data + (int64_t)ri.b * a.q.sb + (int64_t)ri.t * a.q.sr;
-  v8bf qv[16 / kWaves];
+  v8bf qb[16];
 #pragma unroll
-  for (int hh = 0; hh < 16 / kWaves; ++hh) qv[hh] = *(const v8bf*)(qp + (h0 + (16 / kWaves) * w + hh) * 512 + 8 * lane);
-
-  // This wave's tiles: w, w + 8, w + 16, ... of the split.
-  const int ntile = (n_here + kTile - 1) / kTile;
-  const int nt = ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0;
-
-  // Row loads: one instruction per entry row, lane L taking elements 8L .. 8L+7 (a
-  // whole row per instruction, the cheapest gather for the memory pipeline), so
-  // the row address is scalar.  An empty or out-of-range slot reads this query's
-  // own row instead (always a valid address) and gets scale -1.  Tile 0 takes its
-  // indices from j0, later tiles from the LDS stage.
-  const gbyte* dummy = (const gbyte*)qp;
-  Raw8<FP8> kr[kRing][kTile];  // [buffer][row]
-  float esc[kRing];            // lane m: entry m's scale (-1 = empty)
-  auto load_tile = [&](int i, int buf) {
-    const int el = (w + kWaves * i) * kTile + m;  // entry offset in the split (operand role)
-    const int e = e_begin + el;
-    const bool cmp = e < ri.n_cmp;
-    const int j = !cmp ? 0 : sel ? (i == 0 ? j0 : sidx[min(el, n_sel - 1)]) : e;
-    const int64_t wr = e - ri.n_cmp;
-    const bool live = i < nt && e < e_end && (!cmp || j >= 0);
-    const gbyte* p = !live ? dummy
-                           : cmp ? (const gbyte*)src.kv0 + (int64_t)j * src.kv_rs
-                                 : (const gbyte*)src.win0 + wr * src.raw_rs;
-    float sc = live ? 1.f : -1.f;
-    if constexpr (FP8) {
-      const float* sp = nullptr;
-      if (live) sp = cmp ? (src.kv_sc ? src.kv_sc + (int64_t)j * src.kv_ss : nullptr)
-                         : (src.win_sc ? src.win_sc + wr * src.raw_ss : nullptr);
-      const float v = *(const __attribute__((address_space(1))) float*)(sp ? sp : (const float*)qp);
-      if (sp) sc = v;
-    }
-    esc[buf] = sc;
-    const uint64_t pu = (uint64_t)(uintptr_t)p;
-#pragma unroll
-    for (int r = 0; r < kTile; ++r) {
-      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pu, r), hi = __builtin_amdgcn_readlane((uint32_t)(pu >> 32), r);
-      const gbyte* pr = (const gbyte*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-      kr[buf][r] = load_raw8<FP8>(pr, 8 * lane);
-    }
-  };
-  // the first tile's rows, before the stage and the barrier
-  static_assert(kRing == 1, "the prologue issues exactly one tile ahead");
-  load_tile(0, 0);
-#pragma unroll
-  for (int q = 0; q < kStagePer; ++q)
-    if (q * kThreads < n_sel && q * kThreads + (int)threadIdx.x < n_sel) sidx[q * kThreads + threadIdx.x] = stv[q];
-#pragma unroll
-  for (int hh = 0; hh < 16 / kWaves; ++hh) *(v8bf*)&Qs[(16 / kWaves) * w + hh][8 * lane] = qv[hh];
-  __syncthreads();  // sidx and Qs visible
+  for (int kk = 0; kk < 16; ++kk) qb[kk] = *(const v8bf*)(qp + (h0 + m) * 512 + 32 * kk + 8 * g);
+  const gbyte* dummy = (const gbyte*)qp;  // a finite 1 KB row for empty bf16 slots
 
   const float sl2 = a.scale * kLog2e;
-  float m_run = kNegInf;  // running max of head m (log2 units), same in all four rows
-  float l_part = 0.f;     // this lane's share of head m's running sum
-  v4f O[32];              // O[ct]: heads 4g + r, latent column 16ct + m
+  // running (max, sum) of heads 4g + r (the PV layout) and max of head m (the QK layout)
+  float mrun[4], lrun[4], mrun_q = kNegInf;
 #pragma unroll
-  for (int ct = 0; ct < 32; ++ct) O[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < 4; ++r) mrun[r] = kNegInf, lrun[r] = 0.f;
+  v4f O[4];  // O[nt]: heads 4g + r, latent column 64w + 16nt + m
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) O[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  typedef __attribute__((address_space(3))) v4bf lds_v4bf;
-  auto step = [&](int i, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    // stage the tile as bf16 rows in the wave's own LDS area (LDS ops of one wave run
-    // in order); an empty fp8 row is zeroed (its stand-in may hold NaN codes)
-#pragma unroll
-    for (int r = 0; r < kTile; ++r) {
-      v8bf v = widen8<FP8>(kr[buf][r]);
-      if (FP8 && __builtin_amdgcn_readlane(__float_as_uint(esc[buf]), r) == __float_as_uint(-1.f)) v = (v8bf){};
-      *(v8bf*)&Vs[w][r][8 * lane] = v;
+  for (int c0 = e_begin; c0 < e_end; c0 += csz) {
+    const int cn = min(csz, e_end - c0);  // entries of this chunk
+    const int nmt = (cn + 15) / 16;       // 16-entry tiles
+    // the chunk's slots (-1 = empty); esl marks live entries (fp8: the row scale,
+    // filled in with the row)
+    if (t < nmt * 16) {
+      const int e = c0 + t;
+      int j = -1;
+      if (t < cn) j = e >= ri.n_cmp ? 0 : idx_row ? jn : e;
+      L.sidx[t] = j;
+      L.esl[t] = j >= 0 ? 1.f : -1.f;
     }
-    if (g == 0) esl[w][m] = esc[buf];
-    // the register buffer is free: issue tile i+2's rows into it
-    __builtin_amdgcn_sched_barrier(0);
-    load_tile(i + kRing, buf);
-    __builtin_amdgcn_sched_barrier(0);
-    // S^T[entry 4g + r][head m] over the full latent width, four independent chains;
-    // A = entry m's columns 32kk + 8g .. +7 read back from the staged tile
-    v4f c4[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) c4[u] = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      __builtin_amdgcn_sched_barrier(0);  // bounded register use: four k blocks at a time
-      v8bf kv[4], qb[4];  // A: entry m's columns; B: Q^T, head m's columns 32kk + 8g .. +7
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        kv[u] = *(const v8bf*)&Vs[w][m][32 * (4 * k4 + u) + 8 * g];
-        qb[u] = *(const v8bf*)&Qs[m][32 * (4 * k4 + u) + 8 * g];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) c4[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[u], qb[u], c4[u], 0, 0, 0);
-    }
-    const v4f acc = (c4[0] + c4[1]) + (c4[2] + c4[3]);
-    const float4 ev = *(const float4*)&esl[w][4 * g];
-    const float evr[4] = {ev.x, ev.y, ev.z, ev.w};
-    float sv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = evr[r] >= 0.f ? (FP8 ? acc[r] * evr[r] : acc[r]) * sl2 : kNegInf;
-    const float tmax = lane_max4rows(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescale) != 0) {  // wave-uniform
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_part *= alpha;
-      m_run = m_new;
-      float ar[4];  // rescale factors of heads 4g + r (held by lanes 4g + r)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r);
-      // Scale in place, then pass each tile through an identity MFMA (0 * 0 + C == C):
-      // every value of O reaching the loop's merge point is then an MFMA result, so
-      // the accumulators stay in accumulation registers instead of being copied out
-      // and back on every tile.
-      // zeros made here (volatile), not hoisted out of the loop into spilled registers
-      u32x4 zu;
-      asm volatile("v_mov_b32 %0, 0" : "=v"(zu[0]));
-      zu[1] = zu[0];
-      zu[2] = zu[0];
-      zu[3] = zu[0];
-      const v8bf zero8 = __builtin_bit_cast(v8bf, zu);
-#pragma unroll
-      for (int ct = 0; ct < 32; ++ct) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) O[ct][r] *= ar[r];
-        O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zero8, zero8, O[ct], 0, 0, 0);
-        if (ct % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bounded register traffic
+    __syncthreads();
+    // rows: wave w loads rows w, w+8, ... of the chunk's tiles
+    for (int r = w; r < nmt * 16; r += kWaves) {
+      const int e = c0 + r;
+      const int j = __builtin_amdgcn_readfirstlane(L.sidx[r]);
+      const bool live = j >= 0;
+      const bool cmp = e < ri.n_cmp;
+      const gbyte* rp = !live ? dummy
+                              : cmp ? (const gbyte*)src.kv0 + (int64_t)j * src.kv_rs
+                                    : (const gbyte*)src.win0 + (int64_t)(e - ri.n_cmp) * src.raw_rs;
+      if constexpr (!FP8) {
+        // lane l fills LDS chunk l of the row with the row's chunk l ^ (r & 15)
+        __builtin_amdgcn_global_load_lds(rp + 16 * (lane ^ (r & 15)), (__attribute__((address_space(3))) void*)&L.rows[r][0],
+                                         16, 0, 0);
+      } else {
+        const float* sp = !live ? nullptr
+                                : cmp ? (src.kv_sc ? src.kv_sc + (int64_t)j * src.kv_ss : nullptr)
+                                      : (src.win_sc ? src.win_sc + (int64_t)(e - ri.n_cmp) * src.raw_ss : nullptr);
+        const u32x2 raw = live ? *(const __attribute__((address_space(1))) u32x2*)(rp + 8 * lane) : (u32x2){0u, 0u};
+        const float sc = sp ? *sp : 1.f;
+        *(v8bf*)&rowb[swz_off(r, lane)] = widen8<true>(raw);
+        if (live && lane == 0) L.esl[r] = sc;
       }
     }
-    float pv[4];
+    // the next chunk's slots, requested while this chunk's rows are in flight
+    jn = -1;
+    if (idx_row && t < csz && c0 + csz + t < min(a.k, e_end)) jn = idx_row[c0 + csz + t];
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // rows in LDS
+
+    // ---- QK: tiles w and w + 8 of the chunk; lane (head m, g) gets entries 16mt + 4g + r
+    float sv[2][4];
+    float lmax = kNegInf;
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      const int mt = w + kWaves * ti;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[ti][r] = kNegInf;
+      if (mt < nmt) {  // wave-uniform
+        v4f c4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) c4[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+        const int er = 16 * mt + m;  // the row this lane reads (A operand: entry m of the tile)
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          v8bf kv[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) kv[u] = *(const v8bf*)&rowb[swz_off(er, 4 * (4 * k4 + u) + g)];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) c4[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[u], qb[4 * k4 + u], c4[u], 0, 0, 0);
+        }
+        const v4f acc = (c4[0] + c4[1]) + (c4[2] + c4[3]);
+        const float4 ev = *(const float4*)&L.esl[16 * mt + 4 * g];
+        const float evr[4] = {ev.x, ev.y, ev.z, ev.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sv[ti][r] = evr[r] >= 0.f ? (FP8 ? acc[r] * evr[r] : acc[r]) * sl2 : kNegInf;
+          lmax = fmaxf(lmax, sv[ti][r]);
+        }
+      }
+    }
+    lmax = lane_max4rows(lmax);
+    if (g == 0) L.red_max[w][m] = lmax;
+    __syncthreads();
+    // chunk maxima, the same in every wave (fixed order)
+    float mc_q = kNegInf;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) mc_q = fmaxf(mc_q, L.red_max[v][m]);
+    const float mnew_q = fmaxf(mrun_q, mc_q);
+    mrun_q = mnew_q;
+    float lsum = 0.f;
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      const int mt = w + kWaves * ti;
+      if (mt < nmt) {
+        float pv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = mnew_q == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sv[ti][r] - mnew_q);
+          lsum += p;
+          pv[r] = FP8 ? p * L.esl[16 * mt + 4 * g + r] : p;
+        }
+        // P as hi + lo bf16 (about 16 significant bits): k = 8g .. 8g+3 hi, 8g+4 .. 8g+7 lo
+        v8bf pa;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const __bf16 hi = (__bf16)pv[r];
+          pa[r] = hi;
+          pa[4 + r] = (__bf16)(pv[r] - (float)hi);
+        }
+        L.p[mt][g][m] = __builtin_bit_cast(uint4, pa);
+      }
+    }
+    lsum = lane_sum4rows(lsum);
+    if (g == 0) L.red_sum[w][m] = lsum;
+    __syncthreads();  // P and the per-wave sums visible
+    // running statistics of heads 4g + r and the accumulator rescale
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m_run);
-      l_part += p;
-      pv[r] = FP8 ? p * evr[r] : p;
+      const int h = 4 * g + r;
+      float mc = kNegInf, ls = 0.f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) mc = fmaxf(mc, L.red_max[v][h]);
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) ls += L.red_sum[v][h];
+      const float mn = fmaxf(mrun[r], mc);
+      const float alpha = mrun[r] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mrun[r] - mn);
+      lrun[r] = lrun[r] * alpha + ls;
+      mrun[r] = mn;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) O[nt][r] *= alpha;
     }
-    // P as hi + lo bf16 terms stacked along the MFMA's k axis: lane (head m, g) holds
-    // k = 8g .. 8g+3 -> hi of entries 4g .. 4g+3 and k = 8g+4 .. 8g+7 -> lo of the same
-    // entries, so one 16x16x32 MFMA per column tile adds P_hi.V + P_lo.V for the tile.
+    // ---- PV: O[16 heads x this wave's 64 columns] += P V over the chunk's tiles
+    typedef __attribute__((address_space(3))) v4bf lds_v4bf;
+    // operands of tile ks: P (16 B per lane) and four transposed V reads (rows
+    // 16ks + 4g .. +3, columns 64w + 16nt .. +15: lane m addresses row m / 4, columns
+    // 4(m % 4) .. +3 and receives column m of the four rows); tile ks + 1's are read
+    // while tile ks's MFMAs run
+    auto pv_load = [&](int ks, v8bf& pa, v4bf (&vt)[4]) {
+      pa = __builtin_bit_cast(v8bf, L.p[ks][g][m]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int rr = 16 * ks + 4 * g + m / 4;
+        const int col = 64 * w + 16 * nt + 4 * (m % 4);
+        vt[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)&rowb[swz_off(rr, col / 8) + 2 * (col % 8)]);
+      }
+    };
     v8bf pa;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const __bf16 hi = (__bf16)pv[r];
-      pa[r] = hi;
-      pa[4 + r] = (__bf16)(pv[r] - (float)hi);
-    }
-    // V operand: lane (m, g) reads staged rows 4g .. 4g+3 at column 16ct + m (the 16 lanes of
-    // a group address 4 rows x 4 column quads) and uses the four values for both halves of k.
-#pragma unroll
-    for (int c4 = 0; c4 < 8; ++c4) {
-      __builtin_amdgcn_sched_barrier(0);
+    v4bf vt[4];
+    pv_load(0, pa, vt);
+    for (int ks = 0; ks < nmt; ++ks) {
+      const v8bf pc = pa;
       v8bf vb[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const v4bf t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_v4bf*)&Vs[w][4 * g + m / 4][16 * (4 * c4 + u) + 4 * (m % 4)]);
-        vb[u] = __builtin_shufflevector(t, t, 0, 1, 2, 3, 0, 1, 2, 3);
-      }
+      for (int nt = 0; nt < 4; ++nt) vb[nt] = __builtin_shufflevector(vt[nt], vt[nt], 0, 1, 2, 3, 0, 1, 2, 3);
+      if (ks + 1 < nmt) pv_load(ks + 1, pa, vt);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        O[4 * c4 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb[u], O[4 * c4 + u], 0, 0, 0);
+      for (int nt = 0; nt < 4; ++nt) O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pc, vb[nt], O[nt], 0, 0, 0);
     }
-  };
-  // One tile's rows are in flight while the previous one is processed; the two
-  // waves sharing a SIMD cover each other's waits.
-  for (int i = 0; i < nt; ++i) step(i, std::integral_constant<int, 0>{});
+    __syncthreads();  // the chunk's rows, P and tables are free for the next chunk
+  }
 
-  // ---- combine the eight waves: (max, sum) per head, then the accumulators
-  const float l_w = lane_sum4rows(l_part);
-  if (g == 0) {
-    wml[w][m][0] = m_run;
-    wml[w][m][1] = l_w;
-  }
-  __syncthreads();
-  float wt[4];  // this wave's weight for heads 4g + r: 2^(m_w - M), 0 where the wave saw nothing
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * g + r;
-    float M = kNegInf;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, wml[v][h][0]);
-    const float mw = wml[w][h][0];
-    wt[r] = mw == kNegInf ? 0.f : exp2f(mw - M);
-  }
-  // per-head totals over the four waves (every thread, from the table above)
-  __shared__ float hML[16][2];
-  if (threadIdx.x < 16) {
-    const int h = threadIdx.x;
-    float Mh = kNegInf, Lh = 0.f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) Mh = fmaxf(Mh, wml[v][h][0]);
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const float mv = wml[v][h][0];
-      Lh += mv == kNegInf ? 0.f : wml[v][h][1] * exp2f(mv - Mh);
-    }
-    hML[h][0] = Mh;
-    hML[h][1] = Lh;
-  }
-  // Two rounds through LDS, every sum in a fixed order: waves 4..7 write their weighted
-  // accumulators, waves 0..3 add them to their own (w + 4 onto w) in place, then every
-  // thread adds the four buffers for (column, 4-head group) items.  A buffer is
-  // [4-head group][column][4 heads]: lane (m, g) stores heads 4g .. 4g+3 of one column
-  // as 16 bytes, consecutive lanes at consecutive addresses.  A wave of 0..3 reads and
-  // then rewrites only its own lanes' entries (LDS ops of one wave run in order), so
-  // the in-place add needs no barrier and no second copy of the accumulator.
-  float* mbuf = (float*)&Vs[0][0][0];  // [4][4][512][4] floats (aliases the staging area)
-  __syncthreads();                     // all waves are done with their staged tiles
-  const int wb = w % 4;
-  if (w >= 4) {
-#pragma unroll
-    for (int ct = 0; ct < 32; ++ct)
-      *(float4*)&mbuf[((wb * 4 + g) * 512 + 16 * ct + m) * 4] =
-          make_float4(O[ct][0] * wt[0], O[ct][1] * wt[1], O[ct][2] * wt[2], O[ct][3] * wt[3]);
-  }
-  __syncthreads();
-  if (w < 4) {
-#pragma unroll
-    for (int ct = 0; ct < 32; ++ct) {
-      float4* p = (float4*)&mbuf[((wb * 4 + g) * 512 + 16 * ct + m) * 4];
-      const float4 x = *p;
-      *p = make_float4(O[ct][0] * wt[0] + x.x, O[ct][1] * wt[1] + x.y, O[ct][2] * wt[2] + x.z,
-                       O[ct][3] * wt[3] + x.w);
-    }
-  }
-  __syncthreads();
+  // ---- output: this wave's 64 columns of the 16 heads
   const int H = a.heads;
-  float* obase = partial ? (float*)a.ws + (((int64_t)row * nsplit_max + s) * H + h0) * 512
-                         : a.out + ((int64_t)row * H + h0) * 512;
-  // item -> (4-head group, column) with the column fastest: a wave reads 64 consecutive
-  // 16-byte buffer entries (no bank conflict) and each of its stores covers 64
-  // consecutive columns of one head
+  if (partial) {
+    float* obase = (float*)a.ws + (((int64_t)row * nsplit_max + s) * H + h0) * 512;
 #pragma unroll
-  for (int it = 0; it < 512 * 4 / kThreads; ++it) {
-    const int item = threadIdx.x + kThreads * it, hq = item / 512, c = item % 512;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {  // fixed order over the four buffers
-      const float4 x = *(const float4*)&mbuf[((v * 4 + hq) * 512 + c) * 4];
-      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+      for (int r = 0; r < 4; ++r) obase[(4 * g + r) * 512 + 64 * w + 16 * nt + m] = O[nt][r];
+    if (w == 0 && m == 0) {
+      float* pml = (float*)a.ws + rows * nsplit_max * H * 512 + (((int64_t)row * nsplit_max + s) * H + h0) * 2;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pml[(4 * g + r) * 2] = mrun[r];
+        pml[(4 * g + r) * 2 + 1] = lrun[r];
+      }
     }
-    const float av[4] = {acc.x, acc.y, acc.z, acc.w};
+  } else {
+    float* obase = a.out + ((int64_t)row * H + h0) * 512;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float L = hML[4 * hq + r][1];
-      const float fs = partial ? 1.f : (L > 0.f ? __fdiv_rn(1.0f, L) : 0.f);
-      if (partial)
-        obase[(4 * hq + r) * 512 + c] = av[r];  // kept in this XCD's L2 for the split merge
-      else
-        __builtin_nontemporal_store(av[r] * fs, &obase[(4 * hq + r) * 512 + c]);  // streamed: read once, elsewhere
+      const float fs = lrun[r] > 0.f ? __fdiv_rn(1.0f, lrun[r]) : 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        __builtin_nontemporal_store(O[nt][r] * fs, &obase[(4 * g + r) * 512 + 64 * w + 16 * nt + m]);
     }
-  }
-  if (threadIdx.x < 16) {
-    const int hglob = h0 + threadIdx.x;
-    const float Mh = hML[threadIdx.x][0], Lh = hML[threadIdx.x][1];
-    if (partial) {
-      float* pml = (float*)a.ws + rows * nsplit_max * H * 512 + (((int64_t)row * nsplit_max + s) * H + hglob) * 2;
-      pml[0] = Mh;
-      pml[1] = Lh;
-    } else if (a.lse) {
-      a.lse[(int64_t)row * H + hglob] = Lh > 0.f ? (Mh + log2f(Lh)) * kLn2 : kNegInf;
+    if (a.lse && w == 0 && m == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        a.lse[(int64_t)row * H + h0 + 4 * g + r] = lrun[r] > 0.f ? (mrun[r] + log2f(lrun[r])) * kLn2 : kNegInf;
     }
   }
 }
@@ -627,10 +572,10 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
   const int64_t pairs = rows * nsplit_max;
   const int64_t blocks = rows >= 8 ? (rows + 7) / 8 * 8 * nsplit_max * nhg : (pairs + 7) / 8 * 8 * nhg;
   if (a.kv.dtype == CSA_FP8_E4M3)
-    hipLaunchKernelGGL(attn_wave_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, split, nsplit_max,
+    hipLaunchKernelGGL(attn_chunk_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, split, nsplit_max,
                        nhg, partial, rows);
   else
-    hipLaunchKernelGGL(attn_wave_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, split, nsplit_max,
+    hipLaunchKernelGGL(attn_chunk_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, split, nsplit_max,
                        nhg, partial, rows);
   if (partial)
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)rows, a.heads), dim3(128), 0, s, a, split, nsplit_max, rows);
@@ -641,14 +586,14 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
 
 // Splits depend only on the call shape (decode or not) and the entry capacity,
 // never on the batch, so each sequence's arithmetic is batch-invariant.  Decode
-// cuts a row's list into eight splits of whole 16-entry tiles, at least one tile
-// per wave (8 rows x 4 head groups x 8 splits fill the 256 CUs at batch 8); calls
-// with many queries per sequence keep each list whole.
+// cuts a row's list into eight splits of whole 16-entry tiles, at least eight
+// tiles each (8 rows x 4 head groups x 8 splits fill the 256 CUs at batch 8);
+// calls with many queries per sequence keep each list whole.
 int attn_split_size(int tq, int n_entries_max) {
   const int n = max(n_entries_max, 1);
-  if (tq != 1) return min(n, kIdxStage);
+  if (tq != 1) return min(n, kAttnMaxSplitEntries);
   const int eighth = ((n + 7) / 8 + kTile - 1) / kTile * kTile;
-  return min(kIdxStage, max(kWaves * kTile, eighth));  // at least a tile per wave
+  return min(kAttnMaxSplitEntries, max(kWaves * kTile, eighth));
 }
 
 size_t attn_workspace_bytes(int64_t rows, int heads, int dim, int n_entries_max, int tq) {
