@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
-SOURCES = ["abi.cpp", "compress.hip", "index.hip", "topk.hip", "attn.hip", "diag.hip"]
+SOURCES = ["abi.cpp", "compress.hip", "index.hip", "topk.hip", "attn.hip", "project.hip", "diag.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [
@@ -25,9 +25,14 @@ COMMON = [
 ]
 
 
+# per-source extras: the attention kernels take their prologue scalars as leading
+# arguments, preloaded into scalar registers at launch
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -52,16 +52,22 @@ struct RowInfo {
   int b, t, pos, w0, n_cmp, n_tot;
 };
 
-__device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int row) {
+// The row's position and entry counts (row is workgroup-uniform in every caller).
+__device__ __forceinline__ RowInfo row_info(const int32_t* q_pos, bool csa, int k, int tq, int window, int m_hc,
+                                            int row) {
   RowInfo r;
-  r.b = row / a.tq;
-  r.t = row % a.tq;
-  r.pos = __builtin_amdgcn_readfirstlane(a.q_pos[row]);  // row is workgroup-uniform in every caller
-  r.w0 = max(0, r.pos - a.window + 1);
-  const int n_win = a.window > 0 ? r.pos - r.w0 + 1 : 0;
-  r.n_cmp = a.idx ? a.k : visible_blocks(r.pos, a.m_hc);
+  r.b = row / tq;
+  r.t = row % tq;
+  r.pos = __builtin_amdgcn_readfirstlane(q_pos[row]);
+  r.w0 = max(0, r.pos - window + 1);
+  const int n_win = window > 0 ? r.pos - r.w0 + 1 : 0;
+  r.n_cmp = csa ? k : visible_blocks(r.pos, m_hc);
   r.n_tot = r.n_cmp + n_win;
   return r;
+}
+
+__device__ __forceinline__ RowInfo row_info(const AttnArgs& a, int row) {
+  return row_info(a.q_pos, a.idx != nullptr, a.k, a.tq, a.window, a.m_hc, row);
 }
 
 // Where a query row's entries live: base addresses and row pitches resolved once
@@ -78,9 +84,10 @@ struct EntrySrc {
 };
 
 // eb: bytes per element of the caches (a compile-time constant at every call site)
-__device__ __forceinline__ EntrySrc entry_src(const AttnArgs& a, const RowInfo& r, int row, int eb) {
+// rb: raw_base[r.b], the absolute position of the sequence's raw row 0.
+__device__ __forceinline__ EntrySrc entry_src(const AttnArgs& a, const RowInfo& r, int row, int eb, int rb) {
   EntrySrc s;
-  const int64_t rr0 = (int64_t)r.w0 - __builtin_amdgcn_readfirstlane(a.raw_base[r.b]);  // raw row of the first window entry
+  const int64_t rr0 = (int64_t)r.w0 - rb;  // raw row of the first window entry
   s.kv0 = (const uint8_t*)a.kv.data + (int64_t)r.b * a.kv.sb * eb;
   s.win0 = (const uint8_t*)a.raw.data + ((int64_t)r.b * a.raw.sb + rr0 * a.raw.sr) * eb;
   s.kv_rs = a.kv.sr * eb;
@@ -173,25 +180,33 @@ __device__ __forceinline__ float lane_sum4rows(float x) {  // fixed-order sum ov
   return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
-// Chunk of a split's entries resident in LDS: kChunkMax rows of 512 bf16 (1 KB),
-// 16-byte chunk c of row r stored at position c ^ (r & 15) so that the 16 rows a
-// QK operand read touches, and the 4 rows of a transposed read, fall on distinct
-// banks.
-constexpr int kChunkMax = 144;               // entries per chunk (9 tiles of 16)
-constexpr int kChunkTiles = kChunkMax / 16;  // 9
+// Chunk of a split's entries resident in LDS: up to kChunkMax rows of 512 bf16 (1
+// KB), 16-byte chunk c of row r stored at position c ^ swz(r) (swz(r) = r mod 16),
+// so that the 16 consecutive rows of a QK operand read fall on distinct banks.  The last 16-entry tile of a full chunk reaches 8 rows past the buffer (into
+// the region after it): those entries are masked out of QK, and PV zeroes what it
+// reads there.
+constexpr int kChunkMax = 136;                    // entries per chunk
+constexpr int kChunkTiles = (kChunkMax + 15) / 16;  // 9
 constexpr int kRowBytes = 1024;
 
 struct ChunkLds {
   __attribute__((aligned(16))) uint8_t rows[kChunkMax][kRowBytes];
-  // P as the PV A operand: [tile][k group g][head m] -> 4 bf16 hi then 4 bf16 lo of
-  // entries 16*tile + 4g .. +3
-  __attribute__((aligned(16))) uint4 p[kChunkTiles][4][16];
-  float esl[kChunkMax];    // entry scale (fp8 row scale, else 1); -1 = empty slot
-  int32_t sidx[kChunkMax];  // CSA selection slots of the chunk
-  float red_max[kWaves][16], red_sum[kWaves][16];
+  union {
+    // the 16 query heads, staged once (same swizzle as the rows) and read into
+    // registers before P is first written
+    __attribute__((aligned(16))) uint8_t q[16][kRowBytes];
+    // P as the PV A operand: [tile][k group g][head m] -> 4 bf16 hi then 4 bf16 lo
+    // of entries 16*tile + 4g .. +3
+    __attribute__((aligned(16))) uint4 p[kChunkTiles][4][16];
+  };
+  float esl[kChunkTiles * 16];     // entry scale (fp8 row scale, else 1); -1 = empty slot
+  int32_t sidx[kChunkTiles * 16];  // slots of the chunk
+  __attribute__((aligned(16))) float red_max[kWaves][16];
+  __attribute__((aligned(16))) float red_sum[kWaves][16];
 };
 
-__device__ __forceinline__ int swz_off(int r, int chunk16) { return r * kRowBytes + ((chunk16 ^ (r & 15)) << 4); }
+__device__ __forceinline__ int swz(int r) { return r & 15; }
+__device__ __forceinline__ int swz_off(int r, int chunk16) { return r * kRowBytes + ((chunk16 ^ swz(r)) << 4); }
 
 // One workgroup: one query row, 16 heads, one split of its entry list, processed in
 // chunks of at most kChunkMax entries.  For each chunk:
@@ -205,9 +220,15 @@ __device__ __forceinline__ int swz_off(int r, int chunk16) { return r * kRowByte
 //  * PV with the latent columns split over the waves (wave w owns columns
 //    64w .. 64w+63 of all 16 heads): the accumulator of a wave is final for its
 //    columns, so the waves never combine accumulators.
+// The scalars the prologue depends on come first in the argument list: they are
+// preloaded into scalar registers at launch (the rest of the arguments is read from
+// memory, one round trip that overlaps the position and slot loads).
 template <bool FP8>
-__global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a, int split, int nsplit_max, int nhg,
-                                                              int partial, int64_t rows) {
+__global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __restrict__ q_pos,
+                                                              const int32_t* __restrict__ idx,
+                                                              const int32_t* __restrict__ raw_base, int k, int tq,
+                                                              int window, int m_hc, int split, int nsplit_max,
+                                                              int nhg, int rows, AttnArgs a) {
   int row, s, hg;
   decode_block(blockIdx.x, nhg, nsplit_max, rows, &row, &s, &hg);
   if (row >= rows) return;
@@ -220,13 +241,17 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a, int sp
   // A CSA row's compressed entries are its k selection slots, known without its
   // position: the first chunk's slots are requested before the position, so the two
   // memory round trips overlap.
-  const int32_t* idx_row = a.idx ? a.idx + (int64_t)row * a.k : nullptr;
+  const int32_t* idx_row = idx ? idx + (int64_t)row * k : nullptr;
   int jn = -1;
-  if (idx_row && t < csz && e_begin + t < a.k) jn = idx_row[e_begin + t];
-  const RowInfo ri = row_info(a, row);
+  if (idx_row && t < csz && e_begin + t < k) jn = idx_row[e_begin + t];
+  const int rb = __builtin_amdgcn_readfirstlane(raw_base[row / tq]);
+  const RowInfo ri = row_info(q_pos, idx != nullptr, k, tq, window, m_hc, row);
+  // (computed before the early exit below: its argument reads then join the
+  // position's round trip)
+  const EntrySrc src = entry_src(a, ri, row, FP8 ? 1 : 2, rb);
+  const int partial = nsplit_max > 1;
   const int nsplit = max(1, (ri.n_tot + split - 1) / split);
   if (s >= nsplit) return;  // workgroup-uniform, before any barrier
-  const EntrySrc src = entry_src(a, ri, row, FP8 ? 1 : 2);
   const int e_end = min(ri.n_tot, e_begin + split);
   const int h0 = hg * 16;
 
@@ -234,12 +259,9 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a, int sp
   uint8_t* const rowb = &L.rows[0][0];  // the chunk's rows as one byte array
 
   // the 16 query heads as the QK B operand: lane (head m, group g) holds columns
-  // 32kk + 8g .. +7 of head m, kk = 0 .. 15 (requested after the slots: they are
-  // first needed after the rows arrive)
+  // 32kk + 8g .. +7 of head m, kk = 0 .. 15 (requested after the first chunk's rows)
   const uint16_t* qp = (const uint16_t*)a.q.data + (int64_t)ri.b * a.q.sb + (int64_t)ri.t * a.q.sr;
   v8bf qb[16];
-#pragma unroll
-  for (int kk = 0; kk < 16; ++kk) qb[kk] = *(const v8bf*)(qp + (h0 + m) * 512 + 32 * kk + 8 * g);
   const gbyte* dummy = (const gbyte*)qp;  // a finite 1 KB row for empty bf16 slots
 
   const float sl2 = a.scale * kLog2e;
@@ -264,18 +286,21 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a, int sp
       L.esl[t] = j >= 0 ? 1.f : -1.f;
     }
     __syncthreads();
-    // rows: wave w loads rows w, w+8, ... of the chunk's tiles
-    for (int r = w; r < nmt * 16; r += kWaves) {
+    // rows: wave w loads rows w, w+8, ... of the chunk's tiles (lane i holds the
+    // slot of the wave's i-th row, so no row waits on an LDS read)
+    const int nrows = min(nmt * 16, kChunkMax);
+    const int jw = lane < (nrows - w + kWaves - 1) / kWaves ? L.sidx[w + kWaves * lane] : -1;
+    for (int r = w, ri8 = 0; r < nrows; r += kWaves, ++ri8) {
       const int e = c0 + r;
-      const int j = __builtin_amdgcn_readfirstlane(L.sidx[r]);
+      const int j = __builtin_amdgcn_readlane(jw, ri8);
       const bool live = j >= 0;
       const bool cmp = e < ri.n_cmp;
       const gbyte* rp = !live ? dummy
                               : cmp ? (const gbyte*)src.kv0 + (int64_t)j * src.kv_rs
                                     : (const gbyte*)src.win0 + (int64_t)(e - ri.n_cmp) * src.raw_rs;
       if constexpr (!FP8) {
-        // lane l fills LDS chunk l of the row with the row's chunk l ^ (r & 15)
-        __builtin_amdgcn_global_load_lds(rp + 16 * (lane ^ (r & 15)), (__attribute__((address_space(3))) void*)&L.rows[r][0],
+        // lane l fills LDS chunk l of the row with the row's chunk l ^ swz(r)
+        __builtin_amdgcn_global_load_lds(rp + 16 * (lane ^ swz(r)), (__attribute__((address_space(3))) void*)&L.rows[r][0],
                                          16, 0, 0);
       } else {
         const float* sp = !live ? nullptr
@@ -287,11 +312,22 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a, int sp
         if (live && lane == 0) L.esl[r] = sc;
       }
     }
+    if (c0 == e_begin) {  // the 16 query heads to LDS, wave w taking heads 2w, 2w + 1
+#pragma unroll
+      for (int hh = 2 * w; hh < 2 * w + 2; ++hh)
+        __builtin_amdgcn_global_load_lds((const gbyte*)(qp + (h0 + hh) * 512) + 16 * (lane ^ swz(hh)),
+                                         (__attribute__((address_space(3))) void*)&L.q[hh][0], 16, 0, 0);
+    }
     // the next chunk's slots, requested while this chunk's rows are in flight
     jn = -1;
-    if (idx_row && t < csz && c0 + csz + t < min(a.k, e_end)) jn = idx_row[c0 + csz + t];
+    if (idx_row && t < csz && c0 + csz + t < min(k, e_end)) jn = idx_row[c0 + csz + t];
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // rows in LDS
+    __syncthreads();  // rows (and the first time, the query heads) in LDS
+    if (c0 == e_begin) {
+      const uint8_t* qs = &L.q[0][0];
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) qb[kk] = *(const v8bf*)&qs[swz_off(m, 4 * kk + g)];
+    }
 
     // ---- QK: tiles w and w + 8 of the chunk; lane (head m, g) gets entries 16mt + 4g + r
     float sv[2][4];
@@ -360,14 +396,17 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a, int sp
     if (g == 0) L.red_sum[w][m] = lsum;
     __syncthreads();  // P and the per-wave sums visible
     // running statistics of heads 4g + r and the accumulator rescale
+    float mcv[4] = {kNegInf, kNegInf, kNegInf, kNegInf}, lsv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {  // heads 4g .. 4g+3: one 16-byte read per table and wave
+      const float4 mx = *(const float4*)&L.red_max[v][4 * g];
+      const float4 sm = *(const float4*)&L.red_sum[v][4 * g];
+      mcv[0] = fmaxf(mcv[0], mx.x), mcv[1] = fmaxf(mcv[1], mx.y), mcv[2] = fmaxf(mcv[2], mx.z), mcv[3] = fmaxf(mcv[3], mx.w);
+      lsv[0] += sm.x, lsv[1] += sm.y, lsv[2] += sm.z, lsv[3] += sm.w;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int h = 4 * g + r;
-      float mc = kNegInf, ls = 0.f;
-#pragma unroll
-      for (int v = 0; v < kWaves; ++v) mc = fmaxf(mc, L.red_max[v][h]);
-#pragma unroll
-      for (int v = 0; v < kWaves; ++v) ls += L.red_sum[v][h];
+      const float mc = mcv[r], ls = lsv[r];
       const float mn = fmaxf(mrun[r], mc);
       const float alpha = mrun[r] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mrun[r] - mn);
       lrun[r] = lrun[r] * alpha + ls;
@@ -378,29 +417,39 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a, int sp
     // ---- PV: O[16 heads x this wave's 64 columns] += P V over the chunk's tiles
     typedef __attribute__((address_space(3))) v4bf lds_v4bf;
     // operands of tile ks: P (16 B per lane) and four transposed V reads (rows
-    // 16ks + 4g .. +3, columns 64w + 16nt .. +15: lane m addresses row m / 4, columns
-    // 4(m % 4) .. +3 and receives column m of the four rows); tile ks + 1's are read
-    // while tile ks's MFMAs run
-    auto pv_load = [&](int ks, v8bf& pa, v4bf (&vt)[4]) {
+    // 16ks + 4g .. +3, columns 64w + 16nt .. +15: lane m addresses row m / 4,
+    // columns 4(m % 4) .. +3 and receives column m of the four rows); two operand
+    // sets alternate, so tile ks + 1's reads are in flight during tile ks's MFMAs
+    const auto pv_load = [&](int ks, v8bf& pa, v4bf (&tv)[4]) {
       pa = __builtin_bit_cast(v8bf, L.p[ks][g][m]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const int rr = 16 * ks + 4 * g + m / 4;
         const int col = 64 * w + 16 * nt + 4 * (m % 4);
-        vt[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)&rowb[swz_off(rr, col / 8) + 2 * (col % 8)]);
+        tv[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_v4bf*)&rowb[swz_off(16 * ks + 4 * g + m / 4, col / 8) + 2 * (col % 8)]);
       }
     };
-    v8bf pa;
-    v4bf vt[4];
-    pv_load(0, pa, vt);
-    for (int ks = 0; ks < nmt; ++ks) {
-      const v8bf pc = pa;
-      v8bf vb[4];
+    const auto pv_mfma = [&](int ks, const v8bf& pa, const v4bf (&tv)[4]) {
+      const bool past = 16 * ks + 4 * g + m / 4 >= kChunkMax;  // the lane read past the buffer: no entry there
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) vb[nt] = __builtin_shufflevector(vt[nt], vt[nt], 0, 1, 2, 3, 0, 1, 2, 3);
-      if (ks + 1 < nmt) pv_load(ks + 1, pa, vt);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pc, vb[nt], O[nt], 0, 0, 0);
+      for (int nt = 0; nt < 4; ++nt) {
+        const v4bf t = past ? (v4bf){} : tv[nt];
+        const v8bf vb = __builtin_shufflevector(t, t, 0, 1, 2, 3, 0, 1, 2, 3);
+        O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, O[nt], 0, 0, 0);
+      }
+    };
+    {
+      v8bf pa0, pa1;
+      v4bf tv0[4], tv1[4];
+      pv_load(0, pa0, tv0);
+      int ks = 0;
+      for (; ks + 1 < nmt; ks += 2) {
+        pv_load(ks + 1, pa1, tv1);
+        pv_mfma(ks, pa0, tv0);
+        if (ks + 2 < nmt) pv_load(ks + 2, pa0, tv0);
+        pv_mfma(ks + 1, pa1, tv1);
+      }
+      if (ks < nmt) pv_mfma(ks, pa0, tv0);
     }
     __syncthreads();  // the chunk's rows, P and tables are free for the next chunk
   }
@@ -414,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a, int sp
 #pragma unroll
       for (int r = 0; r < 4; ++r) obase[(4 * g + r) * 512 + 64 * w + 16 * nt + m] = O[nt][r];
     if (w == 0 && m == 0) {
-      float* pml = (float*)a.ws + rows * nsplit_max * H * 512 + (((int64_t)row * nsplit_max + s) * H + h0) * 2;
+      float* pml = (float*)a.ws + (int64_t)rows * nsplit_max * H * 512 + (((int64_t)row * nsplit_max + s) * H + h0) * 2;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         pml[(4 * g + r) * 2] = mrun[r];
@@ -517,7 +566,7 @@ constexpr int kPlainMaxEntries = 8192;
 __global__ __launch_bounds__(kPlainThreads) void attn_plain_kernel(AttnArgs a) {
   const int row = blockIdx.x, h = blockIdx.y;
   const RowInfo ri = row_info(a, row);
-  const EntrySrc src = entry_src(a, ri, row, 4);
+  const EntrySrc src = entry_src(a, ri, row, 4, a.raw_base[ri.b]);
   __shared__ float logit[kPlainMaxEntries];
   __shared__ float qs[512];
   __shared__ float red[kPlainThreads / kWave];
@@ -572,11 +621,11 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
   const int64_t pairs = rows * nsplit_max;
   const int64_t blocks = rows >= 8 ? (rows + 7) / 8 * 8 * nsplit_max * nhg : (pairs + 7) / 8 * 8 * nhg;
   if (a.kv.dtype == CSA_FP8_E4M3)
-    hipLaunchKernelGGL(attn_chunk_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, split, nsplit_max,
-                       nhg, partial, rows);
+    hipLaunchKernelGGL(attn_chunk_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a.q_pos, a.idx, a.raw_base,
+                       a.k, a.tq, a.window, a.m_hc, split, nsplit_max, nhg, (int)rows, a);
   else
-    hipLaunchKernelGGL(attn_chunk_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, split, nsplit_max,
-                       nhg, partial, rows);
+    hipLaunchKernelGGL(attn_chunk_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a.q_pos, a.idx, a.raw_base,
+                       a.k, a.tq, a.window, a.m_hc, split, nsplit_max, nhg, (int)rows, a);
   if (partial)
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)rows, a.heads), dim3(128), 0, s, a, split, nsplit_max, rows);
   return hipGetLastError();
