@@ -143,6 +143,34 @@ typedef struct csa_compress_job {
 csa_status csa_compress_jobs(const csa_compress_job* jobs, int32_t n_jobs, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Indexer query from the query hidden state (the step before (b)): for every
+ * query row, c = W_dq h (rank r), q_idx = reshape(W_uq c, [n_idx_heads,
+ * idx_dim]) and w = W_w h -- the indexer scores with low-rank projections of
+ * the query hidden state h_t (b-lab.team summary of DeepSeek-V4, Core
+ * Methodological Innovations 1, CSA bullet).  No norm or activation between.
+ *   h      [batch, tq, d_model] BF16 (stride_b, stride_row in elements).
+ *   w_dq   [rank, d_model], w_uq [n_idx_heads * idx_dim, rank] and w_w
+ *          [n_idx_heads, d_model]: BF16, row pitch stride_row (stride_b unused).
+ *   q_idx  [batch, tq, n_idx_heads, idx_dim] F32 or BF16 (stride_b, stride_row in
+ *          elements; a row's n_idx_heads * idx_dim values contiguous).
+ *   w      [batch, tq, n_idx_heads] float, contiguous.
+ *   ws     at least csa_index_query_workspace_size(...) bytes; contents on entry
+ *          do not matter.
+ * Arithmetic: bf16 products summed in fp32, in chunks of 128 along d_model (rank)
+ * added in a fixed order, so results do not depend on batch or tq; c is rounded
+ * to bf16 before the second projection.  d_model and rank must be multiples of
+ * 32 (at most 65536), n_idx_heads * idx_dim at most 65536, every row pitch a
+ * multiple of 8 elements and every pointer 16-byte aligned (CSA_ERR_SHAPE
+ * otherwise).
+ * ------------------------------------------------------------------------- */
+csa_status csa_index_query(const csa_tensor* h, const csa_tensor* w_dq, const csa_tensor* w_uq,
+                           const csa_tensor* w_w, int32_t batch, int32_t tq, int32_t d_model, int32_t rank,
+                           int32_t n_idx_heads, int32_t idx_dim, const csa_tensor* q_idx, float* w, void* ws,
+                           size_t ws_bytes, void* stream);
+size_t csa_index_query_workspace_size(int32_t batch, int32_t tq, int32_t d_model, int32_t rank,
+                                      int32_t n_idx_heads, int32_t idx_dim);
+
+/* ---------------------------------------------------------------------------
  * (b) Lightning-indexer scores.  The indexer scores every compressed block
  * from low-rank projections of the query's hidden state, and its scores pick
  * the k blocks to attend to (b-lab.team summary, Core Methodological

@@ -104,6 +104,10 @@ _c = {
     "hca_attn": _proto("hca_attn", _I32, _TP, _TP, _I32, _I32, _TP, _P, _I32, _P, _I32, _I32, _I32, _I32, _F, _P,
                        _P, _P, _SZ, _P),
     "csa_attn_workspace_size": _proto("csa_attn_workspace_size", _SZ, _I32, _I32, _I32, _I32, _I32),
+    "csa_index_query": _proto("csa_index_query", _I32, _TP, _TP, _TP, _TP, _I32, _I32, _I32, _I32, _I32, _I32, _TP,
+                              _P, _P, _SZ, _P),
+    "csa_index_query_workspace_size": _proto("csa_index_query_workspace_size", _SZ, _I32, _I32, _I32, _I32, _I32,
+                                             _I32),
     "csa_sparse_attn_noalloc": _proto("csa_sparse_attn_noalloc", _I32, _TP, _TP, _P, _I32, _TP, _P, _I32, _P, _I32,
                                       _I32, _I32, _I32, _F, _P, _P, _P),
     "csa_quantize_mxfp4": _proto("csa_quantize_mxfp4", _I32, _P, _I64, _I32, _P, _P, _P),
@@ -239,6 +243,17 @@ def csa_sparse_attn(q, kv_cmp, idx, k, kv_raw, raw_base, window, q_pos, batch, t
     _check(_c["csa_sparse_attn"](ctypes.byref(q), ctypes.byref(kv_cmp), _ptr(idx), k, ctypes.byref(kv_raw),
                                  _ptr(raw_base), window, _ptr(q_pos), batch, tq, heads, dim, scale, _ptr(out),
                                  _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def csa_index_query(h, w_dq, w_uq, w_w, batch, tq, d_model, rank, n_idx_heads, idx_dim, q_idx, w, ws, ws_bytes,
+                    stream=None):
+    _check(_c["csa_index_query"](ctypes.byref(h), ctypes.byref(w_dq), ctypes.byref(w_uq), ctypes.byref(w_w), batch,
+                                 tq, d_model, rank, n_idx_heads, idx_dim, ctypes.byref(q_idx), _ptr(w), _ptr(ws),
+                                 ws_bytes, _stream(stream)))
+
+
+def csa_index_query_workspace_size(batch, tq, d_model, rank, n_idx_heads, idx_dim):
+    return _c["csa_index_query_workspace_size"](batch, tq, d_model, rank, n_idx_heads, idx_dim)
 
 
 def csa_sparse_attn_noalloc(q, kv_cmp, idx, k, kv_raw, raw_base, window, q_pos, batch, tq, heads, dim, scale, out,

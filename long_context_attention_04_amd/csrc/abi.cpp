@@ -326,6 +326,73 @@ csa_status csa_index_topk(const csa_tensor* q_idx, const float* w, const csa_ten
                              ws_bytes, 3, stream);
 }
 
+static bool proj_shape_ok(int32_t batch, int32_t tq, int32_t d_model, int32_t rank, int32_t n_idx_heads,
+                          int32_t idx_dim) {
+  return batch >= 0 && tq >= 0 && d_model >= 32 && d_model <= 65536 && d_model % 32 == 0 && rank >= 32 &&
+         rank <= 65536 && rank % 32 == 0 && n_idx_heads >= 1 && idx_dim >= 1 &&
+         (int64_t)n_idx_heads * idx_dim <= 65536;
+}
+
+size_t csa_index_query_workspace_size(int32_t batch, int32_t tq, int32_t d_model, int32_t rank,
+                                      int32_t n_idx_heads, int32_t idx_dim) {
+  if (!proj_shape_ok(batch, tq, d_model, rank, n_idx_heads, idx_dim)) return 0;
+  return csa::index_query_workspace_bytes((int64_t)batch * tq, d_model, rank, n_idx_heads, idx_dim);
+}
+
+csa_status csa_index_query(const csa_tensor* h, const csa_tensor* w_dq, const csa_tensor* w_uq,
+                           const csa_tensor* w_w, int32_t batch, int32_t tq, int32_t d_model, int32_t rank,
+                           int32_t n_idx_heads, int32_t idx_dim, const csa_tensor* q_idx, float* w, void* ws,
+                           size_t ws_bytes, void* stream) {
+  csa_status st;
+  if ((st = check_tensor(h, "h")) != CSA_OK) return st;
+  if ((st = check_tensor(w_dq, "w_dq")) != CSA_OK) return st;
+  if ((st = check_tensor(w_uq, "w_uq")) != CSA_OK) return st;
+  if ((st = check_tensor(w_w, "w_w")) != CSA_OK) return st;
+  if ((st = check_tensor(q_idx, "q_idx")) != CSA_OK) return st;
+  REQUIRE(w != nullptr, CSA_ERR_NULL, "w is NULL");
+  REQUIRE(h->dtype == CSA_BF16 && w_dq->dtype == CSA_BF16 && w_uq->dtype == CSA_BF16 && w_w->dtype == CSA_BF16,
+          CSA_ERR_DTYPE, "h and the projection weights must be BF16");
+  REQUIRE(q_idx->dtype == CSA_F32 || q_idx->dtype == CSA_BF16, CSA_ERR_DTYPE, "q_idx must be F32 or BF16");
+  REQUIRE(proj_shape_ok(batch, tq, d_model, rank, n_idx_heads, idx_dim), CSA_ERR_SHAPE,
+          "need batch, tq >= 0, d_model and rank multiples of 32 in [32, 65536], n_idx_heads * idx_dim in "
+          "[1, 65536] (got d_model=%d rank=%d heads=%d dim=%d)", d_model, rank, n_idx_heads, idx_dim);
+  const auto aligned = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+  REQUIRE(aligned(h->data) && aligned(w_dq->data) && aligned(w_uq->data) && aligned(w_w->data), CSA_ERR_SHAPE,
+          "h and the weights must be 16-byte aligned");
+  REQUIRE(h->stride_b % 8 == 0 && h->stride_row % 8 == 0 && w_dq->stride_row % 8 == 0 &&
+              w_uq->stride_row % 8 == 0 && w_w->stride_row % 8 == 0,
+          CSA_ERR_SHAPE, "row pitches of h and the weights must be multiples of 8 elements");
+  REQUIRE(w_dq->stride_row >= d_model && w_w->stride_row >= d_model && w_uq->stride_row >= rank, CSA_ERR_SHAPE,
+          "a weight's row pitch is shorter than its row");
+  REQUIRE(tq <= 1 || h->stride_row >= d_model, CSA_ERR_SHAPE, "h's row pitch is shorter than d_model");
+  const size_t need = csa::index_query_workspace_bytes((int64_t)batch * tq, d_model, rank, n_idx_heads, idx_dim);
+  REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "csa_index_query needs %zu workspace bytes, got %zu",
+          need, ws_bytes);
+  csa::IndexQueryArgs a{};
+  a.h = h->data;
+  a.h_sb = h->stride_b;
+  a.h_sr = h->stride_row;
+  a.w_dq = w_dq->data;
+  a.w_uq = w_uq->data;
+  a.w_w = w_w->data;
+  a.ld_dq = w_dq->stride_row;
+  a.ld_uq = w_uq->stride_row;
+  a.ld_w = w_w->stride_row;
+  a.batch = batch;
+  a.tq = tq;
+  a.d_model = d_model;
+  a.rank = rank;
+  a.n_idx_heads = n_idx_heads;
+  a.idx_dim = idx_dim;
+  a.q_out = q_idx->data;
+  a.q_sb = q_idx->stride_b;
+  a.q_sr = q_idx->stride_row;
+  a.q_bf16 = q_idx->dtype == CSA_BF16;
+  a.w_out = w;
+  a.ws = ws;
+  return from_hip(csa::launch_index_query(a, (hipStream_t)stream), "csa_index_query launch");
+}
+
 size_t csa_attn_workspace_size(int32_t batch, int32_t tq, int32_t heads, int32_t dim, int32_t n_entries_max) {
   if (batch < 0 || tq < 0 || heads < 1 || dim < 1 || n_entries_max < 0) return 0;
   return csa::attn_workspace_bytes((int64_t)batch * tq, heads, dim, n_entries_max, tq);

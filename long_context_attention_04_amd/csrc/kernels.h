@@ -145,6 +145,25 @@ int attn_split_size(int tq, int n_entries_max);
 size_t attn_workspace_bytes(int64_t rows, int heads, int dim, int n_entries_max, int tq);
 hipError_t launch_attention(const AttnArgs& a, int n_entries_max, hipStream_t s);
 
+// ---------------------------------------------------------------- indexer query
+// [c | w] = h . [W_dq ; W_w]^T, then q_I = bf16(c) . W_uq^T (project.hip).
+struct IndexQueryArgs {
+  const void* h;  // bf16 [batch, tq, d_model] (element strides h_sb, h_sr)
+  int64_t h_sb, h_sr;
+  const void* w_dq;  // bf16 [rank, d_model], row pitch ld_dq
+  const void* w_uq;  // bf16 [H_I * d_I, rank], row pitch ld_uq
+  const void* w_w;   // bf16 [H_I, d_model], row pitch ld_w
+  int64_t ld_dq, ld_uq, ld_w;
+  int batch, tq, d_model, rank, n_idx_heads, idx_dim;
+  void* q_out;  // f32 or bf16 [batch, tq, H_I * d_I] (element strides q_sb, q_sr)
+  int64_t q_sb, q_sr;
+  int q_bf16;
+  float* w_out;  // [batch, tq, H_I]
+  void* ws;
+};
+size_t index_query_workspace_bytes(int64_t rows, int d_model, int rank, int n_idx_heads, int idx_dim);
+hipError_t launch_index_query(const IndexQueryArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- measurement
 constexpr int kStreamReadBlocks = 2048;  // workgroups of the streaming-read probe (one sink word each)
 hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t s);

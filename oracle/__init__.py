@@ -11,6 +11,7 @@ from .csa import (  # noqa: F401
     csa_layer,
     csa_sparse_attn,
     hca_attn,
+    index_query,
     index_scores,
     merge_weights,
     topk,

@@ -246,6 +246,32 @@ def test_attention_rejects_and_workspace():
     expect(E_UNSUP, hca(ncap=131072), match="entries per query")
 
 
+# ---------------------------------------------------------------------------- indexer query
+
+
+def test_index_query_rejects():
+    need = csa.csa_index_query_workspace_size(8, 1, 4096, 1024, 8, 64)
+    assert need > 0
+    assert csa.csa_index_query_workspace_size(8, 1, 4004, 1024, 8, 64) == 0  # d_model not a multiple of 32
+    Wb = T(csa.BF16, sb=0, sr=4096)
+
+    def call(h=T(csa.BF16, sr=4096), wdq=Wb, wuq=T(csa.BF16, sb=0, sr=1024), ww=Wb, d=4096, r=1024, q=T(csa.F32),
+             w=P, ws=P, wsb=need):
+        return lambda stream: csa.csa_index_query(h, wdq, wuq, ww, 8, 1, d, r, 8, 64, q, w, ws, wsb, stream)
+
+    expect(E_NULL, call(w=None))
+    expect(E_NULL, call(h=T(csa.BF16, data=None)))
+    expect(E_DTYPE, call(h=T(csa.F32)), match="BF16")
+    expect(E_DTYPE, call(q=T(csa.FP8_E4M3)), match="q_idx")
+    expect(E_SHAPE, call(d=4004))
+    expect(E_SHAPE, call(r=0))
+    expect(E_SHAPE, call(h=T(csa.BF16, data=P + 2, sr=4096)), match="aligned")
+    expect(E_SHAPE, call(wdq=T(csa.BF16, sb=0, sr=4092)), match="multiples of 8")
+    expect(E_SHAPE, call(wuq=T(csa.BF16, sb=0, sr=512)), match="shorter")
+    expect(E_WS, call(wsb=need - 1))
+    expect(E_WS, call(ws=None))
+
+
 # ---------------------------------------------------------------------------- quantisers
 
 

@@ -301,6 +301,68 @@ def test_topk_exact(gpu_lib, B, Tq, N, k, mode):
     np.testing.assert_array_equal(got, want)
 
 
+# ----------------------------------------------------------------------------- indexer query
+
+
+def _index_query_bounds(hv, wdq, wuq, ww, HI, dI):
+    """Elementwise error bounds of the library's arithmetic against the fp64 oracle:
+    fp32 sums of exact bf16 products (gamma_K = K u / (1 - K u), u = 2^-24, any
+    summation order), c rounded to bf16 (2^-9 relative) before the second product."""
+    u = 2.0 ** -24
+    d, r = hv.shape[-1], wdq.shape[0]
+    gd, gr = d * u / (1 - d * u), r * u / (1 - r * u)
+    c = hv @ wdq.T
+    A = np.abs(hv) @ np.abs(wdq).T
+    bc = 2.0 ** -9 * (np.abs(c) + gd * A) + gd * A
+    bq = bc @ np.abs(wuq).T + gr * ((np.abs(c) + bc) @ np.abs(wuq).T)
+    bw = gd * (np.abs(hv) @ np.abs(ww).T)
+    return bq.reshape(hv.shape[:-1] + (HI, dI)), bw
+
+
+@pytest.mark.parametrize("B,Tq,d,r,HI,dI,fmt", [
+    (1, 1, 4096, 1024, 4, 32, "f32"),     # the 4k decode's indexer shape (4 heads of 32)
+    (1, 2048, 4096, 1024, 8, 64, "bf16"),  # the 2k prefill chunk (8 heads of 64)
+    (8, 1, 4096, 1024, 8, 64, "f32"),     # the 1M decode batch
+    (3, 5, 96, 64, 2, 16, "f32"),         # ragged: K below one 128-chunk, rows in a partial tile
+    (2, 40, 160, 96, 3, 8, "bf16"),       # K tails in both products, 80 rows (one split)
+])
+def test_index_query(gpu_lib, B, Tq, d, r, HI, dI, fmt):
+    """csa_index_query against the oracle within the derived fp32 / bf16 bounds, and
+    bitwise batch invariance (one row alone gives the same bits)."""
+    csa = gpu_lib
+    rg = _rng(f"iq{B}{Tq}{d}{r}{HI}{dI}{fmt}")
+    h = rg.standard_normal((B, Tq, d)).astype(np.float32)
+    ht, hv = up_bf16(h)
+    wdq_t, wdq = up_bf16((rg.standard_normal((r, d)) / np.sqrt(d)).astype(np.float32))
+    wuq_t, wuq = up_bf16((rg.standard_normal((HI * dI, r)) / np.sqrt(r)).astype(np.float32))
+    ww_t, ww = up_bf16((rg.standard_normal((HI, d)) / np.sqrt(d)).astype(np.float32))
+    # weights are passed as [1, rows, cols]: stride_row is their row pitch
+    W = [csa.desc(x.unsqueeze(0), csa.BF16) for x in (wdq_t, wuq_t, ww_t)]
+
+    def run(hsel, nb):
+        qdt = torch.float32 if fmt == "f32" else torch.bfloat16
+        q = torch.full((nb, Tq, HI, dI), float("nan"), dtype=qdt, device="cuda")
+        w = torch.full((nb, Tq, HI), float("nan"), device="cuda")
+        ws = workspace(csa.csa_index_query_workspace_size(nb, Tq, d, r, HI, dI))
+        ws.fill_(0xA5)  # contents on entry do not matter
+        csa.csa_index_query(csa.desc(hsel, csa.BF16), W[0], W[1], W[2], nb, Tq, d, r, HI, dI,
+                            csa.desc(q, csa.F32 if fmt == "f32" else csa.BF16), w, ws, ws.numel())
+        return down(q), down(w)
+
+    q, w = run(ht, B)
+    want_q, want_w = oracle.index_query(hv, wdq, wuq, ww, HI, dI)
+    bq, bw = _index_query_bounds(hv, wdq, wuq, ww, HI, dI)
+    if fmt == "bf16":
+        bq = bq + 2.0 ** -9 * (np.abs(want_q) + bq)
+    assert np.all(np.isfinite(q)) and np.all(np.isfinite(w))
+    assert np.all(np.abs(q - want_q) <= bq * 1.001), np.max(np.abs(q - want_q) / bq)
+    assert np.all(np.abs(w - want_w) <= bw * 1.001), np.max(np.abs(w - want_w) / bw)
+    # one sequence alone: the same bits (the K sums do not depend on the number of rows)
+    q1, w1 = run(ht[B - 1:B].contiguous(), 1)
+    np.testing.assert_array_equal(q1[0], q[B - 1])
+    np.testing.assert_array_equal(w1[0], w[B - 1])
+
+
 # ----------------------------------------------------------------------------- fused index + top-k
 
 
