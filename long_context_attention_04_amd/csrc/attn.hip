@@ -41,9 +41,7 @@ namespace csa {
 
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / kWave;  // 8: two per SIMD
-constexpr int kTile = 16;                 // entries per MFMA tile
+constexpr int kTile = 16;  // entries per MFMA tile
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -180,55 +178,58 @@ __device__ __forceinline__ float lane_sum4rows(float x) {  // fixed-order sum ov
   return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
-// Chunk of a split's entries resident in LDS: up to kChunkMax rows of 512 bf16 (1
+// Chunk of a split's entries resident in LDS: up to CH rows of 512 bf16 (1
 // KB), 16-byte chunk c of row r stored at position c ^ swz(r) (swz(r) = r mod 16),
 // so that the 16 consecutive rows of a QK operand read fall on distinct banks.  The last 16-entry tile of a full chunk reaches 8 rows past the buffer (into
 // the region after it): those entries are masked out of QK, and PV zeroes what it
 // reads there.
-constexpr int kChunkMax = 136;                    // entries per chunk
-constexpr int kChunkTiles = (kChunkMax + 15) / 16;  // 9
 constexpr int kRowBytes = 1024;
 
+// NW waves per workgroup, chunks of at most CH entries.
+template <int NW, int CH>
 struct ChunkLds {
-  __attribute__((aligned(16))) uint8_t rows[kChunkMax][kRowBytes];
+  static constexpr int kTiles = (CH + 15) / 16;
+  __attribute__((aligned(16))) uint8_t rows[CH][kRowBytes];
   union {
     // the 16 query heads, staged once (same swizzle as the rows) and read into
     // registers before P is first written
     __attribute__((aligned(16))) uint8_t q[16][kRowBytes];
     // P as the PV A operand: [tile][k group g][head m] -> 4 bf16 hi then 4 bf16 lo
     // of entries 16*tile + 4g .. +3
-    __attribute__((aligned(16))) uint4 p[kChunkTiles][4][16];
+    __attribute__((aligned(16))) uint4 p[kTiles][4][16];
   };
-  float esl[kChunkTiles * 16];     // entry scale (fp8 row scale, else 1); -1 = empty slot
-  int32_t sidx[kChunkTiles * 16];  // slots of the chunk
-  __attribute__((aligned(16))) float red_max[kWaves][16];
-  __attribute__((aligned(16))) float red_sum[kWaves][16];
+  float esl[kTiles * 16];     // entry scale (fp8 row scale, else 1); -1 = empty slot
+  int32_t sidx[kTiles * 16];  // slots of the chunk
+  __attribute__((aligned(16))) float red_max[NW][16];
+  __attribute__((aligned(16))) float red_sum[NW][16];
 };
 
 __device__ __forceinline__ int swz(int r) { return r & 15; }
 __device__ __forceinline__ int swz_off(int r, int chunk16) { return r * kRowBytes + ((chunk16 ^ swz(r)) << 4); }
 
 // One workgroup: one query row, 16 heads, one split of its entry list, processed in
-// chunks of at most kChunkMax entries.  For each chunk:
-//  * the chunk's selection slots (and fp8 scales) go to LDS, then every wave issues
-//    its rows (one row per instruction, straight into LDS for bf16; fp8 rows pass
-//    through registers to be widened);
-//  * QK: S^T = K Q^T on 16x16x32 bf16 MFMA, wave w taking 16-entry tiles w and w+8
-//    with the 16 query heads held in registers (B operand) and K read from LDS;
+// chunks of at most CH entries by NW waves.  For each chunk:
+//  * the chunk's selection slots go to LDS, then every wave issues its rows (one
+//    row per instruction, straight into LDS for bf16; fp8 rows pass through
+//    registers to be widened, with their scales);
+//  * QK: S^T = K Q^T on 16x16x32 bf16 MFMA, the waves over the chunk's 16-entry
+//    tiles, with the 16 query heads held in registers (B operand) and K read from LDS;
 //  * one workgroup max per head (online across chunks), P = exp2(s - max) written
 //    to LDS as hi + lo bf16 in the PV operand layout, per-head sums in a fixed order;
-//  * PV with the latent columns split over the waves (wave w owns columns
-//    64w .. 64w+63 of all 16 heads): the accumulator of a wave is final for its
-//    columns, so the waves never combine accumulators.
+//  * PV with the latent columns split over the waves (wave w owns 512 / NW columns
+//    of all 16 heads): the accumulator of a wave is final for its columns, so the
+//    waves never combine accumulators.
 // The scalars the prologue depends on come first in the argument list: they are
 // preloaded into scalar registers at launch (the rest of the arguments is read from
 // memory, one round trip that overlaps the position and slot loads).
-template <bool FP8>
-__global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __restrict__ q_pos,
-                                                              const int32_t* __restrict__ idx,
-                                                              const int32_t* __restrict__ raw_base, int k, int tq,
-                                                              int window, int m_hc, int split, int nsplit_max,
-                                                              int nhg, int rows, AttnArgs a) {
+template <bool FP8, int NW, int CH>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunk_kernel(
+    const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ raw_base, int k, int tq, int window, int m_hc,
+    int split, int nsplit_max, int nhg, int rows, AttnArgs a) {
+  constexpr int kT = (CH + 15) / 16;             // 16-entry tiles of a full chunk
+  constexpr int kQkT = (kT + NW - 1) / NW;       // QK tiles per wave
+  constexpr int kCols = 512 / NW, kNT = kCols / 16;  // PV: latent columns per wave, their 16-column tiles
   int row, s, hg;
   decode_block(blockIdx.x, nhg, nsplit_max, rows, &row, &s, &hg);
   if (row >= rows) return;
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __r
   const int m = lane % 16, g = lane / 16;
   const int t = threadIdx.x;
   const int e_begin = s * split;
-  const int nch = (split + kChunkMax - 1) / kChunkMax;  // chunk size depends on the split only
+  const int nch = (split + CH - 1) / CH;  // chunk size depends on the split only
   const int csz = (split + nch - 1) / nch;
   // A CSA row's compressed entries are its k selection slots, known without its
   // position: the first chunk's slots are requested before the position, so the two
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __r
   const int e_end = min(ri.n_tot, e_begin + split);
   const int h0 = hg * 16;
 
-  __shared__ ChunkLds L;
+  __shared__ ChunkLds<NW, CH> L;
   uint8_t* const rowb = &L.rows[0][0];  // the chunk's rows as one byte array
 
   // the 16 query heads as the QK B operand: lane (head m, group g) holds columns
@@ -269,9 +270,9 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __r
   float mrun[4], lrun[4], mrun_q = kNegInf;
 #pragma unroll
   for (int r = 0; r < 4; ++r) mrun[r] = kNegInf, lrun[r] = 0.f;
-  v4f O[4];  // O[nt]: heads 4g + r, latent column 64w + 16nt + m
+  v4f O[kNT];  // O[nt]: heads 4g + r, latent column kCols * w + 16nt + m
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) O[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < kNT; ++nt) O[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   for (int c0 = e_begin; c0 < e_end; c0 += csz) {
     const int cn = min(csz, e_end - c0);  // entries of this chunk
@@ -288,9 +289,9 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __r
     __syncthreads();
     // rows: wave w loads rows w, w+8, ... of the chunk's tiles (lane i holds the
     // slot of the wave's i-th row, so no row waits on an LDS read)
-    const int nrows = min(nmt * 16, kChunkMax);
-    const int jw = lane < (nrows - w + kWaves - 1) / kWaves ? L.sidx[w + kWaves * lane] : -1;
-    for (int r = w, ri8 = 0; r < nrows; r += kWaves, ++ri8) {
+    const int nrows = min(nmt * 16, CH);
+    const int jw = lane < (nrows - w + NW - 1) / NW ? L.sidx[w + NW * lane] : -1;
+    for (int r = w, ri8 = 0; r < nrows; r += NW, ++ri8) {
       const int e = c0 + r;
       const int j = __builtin_amdgcn_readlane(jw, ri8);
       const bool live = j >= 0;
@@ -312,9 +313,9 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __r
         if (live && lane == 0) L.esl[r] = sc;
       }
     }
-    if (c0 == e_begin) {  // the 16 query heads to LDS, wave w taking heads 2w, 2w + 1
+    if (c0 == e_begin) {  // the 16 query heads to LDS, 16 / NW per wave
 #pragma unroll
-      for (int hh = 2 * w; hh < 2 * w + 2; ++hh)
+      for (int hh = (16 / NW) * w; hh < (16 / NW) * (w + 1); ++hh)
         __builtin_amdgcn_global_load_lds((const gbyte*)(qp + (h0 + hh) * 512) + 16 * (lane ^ swz(hh)),
                                          (__attribute__((address_space(3))) void*)&L.q[hh][0], 16, 0, 0);
     }
@@ -329,12 +330,12 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __r
       for (int kk = 0; kk < 16; ++kk) qb[kk] = *(const v8bf*)&qs[swz_off(m, 4 * kk + g)];
     }
 
-    // ---- QK: tiles w and w + 8 of the chunk; lane (head m, g) gets entries 16mt + 4g + r
-    float sv[2][4];
+    // ---- QK: tiles w, w + NW, ... of the chunk; lane (head m, g) gets entries 16mt + 4g + r
+    float sv[kQkT][4];
     float lmax = kNegInf;
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-      const int mt = w + kWaves * ti;
+    for (int ti = 0; ti < kQkT; ++ti) {
+      const int mt = w + NW * ti;
 #pragma unroll
       for (int r = 0; r < 4; ++r) sv[ti][r] = kNegInf;
       if (mt < nmt) {  // wave-uniform
@@ -366,13 +367,13 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __r
     // chunk maxima, the same in every wave (fixed order)
     float mc_q = kNegInf;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) mc_q = fmaxf(mc_q, L.red_max[v][m]);
+    for (int v = 0; v < NW; ++v) mc_q = fmaxf(mc_q, L.red_max[v][m]);
     const float mnew_q = fmaxf(mrun_q, mc_q);
     mrun_q = mnew_q;
     float lsum = 0.f;
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-      const int mt = w + kWaves * ti;
+    for (int ti = 0; ti < kQkT; ++ti) {
+      const int mt = w + NW * ti;
       if (mt < nmt) {
         float pv[4];
 #pragma unroll
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __r
     // running statistics of heads 4g + r and the accumulator rescale
     float mcv[4] = {kNegInf, kNegInf, kNegInf, kNegInf}, lsv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {  // heads 4g .. 4g+3: one 16-byte read per table and wave
+    for (int v = 0; v < NW; ++v) {  // heads 4g .. 4g+3: one 16-byte read per table and wave
       const float4 mx = *(const float4*)&L.red_max[v][4 * g];
       const float4 sm = *(const float4*)&L.red_sum[v][4 * g];
       mcv[0] = fmaxf(mcv[0], mx.x), mcv[1] = fmaxf(mcv[1], mx.y), mcv[2] = fmaxf(mcv[2], mx.z), mcv[3] = fmaxf(mcv[3], mx.w);
@@ -412,27 +413,27 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __r
       lrun[r] = lrun[r] * alpha + ls;
       mrun[r] = mn;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) O[nt][r] *= alpha;
+      for (int nt = 0; nt < kNT; ++nt) O[nt][r] *= alpha;
     }
-    // ---- PV: O[16 heads x this wave's 64 columns] += P V over the chunk's tiles
+    // ---- PV: O[16 heads x this wave's kCols columns] += P V over the chunk's tiles
     typedef __attribute__((address_space(3))) v4bf lds_v4bf;
-    // operands of tile ks: P (16 B per lane) and four transposed V reads (rows
-    // 16ks + 4g .. +3, columns 64w + 16nt .. +15: lane m addresses row m / 4,
+    // operands of tile ks: P (16 B per lane) and kNT transposed V reads (rows
+    // 16ks + 4g .. +3, columns kCols*w + 16nt .. +15: lane m addresses row m / 4,
     // columns 4(m % 4) .. +3 and receives column m of the four rows); two operand
     // sets alternate, so tile ks + 1's reads are in flight during tile ks's MFMAs
-    const auto pv_load = [&](int ks, v8bf& pa, v4bf (&tv)[4]) {
+    const auto pv_load = [&](int ks, v8bf& pa, v4bf (&tv)[kNT]) {
       pa = __builtin_bit_cast(v8bf, L.p[ks][g][m]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int col = 64 * w + 16 * nt + 4 * (m % 4);
+      for (int nt = 0; nt < kNT; ++nt) {
+        const int col = kCols * w + 16 * nt + 4 * (m % 4);
         tv[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
             (lds_v4bf*)&rowb[swz_off(16 * ks + 4 * g + m / 4, col / 8) + 2 * (col % 8)]);
       }
     };
-    const auto pv_mfma = [&](int ks, const v8bf& pa, const v4bf (&tv)[4]) {
-      const bool past = 16 * ks + 4 * g + m / 4 >= kChunkMax;  // the lane read past the buffer: no entry there
+    const auto pv_mfma = [&](int ks, const v8bf& pa, const v4bf (&tv)[kNT]) {
+      const bool past = 16 * ks + 4 * g + m / 4 >= CH;  // the lane read past the buffer: no entry there
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < kNT; ++nt) {
         const v4bf t = past ? (v4bf){} : tv[nt];
         const v8bf vb = __builtin_shufflevector(t, t, 0, 1, 2, 3, 0, 1, 2, 3);
         O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, O[nt], 0, 0, 0);
@@ -440,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __r
     };
     {
       v8bf pa0, pa1;
-      v4bf tv0[4], tv1[4];
+      v4bf tv0[kNT], tv1[kNT];
       pv_load(0, pa0, tv0);
       int ks = 0;
       for (; ks + 1 < nmt; ks += 2) {
@@ -454,14 +455,14 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __r
     __syncthreads();  // the chunk's rows, P and tables are free for the next chunk
   }
 
-  // ---- output: this wave's 64 columns of the 16 heads
+  // ---- output: this wave's kCols columns of the 16 heads
   const int H = a.heads;
   if (partial) {
     float* obase = (float*)a.ws + (((int64_t)row * nsplit_max + s) * H + h0) * 512;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) obase[(4 * g + r) * 512 + 64 * w + 16 * nt + m] = O[nt][r];
+      for (int r = 0; r < 4; ++r) obase[(4 * g + r) * 512 + kCols * w + 16 * nt + m] = O[nt][r];
     if (w == 0 && m == 0) {
       float* pml = (float*)a.ws + (int64_t)rows * nsplit_max * H * 512 + (((int64_t)row * nsplit_max + s) * H + h0) * 2;
 #pragma unroll
@@ -476,8 +477,8 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(const int32_t* __r
     for (int r = 0; r < 4; ++r) {
       const float fs = lrun[r] > 0.f ? __fdiv_rn(1.0f, lrun[r]) : 0.f;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        __builtin_nontemporal_store(O[nt][r] * fs, &obase[(4 * g + r) * 512 + 64 * w + 16 * nt + m]);
+      for (int nt = 0; nt < kNT; ++nt)
+        __builtin_nontemporal_store(O[nt][r] * fs, &obase[(4 * g + r) * 512 + kCols * w + 16 * nt + m]);
     }
     if (a.lse && w == 0 && m == 0) {
 #pragma unroll
@@ -620,12 +621,19 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
   const int nhg = a.heads / 16;
   const int64_t pairs = rows * nsplit_max;
   const int64_t blocks = rows >= 8 ? (rows + 7) / 8 * 8 * nsplit_max * nhg : (pairs + 7) / 8 * 8 * nhg;
-  if (a.kv.dtype == CSA_FP8_E4M3)
-    hipLaunchKernelGGL(attn_chunk_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a.q_pos, a.idx, a.raw_base,
-                       a.k, a.tq, a.window, a.m_hc, split, nsplit_max, nhg, (int)rows, a);
-  else
-    hipLaunchKernelGGL(attn_chunk_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a.q_pos, a.idx, a.raw_base,
-                       a.k, a.tq, a.window, a.m_hc, split, nsplit_max, nhg, (int)rows, a);
+  // Decode: 8 waves and chunks of 136 entries (one workgroup per CU; a split of 272
+  // entries is two chunks).  Many queries per sequence: 4 waves and chunks of 56
+  // (75 KB of LDS: two workgroups per CU, one computing while the other gathers).
+  const bool fp8 = a.kv.dtype == CSA_FP8_E4M3, many = a.tq != 1;
+  const dim3 grid((unsigned)blocks);
+#define CSA_ATTN_LAUNCH(F, NW, CH)                                                                                \
+  hipLaunchKernelGGL((attn_chunk_kernel<F, NW, CH>), grid, dim3(NW * kWave), 0, s, a.q_pos, a.idx, a.raw_base, a.k, \
+                     a.tq, a.window, a.m_hc, split, nsplit_max, nhg, (int)rows, a)
+  if (fp8 && many) CSA_ATTN_LAUNCH(true, 4, 56);
+  else if (fp8) CSA_ATTN_LAUNCH(true, 8, 136);
+  else if (many) CSA_ATTN_LAUNCH(false, 4, 56);
+  else CSA_ATTN_LAUNCH(false, 8, 136);
+#undef CSA_ATTN_LAUNCH
   if (partial)
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)rows, a.heads), dim3(128), 0, s, a, split, nsplit_max, rows);
   return hipGetLastError();
@@ -642,7 +650,7 @@ int attn_split_size(int tq, int n_entries_max) {
   const int n = max(n_entries_max, 1);
   if (tq != 1) return min(n, kAttnMaxSplitEntries);
   const int eighth = ((n + 7) / 8 + kTile - 1) / kTile * kTile;
-  return min(kAttnMaxSplitEntries, max(kWaves * kTile, eighth));
+  return min(kAttnMaxSplitEntries, max(8 * kTile, eighth));
 }
 
 size_t attn_workspace_bytes(int64_t rows, int heads, int dim, int n_entries_max, int tq) {
