@@ -15,8 +15,9 @@
 //    (quantised to MXFP4 in-kernel once per workgroup).  ReLU, head weights and
 //    the cross-head sum are a short epilogue (one cross-lane add).
 //  * BF16 keys: bf16 MFMA 16x16x32 with (query, head) pairs as rows, keys as
-//    columns; used by decode and by prefill chunks (where it is a dense
-//    contraction of many queries against the same keys).
+//    columns; one kernel for few queries per sequence (decode: the key stream
+//    dominates) and a 32-query x 256-key tile kernel for many (a prefill chunk: a
+//    dense contraction of many queries against the same keys).
 //  * F32 keys: plain fp32 VALU kernel (small shapes).
 #include "common.h"
 #include "compress_block.h"
@@ -124,6 +125,103 @@ __global__ __launch_bounds__(256) void index_bf16_kernel(IndexArgs a) {
       const int key = kbase + 32 * wave + 16 * nt + n;
       if ((g & 1) == 0 && myq < a.tq && key < a.n_cap)
         a.scores[((int64_t)b * a.tq + myq) * a.n_cap + key] = key < Vq ? tot : kNegInf;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ bf16 MFMA, many queries
+// heads == 8, dim == 64, many queries per sequence (a prefill chunk): a dense
+// [queries*8 x 64] x [64 x keys] contraction.  Workgroup tile: 32 queries x 256
+// keys.  The 32 queries' heads are staged once in LDS (A operand, read twice per
+// 2-query row tile); each wave holds its 64 keys in registers as the B operand for
+// all 16 row tiles, so a key is loaded once per workgroup.  The epilogue (ReLU,
+// head weights, the sum over heads) is the same arithmetic in the same order as
+// index_bf16_kernel.
+constexpr int kPfQ = 32;        // queries per workgroup
+constexpr int kPfNT = 8;        // 16-key column tiles per wave
+constexpr int kPfKeys = 4 * 16 * kPfNT;  // keys per workgroup (512)
+
+// the sum of x over lanes i and i ^ 16, bitwise the same in both lanes
+__device__ __forceinline__ float pair16_sum(float x) {
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+__global__ __launch_bounds__(256) void index_bf16_tile_kernel(IndexArgs a) {
+  const int b = blockIdx.z;
+  const int q0 = blockIdx.y * kPfQ;
+  const int kbase = blockIdx.x * kPfKeys;
+  const int t = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(t / kWave), l = t % kWave;
+  const int g = l / 16, n = l % 16;
+  // A operand rows (query q0 + r / 8, head r % 8): 64 bf16 = 8 chunks of 16 B,
+  // chunk c of row r at position c ^ (r & 7) (conflict-free operand reads)
+  __shared__ __attribute__((aligned(16))) uint4 qs[kPfQ * 8][8];
+  __shared__ float wsh[kPfQ][8];
+  __shared__ int vsh[kPfQ];
+  const int nq = min(kPfQ, a.tq - q0);
+#pragma unroll
+  for (int i = 0; i < kPfQ * 8 * 8 / 256; ++i) {
+    const int idx = t + 256 * i, r = idx / 8, c = idx % 8, q = r / 8, h = r % 8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (q < nq)
+      v = *(const uint4*)((const uint16_t*)a.q.data + (int64_t)b * a.q.sb + (int64_t)(q0 + q) * a.q.sr + h * 64 + 8 * c);
+    qs[r][c ^ (r & 7)] = v;
+  }
+  {
+    const int q = t / 8, h = t % 8;
+    wsh[q][h] = q < nq ? a.w[((int64_t)b * a.tq + q0 + q) * 8 + h] : 0.f;
+    if (t < kPfQ) vsh[t] = t < nq ? visible_blocks(a.q_pos[b * a.tq + q0 + t], a.m) : 0;
+  }
+  __syncthreads();
+  int vmax = 0;
+  for (int q = 0; q < kPfQ; ++q) vmax = max(vmax, vsh[q]);
+  const int kw = kbase + 16 * kPfNT * wave;  // this wave's first key
+  float* srow_base = a.scores + ((int64_t)b * a.tq + q0) * a.n_cap;
+  if (kw >= vmax) {  // no query of the tile sees these keys: -inf only
+    for (int q = 0; q < nq; ++q)
+      for (int i = l; i < 16 * kPfNT; i += kWave)
+        if (kw + i < a.n_cap) srow_base[(int64_t)q * a.n_cap + kw + i] = kNegInf;
+    return;
+  }
+  // B operand: key kw + 16nt + n, dims 32ks + 8g .. +7 (keys no query of the tile sees are zero)
+  v8bf B[kPfNT][2];
+#pragma unroll
+  for (int nt = 0; nt < kPfNT; ++nt) {
+    const int key = kw + 16 * nt + n;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      B[nt][ks] = key < vmax ? *(const v8bf*)((const uint16_t*)a.k.data + (int64_t)b * a.k.sb + (int64_t)key * a.k.sr +
+                                              32 * ks + 8 * g)
+                             : (v8bf){};
+  }
+  for (int mt = 0; mt < kPfQ / 2; ++mt) {
+    if (2 * mt >= nq) break;  // wave-uniform
+    // this lane's output rows: 4g + r -> query 2mt + (g >= 2), heads 4(g & 1) + r
+    const int myq = 2 * mt + (g >> 1);
+    const int Vq = vsh[myq];
+    float* srow = srow_base + (int64_t)myq * a.n_cap;
+    const int ra = 16 * mt + n;  // A operand row: query 2mt + n / 8, head n % 8
+    v8bf A[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) A[ks] = __builtin_bit_cast(v8bf, qs[ra][(4 * ks + g) ^ (ra & 7)]);
+    float wv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[r] = wsh[myq][4 * (g & 1) + r];
+    v4f c[kPfNT];
+#pragma unroll
+    for (int nt = 0; nt < kPfNT; ++nt) {
+      c[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+      c[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], B[nt][0], c[nt], 0, 0, 0);
+      c[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], B[nt][1], c[nt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int nt = 0; nt < kPfNT; ++nt) {
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part = fmaf(wv[r], fmaxf(c[nt][r], 0.f), part);
+      const float tot = pair16_sum(part);  // heads 0-3 plus heads 4-7
+      const int key = kw + 16 * nt + n;
+      if ((g & 1) == 0 && myq < nq && key < a.n_cap) srow[key] = key < Vq ? tot : kNegInf;
     }
   }
 }
@@ -372,6 +470,10 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((index_mxfp4_kernel<4, false>), grid, dim3(256), 0, s, a, none, no_compress(nslices, rows));
     else
       hipLaunchKernelGGL((index_mxfp4_kernel<16, false>), grid, dim3(256), 0, s, a, none, no_compress(nslices, rows));
+  } else if (a.k.dtype == CSA_BF16 && a.q.dtype == CSA_BF16 && a.heads == 8 && a.dim == 64 && a.tq >= kPfQ) {
+    // many queries per sequence: the 32-query tile kernel (same arithmetic, same order)
+    dim3 grid((a.n_cap + kPfKeys - 1) / kPfKeys, (a.tq + kPfQ - 1) / kPfQ, a.batch);
+    hipLaunchKernelGGL(index_bf16_tile_kernel, grid, dim3(256), 0, s, a);
   } else if (a.k.dtype == CSA_BF16 && a.q.dtype == CSA_BF16 && a.heads == 8 && a.dim == 64) {
     dim3 grid((a.n_cap + kBfKT - 1) / kBfKT, (a.tq + kBfQT - 1) / kBfQT, a.batch);
     hipLaunchKernelGGL(index_bf16_kernel, grid, dim3(256), 0, s, a);
