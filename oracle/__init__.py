@@ -13,6 +13,8 @@ from .csa import (  # noqa: F401
     hca_attn,
     index_query,
     index_scores,
+    latent_output,
+    latent_query,
     merge_weights,
     topk,
     topk_row,

@@ -127,6 +127,41 @@ def index_query(h, w_dq, w_uq, w_w, n_idx_heads: int, idx_dim: int):
     return q, h @ w_w.T
 
 
+def latent_query(q, w_uk):
+    """MLA absorbed query (R-latent): the head's key up-projection moved onto the
+    query.  Head h reads the shared latent row c through the key k_h = W_uk[h] c, so
+    <q_h, W_uk[h] c> = <W_uk[h]^T q_h, c>: the attention score needs only the
+    absorbed query q_lat_h = W_uk[h]^T q_h against the stored latent rows.
+
+    q [..., H, dh], w_uk [H, dh, D] -> q_lat [..., H, D].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    H, dh, D = w_uk.shape
+    assert q.shape[-2:] == (H, dh)
+    out = np.empty(q.shape[:-1] + (D,))
+    for h in range(H):
+        out[..., h, :] = q[..., h, :] @ w_uk[h]
+    return out
+
+
+def latent_output(o_lat, w_uv):
+    """MLA output up-projection (R-latent): the value of head h is v_h = W_uv[h] c, and
+    attention is linear in its values, so sum_j p_j W_uv[h] c_j = W_uv[h] (sum_j p_j c_j):
+    the head's output is its latent attention output mapped by W_uv[h].
+
+    o_lat [..., H, D], w_uv [H, dh, D] -> o [..., H, dh].
+    """
+    o_lat = np.asarray(o_lat, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    H, dh, D = w_uv.shape
+    assert o_lat.shape[-2:] == (H, D)
+    out = np.empty(o_lat.shape[:-1] + (dh,))
+    for h in range(H):
+        out[..., h, :] = o_lat[..., h, :] @ w_uv[h].T
+    return out
+
+
 # ----------------------------------------------------------------------------
 # (b) lightning-indexer scores
 # ----------------------------------------------------------------------------

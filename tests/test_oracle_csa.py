@@ -139,6 +139,47 @@ def test_index_query_has_rank_at_most_r_and_is_linear():
     np.testing.assert_allclose(w2, a * w[0] + b * w[1], atol=1e-10)
 
 
+def test_latent_projections_hand_derived_golden():
+    g = json.load(open(os.path.join(GOLDEN, "latent_proj_hand.json")))
+    np.testing.assert_array_equal(O.latent_query(np.array(g["q"]), np.array(g["w_uk"])),
+                                  np.array(g["expected_q_lat"], dtype=np.float64))
+    np.testing.assert_array_equal(O.latent_output(np.array(g["o_lat"]), np.array(g["w_uv"])),
+                                  np.array(g["expected_o"], dtype=np.float64))
+
+
+def test_latent_projections_brute_force_loops():
+    r = np.random.default_rng(13)
+    H, dh, D = 3, 4, 5
+    q, o = r.standard_normal((2, H, dh)), r.standard_normal((2, H, D))
+    wuk, wuv = r.standard_normal((H, dh, D)), r.standard_normal((H, dh, D))
+    ql, oo = O.latent_query(q, wuk), O.latent_output(o, wuv)
+    for t in range(2):
+        for h in range(H):
+            for j in range(D):
+                assert abs(ql[t, h, j] - sum(wuk[h, i, j] * q[t, h, i] for i in range(dh))) < 1e-12
+            for i in range(dh):
+                assert abs(oo[t, h, i] - sum(wuv[h, i, j] * o[t, h, j] for j in range(D))) < 1e-12
+
+
+def test_absorbed_latent_attention_equals_per_head_sdpa():
+    """MLA absorption: attention of the absorbed queries over the shared latent rows,
+    mapped by the value up-projection, equals ordinary multi-head attention with each
+    head's own keys K_h = C W_uk[h]^T and values V_h = C W_uv[h]^T (torch SDPA, fp64)."""
+    import torch
+    r = np.random.default_rng(14)
+    H, dh, D, n = 4, 6, 10, 9
+    q = r.standard_normal((H, dh))
+    C = r.standard_normal((n, D))
+    wuk, wuv = r.standard_normal((H, dh, D)) / 3, r.standard_normal((H, dh, D))
+    scale = 0.37
+    o_lat, _ = O.attend(O.latent_query(q, wuk), C, scale)
+    got = O.latent_output(o_lat, wuv)
+    K = torch.tensor(np.stack([C @ wuk[h].T for h in range(H)]))  # [H, n, dh]
+    V = torch.tensor(np.stack([C @ wuv[h].T for h in range(H)]))
+    want = torch.nn.functional.scaled_dot_product_attention(torch.tensor(q)[:, None], K, V, scale=scale)[:, 0]
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- indexer
 
 
