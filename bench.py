@@ -92,6 +92,54 @@ def launch_us(torch, n, reps, launch) -> float:
     return float(e0.elapsed_time(e1) * 1e3 / reps)
 
 
+def projection_timings(torch, rows=8, d_model=4096, rank=1024, HI=8, dI=64, H=64, dh=128, D=512, sets=40) -> dict:
+    """The projections either side of the decode step, timed alone at batch `rows`: the
+    indexer query (c = W_dq h, q_I = W_uq c, w = W_w h) and the MLA absorbed query and
+    output up-projection.  Each is bound by its bf16 weight stream; `sets` weight copies
+    rotate so that the weights come from HBM, not the last-level cache."""
+    import long_context_attention_04_amd as csa
+    dev, bf = "cuda", torch.bfloat16
+
+    def rnd(*shape):
+        return (torch.randn(*shape, device=dev) / np.sqrt(shape[-1])).to(bf)
+
+    res = {}
+    # indexer query
+    h = rnd(rows, 1, d_model)
+    W = [(rnd(1, rank, d_model), rnd(1, HI * dI, rank), rnd(1, HI, d_model)) for _ in range(sets)]
+    qi = torch.empty(rows, 1, HI, dI, device=dev)
+    w = torch.empty(rows, 1, HI, device=dev)
+    ws = torch.empty(csa.csa_index_query_workspace_size(rows, 1, d_model, rank, HI, dI), dtype=torch.uint8, device=dev)
+    D3 = [[csa.desc(x, csa.BF16) for x in ws3] for ws3 in W]
+    hd, qd = csa.desc(h, csa.BF16), csa.desc(qi, csa.F32)
+    us = launch_us(torch, sets, 4 * sets, lambda i: csa.csa_index_query(hd, *D3[i], rows, 1, d_model, rank, HI, dI, qd,
+                                                                        w, ws, ws.numel()))
+    nb = 2 * (rank * d_model + HI * dI * rank + HI * d_model) + rows * (2 * d_model + 4 * HI * dI + 4 * HI)
+    res["index_query"] = {"us": round(us, 2), "bytes": nb, "gb_s": round(nb / us * 1e-3, 1),
+                          "shape": f"rows {rows}, d_model {d_model}, rank {rank}, {HI} x {dI}"}
+    # MLA absorbed query and output up-projection
+    q = rnd(rows, H, dh)
+    Wk = [rnd(H, D, dh) for _ in range(sets)]
+    Wv = [rnd(H, dh, D) for _ in range(sets)]
+    ql = torch.empty(rows, H, D, dtype=bf, device=dev)
+    ol = torch.randn(rows, H, D, device=dev)
+    o = torch.empty(rows, H, dh, dtype=bf, device=dev)
+    wq = torch.empty(max(csa.csa_latent_query_workspace_size(rows, H, dh, D), 1), dtype=torch.uint8, device=dev)
+    wo = torch.empty(max(csa.csa_latent_output_workspace_size(rows, H, dh, D), 1), dtype=torch.uint8, device=dev)
+    us = launch_us(torch, sets, 4 * sets, lambda i: csa.csa_latent_query(q, Wk[i], rows, H, dh, D, ql, wq, wq.numel()))
+    nb = 2 * H * D * dh + rows * H * (2 * dh + 2 * D)
+    res["latent_query"] = {"us": round(us, 2), "bytes": nb, "gb_s": round(nb / us * 1e-3, 1),
+                           "shape": f"rows {rows}, {H} heads of {dh} onto {D}"}
+    us = launch_us(torch, sets, 4 * sets, lambda i: csa.csa_latent_output(ol, Wv[i], rows, H, dh, D, o, csa.BF16, wo,
+                                                                           wo.numel()))
+    nb = 2 * H * D * dh + rows * H * (4 * D + 2 * dh)
+    res["latent_output"] = {"us": round(us, 2), "bytes": nb, "gb_s": round(nb / us * 1e-3, 1),
+                            "shape": f"rows {rows}, {H} heads: {D} -> {dh}"}
+    for v in res.values():
+        v["frac"] = round(v["gb_s"] / HBM_PEAK_GBS, 4)
+    return res
+
+
 def stream_ceiling(torch) -> dict:
     """HBM streaming-read ceiling: csa_stream_read over 2 GiB, best of 5."""
     from long_context_attention_04_amd import csa_stream_read, csa_stream_read_sink_size
@@ -198,7 +246,8 @@ class CsaDecode:
         L = self.layers
         return {"attention_call_us": round(launch_us(self.torch, len(L), 40, lambda i: L[i].attend()), 2),
                 "index_topk_call_us": round(launch_us(self.torch, len(L), 40,
-                                                      lambda i: L[i].compress_index_topk(3)), 2)}
+                                                      lambda i: L[i].compress_index_topk(3)), 2),
+                "projections": projection_timings(self.torch, rows=L[0].B)}
 
     def traffic(self):
         return pmc_traffic()
@@ -371,6 +420,68 @@ class HcaDecode:
         return time_oracle(sample, seconds, n_seq)
 
 
+class HcaPrefill:
+    """HCA prefill: a 2048-query chunk over a 64k context; the step compresses the 16 blocks
+    the chunk completes, then every query attends densely over its visible blocks and its
+    window (MFMA-bound)."""
+
+    def __init__(self, name, sets, torch):
+        from long_context_attention_04_amd import workloads
+        import synth
+        self.wl = wl = synth.WORKLOADS[name]
+        self.layers = [workloads.build(name, salt=s) for s in range(sets)]
+        L = self.layers[0]
+        self.tokens = L.B * L.tq
+        t = L.host["t"]
+        entries = int(np.sum((t + 1) // L.m_hc + np.minimum(L.W, t + 1)))
+        flops = entries * L.H * 4 * L.D
+        self.dominant = {"kernel": "attn_chunk_kernel (hca_attn)", "bound": "mfma", "work": flops,
+                         "work_note": "4 * D flops per (query, head, visible entry): QK^T and PV, causal"}
+        nb = L.max_blocks
+        self.bytes = {"entries_unique": L.B * L.n_cap * L.D * 2, "window_raw": L.B * (L.W + L.tq) * L.D * 2,
+                      "compress": L.B * nb * L.D * 2, "q_out_lse": L.B * L.tq * L.H * (L.D * 2 + L.D * 4 + 4)}
+        self.excluded = {}
+        self.dtype = "bf16"
+        self.config = {"workload": name, "batch": wl.batch, "queries": wl.tq, "context": wl.extra["context"],
+                       "heads": wl.heads, "latent_dim": wl.dim, "m_hc": wl.m_hc, "window": wl.window,
+                       "kv": wl.kv_dtype}
+        self.metric = "HCA prefill chunk tokens/s (2048 queries over 64k ctx) on 1 GPU; attention TFLOP/s vs bf16 MFMA peak"
+        self.torch = torch
+
+    def step(self, i):
+        self.layers[i].step()
+
+    def dominant_launch(self, i):
+        self.layers[i].attend()
+
+    def extra_timings(self):
+        L = self.layers
+        return {"compress_call_us": round(launch_us(self.torch, len(L), 10, lambda i: L[i].compress()), 2)}
+
+    def traffic(self):
+        return None
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        L, nq = self.layers[0], 4
+        raw = L.raw_kv.data.double().cpu().numpy()
+        kv0 = L.kv_hc.data.double().cpu().numpy()
+        q = L.q.data.double().cpu().numpy()
+        z = L.z_hc.cpu().numpy().astype(np.float64)
+        base, n0, nb = L.host["raw_base"], L.host["n0"], L.max_blocks
+        rows = np.linspace(0, L.tq - 1, nq).astype(int)
+
+        def sample():
+            kv = kv0.copy()
+            blocks = oracle.compress(raw, base, z, L.m_hc, [n0], [nb])[0][1]
+            kv[0, n0:n0 + nb] = blocks
+            for r in rows:
+                oracle.hca_attn(q[:, r:r + 1], kv, L.m_hc, raw, base, L.W, L.host["t"][:, r:r + 1], L.scale)
+            return f"compress the chunk's {nb} blocks + {nq} of {L.tq} chunk queries (dense over their visible blocks)"
+
+        return time_oracle(sample, seconds, nq)
+
+
 class HybridDecode:
     """The hybrid layer pair: a CSA layer (bf16 indexer, top-1024) and an HCA layer, batch 32,
     262k contexts, bf16 or fp8 KV; each step first compresses the blocks the new token completes."""
@@ -458,6 +569,8 @@ def make_job(args, torch):
         return CsaPrefill(args.workload, min(args.sets, 3), torch)
     if kind == "hca_decode":
         return HcaDecode(args.workload, args.sets, torch)
+    if kind == "hca_prefill":
+        return HcaPrefill(args.workload, min(args.sets, 3), torch)
     if kind == "hybrid_decode":
         return HybridDecode(args.workload, min(args.sets, 4), torch, args.kv)
     print(f"bench.py times the 1M decode, prefill, HCA and hybrid workloads; {args.workload} is covered by the "

@@ -408,6 +408,30 @@ def build_hca_decode(wl: synth.Workload, salt: int = 0) -> HcaLayer:
     return layer
 
 
+def build_hca_prefill(wl: synth.Workload, salt: int = 0) -> HcaLayer:
+    """HCA prefill: a chunk of Tq queries at positions L .. L+Tq-1 over an L-token context.
+    The L/m_hc blocks before the chunk are drawn directly; the Tq/m_hc blocks the chunk
+    completes are compressed by the step (block j is visible to query t once 128j+127 <= t).
+    Raw rows kept: positions L-W .. L+Tq-1 (every query's window and the chunk's blocks)."""
+    B, H, D, W, mh, Tq = wl.batch, wl.heads, wl.dim, wl.window, wl.m_hc, wl.tq
+    L = wl.extra["context"]
+    n0 = L // mh
+    N = (L + Tq) // mh
+    rbase = L - W
+    raw = store(synth.device_normal(wl, "raw_kv", (B, W + Tq, D), DEV, salt=salt), wl.kv_dtype)
+    kv = Stored(synth.device_normal(wl, "kv_hc", (B, N, D), DEV, dtype=torch.bfloat16, salt=salt), BF16)
+    kv.data[:, n0:] = float("nan")  # written by the step's compression
+    pos = L + np.arange(Tq)[None].repeat(B, 0)
+    q = Stored(_bf16(synth.normal(wl, "q", (B, Tq, H, D), salt)), BF16)
+    layer = HcaLayer(B=B, tq=Tq, m_hc=mh, H=H, D=D, W=W, n_cap=N, scale=wl.scale, kv_hc=kv, raw_kv=raw,
+                     raw_base=_i32(np.full(B, rbase)), z_hc=_f32(synth.normal(wl, "z_hc", (mh,), salt)), q=q,
+                     q_pos=_i32(pos), blk_first=_i32(np.full(B, n0)), blk_count=_i32(np.full(B, N - n0)),
+                     max_blocks=N - n0)
+    layer.host = {"t": pos, "raw_base": np.full(B, rbase), "n0": n0, "L": L}
+    layer.alloc_outputs()
+    return layer
+
+
 def build_hybrid_decode(wl: synth.Workload, kv_fmt: str = "bf16", salt: int = 0):
     """A CSA layer and an HCA layer decoding one new token per sequence at t_b = L_b over
     L_b = 262144 + tail_b tokens.  The step first compresses the CSA block ((t_b+1) % 4 == 0)
@@ -475,6 +499,8 @@ def build(name: str, salt: int = 0, kv_fmt: str | None = None):
         return build_csa_prefill(wl, salt)
     if wl.kind == "hca_decode":
         return build_hca_decode(wl, salt)
+    if wl.kind == "hca_prefill":
+        return build_hca_prefill(wl, salt)
     if wl.kind == "hybrid_decode":
         return build_hybrid_decode(wl, kv_fmt or wl.kv_dtype, salt)
     raise ValueError(name)

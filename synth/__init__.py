@@ -28,7 +28,7 @@ class Workload:
 
     name: str
     wid: int
-    kind: str  # "csa_decode" | "csa_prefill" | "hca_decode" | "hybrid_decode"
+    kind: str  # "csa_decode" | "csa_prefill" | "hca_decode" | "hca_prefill" | "hybrid_decode"
     batch: int
     tq: int
     heads: int
@@ -86,6 +86,13 @@ WORKLOADS = {
             idx_dim=64, topk=1024, idx_dtype="bf16",
             notes="262144 + tail tokens, tail uniform in [0, 127]; bf16 or fp8 e4m3 KV",
             extra={"context": 262144, "tail_hi": 127},
+        ),
+        Workload(
+            name="hca_prefill_2k_on_64k", wid=6, kind="hca_prefill", batch=1, tq=2048,
+            heads=64, dim=512, window=128, kv_dtype="bf16", m_hc=128,
+            notes="2048 new queries at positions 65536..67583 over a 65536-token context; the chunk "
+                  "completes 16 heavily compressed blocks, which the step compresses",
+            extra={"context": 65536},
         ),
     ]
 }

@@ -364,6 +364,67 @@ def test_index_query(gpu_lib, B, Tq, d, r, HI, dI, fmt):
     np.testing.assert_array_equal(w1[0], w[B - 1])
 
 
+# ----------------------------------------------------------------------------- MLA projections
+
+
+@pytest.mark.parametrize("rows,H,dh,D", [
+    (8, 64, 128, 512),    # the 1M decode batch: 64 heads of 128 onto the 512-wide latent
+    (2048, 2, 128, 512),  # a prefill chunk's rows (one split per tile)
+    (70, 4, 96, 160),     # ragged: K tails below and above one 128-chunk, rows in a partial tile
+    (1, 3, 32, 64),
+])
+def test_latent_projections(gpu_lib, rows, H, dh, D):
+    """csa_latent_query / csa_latent_output against the oracle within derived bounds (fp32
+    sums of exact bf16 products: gamma_K = K u / (1 - K u), u = 2^-24; bf16 outputs add
+    half an ulp, 2^-9 relative; o_lat = hi + lo to 2^-18 relative), and bitwise
+    batch invariance (a few rows alone give the same bits)."""
+    csa = gpu_lib
+    rg = _rng(f"lat{rows}{H}{dh}{D}")
+    qt, qv = up_bf16(rg.standard_normal((rows, H, dh)).astype(np.float32))
+    wuk_t, wuk = up_bf16((rg.standard_normal((H, dh, D)) / np.sqrt(dh)).astype(np.float32))
+    wuv_t, wuv = up_bf16((rg.standard_normal((H, dh, D)) / np.sqrt(D)).astype(np.float32))
+    o_lat = rg.standard_normal((rows, H, D)).astype(np.float32)
+    o_t = up(o_lat)
+    wuk_tt = wuk_t.transpose(1, 2).contiguous()  # [H, D, dh]: the absorbed form's row layout
+
+    def gamma(k):
+        return k * 2.0 ** -24 / (1 - k * 2.0 ** -24)
+
+    def query(qsel, n):
+        out = torch.full((n, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        ws = workspace(csa.csa_latent_query_workspace_size(n, H, dh, D))
+        ws.fill_(0xA5)
+        csa.csa_latent_query(qsel, wuk_tt, n, H, dh, D, out, ws, ws.numel())
+        return down(out)
+
+    def output(osel, n, dt):
+        out = torch.full((n, H, dh), float("nan"), dtype=torch.float32 if dt == csa.F32 else torch.bfloat16,
+                         device="cuda")
+        ws = workspace(csa.csa_latent_output_workspace_size(n, H, dh, D))
+        ws.fill_(0xA5)
+        csa.csa_latent_output(osel, wuv_t, n, H, dh, D, out, dt, ws, ws.numel())
+        return down(out)
+
+    got = query(qt, rows)
+    want = oracle.latent_query(qv, wuk)
+    b = gamma(dh) * oracle.latent_query(np.abs(qv), np.abs(wuk))
+    b = b + 2.0 ** -9 * (np.abs(want) + b)
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - want) <= b * 1.001), np.max(np.abs(got - want) / b)
+    want_o = oracle.latent_output(o_lat, wuv)
+    bo = (2.0 ** -18 + gamma(2 * D) * (1 + 2.0 ** -8)) * oracle.latent_output(np.abs(o_lat), np.abs(wuv))
+    got_o = output(o_t, rows, csa.F32)
+    assert np.all(np.isfinite(got_o))
+    assert np.all(np.abs(got_o - want_o) <= bo * 1.001), np.max(np.abs(got_o - want_o) / bo)
+    got_ob = output(o_t, rows, csa.BF16)
+    bob = bo + 2.0 ** -9 * (np.abs(want_o) + bo)
+    assert np.all(np.abs(got_ob - want_o) <= bob * 1.001), np.max(np.abs(got_ob - want_o) / bob)
+    # a few rows alone: the same bits whatever the number of rows (and the split of K)
+    r0, n = rows // 2, min(3, rows - rows // 2)
+    np.testing.assert_array_equal(query(qt[r0:r0 + n].contiguous(), n), got[r0:r0 + n])
+    np.testing.assert_array_equal(output(o_t[r0:r0 + n].contiguous(), n, csa.F32), got_o[r0:r0 + n])
+
+
 # ----------------------------------------------------------------------------- fused index + top-k
 
 
@@ -515,18 +576,28 @@ def test_csa_sparse_attn(gpu_lib, B, Tq, H, D, k, W, fmt, tol):
     assert np.max(np.abs(down(lse) - want_lse)) < tol
 
 
-@pytest.mark.parametrize("B,H,mhc,ncap,W,fmt,tol", [
-    (4, 64, 128, 40, 128, "bf16", 2e-3),
-    (3, 64, 16, 700, 33, "bf16", 2e-3),
-    (2, 32, 128, 20, 128, "fp8", 5e-3),
+@pytest.mark.parametrize("B,Tq,H,mhc,ncap,W,fmt,tol", [
+    (4, 1, 64, 128, 40, 128, "bf16", 2e-3),
+    (3, 1, 64, 16, 700, 33, "bf16", 2e-3),
+    (2, 1, 32, 128, 20, 128, "fp8", 5e-3),
+    # prefill chunks: consecutive queries, blocks completing inside the chunk
+    (2, 37, 64, 16, 90, 128, "bf16", 2e-3),
+    (1, 200, 64, 8, 300, 33, "bf16", 2e-3),
+    (2, 70, 32, 16, 60, 20, "fp8", 5e-3),
 ])
-def test_hca_attn(gpu_lib, B, H, mhc, ncap, W, fmt, tol):
+def test_hca_attn(gpu_lib, B, Tq, H, mhc, ncap, W, fmt, tol):
     csa = gpu_lib
-    D, Tq = 512, 1
+    D = 512
     R = 512
-    r, q, kvh, raw = _attn_inputs(f"hca{B}{H}{mhc}{ncap}{fmt}", B, Tq, H, D, ncap, R, fmt)
-    pos = r.integers(mhc * ncap // 2, mhc * ncap, (B, Tq)).astype(np.int32)
-    pos[0, 0] = mhc - 2  # no complete block yet: window only
+    r, q, kvh, raw = _attn_inputs(f"hca{B}{Tq}{H}{mhc}{ncap}{fmt}", B, Tq, H, D, ncap, R, fmt)
+    if Tq == 1:
+        pos = r.integers(mhc * ncap // 2, mhc * ncap, (B, Tq)).astype(np.int32)
+        pos[0, 0] = mhc - 2  # no complete block yet: window only
+    else:  # a chunk of consecutive positions per sequence; sequence 0's chunk starts at 0
+        p0 = r.integers(mhc * ncap // 2, mhc * ncap - Tq, B)
+        p0[0] = 0
+        pos = (p0[:, None] + np.arange(Tq)[None]).astype(np.int32)
+    assert R >= W + Tq + 3
     raw_base = np.maximum(0, pos[:, 0] - W - 3).astype(np.int32)
     qd, qv = csa.desc(up_bf16(q)[0], csa.BF16), up_bf16(q)[1]
     kvd, kvv, _ = _store_kv(csa, kvh, fmt)

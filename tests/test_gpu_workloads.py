@@ -174,6 +174,39 @@ def test_csa_prefill_2k_on_64k(gpu_lib):
     np.testing.assert_array_equal(_np(L.out)[0], g_out)
 
 
+def test_hca_prefill_2k_on_64k(gpu_lib):
+    """The chunk's 16 new blocks match the compressor's oracle; 64 query rows spread over the
+    chunk (tile edges, both ends) match the oracle's dense attention over their visible
+    blocks and window; a second step gives bitwise the same outputs."""
+    from long_context_attention_04_amd import workloads
+    name = "hca_prefill_2k_on_64k"
+    wl = synth.WORKLOADS[name]
+    L = workloads.build(name)
+    L.step()
+    torch.cuda.synchronize()
+    mh, W = wl.m_hc, wl.window
+    n0, nb = L.host["n0"], L.max_blocks
+    raw = _np(L.raw_kv.data)
+    base = L.host["raw_base"]
+    z = _np(L.z_hc).astype(np.float64)
+    want_blk = oracle.compress(raw, base, z, mh, [n0], [nb])[0][1]
+    g_kv = _np(L.kv_hc.data)[0]
+    # bf16 store of an fp32 merge: one bf16 ulp plus the fp32 merge error (2 m_hc + 4) 2^-24 max|x|
+    xmax = np.abs(raw[0, W:W + nb * mh].reshape(nb, mh, -1)).max(axis=1)
+    assert np.all(np.abs(g_kv[n0:] - want_blk) <= np.abs(want_blk) * 2.0 ** -7 + (2 * mh + 4) * 2.0 ** -24 * xmax)
+    kv = g_kv.astype(np.float64)  # attention is checked on the stored rows
+    g_out, g_lse = _np(L.out)[0], _np(L.lse)[0]
+    q = _np(L.q.data)[0]
+    rows = sorted(set(np.linspace(0, wl.tq - 1, 58).astype(int)) | {0, 1, 55, 56, 127, 128, wl.tq - 1})
+    for r in rows:
+        out, lse = oracle.hca_attn(q[None, r:r + 1], kv[None], mh, raw, base, W, L.host["t"][:, r:r + 1], wl.scale)
+        assert row_rel_err(g_out[r:r + 1], out[0]) < 2e-3
+        assert np.max(np.abs(g_lse[r] - lse[0, 0])) < 2e-3
+    L.out.fill_(float("nan"))
+    L.step()
+    np.testing.assert_array_equal(_np(L.out)[0], g_out)
+
+
 def test_hca_decode_b64_128k(gpu_lib):
     from long_context_attention_04_amd import workloads
     name = "hca_decode_b64_128k"
