@@ -171,6 +171,39 @@ size_t csa_index_query_workspace_size(int32_t batch, int32_t tq, int32_t d_model
                                       int32_t n_idx_heads, int32_t idx_dim);
 
 /* ---------------------------------------------------------------------------
+ * MLA projections on either side of attention over the shared latent rows
+ * (b-lab.team summary of DeepSeek-V4, Core Methodological Innovations 1, CSA
+ * bullet: attention reads the compressed latent entries; head h's key is
+ * W_uk[h] c and its value W_uv[h] c for a latent row c, so the key projection
+ * moves onto the query and the value projection onto the output):
+ *   csa_latent_query:  q_lat[r, h, :] = W_uk[h]^T q[r, h, :]
+ *   csa_latent_output: out[r, h, :]  = W_uv[h] o_lat[r, h, :]
+ * rows = batch * tq query rows; every array contiguous.
+ *   q       [rows, heads, head_dim] BF16.
+ *   w_uk_t  [heads, dim, head_dim] BF16: each head's key up-projection stored
+ *           transposed (row j holds column j of W_uk[h]).
+ *   q_lat   [rows, heads, dim] BF16 (the BF16 query csa_sparse_attn takes).
+ *   o_lat   [rows, heads, dim] F32 (the attention output as csa_sparse_attn /
+ *           hca_attn write it).
+ *   w_uv    [heads, head_dim, dim] BF16: each head's value up-projection.
+ *   out     [rows, heads, head_dim] of out_dtype, F32 or BF16.
+ *   ws      at least the matching *_workspace_size(...) bytes; contents on entry
+ *           do not matter.
+ * Arithmetic: bf16 products summed in fp32 in chunks of 128 along the summed
+ * dimension, added in a fixed order (results do not depend on rows); o_lat
+ * enters as bf16 hi + lo (about 16 significant bits).  Limits: rows <= 1048576,
+ * heads in [1, 65535], head_dim and dim multiples of 32 in [32, 65536], inputs
+ * and weights 16-byte aligned (CSA_ERR_SHAPE otherwise).  The workspace-size
+ * functions return 0 for unsupported shapes.
+ * ------------------------------------------------------------------------- */
+csa_status csa_latent_query(const void* q, const void* w_uk_t, int32_t rows, int32_t heads, int32_t head_dim,
+                            int32_t dim, void* q_lat, void* ws, size_t ws_bytes, void* stream);
+size_t csa_latent_query_workspace_size(int32_t rows, int32_t heads, int32_t head_dim, int32_t dim);
+csa_status csa_latent_output(const float* o_lat, const void* w_uv, int32_t rows, int32_t heads, int32_t head_dim,
+                             int32_t dim, void* out, csa_dtype out_dtype, void* ws, size_t ws_bytes, void* stream);
+size_t csa_latent_output_workspace_size(int32_t rows, int32_t heads, int32_t head_dim, int32_t dim);
+
+/* ---------------------------------------------------------------------------
  * (b) Lightning-indexer scores.  The indexer scores every compressed block
  * from low-rank projections of the query's hidden state, and its scores pick
  * the k blocks to attend to (b-lab.team summary, Core Methodological

@@ -108,6 +108,10 @@ _c = {
                               _P, _P, _SZ, _P),
     "csa_index_query_workspace_size": _proto("csa_index_query_workspace_size", _SZ, _I32, _I32, _I32, _I32, _I32,
                                              _I32),
+    "csa_latent_query": _proto("csa_latent_query", _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P),
+    "csa_latent_query_workspace_size": _proto("csa_latent_query_workspace_size", _SZ, _I32, _I32, _I32, _I32),
+    "csa_latent_output": _proto("csa_latent_output", _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _I32, _P, _SZ, _P),
+    "csa_latent_output_workspace_size": _proto("csa_latent_output_workspace_size", _SZ, _I32, _I32, _I32, _I32),
     "csa_sparse_attn_noalloc": _proto("csa_sparse_attn_noalloc", _I32, _TP, _TP, _P, _I32, _TP, _P, _I32, _P, _I32,
                                       _I32, _I32, _I32, _F, _P, _P, _P),
     "csa_quantize_mxfp4": _proto("csa_quantize_mxfp4", _I32, _P, _I64, _I32, _P, _P, _P),
@@ -254,6 +258,24 @@ def csa_index_query(h, w_dq, w_uq, w_w, batch, tq, d_model, rank, n_idx_heads, i
 
 def csa_index_query_workspace_size(batch, tq, d_model, rank, n_idx_heads, idx_dim):
     return _c["csa_index_query_workspace_size"](batch, tq, d_model, rank, n_idx_heads, idx_dim)
+
+
+def csa_latent_query(q, w_uk_t, rows, heads, head_dim, dim, q_lat, ws, ws_bytes, stream=None):
+    _check(_c["csa_latent_query"](_ptr(q), _ptr(w_uk_t), rows, heads, head_dim, dim, _ptr(q_lat), _ptr(ws), ws_bytes,
+                                  _stream(stream)))
+
+
+def csa_latent_query_workspace_size(rows, heads, head_dim, dim):
+    return _c["csa_latent_query_workspace_size"](rows, heads, head_dim, dim)
+
+
+def csa_latent_output(o_lat, w_uv, rows, heads, head_dim, dim, out, out_dtype, ws, ws_bytes, stream=None):
+    _check(_c["csa_latent_output"](_ptr(o_lat), _ptr(w_uv), rows, heads, head_dim, dim, _ptr(out), out_dtype,
+                                   _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def csa_latent_output_workspace_size(rows, heads, head_dim, dim):
+    return _c["csa_latent_output_workspace_size"](rows, heads, head_dim, dim)
 
 
 def csa_sparse_attn_noalloc(q, kv_cmp, idx, k, kv_raw, raw_base, window, q_pos, batch, tq, heads, dim, scale, out,

@@ -164,6 +164,22 @@ struct IndexQueryArgs {
 size_t index_query_workspace_bytes(int64_t rows, int d_model, int rank, int n_idx_heads, int idx_dim);
 hipError_t launch_index_query(const IndexQueryArgs& a, hipStream_t s);
 
+// Per-head products Y_z = X_z . W_z^T (MLA absorbed query, output up-projection):
+// X [rows, heads, K] (bf16, or fp32 taken as bf16 hi + lo), W [heads, N, K] bf16,
+// Y [rows, heads, N] fp32 or bf16; ws holds latent_proj_workspace_bytes.
+struct LatentProjArgs {
+  const void* x;
+  int x_f32;
+  const void* w;
+  int64_t rows;
+  int heads, K, N;
+  void* y;
+  int y_bf16;
+  void* ws;
+};
+size_t latent_proj_workspace_bytes(int64_t rows, int heads, int K, int N);
+hipError_t launch_latent_proj(const LatentProjArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- measurement
 constexpr int kStreamReadBlocks = 2048;  // workgroups of the streaming-read probe (one sink word each)
 hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t s);
