@@ -58,7 +58,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=120)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="csa_decode_1m_b8")
-    ap.add_argument("--kv", choices=("bf16", "fp8"), default="bf16", help="KV format of the hybrid pair")
+    ap.add_argument("--kv", choices=("bf16", "fp8", "mxfp4"), default="bf16",
+                    help="KV format: hybrid pair bf16 | fp8; 1M decode bf16 | mxfp4 (FP4 KV caching)")
     ap.add_argument("--sets", type=int, default=6)
     ap.add_argument("--no-graph", action="store_true", help="time plain launches instead of graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -209,17 +210,18 @@ def time_oracle(sample, seconds, units) -> dict:
 class CsaDecode:
     """The headline: CSA decode at 1M context, batch 8, MXFP4 indexer (fused index+top-k)."""
 
-    def __init__(self, name, sets, torch):
+    def __init__(self, name, sets, torch, kv="bf16"):
         from long_context_attention_04_amd import workloads
         import synth
         self.wl = synth.WORKLOADS[name]
-        self.layers = [workloads.build(name, salt=s) for s in range(sets)]
+        self.layers = [workloads.build(name, salt=s, kv_fmt=kv) for s in range(sets)]
         L = self.layers[0]
         self.tokens = L.B
         B, N, k, W, H, D = L.B, L.n_cap, L.k, L.W, L.H, L.D
-        comp = B * (L.m * (D * 2 + L.dI * 4) + D * 2 + KEY_BYTES)  # the step's compressions
+        row = D * 2 if kv == "bf16" else D // 2 + D // 32  # stored bytes per KV row (MXFP4: codes + scales)
+        comp = B * (L.m * (row + L.dI * 4) + row + KEY_BYTES)  # the step's compressions
         qw = B * L.HI * (L.dI * 4 + 4)
-        self.bytes = {"keys": B * N * KEY_BYTES, "gather": B * (k + W) * D * 2,
+        self.bytes = {"keys": B * N * KEY_BYTES, "gather": B * (k + W) * row,
                       "q_out_lse": B * H * D * 2 + B * H * D * 4 + B * H * 4, "idx": B * k * 4, "q_idx_w": qw,
                       "compress": comp}
         ns = (N + SLICE - 1) // SLICE
@@ -229,10 +231,11 @@ class CsaDecode:
                          "bound": "hbm", "work": self.bytes["keys"] + qw + comp,
                          "work_note": "keys read once + q_idx and w + the step's compressions"}
         self.dtype = "bf16+mxfp4"
+        self.kv = kv
         wl = self.wl
         self.config = {"workload": name, "batch": wl.batch, "context": wl.extra["context"], "heads": wl.heads,
                        "latent_dim": wl.dim, "idx_heads": wl.idx_heads, "idx_dim": wl.idx_dim, "topk": wl.topk,
-                       "window": wl.window, "m": wl.m, "kv": wl.kv_dtype, "indexer": wl.idx_dtype}
+                       "window": wl.window, "m": wl.m, "kv": kv, "indexer": wl.idx_dtype}
         self.metric = METRIC
         self.torch = torch
 
@@ -564,7 +567,10 @@ def make_job(args, torch):
     import synth
     kind = synth.WORKLOADS[args.workload].kind
     if kind == "csa_decode" and args.workload == "csa_decode_1m_b8":
-        return CsaDecode(args.workload, args.sets, torch)
+        if args.kv == "fp8":
+            print("the 1M decode runs with bf16 or mxfp4 KV", file=sys.stderr)
+            sys.exit(2)
+        return CsaDecode(args.workload, args.sets, torch, args.kv)
     if kind == "csa_prefill":
         return CsaPrefill(args.workload, min(args.sets, 3), torch)
     if kind == "hca_decode":

@@ -393,6 +393,55 @@ csa_status csa_index_query(const csa_tensor* h, const csa_tensor* w_dq, const cs
   return from_hip(csa::launch_index_query(a, (hipStream_t)stream), "csa_index_query launch");
 }
 
+static bool latent_shape_ok(int32_t rows, int32_t heads, int32_t head_dim, int32_t dim) {
+  const auto dim_ok = [](int32_t x) { return x >= 32 && x <= 65536 && x % 32 == 0; };
+  return rows >= 0 && rows <= (1 << 20) && heads >= 1 && heads <= 65535 && dim_ok(head_dim) && dim_ok(dim);
+}
+
+size_t csa_latent_query_workspace_size(int32_t rows, int32_t heads, int32_t head_dim, int32_t dim) {
+  if (!latent_shape_ok(rows, heads, head_dim, dim)) return 0;
+  return csa::latent_proj_workspace_bytes(rows, heads, head_dim, dim);
+}
+
+size_t csa_latent_output_workspace_size(int32_t rows, int32_t heads, int32_t head_dim, int32_t dim) {
+  if (!latent_shape_ok(rows, heads, head_dim, dim)) return 0;
+  return csa::latent_proj_workspace_bytes(rows, heads, dim, head_dim);
+}
+
+static csa_status latent_common(const char* name, const void* x, const void* w, int32_t rows, int32_t heads,
+                                int32_t head_dim, int32_t dim, const void* y, void* ws, size_t ws_bytes, size_t need) {
+  REQUIRE(x && w && y, CSA_ERR_NULL, "%s: an input, weight or output pointer is NULL", name);
+  REQUIRE(latent_shape_ok(rows, heads, head_dim, dim), CSA_ERR_SHAPE,
+          "%s: need 0 <= rows <= 1048576, heads in [1, 65535], head_dim and dim multiples of 32 in [32, 65536] "
+          "(got rows=%d heads=%d head_dim=%d dim=%d)", name, rows, heads, head_dim, dim);
+  const auto aligned = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+  REQUIRE(aligned(x) && aligned(w), CSA_ERR_SHAPE, "%s: input and weights must be 16-byte aligned", name);
+  REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "%s needs %zu workspace bytes, got %zu", name, need,
+          ws_bytes);
+  return CSA_OK;
+}
+
+csa_status csa_latent_query(const void* q, const void* w_uk_t, int32_t rows, int32_t heads, int32_t head_dim,
+                            int32_t dim, void* q_lat, void* ws, size_t ws_bytes, void* stream) {
+  const size_t need = latent_shape_ok(rows, heads, head_dim, dim)
+                          ? csa::latent_proj_workspace_bytes(rows, heads, head_dim, dim) : 0;
+  csa_status st = latent_common("csa_latent_query", q, w_uk_t, rows, heads, head_dim, dim, q_lat, ws, ws_bytes, need);
+  if (st != CSA_OK) return st;
+  const csa::LatentProjArgs a{q, 0, w_uk_t, rows, heads, head_dim, dim, q_lat, 1, ws};
+  return from_hip(csa::launch_latent_proj(a, (hipStream_t)stream), "csa_latent_query launch");
+}
+
+csa_status csa_latent_output(const float* o_lat, const void* w_uv, int32_t rows, int32_t heads, int32_t head_dim,
+                             int32_t dim, void* out, csa_dtype out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  const size_t need = latent_shape_ok(rows, heads, head_dim, dim)
+                          ? csa::latent_proj_workspace_bytes(rows, heads, dim, head_dim) : 0;
+  csa_status st = latent_common("csa_latent_output", o_lat, w_uv, rows, heads, head_dim, dim, out, ws, ws_bytes, need);
+  if (st != CSA_OK) return st;
+  REQUIRE(out_dtype == CSA_F32 || out_dtype == CSA_BF16, CSA_ERR_DTYPE, "csa_latent_output: out must be F32 or BF16");
+  const csa::LatentProjArgs a{o_lat, 1, w_uv, rows, heads, dim, head_dim, out, out_dtype == CSA_BF16, ws};
+  return from_hip(csa::launch_latent_proj(a, (hipStream_t)stream), "csa_latent_output launch");
+}
+
 size_t csa_attn_workspace_size(int32_t batch, int32_t tq, int32_t heads, int32_t dim, int32_t n_entries_max) {
   if (batch < 0 || tq < 0 || heads < 1 || dim < 1 || n_entries_max < 0) return 0;
   return csa::attn_workspace_bytes((int64_t)batch * tq, heads, dim, n_entries_max, tq);
@@ -445,23 +494,39 @@ static csa_status attn_common(const csa_tensor* q, const csa_tensor* kv, const i
   REQUIRE(raw_base && q_pos && out, CSA_ERR_NULL, "raw_base/q_pos/out is NULL");
   REQUIRE(batch >= 0 && tq >= 0 && window >= 0, CSA_ERR_SHAPE, "negative batch, tq or window");
   REQUIRE(heads >= 1 && dim >= 1, CSA_ERR_SHAPE, "heads and dim must be >= 1");
-  REQUIRE(kv->dtype == kv_raw->dtype, CSA_ERR_DTYPE, "compressed and raw rows must share a dtype");
+  REQUIRE(kv->dtype == kv_raw->dtype || (kv->dtype == CSA_MXFP4 && kv_raw->dtype == CSA_BF16), CSA_ERR_DTYPE,
+          "compressed and raw rows must share a dtype (MXFP4 compressed rows take BF16 raw rows)");
+  REQUIRE(kv_raw->dtype != CSA_MXFP4, CSA_ERR_DTYPE, "raw rows are F32, BF16 or FP8_E4M3 (MXFP4 compressed rows "
+          "take BF16 raw rows)");
   if (kv->dtype == CSA_F32) {
     REQUIRE(q->dtype == CSA_F32, CSA_ERR_DTYPE, "F32 caches take an F32 query");
     REQUIRE(dim <= 512 && dim % 4 == 0 && heads <= 64, CSA_ERR_UNSUPPORTED,
             "F32 attention supports dim <= 512 (multiple of 4) and heads <= 64");
     REQUIRE(csa::attn_plain_fits(n_entries_max), CSA_ERR_UNSUPPORTED, "F32 attention supports at most 8192 entries per query");
-  } else if (kv->dtype == CSA_BF16 || kv->dtype == CSA_FP8_E4M3) {
-    REQUIRE(q->dtype == CSA_BF16, CSA_ERR_DTYPE, "BF16/FP8 caches take a BF16 query");
+  } else if (kv->dtype == CSA_BF16 || kv->dtype == CSA_FP8_E4M3 || kv->dtype == CSA_MXFP4) {
+    REQUIRE(q->dtype == CSA_BF16, CSA_ERR_DTYPE, "BF16/FP8/MXFP4 caches take a BF16 query");
     REQUIRE(dim == 512 && heads % 16 == 0 && heads <= 64, CSA_ERR_UNSUPPORTED,
-            "BF16/FP8 attention supports dim == 512 and heads a multiple of 16 up to 64 (got %d, %d)", dim, heads);
+            "BF16/FP8/MXFP4 attention supports dim == 512 and heads a multiple of 16 up to 64 (got %d, %d)", dim,
+            heads);
+    // rows are read 16 (BF16), 8 (FP8) or 4 (MXFP4) bytes per lane; the query 16 bytes per lane
+    const int64_t align = kv->dtype == CSA_BF16 ? 16 : kv->dtype == CSA_FP8_E4M3 ? 8 : 4;
+    const int64_t esz = kv->dtype == CSA_BF16 ? 2 : 1;  // stride units in bytes (MXFP4 strides are bytes)
+    const auto rows_aligned = [](const csa_tensor* t, int64_t al, int64_t es) {
+      return (uintptr_t)t->data % al == 0 && (t->stride_b * es) % al == 0 && (t->stride_row * es) % al == 0;
+    };
+    const bool raw_bf16 = kv_raw->dtype == CSA_BF16;
+    REQUIRE(rows_aligned(kv, align, esz) && rows_aligned(kv_raw, raw_bf16 ? 16 : align, raw_bf16 ? 2 : esz),
+            CSA_ERR_SHAPE, "cache rows must start on %lld-byte boundaries (data and strides; BF16 rows 16)",
+            (long long)align);
+    REQUIRE((uintptr_t)q->data % 16 == 0 && q->stride_b % 8 == 0 && q->stride_row % 8 == 0, CSA_ERR_SHAPE,
+            "q must be 16-byte aligned with strides a multiple of 8 elements");
     const int split = csa::attn_split_size(tq, n_entries_max);
     const int64_t nsplit = ((int64_t)std::max(n_entries_max, 1) + split - 1) / split;
     REQUIRE(nsplit <= csa::kAttnMaxSplits, CSA_ERR_UNSUPPORTED,
-            "BF16/FP8 attention supports at most %d entries per query (got %d)",
+            "BF16/FP8/MXFP4 attention supports at most %d entries per query (got %d)",
             csa::kAttnMaxSplits * csa::kAttnMaxSplitEntries, n_entries_max);
   } else {
-    return fail(CSA_ERR_DTYPE, "attention caches must be F32, BF16 or FP8_E4M3");
+    return fail(CSA_ERR_DTYPE, "attention caches must be F32, BF16, FP8_E4M3 or MXFP4");
   }
   const size_t need = csa::attn_workspace_bytes((int64_t)batch * tq, heads, dim, n_entries_max, tq);
   if (need > 0 && !use_scratch)

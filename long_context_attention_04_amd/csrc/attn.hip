@@ -77,22 +77,28 @@ struct EntrySrc {
   int64_t kv_rs, raw_rs;  // row pitches in bytes
   const float* kv_sc;   // fp8 row scales (nullptr otherwise)
   const float* win_sc;
-  int64_t kv_ss, raw_ss;
+  const uint8_t* kv_bs;   // MXFP4 block scales: dim / 32 bytes per row (nullptr otherwise)
+  const uint8_t* win_bs;
+  int64_t kv_ss, raw_ss;  // scale row pitches (fp8: floats, MXFP4: bytes)
   const int32_t* idx_row;  // CSA selection of this query row (nullptr: HCA, entry e is block e)
 };
 
-// eb: bytes per element of the caches (a compile-time constant at every call site)
+// eb, ebr: bytes per stride unit of the compressed and of the raw rows (elements;
+// MXFP4 strides are in bytes), compile-time constants at every call site
 // rb: raw_base[r.b], the absolute position of the sequence's raw row 0.
-__device__ __forceinline__ EntrySrc entry_src(const AttnArgs& a, const RowInfo& r, int row, int eb, int rb) {
+__device__ __forceinline__ EntrySrc entry_src(const AttnArgs& a, const RowInfo& r, int row, int eb, int ebr, int rb) {
   EntrySrc s;
   const int64_t rr0 = (int64_t)r.w0 - rb;  // raw row of the first window entry
   s.kv0 = (const uint8_t*)a.kv.data + (int64_t)r.b * a.kv.sb * eb;
-  s.win0 = (const uint8_t*)a.raw.data + ((int64_t)r.b * a.raw.sb + rr0 * a.raw.sr) * eb;
+  s.win0 = (const uint8_t*)a.raw.data + ((int64_t)r.b * a.raw.sb + rr0 * a.raw.sr) * ebr;
   s.kv_rs = a.kv.sr * eb;
-  s.raw_rs = a.raw.sr * eb;
+  s.raw_rs = a.raw.sr * ebr;
   const bool fp8 = a.kv.dtype == CSA_FP8_E4M3;
   s.kv_sc = fp8 && a.kv.scale ? (const float*)a.kv.scale + (int64_t)r.b * a.kv.ssb : nullptr;
   s.win_sc = fp8 && a.raw.scale ? (const float*)a.raw.scale + (int64_t)r.b * a.raw.ssb + rr0 * a.raw.ssr : nullptr;
+  const bool fp4 = a.kv.dtype == CSA_MXFP4;
+  s.kv_bs = fp4 ? (const uint8_t*)a.kv.scale + (int64_t)r.b * a.kv.ssb : nullptr;
+  s.win_bs = nullptr;  // MXFP4 caches take bf16 window rows
   s.kv_ss = a.kv.ssr;
   s.raw_ss = a.raw.ssr;
   s.idx_row = a.idx ? a.idx + (int64_t)row * a.k : nullptr;
@@ -164,6 +170,22 @@ __device__ __forceinline__ void decode_block(int id, int nhg, int nsplit_max, in
   *split = c % nsplit_max;
 }
 
+// Row formats of the MFMA path.
+constexpr int kFmtBf16 = 0, kFmtFp8 = 1, kFmtFp4 = 2;
+
+// Eight MXFP4 elements (one 32-bit word of codes, element 2i in the low nibble of
+// byte i) times their block scale 2^(sb - 127), as bf16: exact for every code and
+// every scale that keeps the value in the normal range (the products are powers of
+// two times at most two significant bits).
+__device__ __forceinline__ v8bf fp4x8_to_bf16(uint32_t codes, uint32_t sb) {
+  const float sc = __uint_as_float(sb ? sb << 23 : 0x00400000u);  // 2^(sb-127); sb = 0 is 2^-127
+  const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0);
+  const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1);
+  const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2);
+  const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3);
+  return (v8bf){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 __device__ __forceinline__ float lane_max4rows(float x) {  // max over the 4 lanes n, n+16, n+32, n+48
   auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
@@ -222,7 +244,7 @@ __device__ __forceinline__ int swz_off(int r, int chunk16) { return r * kRowByte
 // The scalars the prologue depends on come first in the argument list: they are
 // preloaded into scalar registers at launch (the rest of the arguments is read from
 // memory, one round trip that overlaps the position and slot loads).
-template <bool FP8, int NW, int CH>
+template <int FMT, int NW, int CH>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunk_kernel(
     const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ raw_base, int k, int tq, int window, int m_hc,
@@ -230,6 +252,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   constexpr int kT = (CH + 15) / 16;             // 16-entry tiles of a full chunk
   constexpr int kQkT = (kT + NW - 1) / NW;       // QK tiles per wave
   constexpr int kCols = 512 / NW, kNT = kCols / 16;  // PV: latent columns per wave, their 16-column tiles
+  constexpr int kRW = (CH + NW - 1) / NW;        // rows a wave loads per chunk
+  constexpr bool FP8 = FMT == kFmtFp8;
   int row, s, hg;
   decode_block(blockIdx.x, nhg, nsplit_max, rows, &row, &s, &hg);
   if (row >= rows) return;
@@ -249,7 +273,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   const RowInfo ri = row_info(q_pos, idx != nullptr, k, tq, window, m_hc, row);
   // (computed before the early exit below: its argument reads then join the
   // position's round trip)
-  const EntrySrc src = entry_src(a, ri, row, FP8 ? 1 : 2, rb);
+  const EntrySrc src = entry_src(a, ri, row, FMT == kFmtBf16 ? 2 : 1, FMT == kFmtFp8 ? 1 : 2, rb);
   const int partial = nsplit_max > 1;
   const int nsplit = max(1, (ri.n_tot + split - 1) / split);
   if (s >= nsplit) return;  // workgroup-uniform, before any barrier
@@ -291,26 +315,48 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     // slot of the wave's i-th row, so no row waits on an LDS read)
     const int nrows = min(nmt * 16, CH);
     const int jw = lane < (nrows - w + NW - 1) / NW ? L.sidx[w + NW * lane] : -1;
-    for (int r = w, ri8 = 0; r < nrows; r += NW, ++ri8) {
-      const int e = c0 + r;
-      const int j = __builtin_amdgcn_readlane(jw, ri8);
-      const bool live = j >= 0;
-      const bool cmp = e < ri.n_cmp;
-      const gbyte* rp = !live ? dummy
-                              : cmp ? (const gbyte*)src.kv0 + (int64_t)j * src.kv_rs
-                                    : (const gbyte*)src.win0 + (int64_t)(e - ri.n_cmp) * src.raw_rs;
-      if constexpr (!FP8) {
+    // fp8 / MXFP4 rows pass through registers: all of the wave's rows are requested
+    // first, then widened into LDS once the query heads and next slots are in flight
+    // (MXFP4 caches take bf16 window rows, which go straight to LDS)
+    uint32_t rc[kRW][FP8 ? 2 : 1];  // the lane's 8 elements as stored
+    uint32_t rs[kRW];               // fp8: row scale bits; MXFP4: block scale byte
+    if constexpr (FMT == kFmtBf16) {
+      for (int r = w, ri8 = 0; r < nrows; r += NW, ++ri8) {
+        const int e = c0 + r;
+        const int j = __builtin_amdgcn_readlane(jw, ri8);
+        const gbyte* rp = j < 0 ? dummy
+                                : e < ri.n_cmp ? (const gbyte*)src.kv0 + (int64_t)j * src.kv_rs
+                                               : (const gbyte*)src.win0 + (int64_t)(e - ri.n_cmp) * src.raw_rs;
         // lane l fills LDS chunk l of the row with the row's chunk l ^ swz(r)
         __builtin_amdgcn_global_load_lds(rp + 16 * (lane ^ swz(r)), (__attribute__((address_space(3))) void*)&L.rows[r][0],
                                          16, 0, 0);
-      } else {
-        const float* sp = !live ? nullptr
-                                : cmp ? (src.kv_sc ? src.kv_sc + (int64_t)j * src.kv_ss : nullptr)
-                                      : (src.win_sc ? src.win_sc + (int64_t)(e - ri.n_cmp) * src.raw_ss : nullptr);
-        const u32x2 raw = live ? *(const __attribute__((address_space(1))) u32x2*)(rp + 8 * lane) : (u32x2){0u, 0u};
-        const float sc = sp ? *sp : 1.f;
-        *(v8bf*)&rowb[swz_off(r, lane)] = widen8<true>(raw);
-        if (live && lane == 0) L.esl[r] = sc;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kRW; ++i) {
+        const int r = w + NW * i, e = c0 + r;
+        rc[i][0] = 0u;
+        if constexpr (FP8) rc[i][1] = 0u;
+        rs[i] = FP8 ? __float_as_uint(1.f) : 127u;
+        const int j = __builtin_amdgcn_readlane(jw, i);
+        if (r < nrows && j >= 0) {  // wave-uniform
+          const bool cmp = e < ri.n_cmp;
+          const int64_t er = cmp ? j : e - ri.n_cmp;
+          const gbyte* rp = (const gbyte*)(cmp ? src.kv0 : src.win0) + er * (cmp ? src.kv_rs : src.raw_rs);
+          if constexpr (FP8) {
+            const u32x2 v = *(const __attribute__((address_space(1))) u32x2*)(rp + 8 * lane);
+            rc[i][0] = v[0];
+            rc[i][1] = v[1];
+            const float* sp = cmp ? src.kv_sc : src.win_sc;
+            if (sp) rs[i] = __float_as_uint(sp[er * (cmp ? src.kv_ss : src.raw_ss)]);
+          } else if (cmp) {
+            rc[i][0] = *(const __attribute__((address_space(1))) uint32_t*)(rp + 4 * lane);
+            rs[i] = *(const __attribute__((address_space(1))) uint8_t*)(src.kv_bs + er * src.kv_ss + lane / 4);
+          } else {  // bf16 window row
+            __builtin_amdgcn_global_load_lds(rp + 16 * (lane ^ swz(r)),
+                                             (__attribute__((address_space(3))) void*)&L.rows[r][0], 16, 0, 0);
+          }
+        }
       }
     }
     if (c0 == e_begin) {  // the 16 query heads to LDS, 16 / NW per wave
@@ -322,6 +368,20 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     // the next chunk's slots, requested while this chunk's rows are in flight
     jn = -1;
     if (idx_row && t < csz && c0 + csz + t < min(k, e_end)) jn = idx_row[c0 + csz + t];
+    if constexpr (FMT != kFmtBf16) {
+#pragma unroll
+      for (int i = 0; i < kRW; ++i) {
+        const int r = w + NW * i;
+        if (r < nrows) {
+          if constexpr (FP8) {
+            *(v8bf*)&rowb[swz_off(r, lane)] = widen8<true>((u32x2){rc[i][0], rc[i][1]});
+            if (lane == 0 && __builtin_amdgcn_readlane(jw, i) >= 0) L.esl[r] = __uint_as_float(rs[i]);
+          } else if (!(c0 + r >= ri.n_cmp && __builtin_amdgcn_readlane(jw, i) >= 0)) {  // not a window row
+            *(v8bf*)&rowb[swz_off(r, lane)] = fp4x8_to_bf16(rc[i][0], rs[i]);
+          }
+        }
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // rows (and the first time, the query heads) in LDS
     if (c0 == e_begin) {
@@ -567,7 +627,7 @@ constexpr int kPlainMaxEntries = 8192;
 __global__ __launch_bounds__(kPlainThreads) void attn_plain_kernel(AttnArgs a) {
   const int row = blockIdx.x, h = blockIdx.y;
   const RowInfo ri = row_info(a, row);
-  const EntrySrc src = entry_src(a, ri, row, 4, a.raw_base[ri.b]);
+  const EntrySrc src = entry_src(a, ri, row, 4, 4, a.raw_base[ri.b]);
   __shared__ float logit[kPlainMaxEntries];
   __shared__ float qs[512];
   __shared__ float red[kPlainThreads / kWave];
@@ -624,15 +684,23 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
   // Decode: 8 waves and chunks of 136 entries (one workgroup per CU; a split of 272
   // entries is two chunks).  Many queries per sequence: 4 waves and chunks of 56
   // (75 KB of LDS: two workgroups per CU, one computing while the other gathers).
-  const bool fp8 = a.kv.dtype == CSA_FP8_E4M3, many = a.tq != 1;
+  const int fmt = a.kv.dtype == CSA_FP8_E4M3 ? kFmtFp8 : a.kv.dtype == CSA_MXFP4 ? kFmtFp4 : kFmtBf16;
+  const bool many = a.tq != 1;
   const dim3 grid((unsigned)blocks);
 #define CSA_ATTN_LAUNCH(F, NW, CH)                                                                                \
   hipLaunchKernelGGL((attn_chunk_kernel<F, NW, CH>), grid, dim3(NW * kWave), 0, s, a.q_pos, a.idx, a.raw_base, a.k, \
                      a.tq, a.window, a.m_hc, split, nsplit_max, nhg, (int)rows, a)
-  if (fp8 && many) CSA_ATTN_LAUNCH(true, 4, 56);
-  else if (fp8) CSA_ATTN_LAUNCH(true, 8, 136);
-  else if (many) CSA_ATTN_LAUNCH(false, 4, 56);
-  else CSA_ATTN_LAUNCH(false, 8, 136);
+#define CSA_ATTN_SHAPES(F)              \
+  if (many) CSA_ATTN_LAUNCH(F, 4, 56); \
+  else CSA_ATTN_LAUNCH(F, 8, 136);
+  if (fmt == kFmtFp8) {
+    CSA_ATTN_SHAPES(kFmtFp8)
+  } else if (fmt == kFmtFp4) {
+    CSA_ATTN_SHAPES(kFmtFp4)
+  } else {
+    CSA_ATTN_SHAPES(kFmtBf16)
+  }
+#undef CSA_ATTN_SHAPES
 #undef CSA_ATTN_LAUNCH
   if (partial)
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)rows, a.heads), dim3(128), 0, s, a, split, nsplit_max, rows);

@@ -297,10 +297,12 @@ def _poison_beyond(st: Stored, visible: np.ndarray):
         st.data[b, int(v):] = float("nan")
 
 
-def build_csa_decode(wl: synth.Workload, salt: int = 0) -> CsaLayer:
+def build_csa_decode(wl: synth.Workload, salt: int = 0, kv_fmt: str | None = None) -> CsaLayer:
     """A CSA decode step at position L-1 over a context of L tokens (L % m == 0, so the
     step completes block L/m - 1).  Blocks before it are drawn directly for contexts
-    beyond 64k tokens and produced by the compressor from raw rows otherwise."""
+    beyond 64k tokens and produced by the compressor from raw rows otherwise.  kv_fmt
+    overrides the workload's KV format (e.g. "mxfp4": FP4 KV caching of the compressed
+    entries and the window rows)."""
     B, m, H, D, HI, dI, k, W = wl.batch, wl.m, wl.heads, wl.dim, wl.idx_heads, wl.idx_dim, wl.topk, wl.window
     L = wl.extra["context"]
     N = L // m
@@ -312,9 +314,9 @@ def build_csa_decode(wl: synth.Workload, salt: int = 0) -> CsaLayer:
         synth.device_normal(wl, "raw_kv", (B, R, D), DEV, salt=salt)
     raw_ik = torch.as_tensor(synth.normal(wl, "raw_ik", (B, R, dI), salt), device=DEV) if not direct else \
         synth.device_normal(wl, "raw_ik", (B, R, dI), DEV, salt=salt)
-    kv_fmt = wl.kv_dtype
+    kv_fmt = kv_fmt or wl.kv_dtype
     ik_fmt = wl.idx_dtype
-    raw_kv_s = store(raw_kv, kv_fmt)
+    raw_kv_s = store(raw_kv, "bf16" if kv_fmt == "mxfp4" else kv_fmt)  # MXFP4 caches keep bf16 raw rows
     raw_ik_s = Stored(raw_ik.contiguous(), F32)
     z_kv = _f32(synth.normal(wl, "z_kv", (m,), salt))
     z_ik = _f32(synth.normal(wl, "z_ik", (m,), salt))
@@ -333,6 +335,8 @@ def build_csa_decode(wl: synth.Workload, salt: int = 0) -> CsaLayer:
             k_idx.data[:, N - 1] = float("nan")
         if kv_cmp.dtype in (F32, BF16):
             kv_cmp.data[:, N - 1] = float("nan")
+        elif kv_cmp.dtype == MXFP4:
+            kv_cmp.scale[:, N - 1] = 0xFF  # NaN scale until the step compresses the block
     else:
         kv_cmp = empty_stored(B, N, D, kv_fmt)
         k_idx = empty_stored(B, N, dI, ik_fmt)
@@ -494,7 +498,7 @@ def build_hybrid_decode(wl: synth.Workload, kv_fmt: str = "bf16", salt: int = 0)
 def build(name: str, salt: int = 0, kv_fmt: str | None = None):
     wl = synth.WORKLOADS[name]
     if wl.kind == "csa_decode":
-        return build_csa_decode(wl, salt)
+        return build_csa_decode(wl, salt, kv_fmt)
     if wl.kind == "csa_prefill":
         return build_csa_prefill(wl, salt)
     if wl.kind == "hca_decode":

@@ -217,7 +217,13 @@ def test_attention_rejects_and_workspace():
     expect(E_UNSUP, sparse(heads=80))
     expect(E_WS, sparse(wsb=need - 1))
     expect(E_WS, sparse(ws=None))
-    expect(E_DTYPE, sparse(kv=T(csa.MXFP4, scale=P), raw=T(csa.MXFP4, scale=P)))
+    expect(E_DTYPE, sparse(kv=T(csa.MXFP4, scale=P), raw=T(csa.FP8_E4M3)), match="share a dtype")
+    expect(E_DTYPE, sparse(kv=T(csa.MXFP4, scale=P), raw=T(csa.MXFP4, scale=P)), match="raw rows")
+    expect(E_NULL, sparse(kv=T(csa.MXFP4), raw=T(csa.BF16)))  # MXFP4 rows need their scales
+    expect(E_SHAPE, sparse(kv=T(csa.MXFP4, scale=P, sr=270), raw=T(csa.BF16)), match="boundaries")
+    expect(E_SHAPE, sparse(kv=T(csa.MXFP4, scale=P), raw=T(csa.BF16, sr=260)), match="boundaries")
+    expect(E_SHAPE, sparse(kv=T(csa.BF16, data=P + 8)), match="boundaries")
+    expect(E_SHAPE, sparse(q=T(csa.BF16, sr=500)), match="16-byte")
     expect(E_UNSUP, sparse(q=T(csa.F32), kv=T(csa.F32), raw=T(csa.F32), k=9000, W=0, heads=16, dim=128))
     # more than 64 splits of 2048 entries: rejected on the host, not by a failed launch
     big = csa.csa_attn_workspace_size(8, 1, 64, 512, 131072 + 129)
@@ -270,6 +276,31 @@ def test_index_query_rejects():
     expect(E_SHAPE, call(wuq=T(csa.BF16, sb=0, sr=512)), match="shorter")
     expect(E_WS, call(wsb=need - 1))
     expect(E_WS, call(ws=None))
+
+
+def test_latent_projections_reject():
+    nq = csa.csa_latent_query_workspace_size(8, 64, 128, 512)
+    no = csa.csa_latent_output_workspace_size(8, 64, 128, 512)
+    assert nq > 0 and no > 0
+    assert csa.csa_latent_query_workspace_size(8, 64, 100, 512) == 0  # head_dim not a multiple of 32
+    assert csa.csa_latent_output_workspace_size(8, 0, 128, 512) == 0
+
+    def query(q=P, w=P, rows=8, heads=64, dh=128, d=512, out=P, ws=P, wsb=nq):
+        return lambda stream: csa.csa_latent_query(q, w, rows, heads, dh, d, out, ws, wsb, stream)
+
+    def output(o=P, w=P, rows=8, heads=64, dh=128, d=512, out=P, dt=csa.F32, ws=P, wsb=no):
+        return lambda stream: csa.csa_latent_output(o, w, rows, heads, dh, d, out, dt, ws, wsb, stream)
+
+    expect(E_NULL, query(q=None))
+    expect(E_NULL, output(out=None))
+    expect(E_SHAPE, query(dh=100))
+    expect(E_SHAPE, query(d=65568))
+    expect(E_SHAPE, output(heads=0))
+    expect(E_SHAPE, output(rows=-1))
+    expect(E_SHAPE, query(w=P + 8), match="aligned")
+    expect(E_WS, query(wsb=nq - 1))
+    expect(E_WS, output(ws=None))
+    expect(E_DTYPE, output(dt=csa.FP8_E4M3), match="F32 or BF16")
 
 
 # ---------------------------------------------------------------------------- quantisers

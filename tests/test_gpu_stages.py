@@ -572,7 +572,7 @@ def test_csa_sparse_attn(gpu_lib, B, Tq, H, D, k, W, fmt, tol):
     qd = csa.desc(up(q), csa.F32) if fmt == "f32" else csa.desc(up_bf16(q)[0], csa.BF16)
     qv = q.astype(np.float64) if fmt == "f32" else up_bf16(q)[1]
     kvd, kvv, _ = _store_kv(csa, kvc, fmt)
-    rawd, rawv, _ = _store_kv(csa, raw, fmt)
+    rawd, rawv, _ = _store_kv(csa, raw, "bf16" if fmt == "fp4" else fmt)  # MXFP4 caches take bf16 raw rows
     out = torch.full((B, Tq, H, D), float("nan"), device="cuda")
     lse = torch.full((B, Tq, H), float("nan"), device="cuda")
     ws = workspace(csa.csa_attn_workspace_size(B, Tq, H, D, k + W))
@@ -611,7 +611,7 @@ def test_hca_attn(gpu_lib, B, Tq, H, mhc, ncap, W, fmt, tol):
     raw_base = np.maximum(0, pos[:, 0] - W - 3).astype(np.int32)
     qd, qv = csa.desc(up_bf16(q)[0], csa.BF16), up_bf16(q)[1]
     kvd, kvv, _ = _store_kv(csa, kvh, fmt)
-    rawd, rawv, _ = _store_kv(csa, raw, fmt)
+    rawd, rawv, _ = _store_kv(csa, raw, "bf16" if fmt == "fp4" else fmt)  # MXFP4 caches take bf16 raw rows
     out = torch.full((B, Tq, H, D), float("nan"), device="cuda")
     lse = torch.full((B, Tq, H), float("nan"), device="cuda")
     ws = workspace(csa.csa_attn_workspace_size(B, Tq, H, D, ncap + W))

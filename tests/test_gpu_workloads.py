@@ -113,6 +113,44 @@ def test_csa_decode_1m_b8(gpu_lib):
     np.testing.assert_array_equal(_np(L.lse), g_lse)
 
 
+def test_csa_decode_1m_b8_mxfp4_kv(gpu_lib):
+    """FP4 KV caching: the 1M decode with MXFP4 compressed entries (bf16 window rows).  The
+    selection is the bf16-KV step's (the indexer does not read the KV cache); the new block
+    is compressed into MXFP4 within the format's error of the oracle's merge; attention over the
+    stored (dequantised) rows matches the oracle for all 8 sequences."""
+    from long_context_attention_04_amd import workloads
+    name = "csa_decode_1m_b8"
+    wl = synth.WORKLOADS[name]
+    Lb = workloads.build(name)
+    Lb.step()
+    torch.cuda.synchronize()
+    idx_bf16 = _np(Lb.idx)
+    del Lb
+    L = workloads.build(name, kv_fmt="mxfp4")
+    assert L.kv_cmp.dtype == gpu_lib.MXFP4 and L.raw_kv.dtype == gpu_lib.BF16
+    L.step()
+    torch.cuda.synchronize()
+    g_idx, g_out, g_lse = _np(L.idx), _np(L.out), _np(L.lse)
+    np.testing.assert_array_equal(g_idx, idx_bf16)
+    B, N, m, t = wl.batch, L.n_cap, wl.m, wl.extra["context"] - 1
+    raw_kv = _np(L.raw_kv.data)
+    base = L.host["raw_base"]
+    z_kv = _np(L.z_kv).astype(np.float64)
+    for b in range(B):
+        sel = torch.as_tensor(g_idx[b, 0], device="cuda")
+        rows = OF.dequantize_mxfp4(_np(L.kv_cmp.data[b].index_select(0, sel)), _np(L.kv_cmp.scale[b].index_select(0, sel)))
+        # the block the step completed: within 2 * 2^e of the oracle's merge (block scale 2^e: rounding
+        # moves a value by at most 2^e, saturation at 6 * 2^e of a block maximum below 8 * 2^e by 2 * 2^e)
+        new = oracle.compress(raw_kv[b:b + 1], base[b:b + 1], z_kv, m, [N - 1], [1])[0][1][0]
+        got = OF.dequantize_mxfp4(_np(L.kv_cmp.data[b, N - 1]), _np(L.kv_cmp.scale[b, N - 1]))
+        step = np.repeat(np.exp2(_np(L.kv_cmp.scale[b, N - 1]).astype(np.float64) - 127), 32)
+        assert np.all(np.abs(got - new) <= 2 * step * 1.001)
+        out, lse = oracle.csa_sparse_attn(_np(L.q.data[b:b + 1]), rows[None], np.arange(wl.topk)[None, None],
+                                          raw_kv[b:b + 1], base[b:b + 1], wl.window, np.array([[t]]), wl.scale)
+        assert row_rel_err(g_out[b:b + 1], out) < 2e-3
+        assert np.max(np.abs(g_lse[b:b + 1] - lse)) < 2e-3
+
+
 def test_csa_decode_1m_b8_batch_invariant(gpu_lib):
     """Compress, index, top-k and attention of each sequence alone give bitwise the batch-8
     step's selection, output and lse (no scores kept, as the bench runs it)."""
