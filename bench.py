@@ -6,10 +6,11 @@ Default workload (the headline): one decode step of a CSA layer over a batch of
 blocks each): compress the block the new token completes (KV entry and MXFP4
 indexer key), score every block with the MXFP4 lightning indexer, select the top
 2048, and attend over them plus a 128-token window with 64 heads on the shared
-512-wide latent.  --workload picks another: the 2048-query prefill chunk over a
-64k context (its indexer is MFMA-bound), HCA decode at batch 64, or the hybrid
-CSA + HCA layer pair at batch 32 (--kv bf16 or fp8).  Inputs are seeded synthetic
-data already resident in HBM.
+512-wide latent (--kv mxfp4: FP4 KV caching of the compressed entries).
+--workload picks another: the 2048-query CSA or HCA prefill chunk over a 64k
+context (MFMA-bound), HCA decode at batch 64, the hybrid CSA + HCA layer pair at
+batch 32 (--kv bf16 or fp8), or a CSA2 group of layers sharing one cache and one
+top-k at 1M context.  Inputs are seeded synthetic data already resident in HBM.
 
 Timed region: exactly K steps, bracketed by synchronizations.  Several
 independent input sets are cycled so consecutive steps do not find their working
@@ -27,7 +28,7 @@ stream between two HIP events.  Peaks: 8 TB/s HBM, 2.5 PFLOP/s dense bf16 MFMA;
 the measured streaming-read ceiling (csa_stream_read over 2 GiB) is reported
 beside them.  The oracle is timed on a bounded sample on the host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--kv bf16|fp8]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--kv bf16|fp8|mxfp4]
 """
 from __future__ import annotations
 
@@ -58,8 +59,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=120)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="csa_decode_1m_b8")
-    ap.add_argument("--kv", choices=("bf16", "fp8", "mxfp4"), default="bf16",
-                    help="KV format: hybrid pair bf16 | fp8; 1M decode bf16 | mxfp4 (FP4 KV caching)")
+    ap.add_argument("--kv", choices=("bf16", "fp8", "mxfp4"), default=None,
+                    help="KV format: hybrid pair bf16 (default) | fp8; 1M decode bf16 (default) | mxfp4 "
+                         "(FP4 KV caching); CSA2 group mxfp4 (default) | bf16")
     ap.add_argument("--sets", type=int, default=6)
     ap.add_argument("--no-graph", action="store_true", help="time plain launches instead of graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -302,6 +304,83 @@ class CsaDecode:
                     f"top-{L.k}, attention over {L.k}+{L.W} entries")
 
         sample()  # warm the marshalling cache (device reads are not oracle work)
+        return time_oracle(sample, seconds, n_seq)
+
+
+class Csa2Decode:
+    """CSA2 cross-layer reuse: a group of layers sharing one compressed cache (MXFP4 entries
+    by default, bf16 window rows) and one top-k at 1M context, batch 8.  A step is the
+    group's decode step: compress + index + top-k once, then one attention per layer."""
+
+    def __init__(self, name, sets, torch, kv="mxfp4"):
+        from long_context_attention_04_amd import workloads
+        import synth
+        self.wl = wl = synth.WORKLOADS[name]
+        self.layers = [workloads.build(name, salt=s, kv_fmt=kv) for s in range(sets)]
+        G = self.layers[0]
+        L = G.base
+        nl = G.layers
+        self.tokens = L.B
+        B, N, k, W, H, D = L.B, L.n_cap, L.k, L.W, L.H, L.D
+        row = D * 2 if kv == "bf16" else D // 2 + D // 32
+        comp = B * (L.m * (D * 2 + L.dI * 4) + row + KEY_BYTES)
+        qw = B * L.HI * (L.dI * 4 + 4)
+        self.bytes = {"keys": B * N * KEY_BYTES, "q_idx_w": qw, "compress": comp, "idx": B * k * 4,
+                      "gather_per_layer_x_layers": nl * B * (k * row + W * D * 2),
+                      "q_out_lse_x_layers": nl * B * H * (D * 2 + D * 4 + 4)}
+        self.excluded = {"attention_split_partials": nl * 2 * B * 8 * H * (D + 2) * 4}
+        self.dominant = {"kernel": "index_mxfp4_kernel<4, true> (csa_compress_index_topk part 1)",
+                         "bound": "hbm", "work": self.bytes["keys"] + qw + comp,
+                         "work_note": "keys read once + q_idx and w + the step's compressions (once per group)"}
+        self.dtype = f"{kv}+mxfp4"
+        self.config = {"workload": name, "batch": wl.batch, "context": wl.extra["context"], "layers": nl,
+                       "heads": wl.heads, "latent_dim": wl.dim, "idx_heads": wl.idx_heads, "idx_dim": wl.idx_dim,
+                       "topk": wl.topk, "window": wl.window, "m": wl.m, "kv": kv, "indexer": wl.idx_dtype}
+        self.metric = (f"CSA2 layer-group decode tokens/s ({nl} layers sharing one cache and top-k, 1M ctx, "
+                       "batch 8) on 1 GPU")
+        self.torch = torch
+
+    def step(self, i):
+        self.layers[i].step()
+
+    def dominant_launch(self, i):
+        self.layers[i].base.compress_index_topk(1)
+
+    def extra_timings(self):
+        G = self.layers
+        att = launch_us(self.torch, len(G), 40, lambda i: G[i].attend_layer(1))
+        sel = launch_us(self.torch, len(G), 40, lambda i: G[i].base.compress_index_topk(3))
+        return {"attention_call_us": round(att, 2), "index_topk_call_us": round(sel, 2)}
+
+    def traffic(self):
+        return None
+
+    def cpu_baseline(self, seconds):
+        import oracle
+        from oracle import formats as OF
+        G = self.layers[0]
+        L, n_seq = G.base, 2
+        t = L.host["t"]
+        base = L.host["raw_base"]
+        raw_kv = L.raw_kv.data.double().cpu().numpy()
+        idx = L.idx.cpu().numpy()  # the shared selection (the oracle's selection is timed in the 1M decode line)
+        qs = [L.q.data.double().cpu().numpy()] + [q.data.double().cpu().numpy() for q in G.q]
+        data = []
+        for b in range(n_seq):
+            sel = self.torch.as_tensor(idx[b, 0], device="cuda")
+            c = L.kv_cmp.data[b].index_select(0, sel).cpu().numpy()
+            sc = L.kv_cmp.scale[b].index_select(0, sel).cpu().numpy()
+            data.append((c, sc))
+
+        def sample():
+            for b, (c, sc) in enumerate(data):
+                rows = OF.dequantize_mxfp4(c, sc)[None]
+                for q in qs:
+                    oracle.csa_sparse_attn(q[b:b + 1], rows, np.arange(L.k)[None, None], raw_kv[b:b + 1],
+                                           base[b:b + 1], L.W, t[b:b + 1], L.scale)
+            return (f"{n_seq} of {L.B} sequences: dequantise the {L.k} shared MXFP4 rows, attention for each of the "
+                    f"{G.layers} layers (selection not included)")
+
         return time_oracle(sample, seconds, n_seq)
 
 
@@ -570,7 +649,12 @@ def make_job(args, torch):
         if args.kv == "fp8":
             print("the 1M decode runs with bf16 or mxfp4 KV", file=sys.stderr)
             sys.exit(2)
-        return CsaDecode(args.workload, args.sets, torch, args.kv)
+        return CsaDecode(args.workload, args.sets, torch, args.kv or "bf16")
+    if kind == "csa2_decode":
+        if args.kv == "fp8":
+            print("CSA2 runs with mxfp4 or bf16 KV", file=sys.stderr)
+            sys.exit(2)
+        return Csa2Decode(args.workload, args.sets, torch, args.kv or "mxfp4")
     if kind == "csa_prefill":
         return CsaPrefill(args.workload, min(args.sets, 3), torch)
     if kind == "hca_decode":
@@ -578,7 +662,10 @@ def make_job(args, torch):
     if kind == "hca_prefill":
         return HcaPrefill(args.workload, min(args.sets, 3), torch)
     if kind == "hybrid_decode":
-        return HybridDecode(args.workload, min(args.sets, 4), torch, args.kv)
+        if args.kv == "mxfp4":
+            print("the hybrid pair runs with bf16 or fp8 KV", file=sys.stderr)
+            sys.exit(2)
+        return HybridDecode(args.workload, min(args.sets, 4), torch, args.kv or "bf16")
     print(f"bench.py times the 1M decode, prefill, HCA and hybrid workloads; {args.workload} is covered by the "
           "parity tests", file=sys.stderr)
     sys.exit(2)

@@ -137,14 +137,12 @@ template <bool FP8>
 __device__ __forceinline__ v8bf widen8(Raw8<FP8> r) {
   if constexpr (!FP8) {
     return __builtin_bit_cast(v8bf, r);
-  } else {
-    v8bf v;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t byte = ((i < 4 ? r[0] : r[1]) >> (8 * (i & 3))) & 0xffu;
-      v[i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(e4m3_to_f32(byte)) >> 16));  // exact
-    }
-    return v;
+  } else {  // OCP e4m3 -> bf16 in hardware (exact: 3 mantissa bits, exponents within range)
+    const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[0], 1.0f, false);
+    const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[0], 1.0f, true);
+    const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[1], 1.0f, false);
+    const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[1], 1.0f, true);
+    return (v8bf){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
   }
 }
 

@@ -358,6 +358,62 @@ def build_csa_decode(wl: synth.Workload, salt: int = 0, kv_fmt: str | None = Non
     return layer
 
 
+@dataclass
+class Csa2Group:
+    """CSA2 cross-layer reuse: a group of layers sharing one compressed cache and one
+    top-k selection.  The group's step compresses the new block and selects once (with
+    the first layer's indexer query), then every layer attends over the shared entries
+    with its own query; layer 0 is an ordinary CSA layer."""
+
+    base: CsaLayer
+    q: list          # per layer l >= 1: Stored [B, tq, H, D]
+    out: list        # per layer l >= 1: [B, tq, H, D] f32
+    lse: list
+    ws_attn: list
+
+    @property
+    def layers(self):
+        return 1 + len(self.q)
+
+    def attend_layer(self, l, stream=None):
+        L = self.base
+        if l == 0:
+            L.attend(stream)
+            return
+        csa_sparse_attn(self.q[l - 1].desc(), L.kv_cmp.desc(), L.idx, L.k, L.raw_kv.desc(), L.raw_base, L.W, L.q_pos,
+                        L.B, L.tq, L.H, L.D, L.scale, self.out[l - 1], self.lse[l - 1], self.ws_attn[l - 1],
+                        self.ws_attn[l - 1].numel(), stream)
+
+    def attend(self, stream=None):
+        for l in range(self.layers):
+            self.attend_layer(l, stream)
+
+    def step(self, stream=None, marks=None):
+        L = self.base
+        if marks:
+            marks(0)
+        L.compress_index_topk(3, stream)
+        if marks:
+            marks(1)
+        self.attend(stream)
+        if marks:
+            marks(2)
+
+
+def build_csa2_decode(wl: synth.Workload, salt: int = 0, kv_fmt: str | None = None) -> Csa2Group:
+    """The 1M decode's layer state (cache, indexer, window) shared by `layers` layers; the
+    layers after the first draw their own queries."""
+    base = build_csa_decode(wl, salt, kv_fmt)
+    n = wl.extra["layers"]
+    B, H, D = base.B, base.H, base.D
+    qs = [Stored(_bf16(synth.normal(wl, f"q_layer{l}", (B, 1, H, D), salt)), BF16) for l in range(1, n)]
+    outs = [torch.empty((B, 1, H, D), dtype=torch.float32, device=DEV) for _ in range(1, n)]
+    lses = [torch.empty((B, 1, H), dtype=torch.float32, device=DEV) for _ in range(1, n)]
+    nws = csa_attn_workspace_size(B, 1, H, D, base.k + base.W)
+    wss = [torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV) for _ in range(1, n)]
+    return Csa2Group(base=base, q=qs, out=outs, lse=lses, ws_attn=wss)
+
+
 def build_csa_prefill(wl: synth.Workload, salt: int = 0) -> CsaLayer:
     """A prefill chunk of Tq queries at positions L .. L+Tq-1 over an L-token context;
     the chunk completes Tq/m new blocks, which the step compresses."""
@@ -499,6 +555,8 @@ def build(name: str, salt: int = 0, kv_fmt: str | None = None):
     wl = synth.WORKLOADS[name]
     if wl.kind == "csa_decode":
         return build_csa_decode(wl, salt, kv_fmt)
+    if wl.kind == "csa2_decode":
+        return build_csa2_decode(wl, salt, kv_fmt)
     if wl.kind == "csa_prefill":
         return build_csa_prefill(wl, salt)
     if wl.kind == "hca_decode":

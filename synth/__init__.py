@@ -28,7 +28,7 @@ class Workload:
 
     name: str
     wid: int
-    kind: str  # "csa_decode" | "csa_prefill" | "hca_decode" | "hca_prefill" | "hybrid_decode"
+    kind: str  # "csa_decode" | "csa2_decode" | "csa_prefill" | "hca_decode" | "hca_prefill" | "hybrid_decode"
     batch: int
     tq: int
     heads: int
@@ -86,6 +86,14 @@ WORKLOADS = {
             idx_dim=64, topk=1024, idx_dtype="bf16",
             notes="262144 + tail tokens, tail uniform in [0, 127]; bf16 or fp8 e4m3 KV",
             extra={"context": 262144, "tail_hi": 127},
+        ),
+        Workload(
+            name="csa2_decode_1m_b8", wid=7, kind="csa2_decode", batch=8, tq=1,
+            heads=64, dim=512, window=128, kv_dtype="mxfp4", m=4, idx_heads=8, idx_dim=64,
+            topk=2048, idx_dtype="mxfp4",
+            notes="a group of 2 layers sharing one compressed cache (MXFP4 entries, bf16 window) and "
+                  "one top-k; each layer attends with its own query; 1M context as the 1M decode",
+            extra={"context": 1048576, "layers": 2},
         ),
         Workload(
             name="hca_prefill_2k_on_64k", wid=6, kind="hca_prefill", batch=1, tq=2048,

@@ -151,6 +151,38 @@ def test_csa_decode_1m_b8_mxfp4_kv(gpu_lib):
         assert np.max(np.abs(g_lse[b:b + 1] - lse)) < 2e-3
 
 
+def test_csa2_decode_1m_b8(gpu_lib):
+    """CSA2 cross-layer reuse: two layers share the 1M cache (MXFP4 entries) and one top-k.
+    Every layer's attention over the shared selection matches the oracle for all 8
+    sequences; a layer given layer 0's query reproduces layer 0 bitwise."""
+    from long_context_attention_04_amd import workloads
+    name = "csa2_decode_1m_b8"
+    wl = synth.WORKLOADS[name]
+    G = workloads.build(name)
+    L = G.base
+    assert G.layers == wl.extra["layers"] == 2 and L.kv_cmp.dtype == gpu_lib.MXFP4
+    G.step()
+    torch.cuda.synchronize()
+    g_idx = _np(L.idx)
+    outs = [(_np(L.out), _np(L.lse))] + [(_np(o), _np(s)) for o, s in zip(G.out, G.lse)]
+    qs = [_np(L.q.data)] + [_np(q.data) for q in G.q]
+    raw_kv = _np(L.raw_kv.data)
+    base = L.host["raw_base"]
+    t = wl.extra["context"] - 1
+    for b in range(L.B):
+        sel = torch.as_tensor(g_idx[b, 0], device="cuda")
+        rows = OF.dequantize_mxfp4(_np(L.kv_cmp.data[b].index_select(0, sel)), _np(L.kv_cmp.scale[b].index_select(0, sel)))
+        for l in range(G.layers):
+            out, lse = oracle.csa_sparse_attn(qs[l][b:b + 1], rows[None], np.arange(wl.topk)[None, None],
+                                              raw_kv[b:b + 1], base[b:b + 1], wl.window, np.array([[t]]), wl.scale)
+            assert row_rel_err(outs[l][0][b:b + 1], out) < 2e-3, (b, l)
+            assert np.max(np.abs(outs[l][1][b:b + 1] - lse)) < 2e-3, (b, l)
+    G.q[0].data.copy_(L.q.data)
+    G.attend_layer(1)
+    np.testing.assert_array_equal(_np(G.out[0]), outs[0][0])
+    np.testing.assert_array_equal(_np(G.lse[0]), outs[0][1])
+
+
 def test_csa_decode_1m_b8_batch_invariant(gpu_lib):
     """Compress, index, top-k and attention of each sequence alone give bitwise the batch-8
     step's selection, output and lse (no scores kept, as the bench runs it)."""
