@@ -365,12 +365,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6
   // operands of keys completed by this step (not yet stored when loaded) are zeroed
   // before any MFMA sees them: stale bytes may hold a NaN scale, which would spoil the
   // tile's other columns
+  if (own_new) {  // wave-uniform (rare: the wave holding the step's newest keys)
 #pragma unroll
-  for (int u = 0; u < kFp4Unroll; ++u) {
-    const int g = kfirst + 32 * u;
-    const bool drop = own_new && g >= klo && g < khi;
-    c[u] = drop ? (v4i){0, 0, 0, 0} : c[u];
-    sbk[u] = drop ? 127 : sbk[u];
+    for (int u = 0; u < kFp4Unroll; ++u) {
+      const int g = kfirst + 32 * u;
+      const bool drop = g >= klo && g < khi;
+      c[u] = drop ? (v4i){0, 0, 0, 0} : c[u];
+      sbk[u] = drop ? 127 : sbk[u];
+    }
   }
   // 3) scores
   float sc[kFp4Unroll];  // the wave's scores: tile u, key g0 + 32u + m (in lanes l and l ^ kPair)

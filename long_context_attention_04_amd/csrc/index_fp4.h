@@ -123,22 +123,28 @@ __device__ __forceinline__ void fp4_query_operand(const Fp4QueryLds& ql, int hea
 template <int NR>
 __device__ __forceinline__ float fp4_tile_score(const v8i& A, int sa, const float (&wv)[NR], v4i c, int sbk) {
   const v8i Bop = {c[0], c[1], c[2], c[3], 0, 0, 0, 0};
+  // ReLU as one median of three (the products are finite: no NaN reaches here)
+  const auto relu = [](float x) { return __builtin_amdgcn_fmed3f(x, 0.f, __builtin_inff()); };
   float part = 0.f;
   if constexpr (NR == 4) {
     v4f acc = {0.f, 0.f, 0.f, 0.f};
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bop, acc, 4, 4, 0, sa, 0, sbk);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part = fmaf(wv[r], fmaxf(acc[r], 0.f), part);
+    for (int r = 0; r < 4; ++r) part = fmaf(wv[r], relu(acc[r]), part);
   } else {
     v16f acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bop, acc, 4, 4, 0, sa, 0, sbk);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) part = fmaf(wv[r], fmaxf(acc[r], 0.f), part);
+    for (int r = 0; r < NR; ++r) part = fmaf(wv[r], relu(acc[r]), part);
   }
-  const float other = __shfl_xor(part, Fp4Lane<NR>::kPair);
-  return part + other;
+  // part of lane l plus part of lane l ^ kPair: a lane swap within the VALU (no LDS
+  // round trip); the sum is the same in both lanes (addition commutes)
+  const uint32_t x = __float_as_uint(part);
+  const auto t = Fp4Lane<NR>::kPair == 16 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                                          : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 // Scores of chosen 32-key tiles of one row (only keys < V; the rest score as
