@@ -281,7 +281,8 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // hands the row's top-k merge its exact top-kSliceSlots in (key desc, position asc)
 // order, listed in position order.  They are found cheaply: a cut keeps every key >=
 // tau, tau being the 32nd largest of the 64 lane maxima (so the top 32 all pass, and
-// typically about 45 keys do), and the survivors are ranked among themselves.  When
+// typically about 45 keys do), and the survivors, one per lane in position order, are
+// cut again at their own 32nd largest key.  When
 // more than kCutMax keys pass the cut (many equal scores), the top-kSliceSlots are
 // found by a bit-by-bit threshold instead.  Every key left out ranks after the list's
 // last element, so a row's merge is exact unless that element is selected -- which
@@ -292,7 +293,6 @@ constexpr int kSliceSlots = 32;
 constexpr int kCutMax = kWave;  // survivors of the cut ranked in one pass (one per lane)
 
 struct CutLds {
-  __attribute__((aligned(16))) uint32_t lmax[kWave];
   __attribute__((aligned(16))) uint2 res[kCutMax + kWave];  // (key, position) staged; then discard slots
 };
 
@@ -345,33 +345,17 @@ __device__ void wave_topc_exact(const uint32_t (&kv)[kWaveTopN], uint32_t C, Cut
   *T_out = T;
 }
 
-// Rank of each lane's entry among the first `total` staged entries of cl.res in (key
-// desc, position asc) order, i.e. by the 64-bit value key << 32 | ~position (lanes >=
-// total get an entry that ranks last).  Broadcast reads eight at a time (a fixed
-// count, entries past `total` masked): a loop bounded by `total` would wait out one LDS
-// round trip per step.
-__device__ __forceinline__ uint32_t staged_rank(const CutLds& cl, uint32_t total, uint2* mine) {
-  const int L = threadIdx.x % kWave;
-  const uint2 me = (uint32_t)L < total ? cl.res[L] : make_uint2(0u, 0xffffffffu);
-  const uint64_t m64 = ((uint64_t)me.x << 32) | (uint32_t)~me.y;
-  constexpr int kBatch = 8;
-  uint32_t rank = 0;
+// The k-th largest (1 <= k <= 64) of the 64 lanes' values, counting repeats: the
+// largest v with at least k lanes at or above it, built bit by bit (a compare and a
+// ballot count per bit; the result is wave-uniform).
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t x, uint32_t k) {
+  uint32_t T = 0u;
 #pragma unroll
-  for (int i0 = 0; i0 < kCutMax / 2; i0 += kBatch) {
-    if (2 * i0 >= (int)total) break;  // wave-uniform
-    uint4 v[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) v[i] = *(const uint4*)&cl.res[2 * (i0 + i)];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int e = 2 * (i0 + i);
-      const uint64_t a = ((uint64_t)v[i].x << 32) | (uint32_t)~v[i].y;
-      const uint64_t b = ((uint64_t)v[i].z << 32) | (uint32_t)~v[i].w;
-      rank += (uint32_t)(a > m64 && e < (int)total) + (uint32_t)(b > m64 && e + 1 < (int)total);
-    }
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    T = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(x >= cand)) >= k ? cand : T;
   }
-  *mine = me;
-  return rank;
+  return T;
 }
 
 // Writes the list of the n <= 1024 keys one wave holds (absent positions hold key 0,
@@ -389,22 +373,15 @@ __device__ void emit_slice_list(const uint32_t (&kv)[kWaveTopN], int n, uint32_t
     return;
   }
   // tau: the 32nd largest lane maximum, with its 6 low bits cleared.  The maxima are
-  // made distinct by putting 63 - lane in those bits (so a rank is one compare per
-  // maximum); clearing them again keeps every lane at or above the 32nd maximum
-  // passing the cut, so at least 32 keys do.
+  // made distinct by putting 63 - lane in those bits (so the 32nd largest is one
+  // value, found bit by bit over the wave: one compare and a ballot count per bit);
+  // clearing them again keeps every lane at or above the 32nd maximum passing the
+  // cut, so at least 32 keys do.
   uint32_t lmx = 0u;
 #pragma unroll
   for (int j = 0; j < kWaveTopN; ++j) lmx = max(lmx, kv[j]);
   const uint32_t lmu = (lmx & ~63u) | (uint32_t)(63 - L);
-  cl.lmax[L] = lmu;  // LDS ops of one wave run in order
-  uint32_t lrank = 0;
-#pragma unroll
-  for (int i = 0; i < kWave; i += 4) {
-    const uint4 v = *(const uint4*)&cl.lmax[i];  // broadcast reads
-    lrank += (uint32_t)(v.x > lmu) + (uint32_t)(v.y > lmu) + (uint32_t)(v.z > lmu) + (uint32_t)(v.w > lmu);
-  }
-  const uint32_t tau =
-      __builtin_amdgcn_readlane(lmu, __builtin_ctzll(__builtin_amdgcn_ballot_w64(lrank == 31u))) & ~63u;
+  const uint32_t tau = wave_kth_largest(lmu, 32u) & ~63u;
   uint32_t c = 0;
 #pragma unroll
   for (int j = 0; j < kWaveTopN; ++j) c += kv[j] != 0u && kv[j] >= tau;
@@ -415,7 +392,9 @@ __device__ void emit_slice_list(const uint32_t (&kv)[kWaveTopN], int n, uint32_t
   bool keep;
   uint32_t slot;
   if (total <= (uint32_t)kCutMax) {
-    // stage the survivors in position order, rank them, keep the top kSliceSlots
+    // stage the survivors in position order (survivor i in lane i), then keep the
+    // top kSliceSlots: keys above the kSliceSlots-th largest survivor key T, and the
+    // first (lowest-position, i.e. lowest-lane) copies of T
     uint32_t o = incl - c;
 #pragma unroll
     for (int j = 0; j < kWaveTopN; ++j) {
@@ -423,12 +402,19 @@ __device__ void emit_slice_list(const uint32_t (&kv)[kWaveTopN], int n, uint32_t
       cl.res[in ? o : (uint32_t)kCutMax + L] = make_uint2(kv[j], (uint32_t)(kWaveTopN * L + j));
       o += in;
     }
-    const uint32_t rank = staged_rank(cl, total, &e);
-    keep = (uint32_t)L < total && rank < (uint32_t)kSliceSlots;
+    e = (uint32_t)L < total ? cl.res[L] : make_uint2(0u, 0u);  // LDS ops of one wave run in order
+    const uint32_t T = wave_kth_largest(e.x, (uint32_t)kSliceSlots);
+    const uint64_t below = (1ull << L) - 1ull;
+    const uint32_t ngt = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(e.x > T));
+    const uint64_t eqm = __builtin_amdgcn_ballot_w64(e.x == T && (uint32_t)L < total);
+    const uint32_t eqr = (uint32_t)__builtin_popcountll(eqm & below);  // copies of T in lower lanes
+    const uint32_t take = (uint32_t)kSliceSlots - ngt;                  // >= 1: T is the kSliceSlots-th key
+    keep = e.x > T || (e.x == T && (uint32_t)L < total && eqr < take);
     const uint64_t km = __builtin_amdgcn_ballot_w64(keep);
-    slot = (uint32_t)__builtin_popcountll(km & ((1ull << L) - 1ull));  // position order among the kept
-    const int ll = __builtin_ctzll(__builtin_amdgcn_ballot_w64((uint32_t)L < total && rank == kSliceSlots - 1u));
-    lk = __builtin_amdgcn_readlane(e.x, ll);
+    slot = (uint32_t)__builtin_popcountll(km & below);  // position order among the kept
+    // the list's last element in (key desc, position asc) order: the take-th copy of T
+    const int ll = __builtin_ctzll(__builtin_amdgcn_ballot_w64(e.x == T && (uint32_t)L < total && eqr == take - 1u));
+    lk = T;
     li = start + __builtin_amdgcn_readlane(e.y, ll);
   } else {  // many keys at or above tau: the top kSliceSlots by a bit-by-bit threshold
     uint32_t T, tpos;
