@@ -441,9 +441,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 4 ? 6
       kv[4 * q + 2] = v4.z;
       kv[4 * q + 3] = v4.w;
     }
+    if (n < kFusedSlice) {  // positions past the visible ones are absent (wave-uniform test)
 #pragma unroll
-    for (int j = 0; j < kWaveTopN; ++j)
-      if (kWaveTopN * l + j >= n) kv[j] = 0u;  // positions past the visible ones are absent
+      for (int j = 0; j < kWaveTopN; ++j)
+        if (kWaveTopN * l + j >= n) kv[j] = 0u;
+    }
     emit_slice_list(kv, n, (uint32_t)start, cl, co.cand + ((int64_t)row * co.nslices + slice) * kFusedC,
                     co.meta + (int64_t)row * co.nslices + slice);
   }

@@ -381,10 +381,11 @@ __device__ void emit_slice_list(const uint32_t (&kv)[kWaveTopN], int n, uint32_t
 #pragma unroll
   for (int j = 0; j < kWaveTopN; ++j) lmx = max(lmx, kv[j]);
   const uint32_t lmu = (lmx & ~63u) | (uint32_t)(63 - L);
-  const uint32_t tau = wave_kth_largest(lmu, 32u) & ~63u;
+  // (present keys are > 0: "present and >= tau" is one compare against max(tau, 1))
+  const uint32_t tau = max(wave_kth_largest(lmu, 32u) & ~63u, 1u);
   uint32_t c = 0;
 #pragma unroll
-  for (int j = 0; j < kWaveTopN; ++j) c += kv[j] != 0u && kv[j] >= tau;
+  for (int j = 0; j < kWaveTopN; ++j) c += kv[j] >= tau;
   const uint32_t incl = wave_incl_scan(c);
   const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
   uint32_t lk, li;
@@ -398,7 +399,7 @@ __device__ void emit_slice_list(const uint32_t (&kv)[kWaveTopN], int n, uint32_t
     uint32_t o = incl - c;
 #pragma unroll
     for (int j = 0; j < kWaveTopN; ++j) {
-      const bool in = kv[j] != 0u && kv[j] >= tau;
+      const bool in = kv[j] >= tau;
       cl.res[in ? o : (uint32_t)kCutMax + L] = make_uint2(kv[j], (uint32_t)(kWaveTopN * L + j));
       o += in;
     }
