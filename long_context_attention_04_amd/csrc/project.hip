@@ -42,6 +42,14 @@ struct NtArgs {
   int64_t wsh;
   float* part;  // [heads][nsplit][M][n0 + n1] partial sums
   int nsplit, cps;  // splits of the chunk range and chunks per split
+  // with one split (no reduce launch): columns < n0 go straight to y0 (row R at
+  // (R / ytq) * y0sb + (R % ytq) * y0sr, head z at + z * y0sh, fp32 or bf16), the rest to
+  // y1 (fp32 [M][n1])
+  void* y0;
+  int ytq;
+  int64_t y0sb, y0sr, y0sh;
+  int y0_bf16;
+  float* y1;
 };
 
 __device__ __forceinline__ v8bf ld8(const uint16_t* p) { return *(const v8bf*)p; }
@@ -110,6 +118,23 @@ __global__ __launch_bounds__(kProjThreads) void nt_partial_kernel(NtArgs a) {
   // C layout: lane (column i, group g) holds rows 4g + r of the tile
   const int col = 16 * nt + i;
   if (col < N) {
+    if (a.nsplit == 1) {  // every chunk summed here: the result itself
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * mt + 4 * g + r;
+        if (row >= a.M) continue;
+        if (col < a.n0) {
+          const int64_t o = (int64_t)(row / a.ytq) * a.y0sb + (int64_t)(row % a.ytq) * a.y0sr + z * a.y0sh + col;
+          if (a.y0_bf16)
+            ((__bf16*)a.y0)[o] = (__bf16)acc[r];
+          else
+            ((float*)a.y0)[o] = acc[r];
+        } else {
+          a.y1[(int64_t)row * a.n1 + (col - a.n0)] = acc[r];
+        }
+      }
+      return;
+    }
     float* out = a.part + ((int64_t)z * a.nsplit + sp) * a.M * N;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -138,9 +163,18 @@ __global__ __launch_bounds__(256) void nt_reduce_kernel(ReduceArgs a) {
   if (id >= (int64_t)a.M * N) return;
   const int z = blockIdx.y;
   const int row = (int)(id / N), col = (int)(id % N);
-  const float* part = a.part + (int64_t)z * a.nsplit * a.M * N;
+  const float* part = a.part + (int64_t)z * a.nsplit * a.M * N + (int64_t)row * N + col;
+  const int64_t ss = (int64_t)a.M * N;  // between splits
+  // ascending split order, eight loads in flight at a time
   float v = 0.f;
-  for (int sp = 0; sp < a.nsplit; ++sp) v += part[((int64_t)sp * a.M + row) * N + col];
+  for (int sp0 = 0; sp0 < a.nsplit; sp0 += 8) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = sp0 + j < a.nsplit ? part[(sp0 + j) * ss] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (sp0 + j < a.nsplit) v += x[j];
+  }
   if (col < a.n0) {
     const int64_t o = (int64_t)(row / a.tq) * a.y0sb + (int64_t)(row % a.tq) * a.y0sr + z * a.y0sh + col;
     if (a.y0_bf16)
@@ -209,10 +243,19 @@ hipError_t launch_index_query(const IndexQueryArgs& q, hipStream_t s) {
   a1.n1 = q.n_idx_heads;
   a1.part = part;
   a1.nsplit = proj_nsplit(rows, q.d_model);
+  a1.y0 = cbuf;  // c: [rows][rank] bf16, row R at R * rank
+  a1.ytq = 1;
+  a1.y0sb = q.rank;
+  a1.y0sr = 0;
+  a1.y0sh = 0;
+  a1.y0_bf16 = 1;
+  a1.y1 = q.w_out;
   hipError_t e = launch_nt(a1, 1, false, s);
   if (e != hipSuccess) return e;
-  ReduceArgs r1{part, a1.nsplit, (int)rows, q.rank, q.n_idx_heads, 1, cbuf, q.rank, 0, 1, q.w_out, 0};  // c: [rows][rank]
-  if ((e = launch_reduce(r1, 1, s)) != hipSuccess) return e;
+  if (a1.nsplit > 1) {
+    ReduceArgs r1{part, a1.nsplit, (int)rows, q.rank, q.n_idx_heads, 1, cbuf, q.rank, 0, 1, q.w_out, 0};  // c: [rows][rank]
+    if ((e = launch_reduce(r1, 1, s)) != hipSuccess) return e;
+  }
   // projection 2: q_I = c . W_uq^T
   NtArgs a2{};
   a2.x = cbuf;
@@ -229,7 +272,15 @@ hipError_t launch_index_query(const IndexQueryArgs& q, hipStream_t s) {
   a2.n1 = 0;
   a2.part = part;
   a2.nsplit = proj_nsplit(rows, q.rank);
+  a2.y0 = q.q_out;
+  a2.ytq = q.tq;
+  a2.y0sb = q.q_sb;
+  a2.y0sr = q.q_sr;
+  a2.y0sh = 0;
+  a2.y0_bf16 = q.q_bf16;
+  a2.y1 = nullptr;
   if ((e = launch_nt(a2, 1, false, s)) != hipSuccess) return e;
+  if (a2.nsplit == 1) return hipSuccess;
   ReduceArgs r2{part, a2.nsplit, (int)rows, HD, 0, q.tq, q.q_out, q.q_sb, q.q_sr, q.q_bf16, nullptr, 0};
   return launch_reduce(r2, 1, s);
 }
@@ -259,8 +310,16 @@ hipError_t launch_latent_proj(const LatentProjArgs& p, hipStream_t s) {
   a.wsh = (int64_t)p.N * p.K;
   a.part = (float*)p.ws;
   a.nsplit = proj_nsplit(p.rows, p.K);
+  a.y0 = p.y;
+  a.ytq = 1 << 30;
+  a.y0sb = 0;
+  a.y0sr = (int64_t)p.heads * p.N;
+  a.y0sh = p.N;
+  a.y0_bf16 = p.y_bf16;
+  a.y1 = nullptr;
   hipError_t e = launch_nt(a, p.heads, p.x_f32 != 0, s);
   if (e != hipSuccess) return e;
+  if (a.nsplit == 1) return hipSuccess;
   ReduceArgs r{a.part, a.nsplit, (int)p.rows, p.N, 0, 1 << 30, p.y, 0, (int64_t)p.heads * p.N, p.y_bf16, nullptr, p.N};
   return launch_reduce(r, p.heads, s);
 }
