@@ -141,13 +141,19 @@ constexpr int kPfQ = 32;        // queries per workgroup
 constexpr int kPfNT = 8;        // 16-key column tiles per wave
 constexpr int kPfKeys = 4 * 16 * kPfNT;  // keys per workgroup (512)
 
+// max(x, 0) as one integer max on the bits (a negative float is a negative integer;
+// -0 and every negative value give +0): the float max form costs a canonicalize too
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // the sum of x over lanes i and i ^ 16, bitwise the same in both lanes
 __device__ __forceinline__ float pair16_sum(float x) {
   const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
-__global__ __launch_bounds__(256) void index_bf16_tile_kernel(IndexArgs a) {
+// (a 128-register budget: the MFMA accumulators then stay in VGPRs, so the epilogue
+// reads them without AGPR copies)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void index_bf16_tile_kernel(IndexArgs a) {
   const int b = blockIdx.z;
   const int q0 = blockIdx.y * kPfQ;
   const int kbase = blockIdx.x * kPfKeys;
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(256) void index_bf16_tile_kernel(IndexArgs a) {
     for (int nt = 0; nt < kPfNT; ++nt) {
       float part = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part = fmaf(wv[r], fmaxf(c[nt][r], 0.f), part);
+      for (int r = 0; r < 4; ++r) part = fmaf(wv[r], relu_bits(c[nt][r]), part);
       const float tot = pair16_sum(part);  // heads 0-3 plus heads 4-7
       const int key = kw + 16 * nt + n;
       if ((g & 1) == 0 && myq < nq && key < a.n_cap) srow[key] = key < Vq ? tot : kNegInf;

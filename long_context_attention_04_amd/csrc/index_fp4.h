@@ -123,8 +123,9 @@ __device__ __forceinline__ void fp4_query_operand(const Fp4QueryLds& ql, int hea
 template <int NR>
 __device__ __forceinline__ float fp4_tile_score(const v8i& A, int sa, const float (&wv)[NR], v4i c, int sbk) {
   const v8i Bop = {c[0], c[1], c[2], c[3], 0, 0, 0, 0};
-  // ReLU as one median of three (the products are finite: no NaN reaches here)
-  const auto relu = [](float x) { return __builtin_amdgcn_fmed3f(x, 0.f, __builtin_inff()); };
+  // ReLU as one integer max on the bits (a negative float is a negative integer; -0 and
+  // every negative value give +0); the float max form costs a canonicalize too
+  const auto relu = [](float x) { return __int_as_float(max(__float_as_int(x), 0)); };
   float part = 0.f;
   if constexpr (NR == 4) {
     v4f acc = {0.f, 0.f, 0.f, 0.f};
