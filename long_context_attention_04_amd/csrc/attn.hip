@@ -585,8 +585,9 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, int split, 
     const float M = wave_max(ms);
     const float e = (M == kNegInf || s >= nsplit) ? 0.f : exp2f(ms - M);
     // L = sum over splits in ascending order (fixed, independent of scheduling)
+    const float le = ls * e;
     float L = 0.f;
-    for (int i = 0; i < nsplit; ++i) L += __shfl(ls * e, i);
+    for (int i = 0; i < nsplit; ++i) L += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(le), i));
     if (s < kMergeMaxSplits) wts[s] = e;
     if (s == 0) {
       sh_L = L;
