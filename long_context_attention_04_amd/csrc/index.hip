@@ -19,6 +19,8 @@
 //    dominates) and a 32-query x 256-key tile kernel for many (a prefill chunk: a
 //    dense contraction of many queries against the same keys).
 //  * F32 keys: plain fp32 VALU kernel (small shapes).
+#include <type_traits>
+
 #include "common.h"
 #include "compress_block.h"
 #include "kernels.h"
@@ -131,25 +133,23 @@ __global__ __launch_bounds__(256) void index_bf16_kernel(IndexArgs a) {
 
 // ------------------------------------------------------------------ bf16 MFMA, many queries
 // heads == 8, dim == 64, many queries per sequence (a prefill chunk): a dense
-// [queries*8 x 64] x [64 x keys] contraction.  Workgroup tile: 32 queries x 256
-// keys.  The 32 queries' heads are staged once in LDS (A operand, read twice per
-// 2-query row tile); each wave holds its 64 keys in registers as the B operand for
-// all 16 row tiles, so a key is loaded once per workgroup.  The epilogue (ReLU,
-// head weights, the sum over heads) is the same arithmetic in the same order as
-// index_bf16_kernel.
-constexpr int kPfQ = 32;        // queries per workgroup
+// [queries*8 x 64] x [64 x keys] contraction.  Workgroup tile: 36 queries x 512
+// keys.  The 36 queries' heads are staged once in LDS (A operand); each wave holds
+// its 128 keys in registers as the B operand for all 18 row tiles, so a key is
+// loaded once per workgroup.  The epilogue (ReLU, head weights, the sum over heads)
+// is the same arithmetic in the same order as index_bf16_kernel: bit-identical
+// scores.
+// 36 queries (nine quads) per workgroup: 57 x 33 = 1,881 workgroups for 2,048 queries over
+// 16,896 keys, two rounds of the 1,024 that are resident at once (32 queries make
+// 2,112: a third round of 64)
+constexpr int kPfQ = 36;        // queries per workgroup
 constexpr int kPfNT = 8;        // 16-key column tiles per wave
 constexpr int kPfKeys = 4 * 16 * kPfNT;  // keys per workgroup (512)
+static_assert(kPfQ % 4 == 0 && kPfQ * 8 * 8 % 256 == 0, "query quads; whole staging rounds");
 
 // max(x, 0) as one integer max on the bits (a negative float is a negative integer;
 // -0 and every negative value give +0): the float max form costs a canonicalize too
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
-
-// the sum of x over lanes i and i ^ 16, bitwise the same in both lanes
-__device__ __forceinline__ float pair16_sum(float x) {
-  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
-}
 
 // (a 128-register budget: the MFMA accumulators then stay in VGPRs, so the epilogue
 // reads them without AGPR copies)
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   // A operand rows (query q0 + r / 8, head r % 8): 64 bf16 = 8 chunks of 16 B,
   // chunk c of row r at position c ^ (r & 7) (conflict-free operand reads)
   __shared__ __attribute__((aligned(16))) uint4 qs[kPfQ * 8][8];
-  __shared__ float wsh[kPfQ][8];
+  __shared__ __attribute__((aligned(16))) float wsh[kPfQ][8];
   __shared__ int vsh[kPfQ];
   const int nq = min(kPfQ, a.tq - q0);
 #pragma unroll
@@ -173,11 +173,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
       v = *(const uint4*)((const uint16_t*)a.q.data + (int64_t)b * a.q.sb + (int64_t)(q0 + q) * a.q.sr + h * 64 + 8 * c);
     qs[r][c ^ (r & 7)] = v;
   }
-  {
-    const int q = t / 8, h = t % 8;
+  for (int i = t; i < kPfQ * 8; i += 256) {
+    const int q = i / 8, h = i % 8;
     wsh[q][h] = q < nq ? a.w[((int64_t)b * a.tq + q0 + q) * 8 + h] : 0.f;
-    if (t < kPfQ) vsh[t] = t < nq ? visible_blocks(a.q_pos[b * a.tq + q0 + t], a.m) : 0;
   }
+  if (t < kPfQ) vsh[t] = t < nq ? visible_blocks(a.q_pos[b * a.tq + q0 + t], a.m) : 0;
   __syncthreads();
   int vmax = 0;
   for (int q = 0; q < kPfQ; ++q) vmax = max(vmax, vsh[q]);
@@ -200,35 +200,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
                                               32 * ks + 8 * g)
                              : (v8bf){};
   }
-  for (int mt = 0; mt < kPfQ / 2; ++mt) {
-    if (2 * mt >= nq) break;  // wave-uniform
-    // this lane's output rows: 4g + r -> query 2mt + (g >= 2), heads 4(g & 1) + r
-    const int myq = 2 * mt + (g >> 1);
+  // Query quads: two row tiles per quad, X = heads 0-3 and Y = heads 4-7 of its four
+  // queries (row r: query 4it + r / 4, head r % 4, or 4 + r % 4), so that lane (key n,
+  // g) holds all eight heads of query 4it + g for key kw + 16nt + n and sums them
+  // without a lane exchange.  Heads 0-3 and 4-7 are summed in separate chains and then
+  // added, as in index_bf16_kernel.
+  for (int it = 0; it < kPfQ / 4; ++it) {
+    if (4 * it >= nq) break;  // wave-uniform
+    const int myq = 4 * it + g;
     const int Vq = vsh[myq];
     float* srow = srow_base + (int64_t)myq * a.n_cap;
-    const int ra = 16 * mt + n;  // A operand row: query 2mt + n / 8, head n % 8
-    v8bf A[2];
+    const int rx = 8 * (4 * it + n / 4) + n % 4, ry = rx + 4;
+    v8bf AX[2], AY[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) A[ks] = __builtin_bit_cast(v8bf, qs[ra][(4 * ks + g) ^ (ra & 7)]);
-    float wv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wv[r] = wsh[myq][4 * (g & 1) + r];
-    v4f c[kPfNT];
-#pragma unroll
-    for (int nt = 0; nt < kPfNT; ++nt) {
-      c[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
-      c[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0], B[nt][0], c[nt], 0, 0, 0);
-      c[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1], B[nt][1], c[nt], 0, 0, 0);
+    for (int ks = 0; ks < 2; ++ks) {
+      AX[ks] = __builtin_bit_cast(v8bf, qs[rx][(4 * ks + g) ^ (rx & 7)]);
+      AY[ks] = __builtin_bit_cast(v8bf, qs[ry][(4 * ks + g) ^ (ry & 7)]);
     }
+    const float4 w0 = *(const float4*)&wsh[myq][0], w1 = *(const float4*)&wsh[myq][4];
+    const float wx[4] = {w0.x, w0.y, w0.z, w0.w}, wy[4] = {w1.x, w1.y, w1.z, w1.w};
+    // a whole quad of 128 in-range keys stores with no per-lane test (no branch in
+    // the tile loop, so the scheduler overlaps one tile's MFMAs with another's epilogue)
+    const auto tiles = [&](auto whole) {
 #pragma unroll
-    for (int nt = 0; nt < kPfNT; ++nt) {
-      float part = 0.f;
+      for (int nt = 0; nt < kPfNT; ++nt) {
+        v4f cx = (v4f){0.f, 0.f, 0.f, 0.f}, cy = cx;
+        cx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(AX[0], B[nt][0], cx, 0, 0, 0);
+        cy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(AY[0], B[nt][0], cy, 0, 0, 0);
+        cx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(AX[1], B[nt][1], cx, 0, 0, 0);
+        cy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(AY[1], B[nt][1], cy, 0, 0, 0);
+        float px = 0.f, py = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part = fmaf(wv[r], relu_bits(c[nt][r]), part);
-      const float tot = pair16_sum(part);  // heads 0-3 plus heads 4-7
-      const int key = kw + 16 * nt + n;
-      if ((g & 1) == 0 && myq < nq && key < a.n_cap) srow[key] = key < Vq ? tot : kNegInf;
-    }
+        for (int r = 0; r < 4; ++r) {
+          px = fmaf(wx[r], relu_bits(cx[r]), px);
+          py = fmaf(wy[r], relu_bits(cy[r]), py);
+        }
+        const int key = kw + 16 * nt + n;
+        // scores are written once and read by another kernel: streamed past the caches
+        if (decltype(whole)::value || (myq < nq && key < a.n_cap))
+          __builtin_nontemporal_store(key < Vq ? px + py : kNegInf, &srow[key]);
+      }
+    };
+    if (4 * it + 4 <= nq && kw + 16 * kPfNT <= a.n_cap)  // wave-uniform
+      tiles(std::true_type{});
+    else
+      tiles(std::false_type{});
   }
 }
 
@@ -514,3 +530,4 @@ hipError_t launch_index_scores_cand(const IndexArgs& a, const CandOut& c, hipStr
 }
 
 }  // namespace csa
+

@@ -11,13 +11,23 @@ namespace csa {
 namespace {
 
 // ------------------------------------------------------------------ block helpers
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts inside each
+// 16-lane row (zeros shifted in), then the three lower rows' totals.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+                 r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x % kWave) / 16;
+  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
 // Inclusive prefix sum over the block (blockDim.x a multiple of 64, <= 1024).
 __device__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp /* >= 16 */, uint32_t* total) {
   const int l = threadIdx.x % kWave, w = threadIdx.x / kWave, nw = blockDim.x / kWave;
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t u = __shfl_up(v, o);
-    if (l >= o) v += u;
-  }
+  v = wave_incl_scan(v);
   if (l == kWave - 1) tmp[w] = v;
   __syncthreads();
   uint32_t base = 0, tot = 0;
@@ -108,12 +118,8 @@ __device__ void radix_threshold(KeyFn key, int n, int k, SelShared& sh, uint32_t
       const int L = threadIdx.x;
       const uint32_t h0 = hist[4 * L], h1 = hist[4 * L + 1], h2 = hist[4 * L + 2], h3 = hist[4 * L + 3];
       const uint32_t mine = h0 + h1 + h2 + h3;
-      uint32_t suf = mine;  // inclusive suffix over lanes >= L
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t u = __shfl_down(suf, o);
-        if (L + o < kWave) suf += u;
-      }
-      uint32_t run = suf - mine;  // keys in bins above this lane's four
+      const uint32_t incl = wave_incl_scan(mine);
+      uint32_t run = __builtin_amdgcn_readlane(incl, kWave - 1) - incl;  // keys in bins above this lane's four
       const uint32_t hh[4] = {h0, h1, h2, h3};
 #pragma unroll
       for (int d = 3; d >= 0; --d) {
@@ -254,21 +260,7 @@ __device__ void compact_selected(KeyFn key, int n, uint32_t T, uint32_t krem, Se
   __syncthreads();
 }
 
-// n fp32 scores -> order-preserving keys in LDS; 8 float4 loads in flight per thread.
 // ------------------------------------------------------------------ one-wave top-32
-// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts inside each
-// 16-lane row (zeros shifted in), then the three lower rows' totals.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);  // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);  // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);  // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);  // row_shr:8
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
-                 r2 = __builtin_amdgcn_readlane(v, 47);
-  const int row = (threadIdx.x % kWave) / 16;
-  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
-}
-
 constexpr int kWaveTopN = 16;  // keys per lane of a one-wave slice selection: 1024 per wave
 
 // The float a key came from (inverse of float_key).
