@@ -133,19 +133,43 @@ __global__ __launch_bounds__(256) void index_bf16_kernel(IndexArgs a) {
 
 // ------------------------------------------------------------------ bf16 MFMA, many queries
 // heads == 8, dim == 64, many queries per sequence (a prefill chunk): a dense
-// [queries*8 x 64] x [64 x keys] contraction.  Workgroup tile: 36 queries x 512
-// keys.  The 36 queries' heads are staged once in LDS (A operand); each wave holds
-// its 128 keys in registers as the B operand for all 18 row tiles, so a key is
+// [queries*8 x 64] x [64 x keys] contraction.  Workgroup tile: 72 queries x 1024
+// keys, 8 waves.  The 72 queries' heads are staged once in LDS (A operand); each wave
+// holds its 128 keys in registers as the B operand for all 36 row tiles, so a key is
 // loaded once per workgroup.  The epilogue (ReLU, head weights, the sum over heads)
 // is the same arithmetic in the same order as index_bf16_kernel: bit-identical
-// scores.
-// 36 queries (nine quads) per workgroup: 57 x 33 = 1,881 workgroups for 2,048 queries over
-// 16,896 keys, two rounds of the 1,024 that are resident at once (32 queries make
-// 2,112: a third round of 64)
-constexpr int kPfQ = 36;        // queries per workgroup
-constexpr int kPfNT = 8;        // 16-key column tiles per wave
-constexpr int kPfKeys = 4 * 16 * kPfNT;  // keys per workgroup (512)
-static_assert(kPfQ % 4 == 0 && kPfQ * 8 * 8 % 256 == 0, "query quads; whole staging rounds");
+// scores.  The tile is sized so that the whole grid is resident at once (2,048
+// queries over 16,896 keys: 29 x 17 = 493 workgroups, two per CU by LDS): the
+// staging round trip is paid once, not once per round.
+constexpr int kPfQ = 72;        // queries per workgroup
+constexpr int kPfNT = 8;        // 16-key column tiles per wave (a multiple of 4)
+constexpr int kPfWaves = 8;
+constexpr int kPfKeys = kPfWaves * 16 * kPfNT;  // keys per workgroup (1024)
+static_assert(kPfQ % 4 == 0 && kPfQ * 8 * 8 % (64 * kPfWaves) == 0, "query quads; whole staging rounds");
+constexpr int kPfMinTq = 32;  // chunks of fewer queries take index_bf16_kernel
+
+// 4x4 transpose across the four lanes of each lane quad: lane i holds x[0..3] = M[i][.];
+// afterwards lane i holds M[.][i].  Two exchange stages (partner lane i ^ 1, then i ^ 2),
+// each one DPP move and selects per exchanged pair.
+__device__ __forceinline__ void quad_transpose4(float (&x)[4]) {
+  const int i = threadIdx.x & 3;
+  {
+    const bool odd = i & 1;
+    const float r0 = dpp_f32<0xB1>(odd ? x[0] : x[1]), r1 = dpp_f32<0xB1>(odd ? x[2] : x[3]);
+    x[0] = odd ? r0 : x[0];
+    x[1] = odd ? x[1] : r0;
+    x[2] = odd ? r1 : x[2];
+    x[3] = odd ? x[3] : r1;
+  }
+  {
+    const bool hi = i & 2;
+    const float r0 = dpp_f32<0x4E>(hi ? x[0] : x[2]), r1 = dpp_f32<0x4E>(hi ? x[1] : x[3]);
+    x[0] = hi ? r0 : x[0];
+    x[2] = hi ? x[2] : r0;
+    x[1] = hi ? r1 : x[1];
+    x[3] = hi ? x[3] : r1;
+  }
+}
 
 // max(x, 0) as one integer max on the bits (a negative float is a negative integer;
 // -0 and every negative value give +0): the float max form costs a canonicalize too
@@ -153,7 +177,7 @@ __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(
 
 // (a 128-register budget: the MFMA accumulators then stay in VGPRs, so the epilogue
 // reads them without AGPR copies)
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void index_bf16_tile_kernel(IndexArgs a) {
+__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(4))) void index_bf16_tile_kernel(IndexArgs a) {
   const int b = blockIdx.z;
   const int q0 = blockIdx.y * kPfQ;
   const int kbase = blockIdx.x * kPfKeys;
@@ -166,14 +190,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   __shared__ int vsh[kPfQ];
   const int nq = min(kPfQ, a.tq - q0);
 #pragma unroll
-  for (int i = 0; i < kPfQ * 8 * 8 / 256; ++i) {
-    const int idx = t + 256 * i, r = idx / 8, c = idx % 8, q = r / 8, h = r % 8;
+  for (int i = 0; i < kPfQ * 8 * 8 / (64 * kPfWaves); ++i) {
+    const int idx = t + 64 * kPfWaves * i, r = idx / 8, c = idx % 8, q = r / 8, h = r % 8;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (q < nq)
       v = *(const uint4*)((const uint16_t*)a.q.data + (int64_t)b * a.q.sb + (int64_t)(q0 + q) * a.q.sr + h * 64 + 8 * c);
     qs[r][c ^ (r & 7)] = v;
   }
-  for (int i = t; i < kPfQ * 8; i += 256) {
+  for (int i = t; i < kPfQ * 8; i += 64 * kPfWaves) {
     const int q = i / 8, h = i % 8;
     wsh[q][h] = q < nq ? a.w[((int64_t)b * a.tq + q0 + q) * 8 + h] : 0.f;
   }
@@ -183,6 +207,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   for (int q = 0; q < kPfQ; ++q) vmax = max(vmax, vsh[q]);
   const int kw = kbase + 16 * kPfNT * wave;  // this wave's first key
   float* srow_base = a.scores + ((int64_t)b * a.tq + q0) * a.n_cap;
+  const bool rows16 = (a.n_cap & 3) == 0 && ((uintptr_t)a.scores & 15) == 0;  // 16-byte aligned rows
   if (kw >= vmax) {  // no query of the tile sees these keys: -inf only
     for (int q = 0; q < nq; ++q)
       for (int i = l; i < 16 * kPfNT; i += kWave)
@@ -210,20 +235,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     const int myq = 4 * it + g;
     const int Vq = vsh[myq];
     float* srow = srow_base + (int64_t)myq * a.n_cap;
-    const int rx = 8 * (4 * it + n / 4) + n % 4, ry = rx + 4;
+    // X row 8(4it + n/4) + n%4 holds dims chunk 4ks + g at position 4ks + c0 (c0 = g ^ n%4);
+    // the Y row, 4 further, at 4(1 - ks) + c0: one address plus constant offsets
+    const uint4* ap = &qs[8 * (4 * it + n / 4) + n % 4][g ^ (n % 4)];
     v8bf AX[2], AY[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      AX[ks] = __builtin_bit_cast(v8bf, qs[rx][(4 * ks + g) ^ (rx & 7)]);
-      AY[ks] = __builtin_bit_cast(v8bf, qs[ry][(4 * ks + g) ^ (ry & 7)]);
-    }
+    AX[0] = __builtin_bit_cast(v8bf, ap[0]);
+    AX[1] = __builtin_bit_cast(v8bf, ap[4]);
+    AY[0] = __builtin_bit_cast(v8bf, ap[4 * 8 + 4]);
+    AY[1] = __builtin_bit_cast(v8bf, ap[4 * 8]);
     const float4 w0 = *(const float4*)&wsh[myq][0], w1 = *(const float4*)&wsh[myq][4];
     const float wx[4] = {w0.x, w0.y, w0.z, w0.w}, wy[4] = {w1.x, w1.y, w1.z, w1.w};
-    // a whole quad of 128 in-range keys stores with no per-lane test (no branch in
-    // the tile loop, so the scheduler overlaps one tile's MFMAs with another's epilogue)
-    const auto tiles = [&](auto whole) {
+    const int vrel = Vq - kw - n;  // (one register for the eight visibility tests)
+    // a whole quad of 128 in-range keys in 16-byte aligned rows takes vector stores
+    // with no per-lane test (wave-uniform)
+    const bool whole = rows16 && 4 * it + 4 <= nq && kw + 16 * kPfNT <= a.n_cap;
+    // tiles 4c .. 4c+3 at a time (four scores live per lane)
 #pragma unroll
-      for (int nt = 0; nt < kPfNT; ++nt) {
+    for (int c = 0; c < kPfNT / 4; ++c) {
+      float x[4];  // this lane's scores: query 4it + g, keys kw + 16(4c + i) + n
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int nt = 4 * c + i;
         v4f cx = (v4f){0.f, 0.f, 0.f, 0.f}, cy = cx;
         cx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(AX[0], B[nt][0], cx, 0, 0, 0);
         cy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(AY[0], B[nt][0], cy, 0, 0, 0);
@@ -235,16 +267,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
           px = fmaf(wx[r], relu_bits(cx[r]), px);
           py = fmaf(wy[r], relu_bits(cy[r]), py);
         }
-        const int key = kw + 16 * nt + n;
-        // scores are written once and read by another kernel: streamed past the caches
-        if (decltype(whole)::value || (myq < nq && key < a.n_cap))
-          __builtin_nontemporal_store(key < Vq ? px + py : kNegInf, &srow[key]);
+        x[i] = 16 * nt < vrel ? px + py : kNegInf;  // key kw + 16nt + n < Vq
       }
-    };
-    if (4 * it + 4 <= nq && kw + 16 * kPfNT <= a.n_cap)  // wave-uniform
-      tiles(std::true_type{});
-    else
-      tiles(std::false_type{});
+      // scores are written once and read by another kernel: streamed past the caches
+      if (whole) {
+        // a 4x4 transpose across each lane quad gives lane n = 4j + i the four
+        // consecutive keys 64c + 16i + 4j .. +3: one 16-byte store per lane writes 256
+        // contiguous bytes of each query row
+        quad_transpose4(x);
+        __builtin_nontemporal_store((v4f){x[0], x[1], x[2], x[3]},
+                                    (v4f*)&srow[kw + 64 * c + 16 * (n & 3) + 4 * (n >> 2)]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kw + 16 * (4 * c + i) + n;
+          if (myq < nq && key < a.n_cap) __builtin_nontemporal_store(x[i], &srow[key]);
+        }
+      }
+    }
   }
 }
 
@@ -496,10 +536,10 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((index_mxfp4_kernel<4, false>), grid, dim3(256), 0, s, a, none, no_compress(nslices, rows));
     else
       hipLaunchKernelGGL((index_mxfp4_kernel<16, false>), grid, dim3(256), 0, s, a, none, no_compress(nslices, rows));
-  } else if (a.k.dtype == CSA_BF16 && a.q.dtype == CSA_BF16 && a.heads == 8 && a.dim == 64 && a.tq >= kPfQ) {
+  } else if (a.k.dtype == CSA_BF16 && a.q.dtype == CSA_BF16 && a.heads == 8 && a.dim == 64 && a.tq >= kPfMinTq) {
     // many queries per sequence: the 32-query tile kernel (same arithmetic, same order)
     dim3 grid((a.n_cap + kPfKeys - 1) / kPfKeys, (a.tq + kPfQ - 1) / kPfQ, a.batch);
-    hipLaunchKernelGGL(index_bf16_tile_kernel, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(index_bf16_tile_kernel, grid, dim3(64 * kPfWaves), 0, s, a);
   } else if (a.k.dtype == CSA_BF16 && a.q.dtype == CSA_BF16 && a.heads == 8 && a.dim == 64) {
     dim3 grid((a.n_cap + kBfKT - 1) / kBfKT, (a.tq + kBfQT - 1) / kBfQT, a.batch);
     hipLaunchKernelGGL(index_bf16_kernel, grid, dim3(256), 0, s, a);

@@ -208,7 +208,8 @@ def _index_case(name, B, Tq, HI, dI, N, m, kfmt):
 @pytest.mark.parametrize("B,Tq,HI,dI,N,kfmt", [
     (1, 1, 4, 32, 1024, "f32"), (2, 3, 4, 32, 777, "f32"),
     (2, 1, 8, 64, 5000, "bf16"), (1, 37, 8, 64, 3000, "bf16"),
-    (2, 70, 8, 64, 5000, "bf16"),  # many queries: the 36-query tile kernel, ragged query and key tails
+    (2, 150, 8, 64, 5000, "bf16"),  # many queries: the 72-query tile kernel, ragged query and key tails
+    (1, 40, 8, 64, 777, "bf16"),  # tile kernel, rows not 16-byte aligned (scalar score stores)
     (3, 1, 8, 64, 9000, "mxfp4"), (2, 5, 8, 64, 4100, "mxfp4"), (1, 1, 32, 64, 700, "mxfp4"),
 ])
 def test_index_scores(gpu_lib, B, Tq, HI, dI, N, kfmt):
