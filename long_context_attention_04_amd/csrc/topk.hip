@@ -10,8 +10,10 @@
 // fp32 score (-0 folded onto +0), with ties broken by index, followed by an
 // ascending-order compaction.  Integer histograms only, so results are exact
 // and do not depend on scheduling.
-//  * Rows of up to kTopkLdsMax keys: one workgroup per row, the row resident
-//    in LDS, four 8-bit passes, then a block-scan compaction.
+//  * Rows of up to kTopkLdsMax keys: one workgroup per row.  For k <= 4096 the row is
+//    held in registers (20 keys per thread at most) and selected with value-linear then
+//    key-space histograms and one block scan; otherwise the row is resident in LDS,
+//    radix passes over the live key range, then a block-scan compaction.
 //  * Longer rows (1M-token decode: 262,144 blocks per row and only 8 rows):
 //    two kernels and no communication between workgroups of one kernel
 //    (on this chip a device-scope fence writes back / invalidates the XCD's
@@ -461,6 +463,80 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge_slices_kernel(Merge
   }
 }
 
+// Rows of up to 1024 * NPT keys (a prefill chunk's rows), register-resident: thread t
+// holds positions NPT*t .. NPT*t+NPT-1, so slot order is index order.  The threshold is
+// found on the registers (block_threshold_regs: value-linear bins first, then key-space
+// bins, exact) and the compaction is one block scan, as in the slice-list merge.  A
+// present key is made nonzero (0 marks the positions past the row's visible count; only
+// the all-ones NaN pattern maps to 0 and is folded onto the next key).
+constexpr int kTopkRegsMaxK = 4096;  // selections staged in LDS before the coalesced write
+
+template <int NPT>
+__global__ __launch_bounds__(kRegSelThreads) void topk_regs_kernel(const float* __restrict__ scores,
+                                                                   const int32_t* __restrict__ q_pos, int n_cap, int m,
+                                                                   int k, int32_t* __restrict__ idx) {
+  __shared__ RegSelLds rs;
+  __shared__ uint32_t ostage[kTopkRegsMaxK + kRegSelThreads];
+  static_assert(NPT % 4 == 0, "float4 loads");  // indices by rank, then discard slots
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int V = min(visible_blocks(q_pos[row], m), n_cap);
+  int32_t* out = idx + row * k;
+  if (V <= k) {
+    for (int i = t; i < k; i += kRegSelThreads) out[i] = i < V ? i : -1;
+    return;
+  }
+  const float* src = scores + row * n_cap;
+  uint32_t kv[NPT];
+  const bool vec = (((uintptr_t)src) & 15) == 0;
+#pragma unroll
+  for (int q = 0; q < NPT / 4; ++q) {
+    const int p0 = NPT * t + 4 * q;
+    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (vec && p0 + 3 < V) {
+      f = *(const float4*)(src + p0);
+    } else {
+      if (p0 < V) f.x = src[p0];
+      if (p0 + 1 < V) f.y = src[p0 + 1];
+      if (p0 + 2 < V) f.z = src[p0 + 2];
+      if (p0 + 3 < V) f.w = src[p0 + 3];
+    }
+    kv[4 * q] = p0 < V ? max(float_key(f.x), 1u) : 0u;
+    kv[4 * q + 1] = p0 + 1 < V ? max(float_key(f.y), 1u) : 0u;
+    kv[4 * q + 2] = p0 + 2 < V ? max(float_key(f.z), 1u) : 0u;
+    kv[4 * q + 3] = p0 + 3 < V ? max(float_key(f.w), 1u) : 0u;
+  }
+  uint32_t lo, hi, M;
+  block_key_range(kv, rs, &lo, &hi, &M);  // M = V > k
+  uint32_t T, krem;
+  block_threshold_regs(kv, lo, hi, (uint32_t)k, rs, &T, &krem);
+  // compaction in position order: one scan of (keys > T) | (copies of T) << 16
+  uint32_t gtc = 0, eqc = 0;
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    gtc += kv[j] > T;
+    eqc += kv[j] == T;
+  }
+  const uint32_t packed = gtc | (eqc << 16);
+  uint32_t tot;
+  const uint32_t excl = block_scan_regsel(packed, rs.scan[2], &tot) - packed;
+  krem = min(krem, tot >> 16);  // "every copy" made a count
+  uint32_t eq_seen = excl >> 16;
+  uint32_t r = (excl & 0xffffu) + min(eq_seen, krem);
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const bool is_eq = kv[j] == T;
+    const bool keep = kv[j] > T || (is_eq && eq_seen < krem);
+    eq_seen += is_eq;
+    ostage[keep && r < (uint32_t)k ? r : (uint32_t)kTopkRegsMaxK + t] = (uint32_t)(NPT * t + j);
+    r += keep;
+  }
+  __syncthreads();
+  for (int i = t; i < k; i += kRegSelThreads) out[i] = (int32_t)ostage[i];
+}
+static_assert(20 * kRegSelThreads >= kTopkLdsMax, "the register path covers every row the LDS path does");
+static_assert(kRegSelThreads * 16 < 65536, "scan halves of 16 bits");
+
 // C for a row length: the merge holds nslices * C candidates in LDS.
 __host__ inline int cand_per_slice(int n_cap, int k) {
   const int ns = (n_cap + kSlice - 1) / kSlice;
@@ -486,6 +562,16 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int
                        int32_t* idx, void* ws, hipStream_t s) {
   const int64_t rows = (int64_t)batch * tq;
   if (rows == 0) return hipSuccess;
+  if (n_cap <= kTopkLdsMax && k <= kTopkRegsMaxK) {
+    const dim3 grid((unsigned)rows), block(kRegSelThreads);
+    if (n_cap <= 8 * kRegSelThreads)
+      hipLaunchKernelGGL(topk_regs_kernel<8>, grid, block, 0, s, scores, q_pos, n_cap, m, k, idx);
+    else if (n_cap <= 16 * kRegSelThreads)
+      hipLaunchKernelGGL(topk_regs_kernel<16>, grid, block, 0, s, scores, q_pos, n_cap, m, k, idx);
+    else
+      hipLaunchKernelGGL(topk_regs_kernel<20>, grid, block, 0, s, scores, q_pos, n_cap, m, k, idx);
+    return hipGetLastError();
+  }
   if (n_cap <= kTopkLdsMax) {
     const size_t lds = (size_t)std::max(n_cap, 1) * 4;
     hipLaunchKernelGGL(topk_lds_kernel, dim3((unsigned)rows), dim3(kLdsThreads), lds, s, scores, q_pos, n_cap, m, k,

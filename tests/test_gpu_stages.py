@@ -254,6 +254,10 @@ def test_index_scores(gpu_lib, B, Tq, HI, dI, N, kfmt):
     (4, 2, 65536, 2048, "partial"), (3, 1, 262144, 2048, "partial"),
     (1, 2, 70000, 1024, "extreme"), (2, 1, 262144, 2048, "extreme"), (1, 1, 16000, 512, "extreme"),
     (1, 2, 70000, 1024, "tiny"), (2, 1, 262144, 2048, "narrow"),
+    # rows of <= 20,480 keys with k <= 4,096: the register-resident kernel
+    (1, 2, 12000, 700, "equal"), (1, 2, 20000, 1024, "tiny"), (2, 1, 9000, 300, "narrow"),
+    (2, 2, 16896, 512, "partial"), (1, 1, 20480, 2048, "extreme"),
+    (1, 2, 9000, 5000, "normal"),  # k > 4,096: the LDS kernel
 ])
 def test_topk_exact(gpu_lib, B, Tq, N, k, mode):
     csa = gpu_lib
