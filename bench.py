@@ -397,7 +397,7 @@ class CsaPrefill:
         pos = L.host["t"]
         vis = (pos + 1) // L.m
         flops = int(np.sum(vis)) * 2 * L.HI * L.dI * L.B
-        self.dominant = {"kernel": "index_bf16_kernel (csa_index_scores)", "bound": "mfma", "work": flops,
+        self.dominant = {"kernel": "index_bf16_tile_kernel (csa_index_scores)", "bound": "mfma", "work": flops,
                          "work_note": "2 * H_I * d_I flops per visible (query, block) pair, causal"}
         self.bytes = {"keys": L.B * L.n_cap * L.dI * 2, "q_idx_w": L.B * L.tq * L.HI * (L.dI * 2 + 4),
                       "gather_unique": L.B * L.n_cap * L.D * 2,
@@ -463,7 +463,7 @@ class HcaDecode:
         q_out = L.B * L.H * (L.D * 2 + L.D * 4 + 4)
         self.bytes = {"entries": gather, "q_out_lse": q_out}
         self.excluded = {"attention_split_partials": 2 * L.B * 8 * L.H * (L.D + 2) * 4}
-        self.dominant = {"kernel": "attn_chunk_kernel<false> + attn_merge_kernel (hca_attn)", "bound": "hbm",
+        self.dominant = {"kernel": "attn_chunk_kernel<bf16, 8, 136> + attn_merge_kernel (hca_attn)", "bound": "hbm",
                          "work": gather + q_out, "work_note": "visible compressed rows + window rows + q, out, lse"}
         self.dtype = "bf16"
         self.config = {"workload": name, "batch": wl.batch, "context": f"U[{wl.extra['len_lo']}, {wl.extra['len_hi']}]",
