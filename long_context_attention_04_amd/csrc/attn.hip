@@ -488,14 +488,27 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
             (lds_v4bf*)&rowb[swz_off(16 * ks + 4 * g + m / 4, col / 8) + 2 * (col % 8)]);
       }
     };
+    // P hi and P lo in two 16x16x16 MFMAs on the same transposed V read (no operand
+    // copies).  Only a chunk's last tile can reach past the buffer (CH not a multiple of
+    // 16): there the lanes that read past it take zeros (whatever lies after the buffer
+    // must not reach other entries' heads, e.g. a NaN in one head's query).
+    typedef short v4s __attribute__((ext_vector_type(4)));
     const auto pv_mfma = [&](int ks, const v8bf& pa, const v4bf (&tv)[kNT]) {
-      const bool past = 16 * ks + 4 * g + m / 4 >= CH;  // the lane read past the buffer: no entry there
+      const v4s ph = __builtin_bit_cast(v4s, __builtin_shufflevector(pa, pa, 0, 1, 2, 3));
+      const v4s pl = __builtin_bit_cast(v4s, __builtin_shufflevector(pa, pa, 4, 5, 6, 7));
+      const auto run = [&](auto masked) {
+        const bool past = decltype(masked)::value && 16 * ks + 4 * g + m / 4 >= CH;
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const v4bf t = past ? (v4bf){} : tv[nt];
-        const v8bf vb = __builtin_shufflevector(t, t, 0, 1, 2, 3, 0, 1, 2, 3);
-        O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, O[nt], 0, 0, 0);
-      }
+        for (int nt = 0; nt < kNT; ++nt) {
+          const v4s vb = past ? (v4s){0, 0, 0, 0} : __builtin_bit_cast(v4s, tv[nt]);
+          O[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vb, O[nt], 0, 0, 0);
+          O[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb, O[nt], 0, 0, 0);
+        }
+      };
+      if (16 * ks + 16 > CH)  // wave-uniform
+        run(std::true_type{});
+      else
+        run(std::false_type{});
     };
     {
       v8bf pa0, pa1;
