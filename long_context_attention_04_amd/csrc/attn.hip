@@ -698,12 +698,16 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
   // (75 KB of LDS: two workgroups per CU, one computing while the other gathers).
   const int fmt = a.kv.dtype == CSA_FP8_E4M3 ? kFmtFp8 : a.kv.dtype == CSA_MXFP4 ? kFmtFp4 : kFmtBf16;
   const bool many = a.tq != 1;
+  // HCA (dense over every visible block; long lists at large batch) also takes the 4-wave
+  // shape: two workgroups per CU, one gathering while the other computes.  The shape is
+  // chosen by the call kind, never by the batch, so results stay batch-invariant.
+  const bool hca = a.idx == nullptr;
   const dim3 grid((unsigned)blocks);
 #define CSA_ATTN_LAUNCH(F, NW, CH)                                                                                \
   hipLaunchKernelGGL((attn_chunk_kernel<F, NW, CH>), grid, dim3(NW * kWave), 0, s, a.q_pos, a.idx, a.raw_base, a.k, \
                      a.tq, a.window, a.m_hc, split, nsplit_max, nhg, (int)rows, a)
 #define CSA_ATTN_SHAPES(F)              \
-  if (many) CSA_ATTN_LAUNCH(F, 4, 56); \
+  if (many || hca) CSA_ATTN_LAUNCH(F, 4, 56); \
   else CSA_ATTN_LAUNCH(F, 8, 136);
   if (fmt == kFmtFp8) {
     CSA_ATTN_SHAPES(kFmtFp8)
