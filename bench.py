@@ -462,7 +462,7 @@ class HcaDecode:
         gather = int(np.sum(vis + L.W)) * L.D * 2
         q_out = L.B * L.H * (L.D * 2 + L.D * 4 + 4)
         self.bytes = {"entries": gather, "q_out_lse": q_out}
-        self.excluded = {"attention_split_partials": 2 * L.B * 8 * L.H * (L.D + 2) * 4}
+        self.excluded = {"attention_split_partials": 2 * L.B * 4 * L.H * (L.D + 2) * 4}  # HCA decode: four splits
         self.dominant = {"kernel": "attn_chunk_kernel<bf16, 4, 56> + attn_merge_kernel (hca_attn)", "bound": "hbm",
                          "work": gather + q_out, "work_note": "visible compressed rows + window rows + q, out, lse"}
         self.dtype = "bf16"

@@ -520,7 +520,7 @@ static csa_status attn_common(const csa_tensor* q, const csa_tensor* kv, const i
             (long long)align);
     REQUIRE((uintptr_t)q->data % 16 == 0 && q->stride_b % 8 == 0 && q->stride_row % 8 == 0, CSA_ERR_SHAPE,
             "q must be 16-byte aligned with strides a multiple of 8 elements");
-    const int split = csa::attn_split_size(tq, n_entries_max);
+    const int split = csa::attn_split_size(tq, n_entries_max, false);  // CSA cuts at least as many as HCA
     const int64_t nsplit = ((int64_t)std::max(n_entries_max, 1) + split - 1) / split;
     REQUIRE(nsplit <= csa::kAttnMaxSplits, CSA_ERR_UNSUPPORTED,
             "BF16/FP8/MXFP4 attention supports at most %d entries per query (got %d)",

@@ -725,20 +725,25 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
 
 }  // namespace
 
-// Splits depend only on the call shape (decode or not) and the entry capacity,
-// never on the batch, so each sequence's arithmetic is batch-invariant.  Decode
-// cuts a row's list into eight splits of whole 16-entry tiles, at least eight
-// tiles each (8 rows x 4 head groups x 8 splits fill the 256 CUs at batch 8);
-// calls with many queries per sequence keep each list whole.
-int attn_split_size(int tq, int n_entries_max) {
+// Splits depend only on the call kind, the call shape (decode or not) and the entry
+// capacity, never on the batch, so each sequence's arithmetic is batch-invariant.
+// CSA decode cuts a row's list into eight splits of whole 16-entry tiles, at least
+// eight tiles each (8 rows x 4 head groups x 8 splits fill the 256 CUs at batch 8);
+// HCA decode (dense lists, large batches) into quarters, which halves the split
+// partials the merge reads (batch 64: 69 -> 61 us per step; the hybrid pair's HCA
+// layer at batch 32: 61 -> 53 us); calls with many queries per sequence keep each list
+// whole.  HCA never cuts more splits than CSA at the same list length, so the CSA
+// workspace size bounds both.
+int attn_split_size(int tq, int n_entries_max, bool dense) {
   const int n = max(n_entries_max, 1);
   if (tq != 1) return min(n, kAttnMaxSplitEntries);
-  const int eighth = ((n + 7) / 8 + kTile - 1) / kTile * kTile;
-  return min(kAttnMaxSplitEntries, max(8 * kTile, eighth));
+  const int parts = dense ? 4 : 8;
+  const int part = ((n + parts - 1) / parts + kTile - 1) / kTile * kTile;
+  return min(kAttnMaxSplitEntries, max(8 * kTile, part));
 }
 
 size_t attn_workspace_bytes(int64_t rows, int heads, int dim, int n_entries_max, int tq) {
-  const int split = attn_split_size(tq, n_entries_max);
+  const int split = attn_split_size(tq, n_entries_max, false);  // the larger of the two policies
   const int64_t nsplit = (n_entries_max + split - 1) / split;
   if (nsplit <= 1) return 0;
   return (size_t)rows * nsplit * heads * (dim + 2) * sizeof(float);
@@ -753,7 +758,7 @@ hipError_t launch_attention(const AttnArgs& a, int n_entries_max, hipStream_t s)
     hipLaunchKernelGGL(attn_plain_kernel, dim3((unsigned)rows, a.heads), dim3(kPlainThreads), 0, s, a);
     return hipGetLastError();
   }
-  const int split = attn_split_size(a.tq, n_entries_max);
+  const int split = attn_split_size(a.tq, n_entries_max, a.idx == nullptr);
   const int nsplit_max = max(1, (n_entries_max + split - 1) / split);
   if (nsplit_max > kMergeMaxSplits) return hipErrorInvalidValue;
   return launch_decode(a, rows, split, nsplit_max, s);

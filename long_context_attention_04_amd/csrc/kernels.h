@@ -141,7 +141,7 @@ struct AttnArgs {
 // kAttnMaxSplitEntries entries each.
 constexpr int kAttnMaxSplits = 64;
 constexpr int kAttnMaxSplitEntries = 2048;
-int attn_split_size(int tq, int n_entries_max);
+int attn_split_size(int tq, int n_entries_max, bool dense);  // dense: HCA (every visible block)
 size_t attn_workspace_bytes(int64_t rows, int heads, int dim, int n_entries_max, int tq);
 hipError_t launch_attention(const AttnArgs& a, int n_entries_max, hipStream_t s);
 
