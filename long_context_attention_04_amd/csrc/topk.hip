@@ -471,68 +471,86 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge_slices_kernel(Merge
 // the all-ones NaN pattern maps to 0 and is folded onto the next key).
 constexpr int kTopkRegsMaxK = 4096;  // selections staged in LDS before the coalesced write
 
-template <int NPT>
+template <int NPT, bool VEC>  // VEC: 16-byte aligned rows (scores 16-byte aligned, n_cap % 4 == 0)
 __global__ __launch_bounds__(kRegSelThreads) void topk_regs_kernel(const float* __restrict__ scores,
                                                                    const int32_t* __restrict__ q_pos, int n_cap, int m,
-                                                                   int k, int32_t* __restrict__ idx) {
+                                                                   int k, int64_t rows, int32_t* __restrict__ idx) {
+  static_assert(NPT % 4 == 0, "float4 loads");
   __shared__ RegSelLds rs;
-  __shared__ uint32_t ostage[kTopkRegsMaxK + kRegSelThreads];
-  static_assert(NPT % 4 == 0, "float4 loads");  // indices by rank, then discard slots
-  const int64_t row = blockIdx.x;
+  __shared__ uint32_t ostage[kTopkRegsMaxK + kRegSelThreads];  // indices by rank, then discard slots
   const int t = threadIdx.x;
-  const int V = min(visible_blocks(q_pos[row], m), n_cap);
-  int32_t* out = idx + row * k;
-  if (V <= k) {
-    for (int i = t; i < k; i += kRegSelThreads) out[i] = i < V ? i : -1;
-    return;
-  }
-  const float* src = scores + row * n_cap;
-  uint32_t kv[NPT];
-  const bool vec = (((uintptr_t)src) & 15) == 0;
+  // a row's scores as stored (every position below the capacity: the visible count is
+  // applied after the loads, so they need not wait for the row's position)
+  // (positions past the capacity read a position inside it instead: no branch around
+  // the loads, and the visible count masks them)
+  const auto load_row = [&](int64_t row, float4 (&f)[NPT / 4]) {
+    const float* src = scores + row * n_cap;
 #pragma unroll
-  for (int q = 0; q < NPT / 4; ++q) {
-    const int p0 = NPT * t + 4 * q;
-    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (vec && p0 + 3 < V) {
-      f = *(const float4*)(src + p0);
-    } else {
-      if (p0 < V) f.x = src[p0];
-      if (p0 + 1 < V) f.y = src[p0 + 1];
-      if (p0 + 2 < V) f.z = src[p0 + 2];
-      if (p0 + 3 < V) f.w = src[p0 + 3];
+    for (int q = 0; q < NPT / 4; ++q) {
+      const int p0 = NPT * t + 4 * q;
+      if constexpr (VEC) {
+        f[q] = *(const float4*)(src + min(p0, n_cap - 4));
+      } else {
+        f[q].x = src[min(p0, n_cap - 1)];
+        f[q].y = src[min(p0 + 1, n_cap - 1)];
+        f[q].z = src[min(p0 + 2, n_cap - 1)];
+        f[q].w = src[min(p0 + 3, n_cap - 1)];
+      }
     }
-    kv[4 * q] = p0 < V ? max(float_key(f.x), 1u) : 0u;
-    kv[4 * q + 1] = p0 + 1 < V ? max(float_key(f.y), 1u) : 0u;
-    kv[4 * q + 2] = p0 + 2 < V ? max(float_key(f.z), 1u) : 0u;
-    kv[4 * q + 3] = p0 + 3 < V ? max(float_key(f.w), 1u) : 0u;
-  }
-  uint32_t lo, hi, M;
-  block_key_range(kv, rs, &lo, &hi, &M);  // M = V > k
-  uint32_t T, krem;
-  block_threshold_regs(kv, lo, hi, (uint32_t)k, rs, &T, &krem);
-  // compaction in position order: one scan of (keys > T) | (copies of T) << 16
-  uint32_t gtc = 0, eqc = 0;
+  };
+  // Workgroup w selects rows w, w + gridDim.x, ...: the next row's scores are requested
+  // before the current row is selected, so its loads overlap the selection.
+  int64_t row = blockIdx.x;
+  float4 cur[NPT / 4];
+  if (row < rows) load_row(row, cur);
+  for (; row < rows; row += gridDim.x) {
+    const int V = min(visible_blocks(q_pos[row], m), n_cap);
+    int32_t* out = idx + row * k;
+    // this row's keys first (its loads were issued a row ago), then the next row's loads
+    uint32_t kv[NPT];
 #pragma unroll
-  for (int j = 0; j < NPT; ++j) {
-    gtc += kv[j] > T;
-    eqc += kv[j] == T;
-  }
-  const uint32_t packed = gtc | (eqc << 16);
-  uint32_t tot;
-  const uint32_t excl = block_scan_regsel(packed, rs.scan[2], &tot) - packed;
-  krem = min(krem, tot >> 16);  // "every copy" made a count
-  uint32_t eq_seen = excl >> 16;
-  uint32_t r = (excl & 0xffffu) + min(eq_seen, krem);
+    for (int q = 0; q < NPT / 4; ++q) {
+      const int p0 = NPT * t + 4 * q;
+      kv[4 * q] = p0 < V ? max(float_key(cur[q].x), 1u) : 0u;
+      kv[4 * q + 1] = p0 + 1 < V ? max(float_key(cur[q].y), 1u) : 0u;
+      kv[4 * q + 2] = p0 + 2 < V ? max(float_key(cur[q].z), 1u) : 0u;
+      kv[4 * q + 3] = p0 + 3 < V ? max(float_key(cur[q].w), 1u) : 0u;
+    }
+    const int64_t nrow = row + gridDim.x;
+    if (nrow < rows) load_row(nrow, cur);
+    if (V <= k) {  // workgroup-uniform
+      for (int i = t; i < k; i += kRegSelThreads) out[i] = i < V ? i : -1;
+    } else {
+      uint32_t lo, hi, M;
+      block_key_range(kv, rs, &lo, &hi, &M);  // M = V > k (its barrier also ends the previous row's LDS use)
+      uint32_t T, krem;
+      block_threshold_regs(kv, lo, hi, (uint32_t)k, rs, &T, &krem);
+      // compaction in position order: one scan of (keys > T) | (copies of T) << 16
+      uint32_t gtc = 0, eqc = 0;
 #pragma unroll
-  for (int j = 0; j < NPT; ++j) {
-    const bool is_eq = kv[j] == T;
-    const bool keep = kv[j] > T || (is_eq && eq_seen < krem);
-    eq_seen += is_eq;
-    ostage[keep && r < (uint32_t)k ? r : (uint32_t)kTopkRegsMaxK + t] = (uint32_t)(NPT * t + j);
-    r += keep;
+      for (int j = 0; j < NPT; ++j) {
+        gtc += kv[j] > T;
+        eqc += kv[j] == T;
+      }
+      const uint32_t packed = gtc | (eqc << 16);
+      uint32_t tot;
+      const uint32_t excl = block_scan_regsel(packed, rs.scan[2], &tot) - packed;
+      krem = min(krem, tot >> 16);  // "every copy" made a count
+      uint32_t eq_seen = excl >> 16;
+      uint32_t r = (excl & 0xffffu) + min(eq_seen, krem);
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) {
+        const bool is_eq = kv[j] == T;
+        const bool keep = kv[j] > T || (is_eq && eq_seen < krem);
+        eq_seen += is_eq;
+        ostage[keep && r < (uint32_t)k ? r : (uint32_t)kTopkRegsMaxK + t] = (uint32_t)(NPT * t + j);
+        r += keep;
+      }
+      __syncthreads();
+      for (int i = t; i < k; i += kRegSelThreads) out[i] = (int32_t)ostage[i];
+      __syncthreads();  // ostage and the tables are free for the next row
+    }
   }
-  __syncthreads();
-  for (int i = t; i < k; i += kRegSelThreads) out[i] = (int32_t)ostage[i];
 }
 static_assert(20 * kRegSelThreads >= kTopkLdsMax, "the register path covers every row the LDS path does");
 static_assert(kRegSelThreads * 16 < 65536, "scan halves of 16 bits");
@@ -563,13 +581,25 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int
   const int64_t rows = (int64_t)batch * tq;
   if (rows == 0) return hipSuccess;
   if (n_cap <= kTopkLdsMax && k <= kTopkRegsMaxK) {
-    const dim3 grid((unsigned)rows), block(kRegSelThreads);
-    if (n_cap <= 8 * kRegSelThreads)
-      hipLaunchKernelGGL(topk_regs_kernel<8>, grid, block, 0, s, scores, q_pos, n_cap, m, k, idx);
-    else if (n_cap <= 16 * kRegSelThreads)
-      hipLaunchKernelGGL(topk_regs_kernel<16>, grid, block, 0, s, scores, q_pos, n_cap, m, k, idx);
-    else
-      hipLaunchKernelGGL(topk_regs_kernel<20>, grid, block, 0, s, scores, q_pos, n_cap, m, k, idx);
+    // one resident workgroup per CU, each walking its rows (the next row's loads in flight)
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    const dim3 grid((unsigned)std::min<int64_t>(rows, std::max(cus, 1))), block(kRegSelThreads);
+    const bool vec = (((uintptr_t)scores) & 15) == 0 && (n_cap & 3) == 0 && n_cap >= 4;
+#define CSA_TOPK_REGS(NPT)                                                                                       \
+  if (vec)                                                                                                       \
+    hipLaunchKernelGGL((topk_regs_kernel<NPT, true>), grid, block, 0, s, scores, q_pos, n_cap, m, k, rows, idx); \
+  else                                                                                                           \
+    hipLaunchKernelGGL((topk_regs_kernel<NPT, false>), grid, block, 0, s, scores, q_pos, n_cap, m, k, rows, idx);
+    if (n_cap <= 8 * kRegSelThreads) {
+      CSA_TOPK_REGS(8)
+    } else if (n_cap <= 16 * kRegSelThreads) {
+      CSA_TOPK_REGS(16)
+    } else {
+      CSA_TOPK_REGS(20)
+    }
+#undef CSA_TOPK_REGS
     return hipGetLastError();
   }
   if (n_cap <= kTopkLdsMax) {
