@@ -206,14 +206,14 @@ __device__ __forceinline__ float lane_sum4rows(float x) {  // fixed-order sum ov
 constexpr int kRowBytes = 1024;
 
 // NW waves per workgroup, chunks of at most CH entries.
-template <int NW, int CH>
+template <int NW, int CH, bool QL>
 struct ChunkLds {
   static constexpr int kTiles = (CH + 15) / 16;
   __attribute__((aligned(16))) uint8_t rows[CH][kRowBytes];
   union {
-    // the 16 query heads, staged once (same swizzle as the rows) and read into
+    // QL: the 16 query heads, staged once (same swizzle as the rows) and read into
     // registers before P is first written
-    __attribute__((aligned(16))) uint8_t q[16][kRowBytes];
+    __attribute__((aligned(16))) uint8_t q[QL ? 16 : 1][kRowBytes];
     // P as the PV A operand: [tile][k group g][head m] -> 4 bf16 hi then 4 bf16 lo
     // of entries 16*tile + 4g .. +3
     __attribute__((aligned(16))) uint4 p[kTiles][4][16];
@@ -242,7 +242,7 @@ __device__ __forceinline__ int swz_off(int r, int chunk16) { return r * kRowByte
 // The scalars the prologue depends on come first in the argument list: they are
 // preloaded into scalar registers at launch (the rest of the arguments is read from
 // memory, one round trip that overlaps the position and slot loads).
-template <int FMT, int NW, int CH>
+template <int FMT, int NW, int CH, bool QL>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunk_kernel(
     const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ raw_base, int k, int tq, int window, int m_hc,
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   const int e_end = min(ri.n_tot, e_begin + split);
   const int h0 = hg * 16;
 
-  __shared__ ChunkLds<NW, CH> L;
+  __shared__ ChunkLds<NW, CH, QL> L;
   uint8_t* const rowb = &L.rows[0][0];  // the chunk's rows as one byte array
 
   // the 16 query heads as the QK B operand: lane (head m, group g) holds columns
@@ -357,11 +357,16 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
         }
       }
     }
-    if (c0 == e_begin) {  // the 16 query heads to LDS, 16 / NW per wave
+    if (c0 == e_begin) {
+      if constexpr (QL) {  // the 16 query heads to LDS, 16 / NW per wave
 #pragma unroll
-      for (int hh = (16 / NW) * w; hh < (16 / NW) * (w + 1); ++hh)
-        __builtin_amdgcn_global_load_lds((const gbyte*)(qp + (h0 + hh) * 512) + 16 * (lane ^ swz(hh)),
-                                         (__attribute__((address_space(3))) void*)&L.q[hh][0], 16, 0, 0);
+        for (int hh = (16 / NW) * w; hh < (16 / NW) * (w + 1); ++hh)
+          __builtin_amdgcn_global_load_lds((const gbyte*)(qp + (h0 + hh) * 512) + 16 * (lane ^ swz(hh)),
+                                           (__attribute__((address_space(3))) void*)&L.q[hh][0], 16, 0, 0);
+      } else {  // each wave reads its operand straight into registers (16 KB per wave)
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) qb[kk] = *(const v8bf*)(qp + (int64_t)(h0 + m) * 512 + 32 * kk + 8 * g);
+      }
     }
     // the next chunk's slots, requested while this chunk's rows are in flight
     jn = -1;
@@ -382,7 +387,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // rows (and the first time, the query heads) in LDS
-    if (c0 == e_begin) {
+    if (QL && c0 == e_begin) {
       const uint8_t* qs = &L.q[0][0];
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) qb[kk] = *(const v8bf*)&qs[swz_off(m, 4 * kk + g)];
@@ -693,9 +698,14 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
   const int nhg = a.heads / 16;
   const int64_t pairs = rows * nsplit_max;
   const int64_t blocks = rows >= 8 ? (rows + 7) / 8 * 8 * nsplit_max * nhg : (pairs + 7) / 8 * 8 * nhg;
-  // Decode: 8 waves and chunks of 136 entries (one workgroup per CU; a split of 272
-  // entries is two chunks).  Many queries per sequence: 4 waves and chunks of 56
-  // (75 KB of LDS: two workgroups per CU, one computing while the other gathers).
+  // CSA decode: 8 waves and chunks of 136 entries (one workgroup per CU; a split of 272
+  // entries is two chunks).  HCA decode: 4 waves and chunks of 56 (75 KB of LDS: two
+  // workgroups per CU, one computing while the other gathers).  Many queries per
+  // sequence: 4 waves and chunks of 64 (whole tiles; a 640-entry list is ten chunks),
+  // the query operand read by each wave from memory so that the 16 KB query staging
+  // does not take LDS (70 KB: still two per CU).  Measured on the 2k prefill chunks:
+  // 56-entry chunks with staged queries 799 (CSA) / 747 (HCA) us, 64-entry chunks 731 /
+  // 731 us; HCA decode keeps the staged 56-entry shape (61 us against 64 at batch 64).
   const int fmt = a.kv.dtype == CSA_FP8_E4M3 ? kFmtFp8 : a.kv.dtype == CSA_MXFP4 ? kFmtFp4 : kFmtBf16;
   const bool many = a.tq != 1;
   // HCA (dense over every visible block; long lists at large batch) also takes the 4-wave
@@ -703,12 +713,13 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
   // chosen by the call kind, never by the batch, so results stay batch-invariant.
   const bool hca = a.idx == nullptr;
   const dim3 grid((unsigned)blocks);
-#define CSA_ATTN_LAUNCH(F, NW, CH)                                                                                \
-  hipLaunchKernelGGL((attn_chunk_kernel<F, NW, CH>), grid, dim3(NW * kWave), 0, s, a.q_pos, a.idx, a.raw_base, a.k, \
-                     a.tq, a.window, a.m_hc, split, nsplit_max, nhg, (int)rows, a)
-#define CSA_ATTN_SHAPES(F)              \
-  if (many || hca) CSA_ATTN_LAUNCH(F, 4, 56); \
-  else CSA_ATTN_LAUNCH(F, 8, 136);
+#define CSA_ATTN_LAUNCH(F, NW, CH, QL)                                                                             \
+  hipLaunchKernelGGL((attn_chunk_kernel<F, NW, CH, QL>), grid, dim3(NW * kWave), 0, s, a.q_pos, a.idx, a.raw_base, \
+                     a.k, a.tq, a.window, a.m_hc, split, nsplit_max, nhg, (int)rows, a)
+#define CSA_ATTN_SHAPES(F)                       \
+  if (many) CSA_ATTN_LAUNCH(F, 4, 64, false);    \
+  else if (hca) CSA_ATTN_LAUNCH(F, 4, 56, true); \
+  else CSA_ATTN_LAUNCH(F, 8, 136, true);
   if (fmt == kFmtFp8) {
     CSA_ATTN_SHAPES(kFmtFp8)
   } else if (fmt == kFmtFp4) {
