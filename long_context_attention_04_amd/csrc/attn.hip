@@ -212,7 +212,8 @@ struct ChunkLds {
   __attribute__((aligned(16))) uint8_t rows[CH][kRowBytes];
   union {
     // QL: the 16 query heads, staged once (same swizzle as the rows) and read into
-    // registers before P is first written
+    // registers before P is first written (otherwise they pass through the rows buffer
+    // before the first chunk)
     __attribute__((aligned(16))) uint8_t q[QL ? 16 : 1][kRowBytes];
     // P as the PV A operand: [tile][k group g][head m] -> 4 bf16 hi then 4 bf16 lo
     // of entries 16*tile + 4g .. +3
@@ -286,6 +287,19 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   const uint16_t* qp = (const uint16_t*)a.q.data + (int64_t)ri.b * a.q.sb + (int64_t)ri.t * a.q.sr;
   v8bf qb[16];
   const gbyte* dummy = (const gbyte*)qp;  // a finite 1 KB row for empty bf16 slots
+  if constexpr (!QL) {
+    // the 16 query heads pass through the (still free) rows buffer once, before the
+    // first chunk: one 16 KB read per workgroup, overlapping the first slots' load
+#pragma unroll
+    for (int hh = (16 / NW) * w; hh < (16 / NW) * (w + 1); ++hh)
+      __builtin_amdgcn_global_load_lds((const gbyte*)(qp + (h0 + hh) * 512) + 16 * (lane ^ swz(hh)),
+                                       (__attribute__((address_space(3))) void*)&L.rows[hh][0], 16, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) qb[kk] = *(const v8bf*)&rowb[swz_off(m, 4 * kk + g)];
+    __syncthreads();  // the rows buffer is free again
+  }
 
   const float sl2 = a.scale * kLog2e;
   // running (max, sum) of heads 4g + r (the PV layout) and max of head m (the QK layout)
@@ -363,9 +377,6 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
         for (int hh = (16 / NW) * w; hh < (16 / NW) * (w + 1); ++hh)
           __builtin_amdgcn_global_load_lds((const gbyte*)(qp + (h0 + hh) * 512) + 16 * (lane ^ swz(hh)),
                                            (__attribute__((address_space(3))) void*)&L.q[hh][0], 16, 0, 0);
-      } else {  // each wave reads its operand straight into registers (16 KB per wave)
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) qb[kk] = *(const v8bf*)(qp + (int64_t)(h0 + m) * 512 + 32 * kk + 8 * g);
       }
     }
     // the next chunk's slots, requested while this chunk's rows are in flight
@@ -702,10 +713,11 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
   // entries is two chunks).  HCA decode: 4 waves and chunks of 56 (75 KB of LDS: two
   // workgroups per CU, one computing while the other gathers).  Many queries per
   // sequence: 4 waves and chunks of 64 (whole tiles; a 640-entry list is ten chunks),
-  // the query operand read by each wave from memory so that the 16 KB query staging
-  // does not take LDS (70 KB: still two per CU).  Measured on the 2k prefill chunks:
-  // 56-entry chunks with staged queries 799 (CSA) / 747 (HCA) us, 64-entry chunks 731 /
-  // 731 us; HCA decode keeps the staged 56-entry shape (61 us against 64 at batch 64).
+  // the query heads staged once through the rows buffer before the first chunk, so
+  // that they take no LDS of their own (70 KB: still two per CU).  Measured on the 2k
+  // prefill chunks: 56-entry chunks 799 (CSA) / 747 (HCA) us; 64-entry chunks with the
+  // query read per wave from memory 731 / 731 us, staged through the rows 706 / 724 us.
+  // HCA decode keeps the 56-entry shape (61 us against 64 at batch 64).
   const int fmt = a.kv.dtype == CSA_FP8_E4M3 ? kFmtFp8 : a.kv.dtype == CSA_MXFP4 ? kFmtFp4 : kFmtBf16;
   const bool many = a.tq != 1;
   // HCA (dense over every visible block; long lists at large batch) also takes the 4-wave
