@@ -11,8 +11,9 @@
 // heads share one 512-wide latent row per entry, so attention is a
 // [heads x 512] x [512 x n] contraction (QK) followed by [heads x n] x [n x 512]
 // (PV), both on bf16 MFMA.  A workgroup takes one query row, one group of 16
-// heads and one contiguous split of the entry list, and walks the split in
-// chunks of up to 144 entries that sit whole in LDS (one 1 KB row per entry):
+// heads (two groups, sharing the gathered rows, for calls with many queries per
+// sequence) and one contiguous split of the entry list, and walks the split in
+// chunks of up to 136 entries that sit whole in LDS (one 1 KB row per entry):
 //  * the chunk's rows are all requested at once, one row per wave instruction,
 //    straight into LDS (bf16; fp8 rows are widened through registers), so a
 //    chunk costs one memory round trip, not one per tile;
@@ -205,8 +206,8 @@ __device__ __forceinline__ float lane_sum4rows(float x) {  // fixed-order sum ov
 // reads there.
 constexpr int kRowBytes = 1024;
 
-// NW waves per workgroup, chunks of at most CH entries.
-template <int NW, int CH, bool QL>
+// NW waves per head group, HG head groups of 16 per workgroup, chunks of at most CH entries.
+template <int NW, int CH, bool QL, int HG>
 struct ChunkLds {
   static constexpr int kTiles = (CH + 15) / 16;
   __attribute__((aligned(16))) uint8_t rows[CH][kRowBytes];
@@ -217,19 +218,21 @@ struct ChunkLds {
     __attribute__((aligned(16))) uint8_t q[QL ? 16 : 1][kRowBytes];
     // P as the PV A operand: [tile][k group g][head m] -> 4 bf16 hi then 4 bf16 lo
     // of entries 16*tile + 4g .. +3
-    __attribute__((aligned(16))) uint4 p[kTiles][4][16];
+    __attribute__((aligned(16))) uint4 p[HG][kTiles][4][16];
   };
   float esl[kTiles * 16];     // entry scale (fp8 row scale, else 1); -1 = empty slot
   int32_t sidx[kTiles * 16];  // slots of the chunk
-  __attribute__((aligned(16))) float red_max[NW][16];
-  __attribute__((aligned(16))) float red_sum[NW][16];
+  __attribute__((aligned(16))) float red_max[NW * HG][16];
+  __attribute__((aligned(16))) float red_sum[NW * HG][16];
 };
 
 __device__ __forceinline__ int swz(int r) { return r & 15; }
 __device__ __forceinline__ int swz_off(int r, int chunk16) { return r * kRowBytes + ((chunk16 ^ swz(r)) << 4); }
 
-// One workgroup: one query row, 16 heads, one split of its entry list, processed in
-// chunks of at most CH entries by NW waves.  For each chunk:
+// One workgroup: one query row, HG groups of 16 heads, one split of its entry list,
+// processed in chunks of at most CH entries by NW waves per head group (the head
+// groups share the chunk's rows; everything after the gather is per head group, so a
+// head's arithmetic is the same for every HG).  For each chunk:
 //  * the chunk's selection slots go to LDS, then every wave issues its rows (one
 //    row per instruction, straight into LDS for bf16; fp8 rows pass through
 //    registers to be widened, with their scales);
@@ -243,20 +246,25 @@ __device__ __forceinline__ int swz_off(int r, int chunk16) { return r * kRowByte
 // The scalars the prologue depends on come first in the argument list: they are
 // preloaded into scalar registers at launch (the rest of the arguments is read from
 // memory, one round trip that overlaps the position and slot loads).
-template <int FMT, int NW, int CH, bool QL>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunk_kernel(
+template <int FMT, int NW, int CH, bool QL, int HG>
+__global__ __launch_bounds__(NW * HG * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunk_kernel(
     const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ raw_base, int k, int tq, int window, int m_hc,
     int split, int nsplit_max, int nhg, int rows, AttnArgs a) {
   constexpr int kT = (CH + 15) / 16;             // 16-entry tiles of a full chunk
   constexpr int kQkT = (kT + NW - 1) / NW;       // QK tiles per wave
   constexpr int kCols = 512 / NW, kNT = kCols / 16;  // PV: latent columns per wave, their 16-column tiles
-  constexpr int kRW = (CH + NW - 1) / NW;        // rows a wave loads per chunk
+  constexpr int NWT = NW * HG;                   // waves of the workgroup
+  constexpr int kRW = (CH + NWT - 1) / NWT;      // rows a wave loads per chunk
   constexpr bool FP8 = FMT == kFmtFp8;
+  static_assert(HG == 1 || !QL, "several head groups stage their query heads through the rows buffer");
   int row, s, hg;
   decode_block(blockIdx.x, nhg, nsplit_max, rows, &row, &s, &hg);
   if (row >= rows) return;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  // wave wt of the workgroup is wave w of head group hgl: every wave loads rows, a head
+  // group's NW waves share its QK tiles and split its PV columns
+  const int wt = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  const int hgl = HG > 1 ? wt / NW : 0, w = HG > 1 ? wt % NW : wt;
   const int m = lane % 16, g = lane / 16;
   const int t = threadIdx.x;
   const int e_begin = s * split;
@@ -277,9 +285,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   const int nsplit = max(1, (ri.n_tot + split - 1) / split);
   if (s >= nsplit) return;  // workgroup-uniform, before any barrier
   const int e_end = min(ri.n_tot, e_begin + split);
-  const int h0 = hg * 16;
+  const int h0 = (hg * HG + hgl) * 16;
 
-  __shared__ ChunkLds<NW, CH, QL> L;
+  __shared__ ChunkLds<NW, CH, QL, HG> L;
   uint8_t* const rowb = &L.rows[0][0];  // the chunk's rows as one byte array
 
   // the 16 query heads as the QK B operand: lane (head m, group g) holds columns
@@ -290,14 +298,15 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   if constexpr (!QL) {
     // the 16 query heads pass through the (still free) rows buffer once, before the
     // first chunk: one 16 KB read per workgroup, overlapping the first slots' load
+    static_assert(CH >= 16 * HG, "query heads fit the rows buffer");
 #pragma unroll
-    for (int hh = (16 / NW) * w; hh < (16 / NW) * (w + 1); ++hh)
-      __builtin_amdgcn_global_load_lds((const gbyte*)(qp + (h0 + hh) * 512) + 16 * (lane ^ swz(hh)),
+    for (int hh = (16 / NW) * wt; hh < (16 / NW) * (wt + 1); ++hh)
+      __builtin_amdgcn_global_load_lds((const gbyte*)(qp + (hg * HG * 16 + hh) * 512) + 16 * (lane ^ swz(hh)),
                                        (__attribute__((address_space(3))) void*)&L.rows[hh][0], 16, 0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) qb[kk] = *(const v8bf*)&rowb[swz_off(m, 4 * kk + g)];
+    for (int kk = 0; kk < 16; ++kk) qb[kk] = *(const v8bf*)&rowb[swz_off(16 * hgl + m, 4 * kk + g)];
     __syncthreads();  // the rows buffer is free again
   }
 
@@ -323,17 +332,17 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       L.esl[t] = j >= 0 ? 1.f : -1.f;
     }
     __syncthreads();
-    // rows: wave w loads rows w, w+8, ... of the chunk's tiles (lane i holds the
-    // slot of the wave's i-th row, so no row waits on an LDS read)
+    // rows: wave wt loads rows wt, wt + NWT, ... of the chunk's tiles (lane i holds
+    // the slot of the wave's i-th row, so no row waits on an LDS read)
     const int nrows = min(nmt * 16, CH);
-    const int jw = lane < (nrows - w + NW - 1) / NW ? L.sidx[w + NW * lane] : -1;
+    const int jw = lane < (nrows - wt + NWT - 1) / NWT ? L.sidx[wt + NWT * lane] : -1;
     // fp8 / MXFP4 rows pass through registers: all of the wave's rows are requested
     // first, then widened into LDS once the query heads and next slots are in flight
     // (MXFP4 caches take bf16 window rows, which go straight to LDS)
     uint32_t rc[kRW][FP8 ? 2 : 1];  // the lane's 8 elements as stored
     uint32_t rs[kRW];               // fp8: row scale bits; MXFP4: block scale byte
     if constexpr (FMT == kFmtBf16) {
-      for (int r = w, ri8 = 0; r < nrows; r += NW, ++ri8) {
+      for (int r = wt, ri8 = 0; r < nrows; r += NWT, ++ri8) {
         const int e = c0 + r;
         const int j = __builtin_amdgcn_readlane(jw, ri8);
         const gbyte* rp = j < 0 ? dummy
@@ -346,7 +355,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     } else {
 #pragma unroll
       for (int i = 0; i < kRW; ++i) {
-        const int r = w + NW * i, e = c0 + r;
+        const int r = wt + NWT * i, e = c0 + r;
         rc[i][0] = 0u;
         if constexpr (FP8) rc[i][1] = 0u;
         rs[i] = FP8 ? __float_as_uint(1.f) : 127u;
@@ -385,7 +394,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     if constexpr (FMT != kFmtBf16) {
 #pragma unroll
       for (int i = 0; i < kRW; ++i) {
-        const int r = w + NW * i;
+        const int r = wt + NWT * i;
         if (r < nrows) {
           if constexpr (FP8) {
             *(v8bf*)&rowb[swz_off(r, lane)] = widen8<true>((u32x2){rc[i][0], rc[i][1]});
@@ -436,12 +445,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       }
     }
     lmax = lane_max4rows(lmax);
-    if (g == 0) L.red_max[w][m] = lmax;
+    if (g == 0) L.red_max[wt][m] = lmax;
     __syncthreads();
     // chunk maxima, the same in every wave (fixed order)
     float mc_q = kNegInf;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) mc_q = fmaxf(mc_q, L.red_max[v][m]);
+    for (int v = 0; v < NW; ++v) mc_q = fmaxf(mc_q, L.red_max[NW * hgl + v][m]);
     const float mnew_q = fmaxf(mrun_q, mc_q);
     mrun_q = mnew_q;
     float lsum = 0.f;
@@ -464,18 +473,18 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
           pa[r] = hi;
           pa[4 + r] = (__bf16)(pv[r] - (float)hi);
         }
-        L.p[mt][g][m] = __builtin_bit_cast(uint4, pa);
+        L.p[hgl][mt][g][m] = __builtin_bit_cast(uint4, pa);
       }
     }
     lsum = lane_sum4rows(lsum);
-    if (g == 0) L.red_sum[w][m] = lsum;
+    if (g == 0) L.red_sum[wt][m] = lsum;
     __syncthreads();  // P and the per-wave sums visible
     // running statistics of heads 4g + r and the accumulator rescale
     float mcv[4] = {kNegInf, kNegInf, kNegInf, kNegInf}, lsv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < NW; ++v) {  // heads 4g .. 4g+3: one 16-byte read per table and wave
-      const float4 mx = *(const float4*)&L.red_max[v][4 * g];
-      const float4 sm = *(const float4*)&L.red_sum[v][4 * g];
+      const float4 mx = *(const float4*)&L.red_max[NW * hgl + v][4 * g];
+      const float4 sm = *(const float4*)&L.red_sum[NW * hgl + v][4 * g];
       mcv[0] = fmaxf(mcv[0], mx.x), mcv[1] = fmaxf(mcv[1], mx.y), mcv[2] = fmaxf(mcv[2], mx.z), mcv[3] = fmaxf(mcv[3], mx.w);
       lsv[0] += sm.x, lsv[1] += sm.y, lsv[2] += sm.z, lsv[3] += sm.w;
     }
@@ -496,7 +505,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     // columns 4(m % 4) .. +3 and receives column m of the four rows); two operand
     // sets alternate, so tile ks + 1's reads are in flight during tile ks's MFMAs
     const auto pv_load = [&](int ks, v8bf& pa, v4bf (&tv)[kNT]) {
-      pa = __builtin_bit_cast(v8bf, L.p[ks][g][m]);
+      pa = __builtin_bit_cast(v8bf, L.p[hgl][ks][g][m]);
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
         const int col = kCols * w + 16 * nt + 4 * (m % 4);
@@ -706,32 +715,40 @@ __global__ __launch_bounds__(kPlainThreads) void attn_plain_kernel(AttnArgs a) {
 
 hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_max, hipStream_t s) {
   const int partial = nsplit_max > 1;
-  const int nhg = a.heads / 16;
   const int64_t pairs = rows * nsplit_max;
-  const int64_t blocks = rows >= 8 ? (rows + 7) / 8 * 8 * nsplit_max * nhg : (pairs + 7) / 8 * 8 * nhg;
   // CSA decode: 8 waves and chunks of 136 entries (one workgroup per CU; a split of 272
   // entries is two chunks).  HCA decode: 4 waves and chunks of 56 (75 KB of LDS: two
   // workgroups per CU, one computing while the other gathers).  Many queries per
-  // sequence: 4 waves and chunks of 64 (whole tiles; a 640-entry list is ten chunks),
-  // the query heads staged once through the rows buffer before the first chunk, so
-  // that they take no LDS of their own (70 KB: still two per CU).  Measured on the 2k
-  // prefill chunks: 56-entry chunks 799 (CSA) / 747 (HCA) us; 64-entry chunks with the
-  // query read per wave from memory 731 / 731 us, staged through the rows 706 / 724 us.
-  // HCA decode keeps the 56-entry shape (61 us against 64 at batch 64).
+  // sequence: two head groups of 4 waves each share chunks of 128 entries (whole
+  // tiles; a 640-entry list is five chunks), the query heads staged once through the
+  // rows buffer into registers before the first chunk (one workgroup per CU; with 16
+  // or 48 heads, one head group and chunks of 64, two workgroups per CU).  Measured on
+  // the 2k prefill chunks (CSA / HCA us per call): one head group, 56-entry chunks
+  // 799 / 747, 64-entry 706 / 711; two head groups with 64-entry chunks 704 / 716 (the
+  // gather is halved, the time is not: the per-chunk chain bounds it), 96-entry 645 /
+  // 619, 128-entry 576 / 602; the query heads read from LDS at every chunk instead of
+  // held in registers (LDS for 112-entry chunks at most) 668 / 634.  HCA decode keeps
+  // the 56-entry shape (61 us against 64 at batch 64).
   const int fmt = a.kv.dtype == CSA_FP8_E4M3 ? kFmtFp8 : a.kv.dtype == CSA_MXFP4 ? kFmtFp4 : kFmtBf16;
   const bool many = a.tq != 1;
   // HCA (dense over every visible block; long lists at large batch) also takes the 4-wave
   // shape: two workgroups per CU, one gathering while the other computes.  The shape is
   // chosen by the call kind, never by the batch, so results stay batch-invariant.
   const bool hca = a.idx == nullptr;
+  // calls with many queries per sequence and 32 or 64 heads: two head groups per
+  // workgroup share one gather of the rows
+  const int hgw = many && a.heads % 32 == 0 ? 2 : 1;
+  const int nhg = a.heads / 16 / hgw;
+  const int64_t blocks = rows >= 8 ? (rows + 7) / 8 * 8 * nsplit_max * nhg : (pairs + 7) / 8 * 8 * nhg;
   const dim3 grid((unsigned)blocks);
-#define CSA_ATTN_LAUNCH(F, NW, CH, QL)                                                                             \
-  hipLaunchKernelGGL((attn_chunk_kernel<F, NW, CH, QL>), grid, dim3(NW * kWave), 0, s, a.q_pos, a.idx, a.raw_base, \
-                     a.k, a.tq, a.window, a.m_hc, split, nsplit_max, nhg, (int)rows, a)
-#define CSA_ATTN_SHAPES(F)                       \
-  if (many) CSA_ATTN_LAUNCH(F, 4, 64, false);    \
-  else if (hca) CSA_ATTN_LAUNCH(F, 4, 56, true); \
-  else CSA_ATTN_LAUNCH(F, 8, 136, true);
+#define CSA_ATTN_LAUNCH(F, NW, CH, QL, HG)                                                                          \
+  hipLaunchKernelGGL((attn_chunk_kernel<F, NW, CH, QL, HG>), grid, dim3(NW * HG * kWave), 0, s, a.q_pos, a.idx,    \
+                     a.raw_base, a.k, a.tq, a.window, a.m_hc, split, nsplit_max, nhg, (int)rows, a)
+#define CSA_ATTN_SHAPES(F)                                  \
+  if (many && hgw > 1) CSA_ATTN_LAUNCH(F, 4, 128, false, 2); \
+  else if (many) CSA_ATTN_LAUNCH(F, 4, 64, false, 1);       \
+  else if (hca) CSA_ATTN_LAUNCH(F, 4, 56, true, 1);         \
+  else CSA_ATTN_LAUNCH(F, 8, 136, true, 1);
   if (fmt == kFmtFp8) {
     CSA_ATTN_SHAPES(kFmtFp8)
   } else if (fmt == kFmtFp4) {

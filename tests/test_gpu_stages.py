@@ -562,7 +562,7 @@ def _store_kv(csa, x, fmt):
     (2, 1, 16, 512, 17, 1, "bf16", 2e-3),
     (1, 5, 48, 512, 64, 32, "bf16", 2e-3),     # 48 heads, several queries (three head groups)
     (2, 3, 64, 512, 200, 64, "fp8", 5e-3),
-    (2, 9, 64, 512, 300, 128, "bf16", 2e-3),   # several queries, 64 heads: seven 64-entry chunks
+    (2, 9, 64, 512, 300, 128, "bf16", 2e-3),   # several queries, 64 heads: two head groups, four 107-entry chunks
     (1, 4, 16, 512, 90, 20, "bf16", 2e-3),     # several queries, one head group
 ])
 def test_csa_sparse_attn(gpu_lib, B, Tq, H, D, k, W, fmt, tol):
