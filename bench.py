@@ -463,7 +463,7 @@ class HcaDecode:
         q_out = L.B * L.H * (L.D * 2 + L.D * 4 + 4)
         self.bytes = {"entries": gather, "q_out_lse": q_out}
         self.excluded = {"attention_split_partials": 2 * L.B * 4 * L.H * (L.D + 2) * 4}  # HCA decode: four splits
-        self.dominant = {"kernel": "attn_chunk_kernel<bf16, 4, 56> + attn_merge_kernel (hca_attn)", "bound": "hbm",
+        self.dominant = {"kernel": "attn_chunk_kernel<bf16, 4, 128, 2 head groups> + attn_merge_kernel (hca_attn)", "bound": "hbm",
                          "work": gather + q_out, "work_note": "visible compressed rows + window rows + q, out, lse"}
         self.dtype = "bf16"
         self.config = {"workload": name, "batch": wl.batch, "context": f"U[{wl.extra['len_lo']}, {wl.extra['len_hi']}]",

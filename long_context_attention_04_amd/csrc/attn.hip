@@ -717,27 +717,27 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
   const int partial = nsplit_max > 1;
   const int64_t pairs = rows * nsplit_max;
   // CSA decode: 8 waves and chunks of 136 entries (one workgroup per CU; a split of 272
-  // entries is two chunks).  HCA decode: 4 waves and chunks of 56 (75 KB of LDS: two
-  // workgroups per CU, one computing while the other gathers).  Many queries per
-  // sequence: two head groups of 4 waves each share chunks of 128 entries (whole
-  // tiles; a 640-entry list is five chunks), the query heads staged once through the
-  // rows buffer into registers before the first chunk (one workgroup per CU; with 16
-  // or 48 heads, one head group and chunks of 64, two workgroups per CU).  Measured on
+  // entries is two chunks).  Many queries per sequence, and HCA: two head groups of 4
+  // waves each share chunks of 128 entries (whole tiles; a 640-entry list is five
+  // chunks), the query heads staged once through the rows buffer into registers before
+  // the first chunk (one workgroup per CU).  With 16 or 48 heads: one head group, chunks
+  // of 64 (many queries) or 56 (HCA decode; 75 KB of LDS), two workgroups per CU.  Measured on
   // the 2k prefill chunks (CSA / HCA us per call): one head group, 56-entry chunks
   // 799 / 747, 64-entry 706 / 711; two head groups with 64-entry chunks 704 / 716 (the
   // gather is halved, the time is not: the per-chunk chain bounds it), 96-entry 645 /
   // 619, 128-entry 576 / 602; the query heads read from LDS at every chunk instead of
-  // held in registers (LDS for 112-entry chunks at most) 668 / 634.  HCA decode keeps
-  // the 56-entry shape (61 us against 64 at batch 64).
+  // held in registers (LDS for 112-entry chunks at most) 668 / 634.  HCA decode at
+  // batch 64: one head group with 56-entry chunks 61.9 us per step, two with 128-entry
+  // chunks 56.7 (96-entry 56.8); the hybrid pair's HCA layer 53.1 -> 48.4 us.
   const int fmt = a.kv.dtype == CSA_FP8_E4M3 ? kFmtFp8 : a.kv.dtype == CSA_MXFP4 ? kFmtFp4 : kFmtBf16;
   const bool many = a.tq != 1;
-  // HCA (dense over every visible block; long lists at large batch) also takes the 4-wave
-  // shape: two workgroups per CU, one gathering while the other computes.  The shape is
-  // chosen by the call kind, never by the batch, so results stay batch-invariant.
+  // HCA (dense over every visible block; long lists at large batch) takes a 4-wave shape
+  // per head group.  The shape is chosen by the call kind and the head count, never by
+  // the batch, so results stay batch-invariant.
   const bool hca = a.idx == nullptr;
-  // calls with many queries per sequence and 32 or 64 heads: two head groups per
-  // workgroup share one gather of the rows
-  const int hgw = many && a.heads % 32 == 0 ? 2 : 1;
+  // calls with many queries per sequence and HCA calls, with 32 or 64 heads: two head
+  // groups per workgroup share one gather of the rows
+  const int hgw = (many || hca) && a.heads % 32 == 0 ? 2 : 1;
   const int nhg = a.heads / 16 / hgw;
   const int64_t blocks = rows >= 8 ? (rows + 7) / 8 * 8 * nsplit_max * nhg : (pairs + 7) / 8 * 8 * nhg;
   const dim3 grid((unsigned)blocks);
@@ -745,7 +745,7 @@ hipError_t launch_decode(const AttnArgs& a, int64_t rows, int split, int nsplit_
   hipLaunchKernelGGL((attn_chunk_kernel<F, NW, CH, QL, HG>), grid, dim3(NW * HG * kWave), 0, s, a.q_pos, a.idx,    \
                      a.raw_base, a.k, a.tq, a.window, a.m_hc, split, nsplit_max, nhg, (int)rows, a)
 #define CSA_ATTN_SHAPES(F)                                  \
-  if (many && hgw > 1) CSA_ATTN_LAUNCH(F, 4, 128, false, 2); \
+  if (hgw > 1) CSA_ATTN_LAUNCH(F, 4, 128, false, 2);         \
   else if (many) CSA_ATTN_LAUNCH(F, 4, 64, false, 1);       \
   else if (hca) CSA_ATTN_LAUNCH(F, 4, 56, true, 1);         \
   else CSA_ATTN_LAUNCH(F, 8, 136, true, 1);
