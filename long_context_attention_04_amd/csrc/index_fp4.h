@@ -156,7 +156,7 @@ __device__ __forceinline__ float fp4_tile_score(const v8i& A, int sa, const floa
 // not write.  Starts and ends with a workgroup barrier (the caller's LDS is free to
 // reuse before; ql and whatever store wrote are readable by the workgroup after).
 template <int NR, typename TileKey, typename Store>
-__device__ void fp4_rescore_tiles(const IndexArgs& a, int row, int V, Fp4QueryLds& ql, int ntile, TileKey tile_key,
+__device__ __forceinline__ void fp4_rescore_tiles(const IndexArgs& a, int row, int V, Fp4QueryLds& ql, int ntile, TileKey tile_key,
                                   Store store) {
   const int b = row / a.tq, t_q = row % a.tq;
   const int t = threadIdx.x, l = t % kWave, w = t / kWave, nw = blockDim.x / kWave;
@@ -201,7 +201,7 @@ __device__ void fp4_rescore_tiles(const IndexArgs& a, int row, int V, Fp4QueryLd
 
 // Every visible score of one row (keys 0 .. V-1) recomputed and written to srow.
 template <int NR>
-__device__ void fp4_rescore_row(const IndexArgs& a, int row, int V, Fp4QueryLds& ql, float* srow) {
+__device__ __forceinline__ void fp4_rescore_row(const IndexArgs& a, int row, int V, Fp4QueryLds& ql, float* srow) {
   fp4_rescore_tiles<NR>(
       a, row, V, ql, (V + 31) / 32, [](int tile) { return 32 * tile; },
       [&](int, int key, float s, bool live) {

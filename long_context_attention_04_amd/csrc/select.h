@@ -60,7 +60,7 @@ struct SelShared {
 // stops as soon as that bin holds <= 64 keys, which one wave then ranks
 // exactly by (key desc, position asc).
 template <typename KeyFn>
-__device__ void radix_threshold(KeyFn key, int n, int k, SelShared& sh, uint32_t* T_out, uint32_t* krem_out) {
+__device__ __forceinline__ void radix_threshold(KeyFn key, int n, int k, SelShared& sh, uint32_t* T_out, uint32_t* krem_out) {
   const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
   // key range
   uint32_t mn = 0xffffffffu, mx = 0u;
@@ -200,7 +200,7 @@ __device__ void radix_threshold(KeyFn key, int n, int k, SelShared& sh, uint32_t
 // step (lane i <-> key base+i, conflict-free); ballots give in-wave ranks and
 // one barrier gives every wave its offsets.
 template <typename KeyFn, typename Emit>
-__device__ void compact_selected(KeyFn key, int n, uint32_t T, uint32_t krem, SelShared& sh, Emit emit) {
+__device__ __forceinline__ void compact_selected(KeyFn key, int n, uint32_t T, uint32_t krem, SelShared& sh, Emit emit) {
   const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
   const int chunk = (n + nw * kWave - 1) / (nw * kWave) * kWave;  // whole 64-key steps per wave
   const int lo = min(n, wv * chunk), hi = min(n, lo + chunk);
@@ -423,29 +423,34 @@ __device__ void emit_slice_list(const uint32_t (&kv)[kWaveTopN], int n, uint32_t
 }
 
 // ------------------------------------------------------------------ block top-k, keys in registers
-constexpr int kRegSelThreads = 1024;  // block size of the register-resident selection
-constexpr int kRegSelBins = 1024;     // histogram bins: one per thread
-constexpr int kRegSelWaves = kRegSelThreads / kWave;
+// Block sizes of the register-resident selection: 256, 512 or 1024 threads (THREADS
+// below).  Fewer threads holding more keys each run the per-wave scans and reductions
+// on fewer waves: with 16 waves on a CU's 4 SIMDs every such step is issued 16 times.
+constexpr int kRegSelMaxThreads = 1024;
+constexpr int kRegSelBins = 1024;     // histogram bins: kRegSelBins / THREADS per thread
+constexpr int kRegSelMaxWaves = kRegSelMaxThreads / kWave;
 
 struct RegSelLds {
   __attribute__((aligned(16))) uint32_t hist[2][kRegSelBins];
-  uint32_t red[3][kRegSelWaves];   // per-wave min, max, count
-  uint32_t scan[3][kRegSelWaves];  // per-wave totals of block scans
+  uint32_t red[3][kRegSelMaxWaves];   // per-wave min, max, count
+  uint32_t scan[3][kRegSelMaxWaves];  // per-wave totals of block scans
   uint32_t bin, above, cnt, nfin, T, krem, jT, bad;
   __attribute__((aligned(16))) uint32_t fk[64];
   __attribute__((aligned(16))) uint32_t fp[64];
 };
 
-// Inclusive prefix sum over a kRegSelThreads block (one barrier; tmp is not
+// Inclusive prefix sum over a block of THREADS threads (one barrier; tmp is not
 // reused by the caller until after a later barrier).
+template <int THREADS>
 __device__ __forceinline__ uint32_t block_scan_regsel(uint32_t v, uint32_t* tmp, uint32_t* total) {
+  static_assert(THREADS % kWave == 0 && THREADS <= kRegSelMaxThreads && kRegSelBins % THREADS == 0, "block size");
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), L = threadIdx.x % kWave;
   const uint32_t incl = wave_incl_scan(v);
   if (L == kWave - 1) tmp[w] = incl;
   __syncthreads();
   uint32_t base = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kRegSelWaves; ++i) {
+  for (int i = 0; i < THREADS / kWave; ++i) {
     const uint32_t x = tmp[i];
     base += i < w ? x : 0u;
     tot += x;
@@ -457,8 +462,8 @@ __device__ __forceinline__ uint32_t block_scan_regsel(uint32_t v, uint32_t* tmp,
 // Min and max present key and the number of present keys of a block holding
 // kv[NPT] per thread (0 = absent); also clears rs.hist[0] and rs.bad for
 // block_threshold_regs and its caller.
-template <int NPT>
-__device__ void block_key_range(const uint32_t (&kv)[NPT], RegSelLds& rs, uint32_t* lo, uint32_t* hi, uint32_t* cnt) {
+template <int NPT, int THREADS>
+__device__ __forceinline__ void block_key_range(const uint32_t (&kv)[NPT], RegSelLds& rs, uint32_t* lo, uint32_t* hi, uint32_t* cnt) {
   const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t / kWave), L = t % kWave;
   uint32_t mn = 0xffffffffu, mx = 0u, c = 0u;
 #pragma unroll
@@ -475,12 +480,13 @@ __device__ void block_key_range(const uint32_t (&kv)[NPT], RegSelLds& rs, uint32
     rs.red[1][w] = mx;
     rs.red[2][w] = c;
   }
-  rs.hist[0][t] = 0u;
+#pragma unroll
+  for (int i = 0; i < kRegSelBins / THREADS; ++i) rs.hist[0][t + i * THREADS] = 0u;
   if (t == 0) rs.bad = 0u;
   __syncthreads();
   mn = 0xffffffffu, mx = 0u, c = 0u;
 #pragma unroll
-  for (int i = 0; i < kRegSelWaves; ++i) {
+  for (int i = 0; i < THREADS / kWave; ++i) {
     mn = min(mn, rs.red[0][i]);
     mx = max(mx, rs.red[1][i]);
     c += rs.red[2][i];
@@ -490,7 +496,7 @@ __device__ void block_key_range(const uint32_t (&kv)[NPT], RegSelLds& rs, uint32
   *cnt = c;
 }
 
-// Exact threshold of the top-k of the keys a kRegSelThreads block holds in
+// Exact threshold of the top-k of the keys a block of THREADS threads holds in
 // registers (thread t: kv[j] is the key of slot NPT*t + j, tie order = slot
 // ascending; 0 = absent, present keys > 0, more than k present; [lo, hi] the
 // present range from block_key_range, whose barrier this call relies on).
@@ -501,27 +507,42 @@ __device__ void block_key_range(const uint32_t (&kv)[NPT], RegSelLds& rs, uint32
 // more than 64 keys; those are ranked exactly by one wave.  A non-decreasing
 // map from key to bin keeps every bin a contiguous range of the key order,
 // which is all the selection needs to stay exact.
-template <int NPT>
-__device__ void block_threshold_regs(const uint32_t (&kv)[NPT], uint32_t lo, uint32_t hi, uint32_t k, RegSelLds& rs,
+template <int NPT, int THREADS, bool KEEP_BINS = true>
+__device__ __forceinline__ void block_threshold_regs(const uint32_t (&kv)[NPT], uint32_t lo, uint32_t hi, uint32_t k, RegSelLds& rs,
                                      uint32_t* T_out, uint32_t* krem_out) {
+  constexpr int NW = THREADS / kWave;
+  constexpr int BPT = kRegSelBins / THREADS;  // bins per thread in the scan
   const int t = threadIdx.x;
   uint32_t krem = k;
   int buf = 0;
-  // one pass: histogram of bins b[j] (-1 = not counted) into rs.hist[buf], then the
+  // one pass: histogram of bins binf(j) (-1 = not counted) into rs.hist[buf], then the
   // bin holding the krem-th key from the top, the keys above it and its count
-  auto pass = [&](const int (&b)[NPT], uint32_t* bin, uint32_t* above, uint32_t* cn) {
+  auto pass = [&](auto binf, uint32_t* bin, uint32_t* above, uint32_t* cn) {
 #pragma unroll
-    for (int j = 0; j < NPT; ++j)
-      if (b[j] >= 0) atomicAdd(&rs.hist[buf][b[j]], 1u);
+    for (int j = 0; j < NPT; ++j) {
+      const int bj = binf(j);
+      if (bj >= 0) atomicAdd(&rs.hist[buf][bj], 1u);
+    }
     __syncthreads();
-    const uint32_t h = rs.hist[buf][kRegSelBins - 1 - t];
-    rs.hist[buf ^ 1][t] = 0u;  // the next pass's histogram
+    // thread t scans bins kRegSelBins - 1 - (BPT t + i), i = 0 .. BPT - 1 (descending)
+    uint32_t h[BPT], hs = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      h[i] = rs.hist[buf][kRegSelBins - 1 - (BPT * t + i)];
+      hs += h[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) rs.hist[buf ^ 1][t + i * THREADS] = 0u;  // the next pass's histogram
     uint32_t tot;
-    const uint32_t incl = block_scan_regsel(h, rs.scan[buf], &tot);  // keys in bins >= 1023 - t
-    if (incl - h < krem && incl >= krem) {
-      rs.bin = (uint32_t)(kRegSelBins - 1 - t);
-      rs.above = incl - h;
-      rs.cnt = h;
+    uint32_t run = block_scan_regsel<THREADS>(hs, rs.scan[buf], &tot) - hs;  // keys in the bins above
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      if (run < krem && run + h[i] >= krem) {
+        rs.bin = (uint32_t)(kRegSelBins - 1 - (BPT * t + i));
+        rs.above = run;
+        rs.cnt = h[i];
+      }
+      run += h[i];
     }
     if (t == 0) rs.nfin = 0u;
     __syncthreads();
@@ -531,17 +552,28 @@ __device__ void block_threshold_regs(const uint32_t (&kv)[NPT], uint32_t lo, uin
     buf ^= 1;
   };
   bool finish = false, by_bin = false;
-  int b[NPT];
   uint32_t fbin = 0, cn_last = 0xffffffffu;  // keys in the final range (unknown before a pass)
   const float xlo = key_float(lo), xhi = key_float(hi);
   const float inv = 1023.99f / (xhi - xlo);
+  // the first pass's bins: kept in registers (KEEP_BINS), or recomputed where needed by
+  // kernels short of registers (the same expression, so the same bins)
+  constexpr bool kKeepBins = KEEP_BINS;
+  auto vbin = [&](int j) { return kv[j] ? min(kRegSelBins - 1, max(0, (int)((key_float(kv[j]) - xlo) * inv))) : -1; };
+  int b[kKeepBins ? NPT : 1];
+  auto first_bin = [&](int j) {
+    if constexpr (kKeepBins)
+      return b[j];
+    else
+      return vbin(j);
+  };
   // NaN and infinite scores, or a span too small to invert, go to the key-space passes
   if (lo != hi && xhi - xlo < __builtin_inff() && inv < __builtin_inff()) {
+    if constexpr (kKeepBins) {
 #pragma unroll
-    for (int j = 0; j < NPT; ++j)
-      b[j] = kv[j] ? min(kRegSelBins - 1, max(0, (int)((key_float(kv[j]) - xlo) * inv))) : -1;
+      for (int j = 0; j < NPT; ++j) b[j] = vbin(j);
+    }
     uint32_t above, cn;
-    pass(b, &fbin, &above, &cn);
+    pass(first_bin, &fbin, &above, &cn);
     krem -= above;
     cn_last = cn;
     if (cn <= 64u || cn == krem) {
@@ -551,7 +583,7 @@ __device__ void block_threshold_regs(const uint32_t (&kv)[NPT], uint32_t lo, uin
       uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
       for (int j = 0; j < NPT; ++j)
-        if (b[j] == (int)fbin) {
+        if (first_bin(j) == (int)fbin) {
           mn = min(mn, kv[j]);
           mx = max(mx, kv[j]);
         }
@@ -565,7 +597,7 @@ __device__ void block_threshold_regs(const uint32_t (&kv)[NPT], uint32_t lo, uin
       lo = 0xffffffffu;
       hi = 0u;
 #pragma unroll
-      for (int i = 0; i < kRegSelWaves; ++i) {
+      for (int i = 0; i < NW; ++i) {
         lo = min(lo, rs.red[0][i]);
         hi = max(hi, rs.red[1][i]);
       }
@@ -576,10 +608,8 @@ __device__ void block_threshold_regs(const uint32_t (&kv)[NPT], uint32_t lo, uin
     by_bin = false;
     const int bits = 32 - __builtin_clz(hi - lo);
     const int shift = bits > 10 ? bits - 10 : 0;
-#pragma unroll
-    for (int j = 0; j < NPT; ++j) b[j] = (kv[j] >= lo && kv[j] <= hi) ? (int)((kv[j] - lo) >> shift) : -1;
     uint32_t bin, above, cn;
-    pass(b, &bin, &above, &cn);
+    pass([&](int j) { return (kv[j] >= lo && kv[j] <= hi) ? (int)((kv[j] - lo) >> shift) : -1; }, &bin, &above, &cn);
     const uint32_t nlo = lo + (bin << shift);
     hi = min(hi, nlo + ((1u << shift) - 1u));
     lo = nlo;
@@ -588,7 +618,7 @@ __device__ void block_threshold_regs(const uint32_t (&kv)[NPT], uint32_t lo, uin
     finish = cn <= 64u || cn == krem;
   }
   uint32_t T = lo;
-  auto in_final = [&](int j) { return by_bin ? b[j] == (int)fbin : (kv[j] >= lo && kv[j] <= hi); };
+  auto in_final = [&](int j) { return by_bin ? first_bin(j) == (int)fbin : (kv[j] >= lo && kv[j] <= hi); };
   if (finish && cn_last == krem) {
     // the final range is taken whole: T is its smallest key, every copy of it taken
     const int w = __builtin_amdgcn_readfirstlane(t / kWave), L = t % kWave;
@@ -600,7 +630,7 @@ __device__ void block_threshold_regs(const uint32_t (&kv)[NPT], uint32_t lo, uin
     __syncthreads();
     T = 0xffffffffu;
 #pragma unroll
-    for (int i = 0; i < kRegSelWaves; ++i) T = min(T, rs.red[0][i]);
+    for (int i = 0; i < NW; ++i) T = min(T, rs.red[0][i]);
     krem = 0xffffffffu;
   } else if (finish && (by_bin || lo != hi)) {
     // gather the <= 64 keys of the final bin with their slots, then rank them in one wave

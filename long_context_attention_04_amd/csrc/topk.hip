@@ -270,17 +270,22 @@ __global__ __launch_bounds__(256) void topk_cand32_kernel(const float* __restric
 // key of those slices rescored with the indexer's arithmetic; else from the whole
 // row rescored.  Rows whose full slices hold too few candidates (short rows) are
 // selected from their scores, which the indexer wrote to `row_scores`.
-constexpr int kMPerThread = kSliceMergeCap / kRegSelThreads;  // 8
-static_assert(kMPerThread * kRegSelThreads == kSliceMergeCap && kSliceSlots % kMPerThread == 0, "slot tiling");
+// The merge runs 1024-thread workgroups (8 slots per thread): its phases are chains of
+// dependent LDS and cross-lane steps, and 16 waves hide more of their latency than 4
+// (256 threads of 32 slots: 13.9 us per call against 8.8 us).
+constexpr int kMergeThreads32 = 1024;
+constexpr int kMPerThread = kSliceMergeCap / kMergeThreads32;  // 8
+static_assert(kMPerThread * kMergeThreads32 == kSliceMergeCap && kSliceSlots % kMPerThread == 0, "slot tiling");
 constexpr int kMergeMaxSlices = kSliceMergeCap / kSliceSlots;  // 256
-static_assert(kMergeMaxSlices % kWave == 0 && kMergeMaxSlices <= kRegSelThreads, "slice flags per wave");
+static_assert(kMergeMaxSlices % kWave == 0 && kMergeMaxSlices <= kMergeThreads32, "slice flags per wave");
 // A failed certificate rescores up to kMaxBadSlices slices into LDS (ostage after
 // the query: kBadKeysOffset words, then kSlice32 keys per slice); more rescore the row.
 constexpr int kMaxBadSlices = 8;
 constexpr int kBadKeysOffset = 512;
-static_assert(sizeof(Fp4QueryLds) <= 4 * kBadKeysOffset &&
-                  kBadKeysOffset + kMaxBadSlices * kSlice32 <= kSliceMergeCap + kRegSelThreads,
-              "rescored slices fit in ostage");
+static_assert(sizeof(Fp4QueryLds) <= 4 * kBadKeysOffset, "query stage fits below the rescored keys");
+// ostage: selected indices by rank, then one discard slot per thread; or the query and
+// the rescored slices
+constexpr int kMergeStage = std::max(kSliceMergeCap + kMergeThreads32, kBadKeysOffset + kMaxBadSlices * kSlice32);
 
 struct MergeArgs {
   const float* scores;    // the row scores, when the caller keeps them (else nullptr)
@@ -295,10 +300,11 @@ struct MergeArgs {
 };
 
 template <int NR>  // 0: no rescoring; 4 / 16: the indexer's MFMA layout (heads <= 8 / <= 32)
-__global__ __launch_bounds__(kRegSelThreads) void topk_merge_slices_kernel(MergeArgs ma) {
+__global__ __launch_bounds__(kMergeThreads32) void topk_merge_slices_kernel(MergeArgs ma) {
+  constexpr int TH = kMergeThreads32;
   __shared__ RegSelLds rs;
   __shared__ SelShared sh;
-  __shared__ __attribute__((aligned(16))) uint32_t ostage[kSliceMergeCap + kRegSelThreads];  // selected indices by rank, then discard slots
+  __shared__ __attribute__((aligned(16))) uint32_t ostage[kMergeStage];
   __shared__ uint64_t badmask[kMergeMaxSlices / kWave];
   __shared__ int badlist[kMaxBadSlices], badstart[kMaxBadSlices];
   const int64_t row = blockIdx.x;
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge_slices_kernel(Merge
   const int V = min(visible_blocks(qpos, ma.m), ma.n_cap);
   int32_t* out = ma.idx + row * k;
   if (V <= k) {
-    for (int i = t; i < k; i += kRegSelThreads) out[i] = i < V ? i : -1;
+    for (int i = t; i < k; i += TH) out[i] = i < V ? i : -1;
     return;
   }
   const float* srow = ma.scores ? ma.scores + row * ma.n_cap : ma.row_scores + row * ma.n_cap;
@@ -344,11 +350,11 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge_slices_kernel(Merge
       for (int j = 0; j < kMPerThread; ++j) kv[j] = iv[j] = 0u;
     }
     uint32_t lo, hi, M;
-    block_key_range(kv, rs, &lo, &hi, &M);
+    block_key_range<kMPerThread, TH>(kv, rs, &lo, &hi, &M);
     full = M <= (uint32_t)k;  // too few candidates to decide (rows of a few slices)
     if (!full) {
       uint32_t T, krem;
-      block_threshold_regs(kv, lo, hi, (uint32_t)k, rs, &T, &krem);
+      block_threshold_regs<kMPerThread, TH>(kv, lo, hi, (uint32_t)k, rs, &T, &krem);
       // compaction in slot order: one scan of (keys > T) | (copies of T) << 16
       uint32_t gtc = 0, eqc = 0;
 #pragma unroll
@@ -358,7 +364,7 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge_slices_kernel(Merge
       }
       const uint32_t packed = gtc | (eqc << 16);
       uint32_t tot;
-      const uint32_t excl = block_scan_regsel(packed, rs.scan[2], &tot) - packed;
+      const uint32_t excl = block_scan_regsel<TH>(packed, rs.scan[2], &tot) - packed;
       krem = min(krem, tot >> 16);  // "every copy" made a count
       uint32_t eq_seen = excl >> 16;
       uint32_t r = (excl & 0xffffu) + min(eq_seen, krem);
@@ -391,7 +397,7 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge_slices_kernel(Merge
       for (int i = 0; i < kMergeMaxSlices / kWave; ++i) nbad += __builtin_popcountll(badmask[i]);
       full = nbad != 0;
       if (!full)
-        for (int i = t; i < k; i += kRegSelThreads) out[i] = (int32_t)ostage[i];
+        for (int i = t; i < k; i += TH) out[i] = (int32_t)ostage[i];
     }
     if constexpr (NR > 0) {
       if (full && !ma.scores && nbad > 0 && nbad <= kMaxBadSlices) {
@@ -463,50 +469,47 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_merge_slices_kernel(Merge
   }
 }
 
-// Rows of up to 1024 * NPT keys (a prefill chunk's rows), register-resident: thread t
+// Rows of up to THREADS * NPT keys (a prefill chunk's rows), register-resident: thread t
 // holds positions NPT*t .. NPT*t+NPT-1, so slot order is index order.  The threshold is
 // found on the registers (block_threshold_regs: value-linear bins first, then key-space
 // bins, exact) and the compaction is one block scan, as in the slice-list merge.  A
 // present key is made nonzero (0 marks the positions past the row's visible count; only
 // the all-ones NaN pattern maps to 0 and is folded onto the next key).
+// Workgroups of 512 threads, two resident per CU, each walking rows w, w + grid, ...:
+// while one selects (barriers, LDS round trips), the other's work fills the SIMDs.
 constexpr int kTopkRegsMaxK = 4096;  // selections staged in LDS before the coalesced write
+constexpr int kTopkRegsThreads = 512;
+constexpr int kTopkRegsPerCu = 2;
 
 template <int NPT, bool VEC>  // VEC: 16-byte aligned rows (scores 16-byte aligned, n_cap % 4 == 0)
-__global__ __launch_bounds__(kRegSelThreads) void topk_regs_kernel(const float* __restrict__ scores,
-                                                                   const int32_t* __restrict__ q_pos, int n_cap, int m,
-                                                                   int k, int64_t rows, int32_t* __restrict__ idx) {
+__global__ __launch_bounds__(kTopkRegsThreads, kTopkRegsPerCu * kTopkRegsThreads / kWave / 4) void topk_regs_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int n_cap, int m, int k, int64_t rows,
+    int32_t* __restrict__ idx) {
   static_assert(NPT % 4 == 0, "float4 loads");
+  constexpr int TH = kTopkRegsThreads;
   __shared__ RegSelLds rs;
-  __shared__ uint32_t ostage[kTopkRegsMaxK + kRegSelThreads];  // indices by rank, then discard slots
+  __shared__ uint32_t ostage[kTopkRegsMaxK + TH];  // indices by rank, then discard slots
   const int t = threadIdx.x;
-  // a row's scores as stored (every position below the capacity: the visible count is
-  // applied after the loads, so they need not wait for the row's position)
-  // (positions past the capacity read a position inside it instead: no branch around
-  // the loads, and the visible count masks them)
-  const auto load_row = [&](int64_t row, float4 (&f)[NPT / 4]) {
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    // the row's scores as stored (every position below the capacity: the visible count
+    // is applied after the loads, so they need not wait for the row's position;
+    // positions past the capacity read a position inside it instead)
     const float* src = scores + row * n_cap;
+    float4 cur[NPT / 4];
 #pragma unroll
     for (int q = 0; q < NPT / 4; ++q) {
       const int p0 = NPT * t + 4 * q;
       if constexpr (VEC) {
-        f[q] = *(const float4*)(src + min(p0, n_cap - 4));
+        cur[q] = *(const float4*)(src + min(p0, n_cap - 4));
       } else {
-        f[q].x = src[min(p0, n_cap - 1)];
-        f[q].y = src[min(p0 + 1, n_cap - 1)];
-        f[q].z = src[min(p0 + 2, n_cap - 1)];
-        f[q].w = src[min(p0 + 3, n_cap - 1)];
+        cur[q].x = src[min(p0, n_cap - 1)];
+        cur[q].y = src[min(p0 + 1, n_cap - 1)];
+        cur[q].z = src[min(p0 + 2, n_cap - 1)];
+        cur[q].w = src[min(p0 + 3, n_cap - 1)];
       }
     }
-  };
-  // Workgroup w selects rows w, w + gridDim.x, ...: the next row's scores are requested
-  // before the current row is selected, so its loads overlap the selection.
-  int64_t row = blockIdx.x;
-  float4 cur[NPT / 4];
-  if (row < rows) load_row(row, cur);
-  for (; row < rows; row += gridDim.x) {
     const int V = min(visible_blocks(q_pos[row], m), n_cap);
     int32_t* out = idx + row * k;
-    // this row's keys first (its loads were issued a row ago), then the next row's loads
     uint32_t kv[NPT];
 #pragma unroll
     for (int q = 0; q < NPT / 4; ++q) {
@@ -516,15 +519,13 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_regs_kernel(const float* 
       kv[4 * q + 2] = p0 + 2 < V ? max(float_key(cur[q].z), 1u) : 0u;
       kv[4 * q + 3] = p0 + 3 < V ? max(float_key(cur[q].w), 1u) : 0u;
     }
-    const int64_t nrow = row + gridDim.x;
-    if (nrow < rows) load_row(nrow, cur);
     if (V <= k) {  // workgroup-uniform
-      for (int i = t; i < k; i += kRegSelThreads) out[i] = i < V ? i : -1;
+      for (int i = t; i < k; i += TH) out[i] = i < V ? i : -1;
     } else {
       uint32_t lo, hi, M;
-      block_key_range(kv, rs, &lo, &hi, &M);  // M = V > k (its barrier also ends the previous row's LDS use)
+      block_key_range<NPT, TH>(kv, rs, &lo, &hi, &M);  // M = V > k (its barrier also ends the previous row's LDS use)
       uint32_t T, krem;
-      block_threshold_regs(kv, lo, hi, (uint32_t)k, rs, &T, &krem);
+      block_threshold_regs<NPT, TH, false>(kv, lo, hi, (uint32_t)k, rs, &T, &krem);
       // compaction in position order: one scan of (keys > T) | (copies of T) << 16
       uint32_t gtc = 0, eqc = 0;
 #pragma unroll
@@ -534,7 +535,7 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_regs_kernel(const float* 
       }
       const uint32_t packed = gtc | (eqc << 16);
       uint32_t tot;
-      const uint32_t excl = block_scan_regsel(packed, rs.scan[2], &tot) - packed;
+      const uint32_t excl = block_scan_regsel<TH>(packed, rs.scan[2], &tot) - packed;
       krem = min(krem, tot >> 16);  // "every copy" made a count
       uint32_t eq_seen = excl >> 16;
       uint32_t r = (excl & 0xffffu) + min(eq_seen, krem);
@@ -547,13 +548,13 @@ __global__ __launch_bounds__(kRegSelThreads) void topk_regs_kernel(const float* 
         r += keep;
       }
       __syncthreads();
-      for (int i = t; i < k; i += kRegSelThreads) out[i] = (int32_t)ostage[i];
+      for (int i = t; i < k; i += TH) out[i] = (int32_t)ostage[i];
       __syncthreads();  // ostage and the tables are free for the next row
     }
   }
 }
-static_assert(20 * kRegSelThreads >= kTopkLdsMax, "the register path covers every row the LDS path does");
-static_assert(kRegSelThreads * 16 < 65536, "scan halves of 16 bits");
+static_assert(40 * kTopkRegsThreads >= kTopkLdsMax, "the register path covers every row the LDS path does");
+static_assert(kTopkRegsThreads * 40 < 65536 && kSliceMergeCap < 65536, "scan halves of 16 bits");
 
 // C for a row length: the merge holds nslices * C candidates in LDS.
 __host__ inline int cand_per_slice(int n_cap, int k) {
@@ -585,19 +586,20 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
-    const dim3 grid((unsigned)std::min<int64_t>(rows, std::max(cus, 1))), block(kRegSelThreads);
+    const dim3 grid((unsigned)std::min<int64_t>(rows, (int64_t)kTopkRegsPerCu * std::max(cus, 1))),
+        block(kTopkRegsThreads);
     const bool vec = (((uintptr_t)scores) & 15) == 0 && (n_cap & 3) == 0 && n_cap >= 4;
 #define CSA_TOPK_REGS(NPT)                                                                                       \
   if (vec)                                                                                                       \
     hipLaunchKernelGGL((topk_regs_kernel<NPT, true>), grid, block, 0, s, scores, q_pos, n_cap, m, k, rows, idx); \
   else                                                                                                           \
     hipLaunchKernelGGL((topk_regs_kernel<NPT, false>), grid, block, 0, s, scores, q_pos, n_cap, m, k, rows, idx);
-    if (n_cap <= 8 * kRegSelThreads) {
-      CSA_TOPK_REGS(8)
-    } else if (n_cap <= 16 * kRegSelThreads) {
+    if (n_cap <= 16 * kTopkRegsThreads) {
       CSA_TOPK_REGS(16)
+    } else if (n_cap <= 32 * kTopkRegsThreads) {
+      CSA_TOPK_REGS(32)
     } else {
-      CSA_TOPK_REGS(20)
+      CSA_TOPK_REGS(40)
     }
 #undef CSA_TOPK_REGS
     return hipGetLastError();
@@ -625,7 +627,7 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int
       ma.cand = cand;
       ma.meta = meta;
       ma.idx = idx;
-      hipLaunchKernelGGL(topk_merge_slices_kernel<0>, dim3((unsigned)rows), dim3(kRegSelThreads), 0, s, ma);
+      hipLaunchKernelGGL(topk_merge_slices_kernel<0>, dim3((unsigned)rows), dim3(kMergeThreads32), 0, s, ma);
       return hipGetLastError();
     }
   }
@@ -654,7 +656,7 @@ bool index_topk_fused_ok(const IndexArgs& a, int k) {
   // MXFP4 keys (the indexer that emits lists), long rows, and lists that fit the merge
   // pass (nslices * 64 slots in registers, one thread per slice for the certificate)
   const int ns = fused_slices(a.n_cap);
-  return a.k.dtype == CSA_MXFP4 && a.n_cap > kTopkLdsMax && ns <= kRegSelThreads &&
+  return a.k.dtype == CSA_MXFP4 && a.n_cap > kTopkLdsMax && ns <= kMergeMaxSlices &&
          (int64_t)ns * kFusedC <= kSliceMergeCap && k <= kSliceMergeCap;
 }
 
@@ -709,9 +711,9 @@ hipError_t launch_index_topk_merge(const IndexArgs& a, int k, int32_t* idx, void
   ma.short_rows = 1;
   ma.rescore = a;
   if (a.heads <= 8)
-    hipLaunchKernelGGL(topk_merge_slices_kernel<4>, dim3((unsigned)rows), dim3(kRegSelThreads), 0, s, ma);
+    hipLaunchKernelGGL(topk_merge_slices_kernel<4>, dim3((unsigned)rows), dim3(kMergeThreads32), 0, s, ma);
   else
-    hipLaunchKernelGGL(topk_merge_slices_kernel<16>, dim3((unsigned)rows), dim3(kRegSelThreads), 0, s, ma);
+    hipLaunchKernelGGL(topk_merge_slices_kernel<16>, dim3((unsigned)rows), dim3(kMergeThreads32), 0, s, ma);
   return hipGetLastError();
 }
 
