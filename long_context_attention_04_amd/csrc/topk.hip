@@ -594,10 +594,16 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int
     hipLaunchKernelGGL((topk_regs_kernel<NPT, true>), grid, block, 0, s, scores, q_pos, n_cap, m, k, rows, idx); \
   else                                                                                                           \
     hipLaunchKernelGGL((topk_regs_kernel<NPT, false>), grid, block, 0, s, scores, q_pos, n_cap, m, k, rows, idx);
+    // the fewest keys per thread (a multiple of 4) that hold the row: slots past the
+    // row still cost their share of every pass
     if (n_cap <= 16 * kTopkRegsThreads) {
       CSA_TOPK_REGS(16)
+    } else if (n_cap <= 24 * kTopkRegsThreads) {
+      CSA_TOPK_REGS(24)
     } else if (n_cap <= 32 * kTopkRegsThreads) {
       CSA_TOPK_REGS(32)
+    } else if (n_cap <= 36 * kTopkRegsThreads) {
+      CSA_TOPK_REGS(36)
     } else {
       CSA_TOPK_REGS(40)
     }

@@ -258,8 +258,8 @@ def test_index_scores(gpu_lib, B, Tq, HI, dI, N, kfmt):
     (1, 2, 12000, 700, "equal"), (1, 2, 20000, 1024, "tiny"), (2, 1, 9000, 300, "narrow"),
     (2, 2, 16896, 512, "partial"), (1, 1, 20480, 2048, "extreme"),
     (1, 2, 9000, 5000, "normal"),  # k > 4,096: the LDS kernel
-    # more rows than CUs: each register-path workgroup walks several rows, loading the next
-    # one during a selection; rows of 16-byte multiples and (777) of odd length
+    # more rows than resident register-path workgroups (two per CU): some walk two rows;
+    # rows of 16-byte multiples and (777) of odd length
     (2, 300, 9000, 300, "normal"), (1, 300, 777, 100, "ties"),
 ])
 def test_topk_exact(gpu_lib, B, Tq, N, k, mode):
