@@ -431,7 +431,9 @@ constexpr int kRegSelBins = 1024;     // histogram bins: kRegSelBins / THREADS p
 constexpr int kRegSelMaxWaves = kRegSelMaxThreads / kWave;
 
 struct RegSelLds {
-  __attribute__((aligned(16))) uint32_t hist[2][kRegSelBins];
+  // kRegSelBins bins, then one never-read bin per lane that absent keys of the first
+  // pass count into (so that pass adds with no per-key branch and no shared address)
+  __attribute__((aligned(16))) uint32_t hist[2][kRegSelBins + kWave];
   uint32_t red[3][kRegSelMaxWaves];   // per-wave min, max, count
   uint32_t scan[3][kRegSelMaxWaves];  // per-wave totals of block scans
   uint32_t bin, above, cnt, nfin, T, krem, jT, bad;
@@ -517,11 +519,17 @@ __device__ __forceinline__ void block_threshold_regs(const uint32_t (&kv)[NPT], 
   int buf = 0;
   // one pass: histogram of bins binf(j) (-1 = not counted) into rs.hist[buf], then the
   // bin holding the krem-th key from the top, the keys above it and its count
-  auto pass = [&](auto binf, uint32_t* bin, uint32_t* above, uint32_t* cn) {
+  // (every_key: binf(j) < 0 goes to this lane's own extra bin instead of being skipped;
+  // used by the first pass with kept bins, where few keys are absent)
+  auto pass = [&](auto binf, auto every_key, uint32_t* bin, uint32_t* above, uint32_t* cn) {
+    const int lane_bin = kRegSelBins + (int)(threadIdx.x % kWave);
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
       const int bj = binf(j);
-      if (bj >= 0) atomicAdd(&rs.hist[buf][bj], 1u);
+      if constexpr (decltype(every_key)::value)
+        atomicAdd(&rs.hist[buf][bj >= 0 ? bj : lane_bin], 1u);
+      else if (bj >= 0)
+        atomicAdd(&rs.hist[buf][bj], 1u);
     }
     __syncthreads();
     // thread t scans bins kRegSelBins - 1 - (BPT t + i), i = 0 .. BPT - 1 (descending)
@@ -558,7 +566,19 @@ __device__ __forceinline__ void block_threshold_regs(const uint32_t (&kv)[NPT], 
   // the first pass's bins: kept in registers (KEEP_BINS), or recomputed where needed by
   // kernels short of registers (the same expression, so the same bins)
   constexpr bool kKeepBins = KEEP_BINS;
-  auto vbin = [&](int j) { return kv[j] ? min(kRegSelBins - 1, max(0, (int)((key_float(kv[j]) - xlo) * inv))) : -1; };
+  // -1 for an absent key.  With the bins kept (registers to spare) this is arithmetic
+  // rather than a select, so the pass takes no branch per key: the clamp is then done in
+  // float, so that an absent key's NaN becomes 0 before the conversion (present keys lie
+  // in [lo, hi], at 0 .. 1023.99 before the clamp: the same bins as an integer clamp
+  // after the conversion)
+  auto vbin = [&](int j) {
+    if constexpr (KEEP_BINS) {
+      const float v = fminf(fmaxf((key_float(kv[j]) - xlo) * inv, 0.f), (float)(kRegSelBins - 1));
+      return (int)v | -(int)(kv[j] == 0u);
+    } else {
+      return kv[j] ? min(kRegSelBins - 1, max(0, (int)((key_float(kv[j]) - xlo) * inv))) : -1;
+    }
+  };
   int b[kKeepBins ? NPT : 1];
   auto first_bin = [&](int j) {
     if constexpr (kKeepBins)
@@ -573,7 +593,7 @@ __device__ __forceinline__ void block_threshold_regs(const uint32_t (&kv)[NPT], 
       for (int j = 0; j < NPT; ++j) b[j] = vbin(j);
     }
     uint32_t above, cn;
-    pass(first_bin, &fbin, &above, &cn);
+    pass(first_bin, std::integral_constant<bool, KEEP_BINS>{}, &fbin, &above, &cn);
     krem -= above;
     cn_last = cn;
     if (cn <= 64u || cn == krem) {
@@ -609,7 +629,8 @@ __device__ __forceinline__ void block_threshold_regs(const uint32_t (&kv)[NPT], 
     const int bits = 32 - __builtin_clz(hi - lo);
     const int shift = bits > 10 ? bits - 10 : 0;
     uint32_t bin, above, cn;
-    pass([&](int j) { return (kv[j] >= lo && kv[j] <= hi) ? (int)((kv[j] - lo) >> shift) : -1; }, &bin, &above, &cn);
+    pass([&](int j) { return (kv[j] >= lo && kv[j] <= hi) ? (int)((kv[j] - lo) >> shift) : -1; }, std::false_type{},
+         &bin, &above, &cn);
     const uint32_t nlo = lo + (bin << shift);
     hi = min(hi, nlo + ((1u << shift) - 1u));
     lo = nlo;
