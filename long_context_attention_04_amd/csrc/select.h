@@ -441,6 +441,27 @@ struct RegSelLds {
   __attribute__((aligned(16))) uint32_t fp[64];
 };
 
+// Combining one value per wave (at most 16 waves): lane i of every wave reads wave i's
+// value, then DPP steps inside the first 16-lane row do the rest (lanes 16.. unused).
+// Inclusive prefix sum over lanes 0 .. 15 (zeros shifted in).
+__device__ __forceinline__ uint32_t row16_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  return v;
+}
+// Minimum or maximum over lanes 0 .. 15, as a wave-uniform value.
+template <bool MAX>
+__device__ __forceinline__ uint32_t row16_reduce(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  return __builtin_amdgcn_readlane(v, 0);
+}
+
 // Inclusive prefix sum over a block of THREADS threads (one barrier; tmp is not
 // reused by the caller until after a later barrier).
 template <int THREADS>
@@ -450,15 +471,11 @@ __device__ __forceinline__ uint32_t block_scan_regsel(uint32_t v, uint32_t* tmp,
   const uint32_t incl = wave_incl_scan(v);
   if (L == kWave - 1) tmp[w] = incl;
   __syncthreads();
-  uint32_t base = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < THREADS / kWave; ++i) {
-    const uint32_t x = tmp[i];
-    base += i < w ? x : 0u;
-    tot += x;
-  }
-  *total = tot;
-  return incl + base;
+  constexpr int NW = THREADS / kWave;
+  const uint32_t wi = row16_incl_scan(L < NW ? tmp[L] : 0u);  // lane i < NW: waves 0 .. i
+  *total = __builtin_amdgcn_readlane(wi, NW - 1);
+  const uint32_t below = __builtin_amdgcn_readlane(wi, max(w, 1) - 1);  // waves 0 .. w-1 (for w > 0)
+  return incl + (w > 0 ? below : 0u);
 }
 
 // Min and max present key and the number of present keys of a block holding
@@ -486,16 +503,10 @@ __device__ __forceinline__ void block_key_range(const uint32_t (&kv)[NPT], RegSe
   for (int i = 0; i < kRegSelBins / THREADS; ++i) rs.hist[0][t + i * THREADS] = 0u;
   if (t == 0) rs.bad = 0u;
   __syncthreads();
-  mn = 0xffffffffu, mx = 0u, c = 0u;
-#pragma unroll
-  for (int i = 0; i < THREADS / kWave; ++i) {
-    mn = min(mn, rs.red[0][i]);
-    mx = max(mx, rs.red[1][i]);
-    c += rs.red[2][i];
-  }
-  *lo = mn;
-  *hi = mx;
-  *cnt = c;
+  constexpr int NW = THREADS / kWave;
+  *lo = row16_reduce<false>(L < NW ? rs.red[0][L] : 0xffffffffu);
+  *hi = row16_reduce<true>(L < NW ? rs.red[1][L] : 0u);
+  *cnt = __builtin_amdgcn_readlane(row16_incl_scan(L < NW ? rs.red[2][L] : 0u), 15);
 }
 
 // Exact threshold of the top-k of the keys a block of THREADS threads holds in
@@ -614,13 +625,8 @@ __device__ __forceinline__ void block_threshold_regs(const uint32_t (&kv)[NPT], 
         rs.red[1][w] = mx;
       }
       __syncthreads();
-      lo = 0xffffffffu;
-      hi = 0u;
-#pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        lo = min(lo, rs.red[0][i]);
-        hi = max(hi, rs.red[1][i]);
-      }
+      lo = row16_reduce<false>(L < NW ? rs.red[0][L] : 0xffffffffu);
+      hi = row16_reduce<true>(L < NW ? rs.red[1][L] : 0u);
     }
   }
   // key-space passes: 32 bits at <= 10 bits per pass end in a single key after 4
@@ -649,9 +655,7 @@ __device__ __forceinline__ void block_threshold_regs(const uint32_t (&kv)[NPT], 
     mn = wave_reduce_u32<false>(mn);
     if (L == 0) rs.red[0][w] = mn;
     __syncthreads();
-    T = 0xffffffffu;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) T = min(T, rs.red[0][i]);
+    T = row16_reduce<false>(L < NW ? rs.red[0][L] : 0xffffffffu);
     krem = 0xffffffffu;
   } else if (finish && (by_bin || lo != hi)) {
     // gather the <= 64 keys of the final bin with their slots, then rank them in one wave
