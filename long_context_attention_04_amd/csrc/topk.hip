@@ -370,20 +370,29 @@ __global__ __launch_bounds__(kMergeThreads32) void topk_merge_slices_kernel(Merg
       uint32_t r = (excl & 0xffffu) + min(eq_seen, krem);
       // the k indices go to LDS (rank order), unwanted stores to this thread's discard
       // slot, then out in one coalesced pass
-      uint32_t my_jT = 0;
-      bool has_t = false;
+      if (__builtin_amdgcn_ballot_w64(eqc != 0u) == 0ull) {  // no copy of T in this wave
 #pragma unroll
-      for (int j = 0; j < kMPerThread; ++j) {
-        const bool is_eq = kv[j] == T;
-        const bool keep = kv[j] > T || (is_eq && eq_seen < krem);
-        const bool last = is_eq && eq_seen == krem - 1u;  // the last copy of T taken
-        my_jT = last ? iv[j] : my_jT;
-        has_t = has_t || last;
-        eq_seen += is_eq;
-        ostage[keep && r < (uint32_t)k ? r : (uint32_t)kSliceMergeCap + t] = iv[j];
-        r += keep;
+        for (int j = 0; j < kMPerThread; ++j) {
+          const bool keep = kv[j] > T;
+          ostage[keep && r < (uint32_t)k ? r : (uint32_t)kSliceMergeCap + t] = iv[j];
+          r += keep;
+        }
+      } else {
+        uint32_t my_jT = 0;
+        bool has_t = false;
+#pragma unroll
+        for (int j = 0; j < kMPerThread; ++j) {
+          const bool is_eq = kv[j] == T;
+          const bool keep = kv[j] > T || (is_eq && eq_seen < krem);
+          const bool last = is_eq && eq_seen == krem - 1u;  // the last copy of T taken
+          my_jT = last ? iv[j] : my_jT;
+          has_t = has_t || last;
+          eq_seen += is_eq;
+          ostage[keep && r < (uint32_t)k ? r : (uint32_t)kSliceMergeCap + t] = iv[j];
+          r += keep;
+        }
+        if (has_t) rs.jT = my_jT;
       }
-      if (has_t) rs.jT = my_jT;
       __syncthreads();
       // exact unless some slice's (last_key, last_idx) is selected: such slices are
       // "bad" (waves 0-3 cover the <= 256 slices)
@@ -539,13 +548,22 @@ __global__ __launch_bounds__(kTopkRegsThreads, kTopkRegsPerCu * kTopkRegsThreads
       krem = min(krem, tot >> 16);  // "every copy" made a count
       uint32_t eq_seen = excl >> 16;
       uint32_t r = (excl & 0xffffu) + min(eq_seen, krem);
+      if (__builtin_amdgcn_ballot_w64(eqc != 0u) == 0ull) {  // no copy of T in this wave
 #pragma unroll
-      for (int j = 0; j < NPT; ++j) {
-        const bool is_eq = kv[j] == T;
-        const bool keep = kv[j] > T || (is_eq && eq_seen < krem);
-        eq_seen += is_eq;
-        ostage[keep && r < (uint32_t)k ? r : (uint32_t)kTopkRegsMaxK + t] = (uint32_t)(NPT * t + j);
-        r += keep;
+        for (int j = 0; j < NPT; ++j) {
+          const bool keep = kv[j] > T;
+          ostage[keep && r < (uint32_t)k ? r : (uint32_t)kTopkRegsMaxK + t] = (uint32_t)(NPT * t + j);
+          r += keep;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+          const bool is_eq = kv[j] == T;
+          const bool keep = kv[j] > T || (is_eq && eq_seen < krem);
+          eq_seen += is_eq;
+          ostage[keep && r < (uint32_t)k ? r : (uint32_t)kTopkRegsMaxK + t] = (uint32_t)(NPT * t + j);
+          r += keep;
+        }
       }
       __syncthreads();
       for (int i = t; i < k; i += TH) out[i] = (int32_t)ostage[i];
