@@ -408,12 +408,12 @@ __global__ __launch_bounds__(kMergeThreads32) void topk_merge_slices_kernel(Merg
       if (!full)
         for (int i = t; i < k; i += TH) out[i] = (int32_t)ostage[i];
     }
-    if constexpr (NR > 0) {
-      if (full && !ma.scores && nbad > 0 && nbad <= kMaxBadSlices) {
-        // Rescore only the bad slices (into LDS), then select over the union of the
-        // good slices' lists and every key of the bad slices.  Exact: a good slice's
-        // omitted keys rank after the candidates' k-th key, and the union's k-th key
-        // ranks at or before it.
+    // With at most kMaxBadSlices bad slices, select over the union of the good slices'
+    // lists and every key of the bad slices (read from the kept scores, or rescored into
+    // LDS).  Exact: a good slice's omitted keys rank after the candidates' k-th key, and
+    // the union's k-th key ranks at or before it.
+    if (full && nbad > 0 && nbad <= kMaxBadSlices && (ma.scores || NR > 0)) {
+      {
         if (t < nbad) {  // the t-th bad slice (ascending) and its start in the union
           int seen = 0, id = 0;
           for (int i = 0; i < kMergeMaxSlices / kWave; ++i) {
@@ -428,16 +428,26 @@ __global__ __launch_bounds__(kMergeThreads32) void topk_merge_slices_kernel(Merg
           badstart[t] = kSliceSlots * id + (kSlice32 - kSliceSlots) * t;
         }
         uint32_t* bkeys = ostage + kBadKeysOffset;
-        fp4_rescore_tiles<NR>(
-            ma.rescore, (int)row, V, *(Fp4QueryLds*)ostage, nbad * (kSlice32 / 32),
-            [&](int tile) { return kSlice32 * badlist[tile / (kSlice32 / 32)] + 32 * (tile % (kSlice32 / 32)); },
-            [&](int tile, int key, float sc, bool live) {
-              bkeys[(tile / (kSlice32 / 32)) * kSlice32 + key % kSlice32] = live ? float_key(sc) : 0u;
-            });
+        if (ma.scores) {
+          __syncthreads();  // the bad-slice list is visible; ostage is free
+          for (int i = t; i < nbad * kSlice32; i += TH) {
+            const int key = kSlice32 * badlist[i / kSlice32] + i % kSlice32;
+            bkeys[i] = key < V ? float_key(srow[key]) : 0u;
+          }
+          __syncthreads();
+        } else if constexpr (NR > 0) {
+          fp4_rescore_tiles<NR>(
+              ma.rescore, (int)row, V, *(Fp4QueryLds*)ostage, nbad * (kSlice32 / 32),
+              [&](int tile) { return kSlice32 * badlist[tile / (kSlice32 / 32)] + 32 * (tile % (kSlice32 / 32)); },
+              [&](int tile, int key, float sc, bool live) {
+                bkeys[(tile / (kSlice32 / 32)) * kSlice32 + key % kSlice32] = live ? float_key(sc) : 0u;
+              });
+        }
         sel_n = kSliceSlots * (ns - nbad) + kSlice32 * nbad;  // > k: it holds every candidate
-      } else if (full && !ma.scores) {  // the row's scores were not kept: recompute them all
-        fp4_rescore_row<NR>(ma.rescore, (int)row, V, *(Fp4QueryLds*)ostage, ma.row_scores + row * ma.n_cap);
       }
+    } else if constexpr (NR > 0) {
+      if (full && !ma.scores)  // the row's scores were not kept: recompute them all
+        fp4_rescore_row<NR>(ma.rescore, (int)row, V, *(Fp4QueryLds*)ostage, ma.row_scores + row * ma.n_cap);
     }
   }
   if (full) {  // select again, from the union above or from the whole row (any input)

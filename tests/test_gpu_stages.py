@@ -254,6 +254,7 @@ def test_index_scores(gpu_lib, B, Tq, HI, dI, N, kfmt):
     (4, 2, 65536, 2048, "partial"), (3, 1, 262144, 2048, "partial"),
     (1, 2, 70000, 1024, "extreme"), (2, 1, 262144, 2048, "extreme"), (1, 1, 16000, 512, "extreme"),
     (1, 2, 70000, 1024, "tiny"), (2, 1, 262144, 2048, "narrow"),
+    (2, 1, 262144, 2048, "hot2"), (1, 2, 70000, 1024, "hot2"), (1, 1, 262144, 2048, "hot12"),
     # rows of <= 20,480 keys with k <= 4,096: the register-resident kernel
     (1, 2, 12000, 700, "equal"), (1, 2, 20000, 1024, "tiny"), (2, 1, 9000, 300, "narrow"),
     (2, 2, 16896, 512, "partial"), (1, 1, 20480, 2048, "extreme"),
@@ -269,13 +270,13 @@ def test_topk_exact(gpu_lib, B, Tq, N, k, mode):
     if mode == "ties":
         s = r.integers(-20, 20, (B, Tq, N)).astype(np.float32)
         s[s == 0] = np.where(r.random(int((s == 0).sum())) < 0.5, -0.0, 0.0).astype(np.float32)
-    elif mode in ("cluster2", "cluster12"):
-        w = np.abs(w)
-        hot = (5, N // 4096) if mode == "cluster2" else tuple(3 + 5 * i for i in range(12))
-        qv = up(q[:, 0, 0])[:, None, :]
+    elif mode in ("hot2", "hot12"):
+        # 1024-key slices holding far more than their 32 listed keys of the row's top-k:
+        # two (each re-read in full from the scores) or twelve (the whole row reselected)
+        s = r.standard_normal((B, Tq, N)).astype(np.float32)
+        hot = (5, N // 4096) if mode == "hot2" else tuple(3 + 5 * i for i in range(12))
         for sl in hot:
-            noise = torch.randn((B, 1024, dI), generator=gen, device="cuda")
-            kraw[:, sl * 1024:(sl + 1) * 1024] = 3.0 * qv + 0.5 * noise
+            s[..., sl * 1024:(sl + 1) * 1024] += 3.0
     elif mode == "equal":
         s = np.zeros((B, Tq, N), np.float32)
     elif mode == "extreme":  # infinities and near-overflow magnitudes among normal scores
