@@ -259,9 +259,11 @@ size_t csa_topk_workspace_size(int32_t batch, int32_t tq, int32_t n_cap, int32_t
  * 20480, at most 262,144), each indexer workgroup also lists its 1024-block
  * slice's candidates as it scores them (every block at or above a cut of the
  * slice's scores), and one merge pass selects the row's top-k from the lists,
- * certified exact; rows the lists cannot decide (rows with few full slices, and
- * the rare rows whose certificate fails) are selected from their scores, which
- * are kept in the workspace or recomputed there when the caller keeps none.
+ * certified exact.  Rows with few full slices are selected from their scores,
+ * kept in the workspace.  The rare rows whose certificate fails are selected
+ * again: over the lists plus every score of the failing slices when at most 8
+ * fail, else over the whole row.  Those scores are the caller's when kept,
+ * otherwise recomputed with the indexer's arithmetic.
  * Other shapes run the two stages one after the other.
  * ------------------------------------------------------------------------- */
 csa_status csa_index_topk(const csa_tensor* q_idx, const float* w, const csa_tensor* k_idx, const int32_t* q_pos,
