@@ -10,22 +10,25 @@
 // fp32 score (-0 folded onto +0), with ties broken by index, followed by an
 // ascending-order compaction.  Integer histograms only, so results are exact
 // and do not depend on scheduling.
-//  * Rows of up to kTopkLdsMax keys: one workgroup per row.  For k <= 4096 the row is
-//    held in registers (20 keys per thread at most) and selected with value-linear then
-//    key-space histograms and one block scan; otherwise the row is resident in LDS,
-//    radix passes over the live key range, then a block-scan compaction.
-//  * Longer rows (1M-token decode: 262,144 blocks per row and only 8 rows):
-//    two kernels and no communication between workgroups of one kernel
-//    (on this chip a device-scope fence writes back / invalidates the XCD's
-//    L2 and returning atomics go to the memory-side unit, so "last workgroup"
-//    tricks cost far more than a kernel boundary).  Pass 1: every 4096-block
-//    slice of a row selects its own exact top-C in LDS (C = 128 for 64
-//    slices) and writes it in ascending index order together with its C-th
-//    element.  Pass 2: one workgroup per row selects the top-k of the ~8192
-//    candidates in LDS; candidate order is ascending index order, so the
-//    compaction needs no sort.  The result is exact whenever no truncated
-//    slice had its C-th kept element selected (then nothing it dropped can
-//    be selected); otherwise the workgroup selects from the whole row itself.
+//  * Rows of up to kTopkLdsMax keys.  For k <= 4096 the row is held in registers (16 to
+//    40 keys per thread, 512-thread workgroups, two resident per CU, each walking its
+//    rows) and selected with value-linear then key-space histograms and one block scan;
+//    otherwise one workgroup per row holds it in LDS: radix passes over the live key
+//    range, then a block-scan compaction.
+//  * Longer rows (the 1M-token decode: 262,144 blocks per row and only 8 rows): two
+//    passes and no communication between workgroups of one kernel (on this chip a
+//    device-scope fence writes back / invalidates the XCD's L2 and returning atomics
+//    go to the memory-side unit, so "last workgroup" tricks cost far more than a kernel
+//    boundary).  Pass 1: every 1024-block slice lists its exact top-32, in ascending
+//    index order, with its 32nd (key, index) (topk_cand32_kernel from stored scores, or
+//    the MXFP4 indexer itself as it scores).  Pass 2: one 1024-thread workgroup per row
+//    selects the top-k of the <= 8192 listed candidates in registers; slot order is
+//    index order, so the compaction needs no sort.  The result is certified exact
+//    whenever no slice had its 32nd listed entry selected (then nothing it left out can
+//    be); otherwise the row is selected again over the other lists plus every key of
+//    the failing slices (at most 8), or over the whole row.
+//  * Rows longer than 262,144 blocks: the same two passes with 4096-block slices listing
+//    up to 128 candidates each, merged in LDS (topk_cand_kernel, topk_merge_kernel).
 #include "common.h"
 #include "kernels.h"
 #include "index_fp4.h"
@@ -610,7 +613,7 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int batch, int
   const int64_t rows = (int64_t)batch * tq;
   if (rows == 0) return hipSuccess;
   if (n_cap <= kTopkLdsMax && k <= kTopkRegsMaxK) {
-    // one resident workgroup per CU, each walking its rows (the next row's loads in flight)
+    // two resident workgroups per CU, each walking rows w, w + grid, ...
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
