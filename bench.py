@@ -167,7 +167,7 @@ def stream_ceiling(torch) -> dict:
 
 def pmc_traffic():
     """HBM bytes per launch of the headline's dominant kernel from the committed rocprofv3 counter
-    summary, when it was taken from this build (else None)."""
+    summary, when it was taken from the kernel's current sources (its source hash matches; else None)."""
     if not os.path.exists(PMC_SUMMARY):
         return None
     vals = {}
